@@ -1,0 +1,266 @@
+"""fp64 NumPy oracle: block-wise multi-constraint pruning of one linear layer.
+
+TEST INFRASTRUCTURE ONLY: used by the tests, the smoke check and the benchmark's
+CPU-baseline leg. The product library never imports it, and it imports nothing
+from the product library.
+
+Sources (titles of the pages and their sections):
+
+* "Pruning LLMs with Thanos" (project blog post) -- sections "The
+  layer-reconstruction lens", "Why magnitude alone misses important weights",
+  "One deletion with compensation: the OBS view", "Contribution one: solve a
+  selected set directly", "Contribution two: keep the budget global and the
+  execution local", "Making irregular row masks batchable".
+* "Weight Pruning in Large Language Models: How SparseGPT, Wanda, and
+  Semi-Structured 2:4 Sparsity ..." (explainer) -- section "SparseGPT:
+  Second-Order Reconstruction at Scale" for the damped Hessian H = 2XX^T + lambda*I
+  and the reconstruction objective; section "Wanda: Pruning by Weights and
+  Activations" for the |W|*||X_q|| score; section "N:M Semi-Structured Sparsity
+  (2:4 Pattern)" for the group constraint.
+
+Every value here is fp64. Inputs are decoded exactly from bf16 or fp32. The
+route deliberately differs from the GPU's: the inverse Hessian comes from an LU
+inverse followed by Schur-complement downdates, row systems are LU solves, and
+the global selection uses a partition plus an explicit tie list.
+
+Readings where the pages are silent (each is also listed in the design notes):
+
+* the factor 2 in H (the blog post's Gram form vs the explainer's 2XX^T): H = 2G + lambda*I;
+* lambda = lambda_rel * mean(diag(2G)) with lambda_rel = 0.01 when relative;
+* score S_kq = W_kq^2 * g_q with g_q = 1/[(H_F)^-1]_qq (OBS, default) or
+  g_q = G_qq (Wanda), F being the active (not yet frozen) columns;
+* k_total = round-half-even(p * c * b);
+* ties are broken by the flat index k*b + q (unstructured) or by q (N:M):
+  the lower index is pruned first;
+* N:M groups are aligned to multiples of M along a row; M-N entries are pruned
+  per group; masks are chosen for every group of the block at block start;
+* pruned coordinates are set to exactly 0.0 after the update.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "NotSPDError", "gram", "damping", "hessian", "k_total", "obs_scores",
+    "select_unstructured", "select_nm", "solve_rows", "schur_downdate",
+    "prune_layer", "reconstruction_error",
+]
+
+
+class NotSPDError(ValueError):
+    """The damped Hessian is not symmetric positive definite."""
+
+
+def _f64(a) -> np.ndarray:
+    """Exact fp64 copy of a NumPy array or a (CPU) torch tensor of bf16/fp32."""
+    if hasattr(a, "detach"):
+        t = a.detach().cpu()
+        if str(t.dtype) == "torch.bfloat16":
+            t = t.float()
+        return t.double().numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
+def gram(X_tok, chunk: int = 8192) -> np.ndarray:
+    """G = X X^T for X (b x n) given token-major as X^T [n, b].
+
+    "Pruning LLMs with Thanos", section "One deletion with compensation: the OBS
+    view": G is the activation Gram matrix. Accumulated over token chunks in fp64.
+    """
+    n, b = X_tok.shape
+    G = np.zeros((b, b), dtype=np.float64)
+    for t0 in range(0, n, chunk):
+        Xc = _f64(X_tok[t0:t0 + chunk])
+        G += Xc.T @ Xc
+    return G
+
+
+def damping(G: np.ndarray, lam: float = 0.01, relative: bool = True) -> float:
+    """lambda = lam * mean(diag(2G)) if relative, else lam (absolute)."""
+    if relative:
+        return float(lam) * float(np.mean(np.diag(2.0 * G)))
+    return float(lam)
+
+
+def hessian(G: np.ndarray, lam_abs: float) -> np.ndarray:
+    """H = 2G + lambda*I (explainer, section "SparseGPT: Second-Order Reconstruction at Scale")."""
+    return 2.0 * G + lam_abs * np.eye(G.shape[0])
+
+
+def k_total(sparsity: float, c: int, b: int) -> int:
+    """Number of weights the layer must lose: round-half-even(p*c*b)."""
+    return int(np.round(np.float64(sparsity) * c * b))
+
+
+def obs_scores(Wc_F: np.ndarray, A_F: np.ndarray) -> np.ndarray:
+    """OBS cost w_q^2 / [A_F]_qq for every (row, active column).
+
+    "Pruning LLMs with Thanos", section "One deletion with compensation: the OBS
+    view": deleting w_q with the other active weights free to move raises the
+    objective in proportion to w_q^2 / [H^-1]_qq; with frozen columns the inverse
+    is that of the active block, A_F = (H_F)^-1.
+    """
+    return Wc_F ** 2 / np.diag(A_F)[None, :]
+
+
+def select_unstructured(S_F: np.ndarray, r: int, blk: int) -> np.ndarray:
+    """Candidates = the r lowest (score, flat index) keys of the active region;
+    return their intersection with the current block (the first ``blk`` columns).
+
+    "Pruning LLMs with Thanos", section "Contribution two: keep the budget global
+    and the execution local" (steps 2-4 of the dynamic residual budget). S_F is
+    c x |F| with F starting at the block; row-major order over (k, q) is the
+    flat-index order k*b + q, which breaks ties.
+    """
+    c, f = S_F.shape
+    sel = np.zeros((c, f), dtype=bool)
+    if r <= 0:
+        return sel[:, :blk]
+    if r >= c * f:
+        sel[:] = True
+        return sel[:, :blk]
+    flat = S_F.ravel()
+    T = np.partition(flat, r - 1)[r - 1]
+    below = flat < T
+    need = r - int(below.sum())
+    eq = np.flatnonzero(flat == T)
+    chosen = below.copy()
+    chosen[eq[:need]] = True
+    return chosen.reshape(c, f)[:, :blk]
+
+
+def select_nm(S_J: np.ndarray, n: int, m: int) -> np.ndarray:
+    """In every aligned group of m columns, prune the m-n lowest (score, column).
+
+    "Pruning LLMs with Thanos", section "The compression target: linear layers"
+    (each group of M keeps exactly N nonzeros) and the explainer's section "N:M
+    Semi-Structured Sparsity (2:4 Pattern)" (groups are contiguous along a row).
+    A stable sort puts the lower column first among equal scores.
+    """
+    c, blk = S_J.shape
+    assert blk % m == 0
+    g = S_J.reshape(c, blk // m, m)
+    order = np.argsort(g, axis=2, kind="stable")
+    sel = np.zeros_like(g, dtype=bool)
+    np.put_along_axis(sel, order[:, :, : m - n], True, axis=2)
+    return sel.reshape(c, blk)
+
+
+def solve_rows(W_J: np.ndarray, A_JJ: np.ndarray, sel: np.ndarray) -> np.ndarray:
+    """Per-row multipliers z with z_Q = u R^-1 (R = [A_F]_{Q,Q}), zero elsewhere.
+
+    "Pruning LLMs with Thanos", section "Contribution one: solve a selected set
+    directly": u collects the selected weights' current values, R-hat is the
+    s x s principal submatrix of the inverse Hessian on the selected set, and the
+    row update is delta = -u R-hat^-1 R with R = [A_F]_{Q,:}. Here the update is
+    returned as the coefficient row z (so delta = -z [A_F]_{J,:}). Each row is an
+    independent LU solve at its true size (rows with equal s are stacked into one
+    batched library call).
+    """
+    c, blk = W_J.shape
+    Z = np.zeros((c, blk), dtype=np.float64)
+    s = sel.sum(axis=1)
+    for sv in np.unique(s):
+        if sv == 0:
+            continue
+        rows = np.flatnonzero(s == sv)
+        Q = np.nonzero(sel[rows])[1].reshape(len(rows), sv)  # ascending per row
+        u = np.take_along_axis(W_J[rows], Q, axis=1)
+        Rh = A_JJ[Q[:, :, None], Q[:, None, :]]
+        z = np.linalg.solve(Rh, u[:, :, None])[:, :, 0]
+        Zr = np.zeros((len(rows), blk))
+        np.put_along_axis(Zr, Q, z, axis=1)
+        Z[rows] = Zr
+    return Z
+
+
+def schur_downdate(A_F: np.ndarray, blk: int) -> np.ndarray:
+    """(H_{F'})^-1 from (H_F)^-1 after freezing the first ``blk`` columns of F.
+
+    Block-inverse identity: inv(H_{F'F'}) = A_{F'F'} - A_{F'J} A_{JJ}^-1 A_{JF'}.
+    """
+    AJJ = A_F[:blk, :blk]
+    AJF = A_F[:blk, blk:]
+    return A_F[blk:, blk:] - A_F[blk:, :blk] @ np.linalg.solve(AJJ, AJF)
+
+
+def prune_layer(W, G: np.ndarray, sparsity: float = 0.5, pattern=None, block: int = 128,
+                lam: float = 0.01, lam_relative: bool = True, score: str = "obs") -> dict:
+    """Block-wise pruning with joint compensation (the layer step of the method).
+
+    pattern: None for unstructured with the dynamic global budget, or (n, m).
+    Returns W_hat (fp64), mask (True = pruned), per-block prune counts, lambda.
+
+    Procedure ("Pruning LLMs with Thanos", sections "The scaling problem, and what
+    SparseGPT changes" (left-to-right blocks, finished columns frozen, updates only
+    into active columns), "Contribution one" (joint solve) and "Contribution two"
+    (dynamic residual budget); N:M keeps the joint solve but uses local group masks):
+
+      H = 2G + lambda*I; A = H^-1 (LU); for each block J = [j0, j0+B) of F = [j0, b):
+        scores over F (unstructured) or J (N:M) from the current weights;
+        unstructured: r = k_total - pruned; candidates = r lowest keys; Q = candidates within J;
+        N:M: per group of m, the m-n lowest;
+        per row: z = u R^-1; W[k,F] -= z A_F[Q,F]; W[k,Q] = 0;
+        pruned += |Q|; A <- inv(H_{F \\ J}) by a Schur downdate.
+    """
+    W0 = _f64(W)
+    G = np.asarray(G, dtype=np.float64)
+    c, b = W0.shape
+    if block < 1:
+        raise ValueError("block must be >= 1")
+    if pattern is not None:
+        n_keep, m = pattern
+        if not (0 <= n_keep <= m) or block % m or b % m:
+            raise ValueError("N:M needs 0<=n<=m, m | block and m | b")
+    lam_abs = damping(G, lam, lam_relative)
+    H = hessian(G, lam_abs)
+    try:
+        np.linalg.cholesky(H)
+    except np.linalg.LinAlgError as exc:
+        raise NotSPDError("damped Hessian is not positive definite") from exc
+    A = np.linalg.inv(H)
+    Wc = W0.copy()
+    mask = np.zeros((c, b), dtype=bool)
+    counts = []
+    ktot = k_total(sparsity, c, b) if pattern is None else None
+    pruned = 0
+    diagG = np.diag(G)
+    for j0 in range(0, b, block):
+        blk = min(block, b - j0)
+        if score == "obs":
+            g = 1.0 / np.diag(A)
+        elif score == "wanda":
+            g = diagG[j0:]
+        else:
+            raise ValueError(score)
+        if pattern is None:
+            S = Wc[:, j0:] ** 2 * g[None, :]
+            sel = select_unstructured(S, ktot - pruned, blk)
+        else:
+            S = Wc[:, j0:j0 + blk] ** 2 * g[None, :blk]
+            sel = select_nm(S, pattern[0], pattern[1])
+        Z = solve_rows(Wc[:, j0:j0 + blk], A[:blk, :blk], sel)
+        Wc[:, j0:] -= Z @ A[:blk, :]
+        blockW = Wc[:, j0:j0 + blk]
+        blockW[sel] = 0.0
+        mask[:, j0:j0 + blk] = sel
+        cnt = int(sel.sum())
+        counts.append(cnt)
+        pruned += cnt
+        if j0 + blk < b:
+            A = schur_downdate(A, blk)
+    return {"W_hat": Wc, "mask": mask, "counts": counts, "lam": lam_abs,
+            "k_total": ktot, "pruned": pruned}
+
+
+def reconstruction_error(W, W_hat, G: np.ndarray):
+    """E = ||(W - W_hat) X||_F^2 = sum_k D_k G D_k^T, and E / ||W X||_F^2.
+
+    "Pruning LLMs with Thanos", section "The layer-reconstruction lens": the
+    objective is the Frobenius norm of the output change and decomposes over rows.
+    """
+    W0 = _f64(W)
+    D = W0 - _f64(W_hat)
+    E = float(np.sum((D @ G) * D))
+    base = float(np.sum((W0 @ G) * W0))
+    return E, (E / base if base > 0 else 0.0)
