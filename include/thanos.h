@@ -1,0 +1,189 @@
+/*
+ * thanos.h -- C ABI of libthanos: block-wise multi-constraint pruning of one
+ * linear layer (Thanos-style) on AMD Instinct MI355X (gfx950).
+ *
+ * Method sources (page titles and sections):
+ *   [BLOG]  "Pruning LLMs with Thanos" (project blog post):
+ *           "The layer-reconstruction lens" (objective ||WX - What X||_F^2,
+ *           decomposition over rows), "One deletion with compensation: the OBS
+ *           view" (damped Hessian, OBS update and cost), "Contribution one: solve
+ *           a selected set directly" (joint update delta = -u Rhat^-1 R),
+ *           "Contribution two: keep the budget global and the execution local"
+ *           (dynamic residual budget), "Making irregular row masks batchable".
+ *   [EXPL]  "Weight Pruning in Large Language Models: How SparseGPT, Wanda, and
+ *           Semi-Structured 2:4 Sparsity ..." (explainer): "SparseGPT:
+ *           Second-Order Reconstruction at Scale" (H = 2XX^T + lambda*I, one
+ *           Cholesky of H^-1 per layer), "Wanda: Pruning by Weights and
+ *           Activations", "N:M Semi-Structured Sparsity (2:4 Pattern)".
+ *   [REPO]  "Thanos - Method of Pruning LLMs" (repository README), "Usage":
+ *           --sparsity_ratio and --sparsity_type {unstructured, 2:4, 4:8}.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless the comment says "host".
+ *   - Matrices are row-major. W is c x b (row = output channel, contiguous over
+ *     the b inputs). X is b x n with tokens as columns; it is passed token-major
+ *     as X^T [n, b] (the same bytes as column-major X), row pitch ldx elements.
+ *   - The caller owns every buffer, including the workspace. The library never
+ *     allocates device memory.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ *     Entry points that return host values or a status that depends on device
+ *     results synchronise that stream before returning.
+ *   - Argument errors are reported before anything is launched. No C++
+ *     exception crosses this interface. th_last_error() gives a message for the
+ *     last non-OK status of the calling thread.
+ *   - Calls that share a workspace or output buffers must not overlap.
+ */
+#ifndef THANOS_H_
+#define THANOS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t* th_stream_t; /* identical to hipStream_t */
+
+typedef enum {
+  TH_OK = 0,
+  TH_ERR_INVALID_ARG = 1, /* bad size, null pointer, unsupported combination */
+  TH_ERR_NOT_SPD = 2,     /* the damped Hessian has a non-positive pivot */
+  TH_ERR_NONFINITE = 3,   /* NaN/Inf in W or in the Hessian's diagonal */
+  TH_ERR_WORKSPACE = 4,   /* workspace smaller than the size query returned */
+  TH_ERR_HIP = 5          /* a HIP runtime call failed */
+} th_status;
+
+typedef enum { TH_F32 = 0, TH_BF16 = 1 } th_dtype;
+typedef enum { TH_UNSTRUCTURED = 0, TH_NM = 1 } th_pattern_kind;
+typedef enum { TH_SCORE_OBS = 0, TH_SCORE_WANDA = 1 } th_score;
+
+typedef struct {
+  int32_t kind; /* th_pattern_kind */
+  int32_t n;    /* N:M: keep n of every m consecutive weights of a row */
+  int32_t m;
+} th_pattern;
+
+typedef struct {
+  /* Unstructured: fraction p in [0,1]; the layer loses
+   * k_total = round-half-even(p*c*b) weights in total [BLOG, "Contribution two"].
+   * N:M: ignored (the pattern fixes 1 - n/m), as with [REPO]'s --sparsity_ratio. */
+  double sparsity;
+  th_pattern pattern;
+  /* Column block size B, 1 <= B <= 128. Blocks run left to right; finished
+   * blocks are frozen [BLOG, "The scaling problem, and what SparseGPT changes"].
+   * N:M needs m | B and m | b. */
+  int64_t block;
+  /* Damping: absolute lambda if lambda_is_relative == 0, else
+   * lambda = lambda * mean(diag(2G)) (typical: 0.01, relative). */
+  double lambda;
+  int32_t lambda_is_relative;
+  /* Score g_q in S_kq = W_kq^2 g_q: OBS g_q = 1/[(H_F)^-1]_qq over the active
+   * columns F [BLOG, "One deletion with compensation"]; Wanda g_q = G_qq
+   * ([EXPL, "Wanda"]; same ordering as |W| ||X_q||). */
+  int32_t score;
+} th_prune_params;
+
+typedef struct {
+  double lambda_used;    /* absolute damping that was applied (or derived, see below) */
+  int64_t total_pruned;  /* number of weights set to zero */
+  int64_t nblocks;       /* number of column blocks */
+} th_stats;
+
+/* H += 2 * X_chunk^T X_chunk on the lower triangle (entries with row >= column).
+ * [EXPL, "SparseGPT: Second-Order Reconstruction at Scale"]: H = 2XX^T (+ lambda I
+ * later). X_chunk: [t, b] token-major, dtype xdt (TH_BF16: products are exact in
+ * fp32 and accumulate in fp32 on the matrix cores; TH_F32: fp32 FMA). ldx >= b
+ * and, for TH_BF16, ldx % 8 == 0 and a 16-byte aligned X. H: b x b fp32, zeroed by
+ * the caller before the first chunk; the strict upper triangle is not touched.
+ * workspace (optional, may be NULL with workspace_bytes 0) lets small b split the
+ * token range over more workgroups; size from th_hessian_workspace_size. The
+ * summation order is fixed, so repeated calls give bit-identical H. Asynchronous. */
+th_status th_hessian_accumulate(float* H, const void* X_chunk, th_dtype xdt, int64_t t,
+                                int64_t b, int64_t ldx, void* workspace,
+                                size_t workspace_bytes, th_stream_t stream);
+th_status th_hessian_workspace_size(int64_t t, int64_t b, size_t* bytes /* host */);
+
+/* Damping and symmetrisation of an accumulated H (= 2G on the lower triangle):
+ * lambda = lambda_rel * mean(diag(H)) if lambda_is_relative else lambda;
+ * H_qq += lambda; the upper triangle is overwritten by the mirror of the lower
+ * [BLOG, "One deletion with compensation"]. *lambda_out (host, optional) gets the
+ * absolute lambda. Synchronises the stream. */
+th_status th_hessian_finalize(float* H, int64_t b, double lambda, int32_t lambda_is_relative,
+                              double* lambda_out, th_stream_t stream);
+
+/* Prune one layer [BLOG, "Contribution one" and "Contribution two"; N:M masks per
+ * "The semi-structured N:M variant" paragraph of "Contribution two"].
+ *   W [c,b] dtype wdt (TH_BF16 or TH_F32): read, then overwritten with What
+ *     rounded to wdt (round-to-nearest-even for bf16).
+ *   Exactly one of X / H is non-NULL:
+ *     X [n,b] token-major (ldx = b), dtype xdt: H = 2XX^T + lambda*I is built
+ *       inside (p->lambda, p->lambda_is_relative);
+ *     H [b,b] fp32, full symmetric and already damped. If p->score is Wanda,
+ *       G_qq is taken as (H_qq - lambda)/2 with lambda = p->lambda (absolute) or
+ *       lambda_rel/(1+lambda_rel) * mean(diag H) (relative; exact for an H that
+ *       th_hessian_finalize produced with the same lambda_rel).
+ *   W_out_f32 [c,b] fp32 (optional): What in fp32.
+ *   mask_out [c,b] uint8 (optional): 1 = pruned.
+ *   workspace: >= th_prune_layer_workspace_size bytes, 256-byte aligned.
+ *   stats_out (host, optional); block_counts (host, optional, nblocks entries):
+ *     weights pruned in each block.
+ * Returns TH_ERR_NOT_SPD if the Cholesky factorisation of the damped Hessian
+ * meets a non-positive pivot, TH_ERR_NONFINITE for NaN/Inf in W or diag(H).
+ * Synchronises the stream once, at the end. */
+th_status th_prune_layer(void* W, th_dtype wdt, int64_t c, int64_t b, const void* X,
+                         th_dtype xdt, int64_t n, const float* H, const th_prune_params* p,
+                         float* W_out_f32, uint8_t* mask_out, void* workspace,
+                         size_t workspace_bytes, th_stats* stats_out,
+                         int64_t* block_counts, th_stream_t stream);
+th_status th_prune_layer_workspace_size(int64_t c, int64_t b, int64_t n, int32_t have_x,
+                                        const th_prune_params* p, size_t* bytes /* host */);
+
+/* E = ||(W - What) X||_F^2 = sum_k D_k G D_k^T and E / ||W X||_F^2
+ * [BLOG, "The layer-reconstruction lens"]. W and What: [c,b] dtype wdt. Exactly
+ * one of X ([n,b] token-major, dtype xdt) or G ([b,b] fp32, full symmetric,
+ * undamped XX^T) is non-NULL. Products on the fp32 matrix cores, sums in fp64.
+ * err_out, rel_err_out: host. Synchronises the stream. */
+th_status th_reconstruction_error(const void* W, const void* What, th_dtype wdt, int64_t c,
+                                  int64_t b, const void* X, th_dtype xdt, int64_t n,
+                                  const float* G, void* workspace, size_t workspace_bytes,
+                                  double* err_out, double* rel_err_out, th_stream_t stream);
+th_status th_reconstruction_error_workspace_size(int64_t c, int64_t b, int32_t have_x,
+                                                 size_t* bytes /* host */);
+
+/* ---- Entry points for parity tests: one step of the path on given inputs ---- */
+
+/* N:M selection on given scores [c, blk] fp32: in every aligned group of m
+ * columns, mark the m-n lowest (score, column) pairs (ties: lower column first)
+ * [BLOG, "The compression target: linear layers"; EXPL, "N:M ..."].
+ * mask_blk [c, blk] uint8, 1 = pruned. Asynchronous. */
+th_status th_debug_select_nm(const float* scores, int64_t c, int64_t blk, int32_t n, int32_t m,
+                             uint8_t* mask_blk, th_stream_t stream);
+
+/* Global residual-budget selection on given scores [c, f] fp32 (f = b_full - j0
+ * active columns, row pitch f): the r lowest keys (score, k*b_full + j0 + q)
+ * form the candidate set; mask_blk [c, blk] (uint8, row pitch blk) gets the
+ * candidates in the first blk columns, s_k [c] (int32, optional) their count per
+ * row [BLOG, "Contribution two"]. workspace: >= 64 KiB. Synchronises. */
+th_status th_debug_select_global(const float* scores, int64_t c, int64_t f, int64_t b_full,
+                                 int64_t j0, int64_t blk, int64_t r, uint8_t* mask_blk,
+                                 int32_t* s_k, void* workspace, size_t workspace_bytes,
+                                 th_stream_t stream);
+
+/* U = upper-triangular factor with H^-1 = U^T U (U = chol_upper(H^-1), the factor
+ * [EXPL, "SparseGPT"] computes once per layer), from a damped, full symmetric H
+ * [b,b] fp32. U [b,b] fp32 (strict lower triangle zero). workspace: >= 2*b*b*4 +
+ * b*128*4 + 4096 bytes. Returns TH_ERR_NOT_SPD on a non-positive pivot.
+ * Synchronises. */
+th_status th_debug_factor(const float* H, int64_t b, float* U, void* workspace,
+                          size_t workspace_bytes, th_stream_t stream);
+
+/* Message for the last non-OK status on this thread (never NULL). */
+const char* th_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* THANOS_H_ */

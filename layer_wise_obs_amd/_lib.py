@@ -1,0 +1,243 @@
+"""ctypes binding of libthanos (include/thanos.h): argument marshalling only.
+
+Every step of the pruning path runs in the HIP library. Tensors provide device
+memory and the current stream; nothing here computes on the CPU. If the library
+has not been built, loading raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libthanos.so")
+
+TH_OK, TH_ERR_INVALID_ARG, TH_ERR_NOT_SPD, TH_ERR_NONFINITE, TH_ERR_WORKSPACE, TH_ERR_HIP = range(6)
+TH_F32, TH_BF16 = 0, 1
+TH_UNSTRUCTURED, TH_NM = 0, 1
+TH_SCORE_OBS, TH_SCORE_WANDA = 0, 1
+STATUS_NAMES = {0: "TH_OK", 1: "TH_ERR_INVALID_ARG", 2: "TH_ERR_NOT_SPD", 3: "TH_ERR_NONFINITE",
+                4: "TH_ERR_WORKSPACE", 5: "TH_ERR_HIP"}
+
+
+class ThanosError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class Pattern(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("n", ctypes.c_int32), ("m", ctypes.c_int32)]
+
+
+class PruneParams(ctypes.Structure):
+    _fields_ = [("sparsity", ctypes.c_double), ("pattern", Pattern), ("block", ctypes.c_int64),
+                ("lam", ctypes.c_double), ("lambda_is_relative", ctypes.c_int32),
+                ("score", ctypes.c_int32)]
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [("lambda_used", ctypes.c_double), ("total_pruned", ctypes.c_int64),
+                ("nblocks", ctypes.c_int64)]
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_SIG = {
+    "th_hessian_accumulate": [_P, _P, _I32, _I64, _I64, _I64, _P, ctypes.c_size_t, _P],
+    "th_hessian_workspace_size": [_I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
+    "th_hessian_finalize": [_P, _I64, ctypes.c_double, _I32, ctypes.POINTER(ctypes.c_double), _P],
+    "th_prune_layer": [_P, _I32, _I64, _I64, _P, _I32, _I64, _P, ctypes.POINTER(PruneParams), _P,
+                       _P, _P, ctypes.c_size_t, ctypes.POINTER(Stats), ctypes.POINTER(_I64), _P],
+    "th_prune_layer_workspace_size": [_I64, _I64, _I64, _I32, ctypes.POINTER(PruneParams),
+                                      ctypes.POINTER(ctypes.c_size_t)],
+    "th_reconstruction_error": [_P, _P, _I32, _I64, _I64, _P, _I32, _I64, _P, _P, ctypes.c_size_t,
+                                ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                                _P],
+    "th_reconstruction_error_workspace_size": [_I64, _I64, _I32, ctypes.POINTER(ctypes.c_size_t)],
+    "th_debug_select_nm": [_P, _I64, _I64, _I32, _I32, _P, _P],
+    "th_debug_select_global": [_P, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P,
+                               ctypes.c_size_t, _P],
+    "th_debug_factor": [_P, _I64, _P, _P, ctypes.c_size_t, _P],
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libthanos.so from the package directory (raises if it is missing)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m layer_wise_obs_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIG.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.th_last_error.argtypes = []
+        L.th_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != TH_OK:
+        raise ThanosError(status, lib().th_last_error().decode())
+
+
+# ------------------------------------------------------------------ helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return TH_BF16
+    if t.dtype == torch.float32:
+        return TH_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(device=None):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def make_params(sparsity=0.5, pattern=None, block=128, lam=0.01, relative=True,
+                score="obs") -> PruneParams:
+    p = PruneParams()
+    p.sparsity = float(sparsity)
+    if pattern is None:
+        p.pattern = Pattern(TH_UNSTRUCTURED, 0, 0)
+    else:
+        p.pattern = Pattern(TH_NM, int(pattern[0]), int(pattern[1]))
+    p.block = int(block)
+    p.lam = float(lam)
+    p.lambda_is_relative = 1 if relative else 0
+    p.score = {"obs": TH_SCORE_OBS, "wanda": TH_SCORE_WANDA}[score]
+    return p
+
+
+def workspace(nbytes: int, device):
+    torch = _torch()
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------- entry points
+
+def hessian_workspace_size(t: int, b: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().th_hessian_workspace_size(t, b, ctypes.byref(out)))
+    return out.value
+
+
+def hessian_accumulate(H, X, ws=None):
+    """H (b x b fp32, lower) += 2 X^T X for token-major X [t, b]."""
+    _require_cuda(H, X)
+    t, b = X.shape
+    _check(lib().th_hessian_accumulate(_ptr(H), _ptr(X), _dtype_code(X), t, b, X.stride(0),
+                                       _ptr(ws), 0 if ws is None else ws.numel(),
+                                       _stream(X.device)))
+
+
+def hessian_finalize(H, lam=0.01, relative=True) -> float:
+    _require_cuda(H)
+    out = ctypes.c_double(0.0)
+    _check(lib().th_hessian_finalize(_ptr(H), H.shape[0], float(lam), 1 if relative else 0,
+                                     ctypes.byref(out), _stream(H.device)))
+    return out.value
+
+
+def prune_layer_workspace_size(c, b, n, have_x, params: PruneParams) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().th_prune_layer_workspace_size(c, b, n, 1 if have_x else 0, ctypes.byref(params),
+                                               ctypes.byref(out)))
+    return out.value
+
+
+def prune_layer(W, X=None, H=None, params: PruneParams | None = None, W_out=None, mask_out=None,
+                ws=None) -> dict:
+    """Prune W (c x b, bf16/fp32) in place; returns stats and per-block counts."""
+    _require_cuda(W, X, H, W_out, mask_out)
+    if params is None:
+        params = make_params()
+    c, b = W.shape
+    n = X.shape[0] if X is not None else 0
+    if ws is None:
+        ws = workspace(prune_layer_workspace_size(c, b, n, X is not None, params), W.device)
+    stats = Stats()
+    nblk = -(-b // params.block)
+    counts = (_I64 * nblk)()
+    _check(lib().th_prune_layer(_ptr(W), _dtype_code(W), c, b, _ptr(X),
+                                _dtype_code(X) if X is not None else 0, n, _ptr(H),
+                                ctypes.byref(params), _ptr(W_out), _ptr(mask_out), _ptr(ws),
+                                ws.numel(), ctypes.byref(stats), counts, _stream(W.device)))
+    return {"lambda": stats.lambda_used, "pruned": stats.total_pruned, "nblocks": stats.nblocks,
+            "counts": list(counts)}
+
+
+def reconstruction_error(W, W_hat, X=None, G=None, ws=None):
+    _require_cuda(W, W_hat, X, G)
+    c, b = W.shape
+    if ws is None:
+        out = ctypes.c_size_t(0)
+        _check(lib().th_reconstruction_error_workspace_size(c, b, 1 if X is not None else 0,
+                                                            ctypes.byref(out)))
+        ws = workspace(out.value, W.device)
+    e = ctypes.c_double(0.0)
+    r = ctypes.c_double(0.0)
+    _check(lib().th_reconstruction_error(_ptr(W), _ptr(W_hat), _dtype_code(W), c, b, _ptr(X),
+                                         _dtype_code(X) if X is not None else 0,
+                                         X.shape[0] if X is not None else 0, _ptr(G), _ptr(ws),
+                                         ws.numel(), ctypes.byref(e), ctypes.byref(r),
+                                         _stream(W.device)))
+    return e.value, r.value
+
+
+def debug_select_nm(scores, n: int, m: int):
+    torch = _torch()
+    _require_cuda(scores)
+    c, blk = scores.shape
+    mask = torch.empty((c, blk), dtype=torch.uint8, device=scores.device)
+    _check(lib().th_debug_select_nm(_ptr(scores), c, blk, n, m, _ptr(mask), _stream(scores.device)))
+    return mask
+
+
+def debug_select_global(scores, b_full: int, j0: int, blk: int, r: int):
+    torch = _torch()
+    _require_cuda(scores)
+    c, f = scores.shape
+    mask = torch.empty((c, blk), dtype=torch.uint8, device=scores.device)
+    s_k = torch.empty((c,), dtype=torch.int32, device=scores.device)
+    ws = workspace(1 << 16, scores.device)
+    _check(lib().th_debug_select_global(_ptr(scores), c, f, b_full, j0, blk, r, _ptr(mask),
+                                        _ptr(s_k), _ptr(ws), ws.numel(), _stream(scores.device)))
+    return mask, s_k
+
+
+def debug_factor(H):
+    torch = _torch()
+    _require_cuda(H)
+    b = H.shape[0]
+    U = torch.empty_like(H)
+    nbytes = 4 * b * b + 4 * (-(-b // 128)) * 128 * 128 + (1 << 16)
+    ws = workspace(nbytes, H.device)
+    _check(lib().th_debug_factor(_ptr(H), b, _ptr(U), _ptr(ws), ws.numel(), _stream(H.device)))
+    return U

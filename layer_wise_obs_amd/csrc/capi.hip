@@ -1,0 +1,423 @@
+// C ABI of libthanos: argument checks, workspace layout and the layer driver.
+//
+// th_prune_layer runs the whole per-layer path on one stream:
+//   Hessian (X given):  H = 2 X^T X (lower)  -> lambda on the device
+//   factor:             S = P H P (+lambda), in-place Cholesky + inverse, U = reverse(S)
+//   slices:             Ublk, [D], [N], R[J,F] = U_JJ^T U[J,F]
+//   block loop (left to right, "Pruning LLMs with Thanos", section "The scaling
+//   problem, and what SparseGPT changes"):
+//       unstructured: threshold by radix select over F, solve, update W[:, F]
+//       N:M:          select + solve in one kernel, update W[:, F]
+//   output:             What cast back to the input dtype
+// The budget, the threshold and every count stay on the device; the host
+// synchronises once, at the end, to read the status flags.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+using namespace th;
+
+namespace {
+
+thread_local std::string g_last_error = "no error";
+
+th_status fail(th_status s, const char* msg) {
+  g_last_error = msg;
+  return s;
+}
+
+th_status hip_fail(hipError_t e, const char* where) {
+  g_last_error = std::string(where) + ": " + hipGetErrorString(e);
+  return TH_ERR_HIP;
+}
+
+#define TH_HIP(call, where)                      \
+  do {                                           \
+    hipError_t e_ = (call);                      \
+    if (e_ != hipSuccess) return hip_fail(e_, where); \
+  } while (0)
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* p) : base((char*)p) {}
+  template <class T>
+  T* take(size_t count) {
+    T* p = base ? (T*)(base + off) : nullptr;
+    off = align256(off + count * sizeof(T));
+    return p;
+  }
+};
+
+struct PruneLayout {
+  DevState* st;
+  unsigned long long* counts;
+  float* S;
+  float* R;
+  float* P;
+  float* Ublk;
+  float* Nblk;
+  float* D;
+  float* gW;
+  float* Z;
+  float* Wf;
+  uint8_t* mask;
+  float* syrk_part;
+  size_t bytes;
+};
+
+bool needs_complement(const th_prune_params* p) {
+  if (p->block <= 64) return false;
+  if (p->pattern.kind == TH_UNSTRUCTURED) return true;
+  return (p->block / p->pattern.m) * (p->pattern.m - p->pattern.n) > 64;
+}
+
+PruneLayout layout_prune(void* ws, int64_t c, int64_t b, int64_t n, bool have_x,
+                         const th_prune_params* p, bool need_wf, bool need_mask, th_dtype xdt) {
+  Carve cv(ws);
+  PruneLayout L;
+  const int64_t B = p->block;
+  const int64_t nblk = cdiv(b, B);
+  L.st = cv.take<DevState>(1);
+  L.counts = cv.take<unsigned long long>(nblk);
+  L.S = cv.take<float>((size_t)b * b);
+  L.R = cv.take<float>((size_t)b * b);
+  L.P = cv.take<float>((size_t)cdiv(b, 128) * 128 * 128);
+  L.Ublk = cv.take<float>((size_t)nblk * B * B);
+  L.Nblk = needs_complement(p) ? cv.take<float>((size_t)nblk * B * B) : nullptr;
+  const bool unstr = p->pattern.kind == TH_UNSTRUCTURED;
+  L.D = (unstr && p->score == TH_SCORE_OBS) ? cv.take<float>((size_t)nblk * b) : nullptr;
+  L.gW = (p->score == TH_SCORE_WANDA) ? cv.take<float>((size_t)b) : nullptr;
+  L.Z = cv.take<float>((size_t)c * B);
+  L.Wf = need_wf ? cv.take<float>((size_t)c * b) : nullptr;
+  L.mask = need_mask ? cv.take<uint8_t>((size_t)c * b) : nullptr;
+  L.syrk_part = nullptr;
+  if (have_x && xdt == TH_BF16) {
+    const int splits = syrk_bf16_splits(n, b);
+    if (splits > 1) {
+      const int64_t nt = cdiv(b, 256);
+      L.syrk_part = cv.take<float>((size_t)splits * (nt * (nt + 1) / 2) * 256 * 256);
+    }
+  }
+  L.bytes = cv.off;
+  return L;
+}
+
+th_status check_params(int64_t c, int64_t b, const th_prune_params* p) {
+  if (!p) return fail(TH_ERR_INVALID_ARG, "params is NULL");
+  if (c < 1 || b < 1) return fail(TH_ERR_INVALID_ARG, "c and b must be >= 1");
+  if (c * b >= (int64_t)1 << 32) return fail(TH_ERR_INVALID_ARG, "c*b must be < 2^32");
+  if (p->block < 1 || p->block > kMaxBlock)
+    return fail(TH_ERR_INVALID_ARG, "block must be in [1, 128]");
+  if (p->score != TH_SCORE_OBS && p->score != TH_SCORE_WANDA)
+    return fail(TH_ERR_INVALID_ARG, "unknown score");
+  if (p->pattern.kind == TH_UNSTRUCTURED) {
+    if (!(p->sparsity >= 0.0 && p->sparsity <= 1.0))
+      return fail(TH_ERR_INVALID_ARG, "sparsity must be in [0, 1]");
+  } else if (p->pattern.kind == TH_NM) {
+    const int n = p->pattern.n, m = p->pattern.m;
+    if (m < 1 || n < 0 || n > m) return fail(TH_ERR_INVALID_ARG, "N:M needs 0 <= n <= m, m >= 1");
+    if (p->block % m || b % m) return fail(TH_ERR_INVALID_ARG, "N:M needs m | block and m | b");
+  } else {
+    return fail(TH_ERR_INVALID_ARG, "unknown pattern kind");
+  }
+  if (!(p->lambda >= 0.0) || !std::isfinite(p->lambda))
+    return fail(TH_ERR_INVALID_ARG, "lambda must be finite and >= 0");
+  return TH_OK;
+}
+
+bool dtype_ok(th_dtype d) { return d == TH_F32 || d == TH_BF16; }
+
+th_status accumulate_into(float* H, const void* X, th_dtype xdt, int64_t t, int64_t b,
+                          int64_t ldx, float* part, hipStream_t s) {
+  if (xdt == TH_BF16) {
+    const int splits = part ? syrk_bf16_splits(t, b) : 1;
+    TH_HIP(launch_syrk_bf16(H, (const unsigned short*)X, t, b, ldx, part, splits, s), "syrk_bf16");
+  } else {
+    TH_HIP(launch_syrk_f32(H, (const float*)X, t, b, ldx, s), "syrk_f32");
+  }
+  return TH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* th_last_error(void) { return g_last_error.c_str(); }
+
+th_status th_hessian_workspace_size(int64_t t, int64_t b, size_t* bytes) {
+  if (!bytes || t < 0 || b < 1) return fail(TH_ERR_INVALID_ARG, "bad arguments");
+  const int splits = syrk_bf16_splits(t, b);
+  const int64_t nt = cdiv(b, 256);
+  *bytes = splits > 1 ? (size_t)splits * (nt * (nt + 1) / 2) * 256 * 256 * sizeof(float) : 0;
+  return TH_OK;
+}
+
+th_status th_hessian_accumulate(float* H, const void* X, th_dtype xdt, int64_t t, int64_t b,
+                                int64_t ldx, void* workspace, size_t workspace_bytes,
+                                th_stream_t stream) {
+  if (!H || !X) return fail(TH_ERR_INVALID_ARG, "H and X must be non-NULL");
+  if (t < 0 || b < 1 || ldx < b) return fail(TH_ERR_INVALID_ARG, "need t >= 0, b >= 1, ldx >= b");
+  if (!dtype_ok(xdt)) return fail(TH_ERR_INVALID_ARG, "unknown dtype");
+  if (xdt == TH_BF16 && (ldx % 8 || ((uintptr_t)X & 15)))
+    return fail(TH_ERR_INVALID_ARG, "bf16 X needs ldx % 8 == 0 and 16-byte alignment");
+  size_t need = 0;
+  th_hessian_workspace_size(t, b, &need);
+  float* part = nullptr;
+  if (workspace && need > 0) {
+    if (workspace_bytes < need) return fail(TH_ERR_WORKSPACE, "workspace too small");
+    part = (float*)workspace;
+  }
+  return accumulate_into(H, X, xdt, t, b, ldx, part, (hipStream_t)stream);
+}
+
+th_status th_hessian_finalize(float* H, int64_t b, double lambda, int32_t rel, double* lambda_out,
+                              th_stream_t stream) {
+  if (!H || b < 1) return fail(TH_ERR_INVALID_ARG, "bad arguments");
+  if (!(lambda >= 0.0) || !std::isfinite(lambda)) return fail(TH_ERR_INVALID_ARG, "bad lambda");
+  hipStream_t s = (hipStream_t)stream;
+  std::vector<float> diag((size_t)b);
+  TH_HIP(hipMemcpy2DAsync(diag.data(), sizeof(float), H, (size_t)(b + 1) * sizeof(float),
+                          sizeof(float), (size_t)b, hipMemcpyDeviceToHost, s),
+         "copy diag");
+  TH_HIP(hipStreamSynchronize(s), "sync");
+  double sum = 0.0;
+  for (int64_t q = 0; q < b; ++q) {
+    if (!std::isfinite(diag[q])) return fail(TH_ERR_NONFINITE, "non-finite Hessian diagonal");
+    sum += diag[q];
+  }
+  const double lam = rel ? lambda * (sum / (double)b) : lambda;
+  TH_HIP(launch_damp_mirror(H, b, (float)lam, s), "damp_mirror");
+  TH_HIP(hipStreamSynchronize(s), "sync");
+  if (lambda_out) *lambda_out = lam;
+  return TH_OK;
+}
+
+th_status th_prune_layer_workspace_size(int64_t c, int64_t b, int64_t n, int32_t have_x,
+                                        const th_prune_params* p, size_t* bytes) {
+  if (!bytes) return fail(TH_ERR_INVALID_ARG, "bytes is NULL");
+  th_status st = check_params(c, b, p);
+  if (st != TH_OK) return st;
+  // worst case: no caller-provided fp32 output or mask, bf16 X
+  PruneLayout L = layout_prune(nullptr, c, b, n, have_x != 0, p, true, true, TH_BF16);
+  *bytes = L.bytes;
+  return TH_OK;
+}
+
+th_status th_prune_layer(void* W, th_dtype wdt, int64_t c, int64_t b, const void* X, th_dtype xdt,
+                         int64_t n, const float* H, const th_prune_params* p, float* W_out_f32,
+                         uint8_t* mask_out, void* workspace, size_t workspace_bytes,
+                         th_stats* stats_out, int64_t* block_counts, th_stream_t stream) {
+  th_status chk = check_params(c, b, p);
+  if (chk != TH_OK) return chk;
+  if (!W) return fail(TH_ERR_INVALID_ARG, "W is NULL");
+  if ((X == nullptr) == (H == nullptr)) return fail(TH_ERR_INVALID_ARG, "pass exactly one of X, H");
+  if (!dtype_ok(wdt) || (X && !dtype_ok(xdt))) return fail(TH_ERR_INVALID_ARG, "unknown dtype");
+  if (X && n < 1) return fail(TH_ERR_INVALID_ARG, "n must be >= 1");
+  if (X && xdt == TH_BF16 && (b % 8 || ((uintptr_t)X & 15)))
+    return fail(TH_ERR_INVALID_ARG, "bf16 X needs b % 8 == 0 and 16-byte alignment");
+  if (!workspace) return fail(TH_ERR_INVALID_ARG, "workspace is NULL");
+  if ((uintptr_t)workspace & 255) return fail(TH_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  PruneLayout L = layout_prune(workspace, c, b, n, X != nullptr, p, W_out_f32 == nullptr,
+                               mask_out == nullptr, xdt);
+  if (workspace_bytes < L.bytes) return fail(TH_ERR_WORKSPACE, "workspace too small");
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t B = p->block;
+  const int64_t nblk = cdiv(b, B);
+  float* Wf = W_out_f32 ? W_out_f32 : L.Wf;
+  uint8_t* mask = mask_out ? mask_out : L.mask;
+  const bool unstr = p->pattern.kind == TH_UNSTRUCTURED;
+  const bool obs = p->score == TH_SCORE_OBS;
+
+  TH_HIP(hipMemsetAsync(L.st, 0, sizeof(DevState), s), "memset state");
+  TH_HIP(hipMemsetAsync(L.counts, 0, nblk * sizeof(unsigned long long), s), "memset counts");
+  long long k_total = 0;
+  if (unstr) {
+    k_total = (long long)std::nearbyint(p->sparsity * (double)c * (double)b);
+    TH_HIP(hipMemcpyAsync(&L.st->budget, &k_total, sizeof(k_total), hipMemcpyHostToDevice, s),
+           "budget");
+  }
+  TH_HIP(launch_to_f32(W, wdt, c * b, Wf, L.st, s), "W to fp32");
+
+  // Hessian and its flipped, damped lower triangle.
+  if (X) {
+    float* Hb = L.R;  // R is free until the factor is reversed into it
+    TH_HIP(hipMemsetAsync(Hb, 0, (size_t)b * b * sizeof(float), s), "memset H");
+    th_status a = accumulate_into(Hb, X, xdt, n, b, b, L.syrk_part, s);
+    if (a != TH_OK) return a;
+    TH_HIP(launch_lambda(Hb, b, p->lambda, p->lambda_is_relative, 0, L.st, s), "lambda");
+    if (!obs) TH_HIP(launch_wanda_diag(Hb, b, L.st, 0, L.gW, s), "wanda diag");
+    TH_HIP(launch_flip_lower(Hb, L.S, b, L.st, 1, s), "flip");
+  } else {
+    TH_HIP(launch_lambda(H, b, p->lambda, p->lambda_is_relative, 1, L.st, s), "lambda");
+    if (!obs) TH_HIP(launch_wanda_diag(H, b, L.st, 1, L.gW, s), "wanda diag");
+    TH_HIP(launch_flip_lower(H, L.S, b, L.st, 0, s), "flip");
+  }
+
+  // U with H^-1 = U^T U, then the per-block slices.
+  TH_HIP(launch_chol_inv_inplace(L.S, b, L.P, L.st, s), "cholesky/inverse");
+  TH_HIP(launch_reverse(L.S, L.R, b, s), "reverse");
+  TH_HIP(launch_save_diag_blocks(L.R, b, B, L.Ublk, s), "diag blocks");
+  if (L.D) TH_HIP(launch_colnorm_downdate(L.R, b, B, L.D, s), "column norms");
+  if (L.Nblk) TH_HIP(launch_block_inverses(L.Ublk, b, B, L.Nblk, s), "block inverses");
+  TH_HIP(launch_transform_rows(L.R, b, B, L.Ublk, s), "transform rows");
+
+  for (int64_t blk = 0; blk < nblk; ++blk) {
+    const int64_t j0 = blk * B;
+    const int64_t Bb = (b - j0) < B ? (b - j0) : B;
+    const float* Nb = L.Nblk ? L.Nblk + blk * B * B : nullptr;
+    if (unstr) {
+      const float* g = obs ? L.D + blk * b : L.gW;
+      TH_HIP(launch_select_init(L.st, 0, blk == 0, (long long)(c * (b - j0)), s), "select init");
+      for (int pass = 0; pass < 6; ++pass) {
+        TH_HIP(launch_select_pass(Wf, c, b, j0, g, obs ? 1 : 0, L.st, s), "select pass");
+        TH_HIP(launch_select_pick(L.st, s), "select pick");
+      }
+      TH_HIP(launch_solve_unstructured(Wf, c, b, j0, B, L.R, Nb, g, obs ? 1 : 0, L.Z, mask, L.st,
+                                       L.counts + blk, s),
+             "solve");
+    } else {
+      TH_HIP(launch_solve_nm(Wf, c, b, j0, B, p->pattern.n, p->pattern.m, L.R, obs ? nullptr : L.gW,
+                             Nb, L.Z, mask, L.st, L.counts + blk, s),
+             "solve");
+    }
+    TH_HIP(launch_update(Wf, c, b, j0, Bb, B, b, L.Z, L.R, mask, s), "update");
+  }
+  TH_HIP(launch_from_f32(Wf, c * b, wdt, W, s), "cast back");
+
+  DevState host;
+  TH_HIP(hipMemcpyAsync(&host, L.st, offsetof(DevState, hist), hipMemcpyDeviceToHost, s), "state");
+  std::vector<unsigned long long> counts((size_t)nblk);
+  TH_HIP(hipMemcpyAsync(counts.data(), L.counts, nblk * sizeof(unsigned long long),
+                        hipMemcpyDeviceToHost, s),
+         "counts");
+  TH_HIP(hipStreamSynchronize(s), "sync");
+  if (stats_out) {
+    stats_out->lambda_used = host.lambda;
+    stats_out->total_pruned = host.pruned;
+    stats_out->nblocks = nblk;
+  }
+  if (block_counts)
+    for (int64_t i = 0; i < nblk; ++i) block_counts[i] = (int64_t)counts[i];
+  if (host.nonfinite) return fail(TH_ERR_NONFINITE, "non-finite value in W or diag(H)");
+  if (host.not_spd) return fail(TH_ERR_NOT_SPD, "damped Hessian is not positive definite");
+  return TH_OK;
+}
+
+th_status th_reconstruction_error_workspace_size(int64_t c, int64_t b, int32_t have_x,
+                                                 size_t* bytes) {
+  if (!bytes || c < 1 || b < 1) return fail(TH_ERR_INVALID_ARG, "bad arguments");
+  Carve cv(nullptr);
+  cv.take<float>((size_t)c * b);
+  cv.take<float>((size_t)c * b);
+  if (have_x) cv.take<float>((size_t)b * b);
+  cv.take<double>((size_t)cdiv(c, 128) * cdiv(b, 128));
+  cv.take<double>(2);
+  *bytes = cv.off;
+  return TH_OK;
+}
+
+th_status th_reconstruction_error(const void* W, const void* What, th_dtype wdt, int64_t c,
+                                  int64_t b, const void* X, th_dtype xdt, int64_t n,
+                                  const float* G, void* workspace, size_t workspace_bytes,
+                                  double* err_out, double* rel_err_out, th_stream_t stream) {
+  if (!W || !What || !workspace) return fail(TH_ERR_INVALID_ARG, "NULL argument");
+  if (c < 1 || b < 1) return fail(TH_ERR_INVALID_ARG, "c and b must be >= 1");
+  if ((X == nullptr) == (G == nullptr)) return fail(TH_ERR_INVALID_ARG, "pass exactly one of X, G");
+  if (!dtype_ok(wdt) || (X && !dtype_ok(xdt))) return fail(TH_ERR_INVALID_ARG, "unknown dtype");
+  if (X && xdt == TH_BF16 && (b % 8 || ((uintptr_t)X & 15)))
+    return fail(TH_ERR_INVALID_ARG, "bf16 X needs b % 8 == 0 and 16-byte alignment");
+  size_t need = 0;
+  th_reconstruction_error_workspace_size(c, b, X != nullptr, &need);
+  if (workspace_bytes < need) return fail(TH_ERR_WORKSPACE, "workspace too small");
+  hipStream_t s = (hipStream_t)stream;
+  Carve cv(workspace);
+  float* D = cv.take<float>((size_t)c * b);
+  float* Wf = cv.take<float>((size_t)c * b);
+  float* Gb = X ? cv.take<float>((size_t)b * b) : nullptr;
+  double* parts = cv.take<double>((size_t)cdiv(c, 128) * cdiv(b, 128));
+  double* out = cv.take<double>(2);
+  double scale = 1.0;
+  if (X) {
+    TH_HIP(hipMemsetAsync(Gb, 0, (size_t)b * b * sizeof(float), s), "memset G");
+    th_status a = accumulate_into(Gb, X, xdt, n, b, b, nullptr, s);  // 2G, lower
+    if (a != TH_OK) return a;
+    TH_HIP(launch_damp_mirror(Gb, b, 0.f, s), "mirror");
+    G = Gb;
+    scale = 0.5;
+  }
+  TH_HIP(launch_diff_f32(W, What, wdt, c * b, D, s), "diff");
+  TH_HIP(launch_to_f32(W, wdt, c * b, Wf, nullptr, s), "W to fp32");
+  int64_t np = 0;
+  TH_HIP(launch_quadform(D, c, b, G, parts, &np, s), "quadform");
+  TH_HIP(launch_sum_partials(parts, np, out, s), "sum");
+  TH_HIP(launch_quadform(Wf, c, b, G, parts, &np, s), "quadform");
+  TH_HIP(launch_sum_partials(parts, np, out + 1, s), "sum");
+  double host[2];
+  TH_HIP(hipMemcpyAsync(host, out, sizeof(host), hipMemcpyDeviceToHost, s), "copy");
+  TH_HIP(hipStreamSynchronize(s), "sync");
+  const double E = host[0] * scale, base = host[1] * scale;
+  if (err_out) *err_out = E;
+  if (rel_err_out) *rel_err_out = base > 0 ? E / base : 0.0;
+  return TH_OK;
+}
+
+th_status th_debug_select_nm(const float* scores, int64_t c, int64_t blk, int32_t n, int32_t m,
+                             uint8_t* mask_blk, th_stream_t stream) {
+  if (!scores || !mask_blk || c < 1 || blk < 1 || blk > 1024)
+    return fail(TH_ERR_INVALID_ARG, "bad arguments (blk must be in [1, 1024])");
+  if (m < 1 || n < 0 || n > m || blk % m) return fail(TH_ERR_INVALID_ARG, "bad N:M");
+  TH_HIP(launch_debug_select_nm(scores, c, blk, n, m, mask_blk, (hipStream_t)stream), "select nm");
+  return TH_OK;
+}
+
+th_status th_debug_select_global(const float* scores, int64_t c, int64_t f, int64_t b_full,
+                                 int64_t j0, int64_t blk, int64_t r, uint8_t* mask_blk,
+                                 int32_t* s_k, void* workspace, size_t workspace_bytes,
+                                 th_stream_t stream) {
+  if (!scores || !mask_blk || !workspace) return fail(TH_ERR_INVALID_ARG, "NULL argument");
+  if (c < 1 || f < 1 || blk < 1 || blk > f || j0 < 0 || j0 + f > b_full || c * b_full >= ((int64_t)1 << 32))
+    return fail(TH_ERR_INVALID_ARG, "bad sizes");
+  if (workspace_bytes < sizeof(DevState)) return fail(TH_ERR_WORKSPACE, "workspace too small");
+  hipStream_t s = (hipStream_t)stream;
+  DevState* st = (DevState*)workspace;
+  TH_HIP(hipMemsetAsync(st, 0, sizeof(DevState), s), "memset");
+  long long budget = r;
+  TH_HIP(hipMemcpyAsync(&st->budget, &budget, sizeof(budget), hipMemcpyHostToDevice, s), "budget");
+  TH_HIP(launch_select_init(st, 0, 1, (long long)(c * f), s), "init");
+  for (int pass = 0; pass < 6; ++pass) {
+    TH_HIP(launch_select_scores_pass(scores, c, f, b_full, j0, st, s), "pass");
+    TH_HIP(launch_select_pick(st, s), "pick");
+  }
+  TH_HIP(launch_debug_mask_from_scores(scores, c, f, b_full, j0, blk, st, mask_blk, s_k, s), "mask");
+  TH_HIP(hipStreamSynchronize(s), "sync");
+  return TH_OK;
+}
+
+th_status th_debug_factor(const float* H, int64_t b, float* U, void* workspace,
+                          size_t workspace_bytes, th_stream_t stream) {
+  if (!H || !U || !workspace || b < 1) return fail(TH_ERR_INVALID_ARG, "bad arguments");
+  Carve cv(workspace);
+  DevState* st = cv.take<DevState>(1);
+  float* S = cv.take<float>((size_t)b * b);
+  float* P = cv.take<float>((size_t)cdiv(b, 128) * 128 * 128);
+  if (workspace_bytes < cv.off) return fail(TH_ERR_WORKSPACE, "workspace too small");
+  hipStream_t s = (hipStream_t)stream;
+  TH_HIP(hipMemsetAsync(st, 0, sizeof(DevState), s), "memset");
+  TH_HIP(launch_flip_lower(H, S, b, st, 0, s), "flip");
+  TH_HIP(launch_chol_inv_inplace(S, b, P, st, s), "cholesky/inverse");
+  TH_HIP(launch_reverse(S, U, b, s), "reverse");
+  int flag = 0;
+  TH_HIP(hipMemcpyAsync(&flag, &st->not_spd, sizeof(int), hipMemcpyDeviceToHost, s), "flag");
+  TH_HIP(hipStreamSynchronize(s), "sync");
+  if (flag) return fail(TH_ERR_NOT_SPD, "damped Hessian is not positive definite");
+  return TH_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,132 @@
+// Shared definitions of the libthanos HIP sources (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/thanos.h"
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+namespace th {
+
+constexpr int kMaxBlock = 128;  // largest column block B the kernels tile for
+constexpr int kSelBits = 11;    // radix-select digit width
+constexpr int kSelBins = 1 << kSelBits;
+
+// Device-side state of one th_prune_layer call (lives in the workspace).
+struct DevState {
+  unsigned long long prefix;   // resolved high bits of the threshold key
+  unsigned long long tbound;   // selection: key < tbound
+  long long rrem;              // rank still to find inside the current bucket
+  long long pruned;            // weights pruned so far (all blocks)
+  long long budget;            // k_total
+  int shift;                   // bit position of the next digit
+  int done;                    // threshold found for this block
+  int not_spd;                 // a pivot was <= 0 or not finite
+  int nonfinite;               // NaN/Inf met in W or diag(H)
+  double lambda;               // absolute damping used
+  double diag_mean;            // mean(diag(2G))
+  unsigned int hist[kSelBins];
+};
+
+// Score S = w^2 * g in fp32, with g = 1/[A_F]_qq (OBS) or G_qq (Wanda).
+// One definition for every kernel that ranks weights, so that keys computed
+// in different passes are bit-identical.
+__device__ __forceinline__ float score_of(float w, float g) {
+  float w2 = __fmul_rn(w, w);
+  return __fmul_rn(w2, g);
+}
+
+__device__ __forceinline__ unsigned long long make_key(float s, unsigned int flat) {
+  return ((unsigned long long)__float_as_uint(s) << 32) | (unsigned long long)flat;
+}
+
+__device__ __forceinline__ float bf16_to_f32(unsigned short h) {
+  return __uint_as_float(((unsigned int)h) << 16);
+}
+
+__device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
+  unsigned int u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) {  // inf or nan
+    return (unsigned short)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  }
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------- launchers
+// hessian.hip
+int syrk_bf16_splits(int64_t t, int64_t b);
+hipError_t launch_syrk_bf16(float* H, const unsigned short* X, int64_t t, int64_t b, int64_t ldx,
+                            float* partials, int splits, hipStream_t s);
+hipError_t launch_syrk_f32(float* H, const float* X, int64_t t, int64_t b, int64_t ldx,
+                           hipStream_t s);
+hipError_t launch_lambda(const float* H, int64_t b, double lam, int rel, int h_is_damped,
+                         DevState* st, hipStream_t s);
+hipError_t launch_damp_mirror(float* H, int64_t b, float lam, hipStream_t s);
+hipError_t launch_flip_lower(const float* H, float* S, int64_t b, const DevState* st,
+                             int add_lambda, hipStream_t s);
+hipError_t launch_wanda_diag(const float* H, int64_t b, const DevState* st, int h_is_damped,
+                             float* gdiag, hipStream_t s);
+
+// factor.hip
+hipError_t launch_chol_inv_inplace(float* S, int64_t b, float* panel, DevState* st,
+                                   hipStream_t s);
+hipError_t launch_reverse(const float* S, float* U, int64_t b, hipStream_t s);
+
+// prep.hip
+hipError_t launch_save_diag_blocks(const float* U, int64_t b, int64_t B, float* Ublk,
+                                   hipStream_t s);
+hipError_t launch_transform_rows(float* R, int64_t b, int64_t B, const float* Ublk,
+                                 hipStream_t s);
+hipError_t launch_colnorm_downdate(const float* U, int64_t b, int64_t B, float* D,
+                                   hipStream_t s);
+hipError_t launch_block_inverses(const float* Ublk, int64_t b, int64_t B, float* Nblk,
+                                 hipStream_t s);
+
+// select.hip
+hipError_t launch_select_init(DevState* st, long long unused, int first, long long ncand,
+                              hipStream_t s);
+hipError_t launch_select_pass(const float* W, int64_t c, int64_t b, int64_t j0,
+                              const float* g, int invert_g, DevState* st, hipStream_t s);
+hipError_t launch_select_scores_pass(const float* scores, int64_t c, int64_t f,
+                                     int64_t b_full, int64_t j0, DevState* st, hipStream_t s);
+hipError_t launch_select_pick(DevState* st, hipStream_t s);
+
+// solve.hip
+hipError_t launch_solve_nm(const float* W, int64_t c, int64_t b, int64_t j0, int64_t B, int n,
+                           int m, const float* R, const float* gW, const float* Nblk, float* Z,
+                           uint8_t* mask, DevState* st, unsigned long long* blk_count,
+                           hipStream_t s);
+hipError_t launch_solve_unstructured(const float* W, int64_t c, int64_t b, int64_t j0, int64_t B,
+                                     const float* R, const float* Nblk, const float* g, int obs,
+                                     float* Z, uint8_t* mask, DevState* st,
+                                     unsigned long long* blk_count, hipStream_t s);
+hipError_t launch_debug_select_nm(const float* scores, int64_t c, int64_t blk, int n, int m,
+                                  uint8_t* mask, hipStream_t s);
+hipError_t launch_debug_mask_from_scores(const float* scores, int64_t c, int64_t f,
+                                         int64_t b_full, int64_t j0, int64_t blk,
+                                         const DevState* st, uint8_t* mask, int32_t* s_k,
+                                         hipStream_t s);
+
+// update.hip
+hipError_t launch_update(float* W, int64_t c, int64_t b, int64_t j0, int64_t Bb, int64_t ldz,
+                         int64_t col_end, const float* Z, const float* R, const uint8_t* mask,
+                         hipStream_t s);
+hipError_t launch_to_f32(const void* src, th_dtype dt, int64_t count, float* dst,
+                         DevState* st, hipStream_t s);
+hipError_t launch_from_f32(const float* src, int64_t count, th_dtype dt, void* dst,
+                           hipStream_t s);
+hipError_t launch_diff_f32(const void* W, const void* What, th_dtype dt, int64_t count,
+                           float* D, hipStream_t s);
+hipError_t launch_quadform(const float* D, int64_t c, int64_t b, const float* G,
+                           double* partials, int64_t* nparts, hipStream_t s);
+hipError_t launch_sum_partials(const double* partials, int64_t n, double* out, hipStream_t s);
+
+}  // namespace th

@@ -1,0 +1,164 @@
+// Per-block slices of the inverse Hessian, prepared once per layer from U.
+//
+// With H^-1 = U^T U (U upper) and F = [j0, b) the active columns of block
+// J = [j0, j0+B), the inverse of the active Hessian is A_F = (H_F)^-1 =
+// U_FF^T U_FF, so its rows J are A_F[J, F] = U_JJ^T U[J, F] and its diagonal is
+// [A_F]_qq = sum_{i=j0..q} U_iq^2. "Pruning LLMs with Thanos", section
+// "Contribution one: solve a selected set directly": R = rows Q of the inverse
+// Hessian, R-hat = its principal submatrix on Q -- both are slices of A_F[J, F].
+//
+//   save_diag_blocks : Ublk[J] = U_JJ                        (B x B, zero padded)
+//   transform_rows   : R[J, F] = U_JJ^T U[J, F] in place      (fp32 MFMA)
+//   colnorm_downdate : D[J][q] = [A_F]_qq for q in F          (OBS score over F)
+//   block_inverses   : N[J] = (A_F[J,J])^-1 = V_JJ V_JJ^T, V_JJ = U_JJ^-1
+//                      (used when a row selects more than half of a block)
+#include "gemm_f32.h"
+
+namespace th {
+
+namespace {
+
+__global__ void save_diag_blocks_kernel(const float* __restrict__ U, int64_t b, int64_t B,
+                                        float* __restrict__ Ublk) {
+  const int64_t blk = blockIdx.x;
+  const int64_t j0 = blk * B;
+  const int64_t Bb = (b - j0) < B ? (b - j0) : B;
+  float* dst = Ublk + blk * B * B;
+  for (int64_t e = threadIdx.x; e < B * B; e += blockDim.x) {
+    const int64_t a = e / B, c = e % B;
+    dst[e] = (a < Bb && c < Bb) ? U[(j0 + a) * b + j0 + c] : 0.f;
+  }
+}
+
+// One workgroup per (block J, 128-wide column tile of F).
+__global__ __launch_bounds__(256) void transform_rows_kernel(float* __restrict__ R, int64_t b,
+                                                             int64_t B, int nblk,
+                                                             const float* __restrict__ Ublk) {
+  __shared__ __attribute__((aligned(16))) float smem[kGemmLdsFloats];
+  int rem = blockIdx.x, blk = 0;
+  int64_t ntile = 0;
+  for (;;) {
+    const int64_t j0 = (int64_t)blk * B;
+    ntile = cdiv(b - j0, 128);
+    if (rem < ntile) break;
+    rem -= (int)ntile;
+    ++blk;
+    if (blk >= nblk) return;
+  }
+  const int64_t j0 = (int64_t)blk * B;
+  const int Bb = (int)((b - j0) < B ? (b - j0) : B);
+  const int64_t col0 = j0 + (int64_t)rem * 128;
+  const int cols = (int)((b - col0) < 128 ? (b - col0) : 128);
+  f32x16_t acc[2][2];
+  gemm_zero(acc);
+  // A[i][kk] = U_JJ[kk][i] (i contiguous), B[kk][jj] = U[j0+kk][col0+jj]
+  gemm_tile_f32<false, false>(Ublk + (int64_t)blk * B * B, B, Bb, R + j0 * b + col0, b, cols, Bb,
+                              acc, smem);
+  gemm_foreach(acc, [&](int r, int c, float v) {
+    if (r < Bb && c < cols) R[(j0 + r) * b + col0 + c] = v;
+  });
+}
+
+// One thread per column q: walk up the column of U accumulating squares and
+// record the partial sums at every block start j0 <= q.
+__global__ void colnorm_kernel(const float* __restrict__ U, int64_t b, int64_t B,
+                               float* __restrict__ D) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= b) return;
+  double s = 0.0;
+  int64_t blk = q / B;
+  for (int64_t i = q; i >= 0; --i) {
+    const double u = U[i * b + q];
+    s += u * u;
+    if (i == blk * B) {
+      D[blk * b + q] = (float)s;
+      --blk;
+    }
+  }
+}
+
+// N = (U_JJ^T U_JJ)^-1 = V V^T with V = U_JJ^-1 (upper), in fp64.
+__global__ __launch_bounds__(1024) void block_inverse_kernel(const float* __restrict__ Ublk,
+                                                             int64_t b, int64_t B,
+                                                             float* __restrict__ Nblk) {
+  extern __shared__ double V[];  // B x (B+1)
+  const int64_t P = B + 1;
+  const int64_t blk = blockIdx.x;
+  const int64_t j0 = blk * B;
+  const int Bb = (int)((b - j0) < B ? (b - j0) : B);
+  const float* Ub = Ublk + blk * B * B;
+  const int tid = threadIdx.x, nth = blockDim.x;
+  for (int64_t e = tid; e < (int64_t)Bb * Bb; e += nth) {
+    const int a = (int)(e / Bb), c = (int)(e % Bb);
+    V[a * P + c] = (c >= a) ? (double)Ub[a * B + c] : 0.0;
+  }
+  __syncthreads();
+  // In-place upper-triangular inverse, first column first:
+  // V_jj = 1/U_jj;  V[0:j, j] = -V_jj * V[0:j, 0:j] U[0:j, j].
+  __shared__ double colv[kMaxBlock];
+  for (int j = 0; j < Bb; ++j) {
+    const double vjj = 1.0 / V[j * P + j];
+    const int i = tid / 8, part = tid % 8;
+    double y = 0.0;
+    if (i < j) {
+      for (int m = i + part; m < j; m += 8) y += V[i * P + m] * V[m * P + j];
+    }
+    y += __shfl_xor(y, 1);
+    y += __shfl_xor(y, 2);
+    y += __shfl_xor(y, 4);
+    __syncthreads();
+    if (i < j && part == 0) colv[i] = -vjj * y;
+    __syncthreads();
+    if (i < j && part == 0) V[i * P + j] = colv[i];
+    if (tid == 0) V[j * P + j] = vjj;
+    __syncthreads();
+  }
+  float* Nb = Nblk + blk * B * B;
+  for (int64_t e = tid; e < B * B; e += nth) {
+    const int a = (int)(e / B), c = (int)(e % B);
+    double s = 0.0;
+    if (a < Bb && c < Bb) {
+      const int from = a > c ? a : c;
+      for (int m = from; m < Bb; ++m) s += V[a * P + m] * V[c * P + m];
+    }
+    Nb[e] = (float)s;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_save_diag_blocks(const float* U, int64_t b, int64_t B, float* Ublk,
+                                   hipStream_t s) {
+  const int nblk = (int)cdiv(b, B);
+  hipLaunchKernelGGL(save_diag_blocks_kernel, dim3(nblk), dim3(256), 0, s, U, b, B, Ublk);
+  return hipGetLastError();
+}
+
+hipError_t launch_transform_rows(float* R, int64_t b, int64_t B, const float* Ublk,
+                                 hipStream_t s) {
+  const int nblk = (int)cdiv(b, B);
+  int64_t total = 0;
+  for (int k = 0; k < nblk; ++k) total += cdiv(b - (int64_t)k * B, 128);
+  hipLaunchKernelGGL(transform_rows_kernel, dim3((unsigned)total), dim3(256), 0, s, R, b, B, nblk,
+                     Ublk);
+  return hipGetLastError();
+}
+
+hipError_t launch_colnorm_downdate(const float* U, int64_t b, int64_t B, float* D,
+                                   hipStream_t s) {
+  hipLaunchKernelGGL(colnorm_kernel, dim3((unsigned)cdiv(b, 256)), dim3(256), 0, s, U, b, B, D);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_inverses(const float* Ublk, int64_t b, int64_t B, float* Nblk,
+                                 hipStream_t s) {
+  const int nblk = (int)cdiv(b, B);
+  const size_t lds = (size_t)B * (B + 1) * sizeof(double);
+  hipError_t a = hipFuncSetAttribute((const void*)block_inverse_kernel,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (a != hipSuccess) return a;
+  hipLaunchKernelGGL(block_inverse_kernel, dim3(nblk), dim3(1024), lds, s, Ublk, b, B, Nblk);
+  return hipGetLastError();
+}
+
+}  // namespace th

@@ -1,0 +1,180 @@
+// Global residual-budget selection for unstructured sparsity.
+//
+// "Pruning LLMs with Thanos", section "Contribution two: keep the budget global
+// and the execution local": for each block, r = (weights still to remove), the
+// scores of the whole active region F are recomputed from the current weights,
+// the r lowest form a provisional candidate set, and only its intersection with
+// the current block is pruned.
+//
+// The r-th smallest key is found exactly by an MSD radix select over 64-bit keys
+// (fp32 score bits << 32 | flat index k*b + q). Keys are unique, so the
+// candidate set is exactly { key < tbound } and ties in the score go to the
+// lower flat index. Each pass histograms one 11-bit digit (LDS histogram per
+// workgroup, integer atomics into the global one, so counts are exact and
+// order-independent); a one-workgroup pick kernel narrows the prefix. Budget,
+// prefix and threshold stay on the device: the host launches a fixed number of
+// passes and finished passes exit at once.
+#include "common.h"
+
+namespace th {
+
+namespace {
+
+// Digits: shifts 53, 42, 31, 20, 9 (11 bits each) then 0 (9 bits).
+__device__ __forceinline__ void digit_of(int shift, int& width) {
+  width = (shift == 0) ? 9 : 11;
+}
+
+__global__ void select_init_kernel(DevState* st, long long ncand) {
+  for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) st->hist[i] = 0u;
+  if (threadIdx.x == 0) {
+    const long long r = st->budget - st->pruned;
+    st->rrem = r;
+    st->prefix = 0ull;
+    st->shift = 53;
+    if (r <= 0) {
+      st->done = 1;
+      st->tbound = 0ull;
+    } else if (r >= ncand) {
+      st->done = 1;
+      st->tbound = ~0ull;
+    } else {
+      st->done = 0;
+      st->tbound = 0ull;
+    }
+  }
+}
+
+template <class KeyF>
+__device__ __forceinline__ void hist_body(DevState* st, int64_t total, KeyF&& keyf) {
+  __shared__ unsigned int sh[kSelBins];
+  const int shift = st->shift;
+  int width;
+  digit_of(shift, width);
+  const int top = shift + width;
+  const unsigned long long prefix = st->prefix;
+  for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) sh[i] = 0u;
+  __syncthreads();
+  const unsigned long long dmask = (1ull << width) - 1ull;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const unsigned long long key = keyf(e);
+    const bool match = (top >= 64) || ((key >> top) == (prefix >> top));
+    if (match) atomicAdd(&sh[(key >> shift) & dmask], 1u);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kSelBins; i += blockDim.x)
+    if (sh[i]) atomicAdd(&st->hist[i], sh[i]);
+}
+
+// Keys recomputed from the current weights: S = W^2 * g, g = 1/D (OBS) or G_qq.
+__global__ __launch_bounds__(256) void select_pass_kernel(const float* __restrict__ W, int64_t c,
+                                                          int64_t b, int64_t j0,
+                                                          const float* __restrict__ g,
+                                                          int invert_g, DevState* st) {
+  if (st->done) return;
+  const int64_t f = b - j0;
+  hist_body(st, c * f, [&](int64_t e) {
+    const int64_t k = e / f, q = j0 + (e - k * f);
+    const float gq = invert_g ? __fdiv_rn(1.0f, g[q]) : g[q];
+    const float s = score_of(W[k * b + q], gq);
+    return make_key(s, (unsigned int)(k * b + q));
+  });
+}
+
+// Keys from given scores [c, f] (parity entry point).
+__global__ __launch_bounds__(256) void select_scores_pass_kernel(const float* __restrict__ S,
+                                                                 int64_t c, int64_t f,
+                                                                 int64_t b_full, int64_t j0,
+                                                                 DevState* st) {
+  if (st->done) return;
+  hist_body(st, c * f, [&](int64_t e) {
+    const int64_t k = e / f, q = e - k * f;
+    return make_key(S[e], (unsigned int)(k * b_full + j0 + q));
+  });
+}
+
+__global__ void select_pick_kernel(DevState* st) {
+  __shared__ unsigned int part[256];
+  if (st->done) return;
+  const int tid = threadIdx.x;
+  const int per = kSelBins / 256;  // 8 bins per thread
+  unsigned int local = 0;
+  for (int i = 0; i < per; ++i) local += st->hist[tid * per + i];
+  part[tid] = local;
+  __syncthreads();
+  if (tid == 0) {
+    const long long r = st->rrem;
+    long long cum = 0;
+    int d = -1;
+    for (int t = 0; t < 256 && d < 0; ++t) {
+      if (cum + (long long)part[t] >= r) {
+        for (int i = 0; i < per; ++i) {
+          const long long h = st->hist[t * per + i];
+          if (cum + h >= r) {
+            d = t * per + i;
+            break;
+          }
+          cum += h;
+        }
+      } else {
+        cum += part[t];
+      }
+    }
+    const int shift = st->shift;
+    if (d < 0) {  // cannot happen when the histogram is consistent
+      st->tbound = st->prefix;
+      st->done = 1;
+    } else {
+      const long long inb = st->hist[d];
+      const long long rnew = r - cum;
+      st->prefix |= ((unsigned long long)d) << shift;
+      st->rrem = rnew;
+      if (inb == rnew || shift == 0) {
+        // every key of the bucket is within the r smallest (shift == 0: inb == 1)
+        st->tbound = st->prefix + (1ull << shift);
+        st->done = 1;
+      } else {
+        st->shift = (shift >= 20) ? shift - 11 : 0;
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < kSelBins; i += blockDim.x) st->hist[i] = 0u;
+}
+
+}  // namespace
+
+hipError_t launch_select_init(DevState* st, long long /*unused*/, int /*first*/, long long ncand,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(select_init_kernel, dim3(1), dim3(256), 0, s, st, ncand);
+  return hipGetLastError();
+}
+
+static unsigned hist_grid(int64_t total) {
+  int64_t g = cdiv(total, 256 * 8);
+  if (g > 2048) g = 2048;
+  if (g < 1) g = 1;
+  return (unsigned)g;
+}
+
+hipError_t launch_select_pass(const float* W, int64_t c, int64_t b, int64_t j0, const float* g,
+                              int invert_g, DevState* st, hipStream_t s) {
+  hipLaunchKernelGGL(select_pass_kernel, dim3(hist_grid(c * (b - j0))), dim3(256), 0, s, W, c, b,
+                     j0, g, invert_g, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_scores_pass(const float* scores, int64_t c, int64_t f, int64_t b_full,
+                                     int64_t j0, DevState* st, hipStream_t s) {
+  hipLaunchKernelGGL(select_scores_pass_kernel, dim3(hist_grid(c * f)), dim3(256), 0, s, scores,
+                     c, f, b_full, j0, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_pick(DevState* st, hipStream_t s) {
+  hipLaunchKernelGGL(select_pick_kernel, dim3(1), dim3(256), 0, s, st);
+  return hipGetLastError();
+}
+
+}  // namespace th

@@ -1,0 +1,179 @@
+// Compensation update, dtype conversions and the reconstruction error.
+//
+// Update ("Pruning LLMs with Thanos", sections "Contribution one" and "The scaling
+// problem, and what SparseGPT changes": compensation goes only into columns that
+// are still active): W[:, F] -= Z [A_F]_{J,F}, a rank-B update on the fp32 matrix
+// cores, followed by W[k, Q_k] = 0 exactly ("makes every coordinate in Q exactly
+// zero").
+//
+// Error ("The layer-reconstruction lens"): E = ||(W - What) X||_F^2 =
+// sum_k D_k G D_k^T, computed as T = D G per 128x128 tile (fp32 MFMA) with the
+// tile's sum of T .* D in fp64; partial sums are reduced in a fixed order.
+#include "gemm_f32.h"
+
+namespace th {
+
+namespace {
+
+// W[row0:, col0:] -= Z[rows, 0:Bb] R[j0:j0+Bb, cols]; zero the pruned entries of J.
+__global__ __launch_bounds__(256) void update_kernel(float* __restrict__ W, int64_t c, int64_t b,
+                                                     int64_t j0, int Bb, int ldz,
+                                                     int64_t col_end, int ncol_tiles,
+                                                     const float* __restrict__ Z,
+                                                     const float* __restrict__ R,
+                                                     const uint8_t* __restrict__ mask) {
+  __shared__ __attribute__((aligned(16))) float smem[kGemmLdsFloats];
+  const int64_t row0 = (int64_t)(blockIdx.x / ncol_tiles) * 128;
+  const int64_t col0 = j0 + (int64_t)(blockIdx.x % ncol_tiles) * 128;
+  const int rows = (int)((c - row0) < 128 ? (c - row0) : 128);
+  const int cols = (int)((col_end - col0) < 128 ? (col_end - col0) : 128);
+  f32x16_t acc[2][2];
+  gemm_zero(acc);
+  gemm_tile_f32<true, false>(Z + row0 * ldz, ldz, rows, R + j0 * b + col0, b, cols, Bb, acc, smem);
+  const int64_t jend = j0 + Bb;
+  gemm_foreach(acc, [&](int r, int cc, float v) {
+    if (r < rows && cc < cols) {
+      const int64_t row = row0 + r, col = col0 + cc;
+      float* dst = W + row * b + col;
+      float nv = *dst - v;
+      if (col < jend && mask[row * b + col]) nv = 0.f;
+      *dst = nv;
+    }
+  });
+}
+
+__global__ void to_f32_kernel(const void* __restrict__ src, int dt, int64_t n,
+                              float* __restrict__ dst, DevState* st) {
+  int bad = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const float v = (dt == TH_BF16) ? bf16_to_f32(((const unsigned short*)src)[i])
+                                    : ((const float*)src)[i];
+    if (!isfinite(v)) bad = 1;
+    dst[i] = v;
+  }
+  if (bad && st) st->nonfinite = 1;
+}
+
+__global__ void from_f32_kernel(const float* __restrict__ src, int64_t n, int dt,
+                                void* __restrict__ dst) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    if (dt == TH_BF16) ((unsigned short*)dst)[i] = f32_to_bf16_rne(src[i]);
+    else ((float*)dst)[i] = src[i];
+  }
+}
+
+__global__ void diff_kernel(const void* __restrict__ A, const void* __restrict__ B, int dt,
+                            int64_t n, float* __restrict__ D) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    float a, bb;
+    if (dt == TH_BF16) {
+      a = bf16_to_f32(((const unsigned short*)A)[i]);
+      bb = bf16_to_f32(((const unsigned short*)B)[i]);
+    } else {
+      a = ((const float*)A)[i];
+      bb = ((const float*)B)[i];
+    }
+    D[i] = a - bb;
+  }
+}
+
+// partial[tile] = sum over the tile of (D G) .* D   (G full symmetric, b x b)
+__global__ __launch_bounds__(256) void quadform_kernel(const float* __restrict__ D, int64_t c,
+                                                       int64_t b, int ncol_tiles,
+                                                       const float* __restrict__ G,
+                                                       double* __restrict__ partials) {
+  __shared__ __attribute__((aligned(16))) float smem[kGemmLdsFloats];
+  __shared__ double red[256];
+  const int64_t row0 = (int64_t)(blockIdx.x / ncol_tiles) * 128;
+  const int64_t col0 = (int64_t)(blockIdx.x % ncol_tiles) * 128;
+  const int rows = (int)((c - row0) < 128 ? (c - row0) : 128);
+  const int cols = (int)((b - col0) < 128 ? (b - col0) : 128);
+  f32x16_t acc[2][2];
+  gemm_zero(acc);
+  gemm_tile_f32<true, false>(D + row0 * b, b, rows, G + col0, b, cols, (int)b, acc, smem);
+  double s = 0.0;
+  gemm_foreach(acc, [&](int r, int cc, float v) {
+    if (r < rows && cc < cols) s += (double)v * (double)D[(row0 + r) * b + col0 + cc];
+  });
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) partials[blockIdx.x] = red[0];
+}
+
+__global__ void sum_kernel(const double* __restrict__ p, int64_t n, double* __restrict__ out) {
+  __shared__ double red[256];
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) s += p[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = red[0];
+}
+
+unsigned ew_grid(int64_t n) {
+  int64_t g = cdiv(n, 256 * 4);
+  if (g > 16384) g = 16384;
+  if (g < 1) g = 1;
+  return (unsigned)g;
+}
+
+}  // namespace
+
+hipError_t launch_update(float* W, int64_t c, int64_t b, int64_t j0, int64_t Bb, int64_t ldz,
+                         int64_t col_end, const float* Z, const float* R, const uint8_t* mask,
+                         hipStream_t s) {
+  if (col_end <= j0) return hipSuccess;
+  const int nct = (int)cdiv(col_end - j0, 128);
+  const int nrt = (int)cdiv(c, 128);
+  hipLaunchKernelGGL(update_kernel, dim3((unsigned)(nct * nrt)), dim3(256), 0, s, W, c, b, j0,
+                     (int)Bb, (int)ldz, col_end, nct, Z, R, mask);
+  return hipGetLastError();
+}
+
+hipError_t launch_to_f32(const void* src, th_dtype dt, int64_t count, float* dst, DevState* st,
+                         hipStream_t s) {
+  hipLaunchKernelGGL(to_f32_kernel, dim3(ew_grid(count)), dim3(256), 0, s, src, (int)dt, count,
+                     dst, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_from_f32(const float* src, int64_t count, th_dtype dt, void* dst,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(from_f32_kernel, dim3(ew_grid(count)), dim3(256), 0, s, src, count, (int)dt,
+                     dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_diff_f32(const void* W, const void* What, th_dtype dt, int64_t count, float* D,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(diff_kernel, dim3(ew_grid(count)), dim3(256), 0, s, W, What, (int)dt, count,
+                     D);
+  return hipGetLastError();
+}
+
+hipError_t launch_quadform(const float* D, int64_t c, int64_t b, const float* G, double* partials,
+                           int64_t* nparts, hipStream_t s) {
+  const int nct = (int)cdiv(b, 128);
+  const int nrt = (int)cdiv(c, 128);
+  *nparts = (int64_t)nct * nrt;
+  hipLaunchKernelGGL(quadform_kernel, dim3((unsigned)(nct * nrt)), dim3(256), 0, s, D, c, b, nct,
+                     G, partials);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_partials(const double* partials, int64_t n, double* out, hipStream_t s) {
+  hipLaunchKernelGGL(sum_kernel, dim3(1), dim3(256), 0, s, partials, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace th

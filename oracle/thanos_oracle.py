@@ -185,11 +185,14 @@ def schur_downdate(A_F: np.ndarray, blk: int) -> np.ndarray:
 
 
 def prune_layer(W, G: np.ndarray, sparsity: float = 0.5, pattern=None, block: int = 128,
-                lam: float = 0.01, lam_relative: bool = True, score: str = "obs") -> dict:
+                lam: float = 0.01, lam_relative: bool = True, score: str = "obs",
+                trace: list | None = None) -> dict:
     """Block-wise pruning with joint compensation (the layer step of the method).
 
     pattern: None for unstructured with the dynamic global budget, or (n, m).
     Returns W_hat (fp64), mask (True = pruned), per-block prune counts, lambda.
+    trace (optional list) receives, per block, the scores the selection saw and
+    the remaining budget (for diagnosing near-ties in comparisons).
 
     Procedure ("Pruning LLMs with Thanos", sections "The scaling problem, and what
     SparseGPT changes" (left-to-right blocks, finished columns frozen, updates only
@@ -239,6 +242,9 @@ def prune_layer(W, G: np.ndarray, sparsity: float = 0.5, pattern=None, block: in
         else:
             S = Wc[:, j0:j0 + blk] ** 2 * g[None, :blk]
             sel = select_nm(S, pattern[0], pattern[1])
+        if trace is not None:
+            trace.append({"j0": j0, "S": S.copy(),
+                          "r": (ktot - pruned) if pattern is None else None})
         Z = solve_rows(Wc[:, j0:j0 + blk], A[:blk, :blk], sel)
         Wc[:, j0:] -= Z @ A[:blk, :]
         blockW = Wc[:, j0:j0 + blk]

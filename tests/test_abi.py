@@ -1,0 +1,87 @@
+"""The C-ABI library builds, loads and exports every entry point include/thanos.h
+declares; argument checks answer before anything touches the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from layer_wise_obs_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "thanos.h")).read()
+    return sorted(set(re.findall(r"\b(th_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_path():
+    names = _declared()
+    for must in ("th_hessian_accumulate", "th_hessian_finalize", "th_prune_layer",
+                 "th_prune_layer_workspace_size", "th_reconstruction_error", "th_debug_select_nm",
+                 "th_debug_select_global", "th_debug_factor", "th_last_error"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_params_struct_matches_header_layout():
+    # double, 3 x int32, (pad), int64, double, int32, int32
+    assert ctypes.sizeof(_lib.PruneParams) == 48
+    assert _lib.PruneParams.block.offset == 24
+    assert ctypes.sizeof(_lib.Stats) == 24
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_invalid_arguments_are_rejected_before_any_launch():
+    L = _lib.lib()
+    out = ctypes.c_size_t(0)
+    ok = _lib.make_params(pattern=(2, 4), block=128)
+    assert L.th_prune_layer_workspace_size(4096, 11008, 262144, 1, ctypes.byref(ok), ctypes.byref(out)) == 0
+    assert out.value > 2 * 11008 * 11008 * 4
+    bad = [
+        _lib.make_params(block=0),
+        _lib.make_params(block=129),
+        _lib.make_params(sparsity=1.5),
+        _lib.make_params(pattern=(2, 4), block=126),  # m does not divide B
+        _lib.make_params(pattern=(5, 4)),
+        _lib.make_params(lam=-1.0),
+    ]
+    for p in bad:
+        assert L.th_prune_layer_workspace_size(64, 128, 10, 1, ctypes.byref(p), ctypes.byref(out)) == 1
+    assert "block" in L.th_last_error().decode() or "lambda" in L.th_last_error().decode()
+    # N:M with b not a multiple of m
+    p = _lib.make_params(pattern=(2, 4), block=8)
+    assert L.th_prune_layer_workspace_size(8, 10, 10, 1, ctypes.byref(p), ctypes.byref(out)) == 1
+    # prune_layer: both X and H given / neither given
+    p = _lib.make_params()
+    dummy = ctypes.c_void_p(16)
+    args = [dummy, 0, 8, 8, dummy, 0, 8, dummy, ctypes.byref(p), None, None, dummy, 1 << 20,
+            None, None, None]
+    assert L.th_prune_layer(*args) == 1
+    args[4] = None
+    args[7] = None
+    assert L.th_prune_layer(*args) == 1
+    # hessian: ldx < b, misaligned bf16
+    assert L.th_hessian_accumulate(dummy, dummy, 1, 10, 16, 8, None, 0, None) == 1
+    assert L.th_hessian_accumulate(dummy, ctypes.c_void_p(18), 1, 10, 16, 16, None, 0, None) == 1
+    assert L.th_debug_select_nm(dummy, 4, 6, 2, 4, dummy, None) == 1
+
+
+def test_workspace_size_queries():
+    L = _lib.lib()
+    out = ctypes.c_size_t(0)
+    assert L.th_hessian_workspace_size(262144, 11008, ctypes.byref(out)) == 0
+    assert out.value == 0  # 946 tiles: no token split
+    assert L.th_hessian_workspace_size(262144, 4096, ctypes.byref(out)) == 0
+    assert out.value > 0  # 136 tiles: token split with a fixed-order reduction
+    assert L.th_reconstruction_error_workspace_size(4096, 11008, 0, ctypes.byref(out)) == 0
+    assert out.value >= 2 * 4096 * 11008 * 4

@@ -1,0 +1,282 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Sizes span several tiles and ragged tails; the oracle finishes each case in
+seconds. Tolerances: H within 1e-4 relative Frobenius; masks bit-exact when the
+selection kernels are fed the oracle's scores; W_hat within 1e-3 relative on rows
+whose masks agree, the rest only through explained fp32 near-ties; E within 1e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from layer_wise_obs_amd import _lib as L
+from layer_wise_obs_amd import synth
+from tests import _parity as P
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _inputs(c, b, n, seed, wdtype=torch.bfloat16, xdtype=torch.bfloat16, relu=False,
+            outliers=3, scale=30.0):
+    W = synth.weights(c, b, 0.02, seed, 100, wdtype)
+    X = synth.activations(n, b, seed, 1, outliers, scale, relu, xdtype)
+    return W, X
+
+
+def _gpu_hessian(X, ws=False):
+    b = X.shape[1]
+    H = torch.zeros((b, b), dtype=torch.float32, device=DEV)
+    Xd = X.to(DEV)
+    w = None
+    if ws:
+        w = L.workspace(L.hessian_workspace_size(X.shape[0], b), DEV)
+    L.hessian_accumulate(H, Xd, w)
+    return H
+
+
+def _tril(a):
+    return np.tril(np.asarray(a, np.float64))
+
+
+# ------------------------------------------------------------------ Hessian
+
+@pytest.mark.parametrize("t,b,ws", [(1000, 520, False), (1000, 520, True), (4096, 1024, True),
+                                    (64, 8, False), (3, 264, True)])
+def test_hessian_bf16_matches_oracle(t, b, ws):
+    _say(f"hessian bf16 t={t} b={b} ws={ws}")
+    _, X = _inputs(4, b, t, 11, relu=True)
+    H = _gpu_hessian(X, ws).cpu().numpy()
+    G = O.gram(X)
+    assert P.rel_fro(_tril(H), _tril(2 * G)) <= P.H_RTOL
+    assert np.all(np.triu(H, 1) == 0.0)  # the strict upper triangle is untouched
+
+
+def test_hessian_f32_and_finalize():
+    _say("hessian f32 + finalize (config 1 shapes)")
+    cfg = synth.config(1)
+    X = cfg.activations("x")
+    H = _gpu_hessian(X)
+    lam = L.hessian_finalize(H, 0.01, True)
+    G = O.gram(X)
+    lam_o = O.damping(G, 0.01)
+    assert abs(lam - lam_o) <= 1e-5 * lam_o
+    assert P.rel_fro(H.cpu().numpy(), O.hessian(G, lam_o)) <= P.H_RTOL
+    Hc = H.cpu().numpy()
+    assert np.array_equal(Hc, Hc.T)
+
+
+def test_hessian_is_deterministic():
+    _say("hessian determinism")
+    _, X = _inputs(4, 1024, 3000, 12)
+    a = _gpu_hessian(X, True)
+    b = _gpu_hessian(X, True)
+    assert torch.equal(a, b)
+
+
+def test_hessian_accumulates_over_chunks():
+    _say("hessian chunked accumulation")
+    _, X = _inputs(4, 512, 2000, 13)
+    b = 512
+    H = torch.zeros((b, b), dtype=torch.float32, device=DEV)
+    Xd = X.to(DEV)
+    for t0 in range(0, 2000, 700):
+        L.hessian_accumulate(H, Xd[t0:t0 + 700].contiguous())
+    assert P.rel_fro(_tril(H.cpu().numpy()), _tril(2 * O.gram(X))) <= P.H_RTOL
+
+
+# ------------------------------------------------------------ factorisation
+
+@pytest.mark.parametrize("b", [130, 300, 512])
+def test_factor_matches_inverse_cholesky(b):
+    _say(f"factor b={b}")
+    _, X = _inputs(4, b, 4 * b, 21, xdtype=torch.float32)
+    G = O.gram(X)
+    H = O.hessian(G, O.damping(G))
+    U = L.debug_factor(torch.tensor(H, dtype=torch.float32, device=DEV)).cpu().numpy()
+    U_ref = np.linalg.cholesky(np.linalg.inv(H)).T
+    assert np.all(np.tril(U, -1) == 0.0)
+    assert P.rel_fro(U, U_ref) <= 5e-4
+    # U H U^T = I
+    R = U.astype(np.float64) @ H @ U.astype(np.float64).T
+    assert np.max(np.abs(R - np.eye(b))) <= 1e-3
+
+
+def test_factor_reports_not_spd():
+    _say("factor not SPD")
+    b = 200
+    rng = np.random.default_rng(3)
+    A = rng.standard_normal((b, b))
+    H = A @ A.T
+    H[50, 50] = -1.0
+    with pytest.raises(L.ThanosError) as ei:
+        L.debug_factor(torch.tensor(H, dtype=torch.float32, device=DEV))
+    assert ei.value.status == L.TH_ERR_NOT_SPD
+
+
+# ------------------------------------------------------ selection (oracle-fed)
+
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8), (1, 4), (3, 8)])
+def test_select_nm_bitexact_on_oracle_scores(n, m):
+    _say(f"select nm {n}:{m}")
+    rng = np.random.default_rng(n * 10 + m)
+    c, blk = 257, 128
+    S = (rng.standard_normal((c, blk)) ** 2).astype(np.float32)
+    S[::3, ::5] = S[::3, 1::5][:, : S[::3, ::5].shape[1]]  # exact ties
+    S[7, :] = 1.0
+    mask = L.debug_select_nm(torch.tensor(S, device=DEV), n, m).cpu().numpy().astype(bool)
+    ref = O.select_nm(S.astype(np.float64), n, m)
+    assert np.array_equal(mask, ref)
+
+
+@pytest.mark.parametrize("ties", [False, True])
+def test_select_global_bitexact_on_oracle_scores(ties):
+    _say(f"select global ties={ties}")
+    rng = np.random.default_rng(5 + ties)
+    c, b_full, j0, blk = 300, 700, 220, 128
+    f = b_full - j0
+    if ties:
+        S = rng.integers(0, 7, size=(c, f)).astype(np.float32) * 0.25
+    else:
+        S = (rng.standard_normal((c, f)) ** 2 * 1e-3).astype(np.float32)
+    S[5, :] = 0.0
+    Sd = torch.tensor(S, device=DEV)
+    for r in [0, 1, 17, c * f // 3, c * f // 2 + 1, c * f - 1, c * f, c * f + 5]:
+        mask, s_k = L.debug_select_global(Sd, b_full, j0, blk, r)
+        ref = O.select_unstructured(S.astype(np.float64), r, blk)
+        assert np.array_equal(mask.cpu().numpy().astype(bool), ref), r
+        assert np.array_equal(s_k.cpu().numpy(), ref.sum(axis=1)), r
+
+
+# --------------------------------------------------------------- whole layer
+
+def _run_gpu(W, X=None, H=None, **kw):
+    Wd = W.to(DEV).contiguous()
+    Wout = torch.empty(W.shape, dtype=torch.float32, device=DEV)
+    mask = torch.empty(W.shape, dtype=torch.uint8, device=DEV)
+    params = L.make_params(**kw)
+    info = L.prune_layer(Wd, X=None if X is None else X.to(DEV), H=H, params=params, W_out=Wout,
+                         mask_out=mask)
+    return Wd, Wout.cpu().numpy(), mask.cpu().numpy().astype(bool), info
+
+
+def _check_layer(W, X, sparsity=0.5, pattern=None, block=128, score="obs", max_flip_frac=0.01):
+    G = O.gram(X)
+    trace = []
+    ora = O.prune_layer(W, G, sparsity=sparsity, pattern=pattern, block=block, score=score,
+                        trace=trace)
+    Wd, Wg, mg, info = _run_gpu(W, X, sparsity=sparsity, pattern=pattern, block=block,
+                                score=score)
+    rep = P.compare_pruned(Wg, mg, ora, block, pattern, trace, max_flip_frac)
+    print(rep, flush=True)
+    assert rep["ok"], rep
+    # exact invariants on the GPU's own output
+    assert np.all(Wg[mg] == 0.0)
+    if pattern is None:
+        assert int(mg.sum()) == info["pruned"] == ora["k_total"]
+    else:
+        n_, m_ = pattern
+        assert np.all(mg.reshape(mg.shape[0], -1, m_).sum(axis=2) == m_ - n_)
+        assert info["pruned"] == mg.sum()
+    assert sum(info["counts"]) == info["pruned"]
+    assert abs(info["lambda"] - ora["lam"]) <= 1e-5 * ora["lam"]
+    # error of the GPU's W_hat, measured on the GPU, against the oracle's error
+    W32 = torch.tensor(O.thanos_oracle._f64(W), dtype=torch.float32, device=DEV)
+    e_gpu, er_gpu = L.reconstruction_error(W32, torch.tensor(Wg, device=DEV),
+                                           G=torch.tensor(G, dtype=torch.float32, device=DEV))
+    e_ora, er_ora = O.reconstruction_error(W, ora["W_hat"], G)
+    assert abs(e_gpu - e_ora) <= P.E_RTOL * e_ora, (e_gpu, e_ora)
+    # the bf16 cast-back of W is the rounded fp32 result
+    if W.dtype == torch.bfloat16:
+        assert torch.equal(Wd.cpu(), torch.tensor(Wg).to(torch.bfloat16))
+    return ora, Wg, mg, info
+
+
+def test_prune_config1_unstructured():
+    _say("prune config 1 (128x256 fp32, 50% unstructured, B=32)")
+    cfg = synth.config(1)
+    W = cfg.weights(cfg.layers[0])
+    X = cfg.activations("x")
+    _check_layer(W, X, sparsity=0.5, pattern=None, block=32)
+
+
+@pytest.mark.parametrize("pattern", [(2, 4), (4, 8), (1, 4)])
+def test_prune_nm_several_tiles(pattern):
+    _say(f"prune N:M {pattern} c=300 b=512")
+    W, X = _inputs(300, 512, 4096, 31, relu=True)
+    _check_layer(W, X, pattern=pattern, block=128)
+
+
+def test_prune_unstructured_ragged_last_block():
+    _say("prune unstructured c=200 b=392 ragged")
+    W, X = _inputs(200, 392, 3000, 32)
+    _check_layer(W, X, sparsity=0.5, pattern=None, block=128)
+
+
+def test_prune_unstructured_high_sparsity_small_block():
+    _say("prune unstructured 70% B=48")
+    W, X = _inputs(96, 240, 2000, 33, relu=True)
+    _check_layer(W, X, sparsity=0.7, pattern=None, block=48)
+
+
+@pytest.mark.parametrize("pattern", [None, (2, 4)])
+def test_prune_wanda_score(pattern):
+    _say(f"prune wanda score {pattern}")
+    W, X = _inputs(128, 256, 2048, 34)
+    _check_layer(W, X, sparsity=0.5, pattern=pattern, block=64, score="wanda")
+
+
+def test_prune_limits():
+    _say("prune limits p=0, p=1")
+    W, X = _inputs(64, 128, 1024, 35)
+    _, Wg, mg, info = _run_gpu(W, X, sparsity=0.0, block=64)
+    assert not mg.any() and np.array_equal(Wg, W.float().numpy())
+    _, Wg, mg, info = _run_gpu(W, X, sparsity=1.0, block=64)
+    assert mg.all() and np.all(Wg == 0.0)
+
+
+def test_prune_from_hessian_equals_from_activations():
+    _say("prune from H vs from X")
+    W, X = _inputs(128, 256, 2048, 36)
+    Hd = _gpu_hessian(X)
+    L.hessian_finalize(Hd, 0.01, True)
+    _, Wa, ma, ia = _run_gpu(W, X, pattern=(2, 4), block=128)
+    _, Wb, mb, ib = _run_gpu(W, H=Hd, pattern=(2, 4), block=128)
+    assert np.array_equal(ma, mb)
+    assert P.rel_fro(Wb, Wa) <= 1e-5
+
+
+def test_prune_is_deterministic():
+    _say("prune determinism")
+    W, X = _inputs(128, 384, 2048, 37)
+    _, Wa, ma, _ = _run_gpu(W, X, sparsity=0.5, block=128)
+    _, Wb, mb, _ = _run_gpu(W, X, sparsity=0.5, block=128)
+    assert np.array_equal(ma, mb) and np.array_equal(Wa, Wb)
+
+
+def test_prune_reports_not_spd_and_nonfinite():
+    _say("prune error statuses")
+    W, X = _inputs(32, 128, 40, 38, xdtype=torch.float32)  # n < b
+    with pytest.raises(L.ThanosError) as ei:
+        _run_gpu(W, X, sparsity=0.5, block=64, lam=0.0, relative=False)
+    assert ei.value.status == L.TH_ERR_NOT_SPD
+    W, X = _inputs(32, 128, 400, 39)
+    W[3, 7] = float("nan")
+    with pytest.raises(L.ThanosError) as ei:
+        _run_gpu(W, X, sparsity=0.5, block=64)
+    assert ei.value.status == L.TH_ERR_NONFINITE
+
+
+def test_reconstruction_error_from_activations():
+    _say("reconstruction error from X")
+    W, X = _inputs(96, 264, 1500, 40)
+    Wh = W.clone()
+    Wh[:, ::3] = 0
+    e, er = L.reconstruction_error(W.to(DEV), Wh.to(DEV), X=X.to(DEV))
+    e_o, er_o = O.reconstruction_error(W, Wh, O.gram(X))
+    assert abs(e - e_o) <= P.E_RTOL * e_o and abs(er - er_o) <= P.E_RTOL * er_o
