@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark: seconds to prune one LLaMA-7B-shaped MLP down_proj layer with 2:4
+block-wise (Thanos-style) pruning on one MI355X, plus the Hessian TFLOP/s.
+
+A step is one call of th_prune_layer on inputs resident in HBM: W (4096 x 11008
+bf16, restored from a pristine copy at the start of the step) and calibration
+activations X (262144 tokens x 11008 bf16, ReLU-like with 110 channels x30). The
+step runs the whole path: H = 2XX^T + lambda*I (bf16 MFMA), factor + inverse,
+per-block 2:4 selection, joint solves and updates (block size 128), and the
+cast back to bf16.
+
+Prints one JSON line. `roofline` is for the dominant kernel (the bf16 syrk),
+timed with HIP events on the stream it runs on; `cpu_baseline` is the fp64
+oracle on a bounded sample of the same workload, scaled to seconds per layer.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--pattern 2:4]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "seconds per layer (4096×11008 down_proj, 2:4) + XXᵀ TFLOP/s vs MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (datasheet)
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 MFMA (datasheet)
+
+
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _ev_time(fn, reps, stream):
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(reps):
+        start.record(stream)
+        fn()
+        end.record(stream)
+        end.synchronize()
+        times.append(start.elapsed_time(end))
+    return times
+
+
+def cpu_baseline(X, W, c, b, n, pattern, block, lam_rel):
+    """fp64 oracle on a bounded sample, scaled to seconds per layer.
+
+    Sample: G from the first 1024 tokens (scaled by n/1024); the Cholesky check
+    and LU inverse of a damped 11008 x 11008 H at full size (unscaled); the first
+    3 column blocks of the block loop with all rows, scaled by the modelled flops
+    of all blocks (Schur downdate 2|F'|^2 B + 2|F'| B^2, update 2 c B |F|,
+    per-row solves c s^3/3)."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    n_s = 1024
+    Xs = X[:n_s].float().cpu().numpy()
+    t0 = time.perf_counter()
+    G = O.gram(Xs)
+    t_g = (time.perf_counter() - t0) * (n / n_s)
+    Wn = W.float().cpu().numpy()
+    k_s = 3
+    t0 = time.perf_counter()
+    O.prune_layer(Wn, G, pattern=pattern, block=block, lam=lam_rel, max_blocks=k_s)
+    t_rest = time.perf_counter() - t0
+    # split t_rest into the (unscaled) inverse and the sampled blocks
+    H = O.hessian(G, O.damping(G, lam_rel))
+    t0 = time.perf_counter()
+    np.linalg.cholesky(H)
+    np.linalg.inv(H)
+    t_inv = time.perf_counter() - t0
+    t_blocks_s = max(t_rest - t_inv, 0.0)
+    s = block * (pattern[1] - pattern[0]) // pattern[1]
+
+    def cost(j0):
+        f = b - j0
+        fp = max(f - block, 0)
+        return 2 * fp * fp * block + 2 * fp * block * block + 2 * c * block * f + c * s ** 3 / 3
+
+    total = sum(cost(j0) for j0 in range(0, b, block))
+    sampled = sum(cost(j0) for j0 in range(0, min(b, k_s * block), block))
+    t_blocks = t_blocks_s * total / sampled
+    value = t_g + t_inv + t_blocks
+    return {"value": value, "unit": "s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"G on {n_s} of {n} tokens (x{n / n_s:.0f}); Cholesky check + LU inverse "
+                       f"at full b={b}; first {k_s} of {-(-b // block)} blocks with all {c} rows, "
+                       f"scaled by modelled flops (x{total / sampled:.1f}); phases s: "
+                       f"G {t_g:.1f}, inverse {t_inv:.1f}, blocks {t_blocks:.1f}")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--pattern", default="2:4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from layer_wise_obs_amd import _lib as L
+    from layer_wise_obs_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = synth.config(3)
+    layer = cfg.layers[0]
+    st = cfg.streams[layer.hessian]
+    c, b, n = layer.c, layer.b, st.n
+    pn, pm = (int(v) for v in args.pattern.split(":"))
+    block, lam_rel = cfg.block, cfg.lambda_rel
+
+    _log(f"generating X [{n} x {b}] bf16 and W [{c} x {b}] on the GPU")
+    X = torch.empty((n, b), dtype=torch.bfloat16, device=dev)
+    cfg.activations(layer.hessian, device=dev, out=X)
+    W0 = cfg.weights(layer, device=dev)
+    W = torch.empty_like(W0)
+    torch.cuda.synchronize()
+
+    params = L.make_params(pattern=(pn, pm), block=block, lam=lam_rel, relative=True)
+    ws = L.workspace(L.prune_layer_workspace_size(c, b, n, True, params), dev)
+    Wout = torch.empty((c, b), dtype=torch.float32, device=dev)
+    mask = torch.empty((c, b), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        W.copy_(W0)
+        return L.prune_layer(W, X=X, params=params, W_out=Wout, mask_out=mask, ws=ws)
+
+    for i in range(args.warmup):
+        _log(f"warmup step {i + 1}/{args.warmup}")
+        info = step()
+    torch.cuda.synchronize()
+    _log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        info = step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1000.0 / max(args.steps, 1)
+    _log(f"{ms_step:.2f} ms per layer")
+
+    # dominant kernel: the bf16 syrk, same launch as inside the step
+    H = torch.zeros((b, b), dtype=torch.float32, device=dev)
+    syrk_ms = _ev_time(lambda: L.hessian_accumulate(H, X), max(args.steps, 3), stream)
+    syrk_avg = sum(syrk_ms) / len(syrk_ms)
+    syrk_flops = float(n) * b * (b + 1)  # one triangle of X^T X: n*b(b+1)
+    achieved = syrk_flops / (syrk_avg * 1e-3) / 1e12
+    _log(f"syrk {syrk_avg:.2f} ms = {achieved:.0f} TFLOP/s")
+
+    # the layer from a given Hessian (factor + block loop only)
+    H.zero_()
+    L.hessian_accumulate(H, X)
+    lam_h = L.hessian_finalize(H, lam_rel, True)
+
+    def step_h():
+        W.copy_(W0)
+        return L.prune_layer(W, H=H, params=params, W_out=Wout, mask_out=mask, ws=ws)
+
+    step_h()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(max(args.steps, 1)):
+        step_h()
+    torch.cuda.synchronize()
+    ms_given_h = (time.perf_counter() - t1) * 1000.0 / max(args.steps, 1)
+
+    # reconstruction error of the last result (reported, not part of the step)
+    W32 = W0.float()
+    t2 = time.perf_counter()
+    E, E_rel = L.reconstruction_error(W32, Wout, G=H_undamped(H, lam_h))
+    ms_err = (time.perf_counter() - t2) * 1000.0
+
+    fact_flops = 2.0 * b ** 3 / 3.0
+    nblk = -(-b // block)
+    fsum = sum(b - j * block for j in range(nblk))
+    upd_flops = 2.0 * block * block * fsum + 2.0 * c * block * fsum
+    floor_ms = (syrk_flops / (PEAK_BF16_TFLOPS * 1e12)
+                + (fact_flops + upd_flops) / (PEAK_FP32_TFLOPS * 1e12)) * 1e3
+    m = mask.bool()
+    nm_ok = bool((m.view(c, -1, pm).sum(dim=2) == pm - pn).all().item())
+
+    out = {
+        "metric": METRIC,
+        "value": ms_step / 1000.0,
+        "unit": "s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16/fp32",
+        "data": "synthetic",
+        "config": {"workload": f"down_proj {c}x{b}, {pn}:{pm}, block {block}, X {n} tokens bf16 "
+                               f"(ReLU-like, {st.outlier_count} channels x{st.outlier_scale:g}), "
+                               f"lambda {lam_rel} relative"},
+        "roofline": {"bound": "mfma", "kernel": "syrk_bf16_kernel", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": None, "launch_ms": syrk_avg,
+                     "algorithmic": f"n*b*(b+1) = {syrk_flops:.4g} flop per launch"},
+        "extra": {
+            "hessian_tflops": achieved,
+            "ms_per_layer_given_H": ms_given_h,
+            "pruned_weights_per_s": info["pruned"] / (ms_step / 1000.0),
+            "pruned": info["pruned"],
+            "nm_exact": nm_ok,
+            "at_peak_floor_ms": floor_ms,
+            "mfma_utilisation_e2e": floor_ms / ms_step,
+            "recon_error_rel": E_rel,
+            "recon_error_ms": ms_err,
+        },
+    }
+    if not args.no_cpu_baseline:
+        _log("timing the fp64 oracle on a bounded sample (CPU)")
+        out["cpu_baseline"] = cpu_baseline(X, W0, c, b, n, (pn, pm), block, lam_rel)
+    print(json.dumps(out), flush=True)
+
+
+def H_undamped(H, lam):
+    """G = (H - lambda I) / 2 from the finalized Hessian (for the error report)."""
+    import torch
+    G = H.clone()
+    G.diagonal().sub_(lam)
+    G.mul_(0.5)
+    return G
+
+
+if __name__ == "__main__":
+    main()

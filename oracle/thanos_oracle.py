@@ -186,13 +186,14 @@ def schur_downdate(A_F: np.ndarray, blk: int) -> np.ndarray:
 
 def prune_layer(W, G: np.ndarray, sparsity: float = 0.5, pattern=None, block: int = 128,
                 lam: float = 0.01, lam_relative: bool = True, score: str = "obs",
-                trace: list | None = None) -> dict:
+                trace: list | None = None, max_blocks: int | None = None) -> dict:
     """Block-wise pruning with joint compensation (the layer step of the method).
 
     pattern: None for unstructured with the dynamic global budget, or (n, m).
     Returns W_hat (fp64), mask (True = pruned), per-block prune counts, lambda.
     trace (optional list) receives, per block, the scores the selection saw and
-    the remaining budget (for diagnosing near-ties in comparisons).
+    the remaining budget (for diagnosing near-ties in comparisons). max_blocks
+    stops after that many blocks (used only to time a bounded sample).
 
     Procedure ("Pruning LLMs with Thanos", sections "The scaling problem, and what
     SparseGPT changes" (left-to-right blocks, finished columns frozen, updates only
@@ -228,7 +229,9 @@ def prune_layer(W, G: np.ndarray, sparsity: float = 0.5, pattern=None, block: in
     ktot = k_total(sparsity, c, b) if pattern is None else None
     pruned = 0
     diagG = np.diag(G)
-    for j0 in range(0, b, block):
+    for bi, j0 in enumerate(range(0, b, block)):
+        if max_blocks is not None and bi >= max_blocks:
+            break
         blk = min(block, b - j0)
         if score == "obs":
             g = 1.0 / np.diag(A)
