@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/thanos.h"
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -56,6 +58,29 @@ __device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
   }
   u += 0x7fffu + ((u >> 16) & 1u);
   return (unsigned short)(u >> 16);
+}
+
+// Wave-level LDS ordering: every LDS access of this wave issued before the call
+// has completed, and the compiler does not move LDS accesses across it.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_wave_barrier();
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E). Used where
+// register arrays must be indexed by constants in fully unrolled code.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Value of v in lane `lane` (lane must be wave-uniform).
+__device__ __forceinline__ float bcast(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }

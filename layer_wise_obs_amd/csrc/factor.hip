@@ -11,8 +11,8 @@
 // over 128-wide block columns, in place on S = P H P (lower triangle):
 //   before step k:  S[k:,k:] = Schur complement,  S[k:,:k] = partial rows of L^-1,
 //                   S[:k,:k] = final rows of L^-1.
-//   step k:  (1) one workgroup factors the diagonal block (fp64 in LDS):
-//                L_kk and X_kk = L_kk^-1, written back as X_kk;
+//   step k:  (1) one workgroup factors the diagonal block (fp32, registers and
+//                LDS): X_kk = L_kk^-1, written back over the block;
 //            (2) panel:  Lp_i = S[i,k] X_kk^T for block rows i > k (to a buffer),
 //                        S[k,:k] = X_kk S[k,:k] (row k of L^-1 is now final);
 //            (3) trailing, one fp32 MFMA GEMM over all tiles (i > k, j <= i):
@@ -26,65 +26,166 @@ namespace th {
 namespace {
 
 constexpr int kNb = 128;
-constexpr int kDP = kNb + 1;  // fp64 LDS pitch
+constexpr int kHalf = 64;
+constexpr int kSP = kNb + 1;  // LDS pitch (floats) of the 128 x 128 diagonal block
 
-// (1) Diagonal block: Cholesky and lower-triangular inverse in fp64.
-__global__ __launch_bounds__(1024) void diag_factor_kernel(float* __restrict__ S, int64_t b,
-                                                           int64_t k0, int nbk, DevState* st) {
-  extern __shared__ double L[];  // nbk x kDP
-  __shared__ double colv[kNb];
-  const int tid = threadIdx.x, nth = blockDim.x;
-  for (int e = tid; e < nbk * nbk; e += nth) {
-    const int i = e / nbk, j = e % nbk;
-    L[i * kDP + j] = (j <= i) ? (double)S[(k0 + i) * b + k0 + j] : 0.0;
+// Copy of the lane id that the compiler cannot hoist or share across the
+// unrolled steps (keeps per-step lane masks short-lived).
+__device__ __forceinline__ int fresh_lane() {
+  int l = threadIdx.x & 63;
+  __asm__ volatile("" : "+v"(l));
+  return l;
+}
+
+// One wave, 64 x 64 SPD block A (lower triangle read from sm, pitch kSP):
+// L = chol(A) into sl and X = L^-1 into sx (both pitch kSP, zeros above the
+// diagonal). All steps are branch-free and fully unrolled so that the row
+// stays in registers.
+// Pass 1, right-looking Cholesky, lane i holds row i: step j needs column j of
+//   the (still symmetric) trailing block -- one LDS store per lane.
+// Pass 2, forward substitution L X = I, lane j holds column j of X: row i of L
+//   is read as an LDS broadcast; no synchronisation inside the loop.
+__device__ __forceinline__ void wave_chol_inv64(const float* sm, float* sx, float* sl,
+                                                float* scol, int* bad) {
+  int flag = 0;
+  {
+    const int lane = threadIdx.x & 63;
+    float reg[kHalf];
+    static_for<0, kHalf>([&](auto C) __attribute__((always_inline)) {
+      constexpr int c = C;
+      reg[c] = (c <= lane) ? sm[lane * kSP + c] : sm[c * kSP + lane];
+    });
+    static_for<0, kHalf>([&](auto J) __attribute__((always_inline)) {
+      constexpr int j = J;
+      const int ln = fresh_lane();
+      const float p0 = bcast(reg[j], j);
+      const bool ok = (p0 > 0.f) && (p0 < 3.0e38f);
+      flag |= ok ? 0 : 1;
+      const float p = ok ? p0 : 1.f;
+      const float sp = __builtin_sqrtf(p);
+      const float rs = __builtin_amdgcn_rcpf(sp);
+      const float rj = reg[j];
+      const float f = (ln > j) ? rj * (rs * rs) : 0.f;
+      float lv = rj * rs;
+      lv = (ln > j) ? lv : 0.f;
+      lv = (ln == j) ? sp : lv;
+      sl[ln * kSP + j] = lv;
+      scol[ln] = rj;
+      wave_sync();
+      static_for<j + 1, kHalf>([&](auto C) __attribute__((always_inline)) {
+        constexpr int c = C;
+        reg[c] = fmaf(-f, scol[c], reg[c]);
+      });
+      wave_sync();
+    });
+  }
+  {
+    float x[kHalf];
+    static_for<0, kHalf>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = I;
+      const int ln = fresh_lane();
+      float acc = (ln == i) ? 1.f : 0.f;
+      static_for<0, i>([&](auto M) __attribute__((always_inline)) {
+        constexpr int m = M;
+        acc = fmaf(-sl[i * kSP + m], x[m], acc);
+      });
+      x[i] = acc * __builtin_amdgcn_rcpf(sl[i * kSP + i]);
+    });
+    const int lane = threadIdx.x & 63;
+    static_for<0, kHalf>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = I;
+      sx[i * kSP + lane] = (i >= lane) ? x[i] : 0.f;
+    });
+  }
+  if (flag && (threadIdx.x & 63) == 0) *bad = 1;
+}
+
+// 32 x 32 tile (this wave) of sum_m A(i, m) B(m, j), m < K, operands in LDS.
+template <class FA, class FB>
+__device__ __forceinline__ f32x16_t lds_mfma_tile(FA&& a, FB&& bop, int K) {
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 31, kk = lane >> 5;
+  f32x16_t acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  for (int m = 0; m < K; m += 2)
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a(i, m + kk), bop(m + kk, i), acc, 0, 0, 0);
+  return acc;
+}
+
+template <class F>
+__device__ __forceinline__ void tile_foreach(const f32x16_t& acc, F&& f) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) f(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), lane & 31, acc[r]);
+}
+
+// (1) Diagonal block: X_kk = L_kk^-1 with A_kk = L_kk L_kk^T, fp32, 256 threads.
+// Split 2 x 2 into 64-blocks:  X11 = chol_inv(A11);  L21 = A21 X11^T;
+// A22 -= L21 L21^T;  X22 = chol_inv(A22);  X21 = -X22 (L21 X11).
+// A block narrower than 128 (the last one) is padded with the identity.
+__global__ __launch_bounds__(256) void diag_factor_kernel(float* __restrict__ S, int64_t b,
+                                                          int64_t k0, int nbk, DevState* st) {
+  __shared__ float sA[kNb * kSP];
+  __shared__ float sX[kNb * kSP];
+  __shared__ float scol[kHalf];
+  __shared__ int bad;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  if (tid == 0) bad = 0;
+  for (int e = tid; e < kNb * kNb; e += blockDim.x) {
+    const int i = e / kNb, j = e % kNb;
+    float v = (i == j) ? 1.f : 0.f;
+    if (i < nbk && j < nbk && j <= i) v = S[(k0 + i) * b + k0 + j];
+    sA[i * kSP + j] = v;
   }
   __syncthreads();
-  // Right-looking Cholesky.
-  for (int j = 0; j < nbk; ++j) {
-    if (tid == 0) {
-      double d = L[j * kDP + j];
-      if (!(d > 0.0) || !isfinite(d)) {
-        st->not_spd = 1;
-        d = 1.0;
-      }
-      L[j * kDP + j] = sqrt(d);
-    }
+  // L11 scratch: the (not yet needed) rows 64.. of sX, columns 0..63
+  if (wave == 0) wave_chol_inv64(sA, sX, sX + kHalf * kSP, scol, &bad);
+  __syncthreads();
+  const int ti = wave >> 1, tj = wave & 1;
+  float* A21 = sA + kHalf * kSP;         // rows 64.., cols 0..63
+  float* A22 = sA + kHalf * kSP + kHalf;  // rows 64.., cols 64..
+  {  // L21 = A21 X11^T  (stored over A21)
+    f32x16_t acc = lds_mfma_tile(
+        [&](int i, int m) { return A21[(32 * ti + i) * kSP + m]; },
+        [&](int m, int j) { return sX[(32 * tj + j) * kSP + m]; }, kHalf);
     __syncthreads();
-    const double inv = 1.0 / L[j * kDP + j];
-    for (int i = j + 1 + tid; i < nbk; i += nth) L[i * kDP + j] *= inv;
-    __syncthreads();
-    const int m = nbk - j - 1;
-    for (int e = tid; e < m * m; e += nth) {
-      const int i = j + 1 + e / m, c = j + 1 + e % m;
-      if (c <= i) L[i * kDP + c] -= L[i * kDP + j] * L[c * kDP + j];
-    }
-    __syncthreads();
+    tile_foreach(acc, [&](int r, int c, float v) { A21[(32 * ti + r) * kSP + 32 * tj + c] = v; });
   }
-  // In-place inverse of the lower factor, last column first:
-  // X_jj = 1/L_jj;  X[j+1:, j] = -X_jj * X[j+1:, j+1:] L[j+1:, j].
-  for (int j = nbk - 1; j >= 0; --j) {
-    const double xjj = 1.0 / L[j * kDP + j];
-    // y_i = sum_{m=j+1..i} X[i][m] L[m][j]; 8 threads per row
-    const int rows = nbk - j - 1;
-    double y = 0.0;
-    const int i = j + 1 + tid / 8, part = tid % 8;
-    if (tid / 8 < rows) {
-      for (int m = j + 1 + part; m <= i; m += 8) y += L[i * kDP + m] * L[m * kDP + j];
-    }
-    y += __shfl_xor(y, 1);
-    y += __shfl_xor(y, 2);
-    y += __shfl_xor(y, 4);
-    __syncthreads();
-    if (tid / 8 < rows && part == 0) colv[i] = -xjj * y;
-    __syncthreads();
-    if (tid / 8 < rows && part == 0) L[i * kDP + j] = colv[i];
-    if (tid == 0) L[j * kDP + j] = xjj;
-    __syncthreads();
+  __syncthreads();
+  {  // A22 -= L21 L21^T
+    f32x16_t acc = lds_mfma_tile(
+        [&](int i, int m) { return A21[(32 * ti + i) * kSP + m]; },
+        [&](int m, int j) { return A21[(32 * tj + j) * kSP + m]; }, kHalf);
+    tile_foreach(acc, [&](int r, int c, float v) { A22[(32 * ti + r) * kSP + 32 * tj + c] -= v; });
   }
-  for (int e = tid; e < nbk * nbk; e += nth) {
+  __syncthreads();
+  float* X22 = sX + kHalf * kSP + kHalf;
+  // L22 scratch: rows 64.. of sX, columns 0..63 (T is written after this)
+  if (wave == 0) wave_chol_inv64(A22, X22, sX + kHalf * kSP, scol, &bad);
+  __syncthreads();
+  float* T = sX + kHalf * kSP;  // rows 64.., cols 0..63 of sX: T = L21 X11
+  {
+    f32x16_t acc = lds_mfma_tile(
+        [&](int i, int m) { return A21[(32 * ti + i) * kSP + m]; },
+        [&](int m, int j) { return sX[m * kSP + 32 * tj + j]; }, kHalf);
+    tile_foreach(acc, [&](int r, int c, float v) { T[(32 * ti + r) * kSP + 32 * tj + c] = v; });
+  }
+  __syncthreads();
+  {  // X21 = -X22 T  (stored over A21)
+    f32x16_t acc = lds_mfma_tile(
+        [&](int i, int m) { return X22[(32 * ti + i) * kSP + m]; },
+        [&](int m, int j) { return T[m * kSP + 32 * tj + j]; }, kHalf);
+    tile_foreach(acc, [&](int r, int c, float v) { A21[(32 * ti + r) * kSP + 32 * tj + c] = -v; });
+  }
+  __syncthreads();
+  for (int e = tid; e < nbk * nbk; e += blockDim.x) {
     const int i = e / nbk, j = e % nbk;
-    S[(k0 + i) * b + k0 + j] = (j <= i) ? (float)L[i * kDP + j] : 0.f;
+    float v = 0.f;
+    if (j <= i) v = (i >= kHalf && j < kHalf) ? sA[i * kSP + j] : sX[i * kSP + j];
+    S[(k0 + i) * b + k0 + j] = v;
   }
+  if (tid == 0 && bad) st->not_spd = 1;
 }
 
 // (2) Panel: blockIdx.x < nrow -> Lp for block row k+1+blockIdx.x;
@@ -162,13 +263,7 @@ hipError_t launch_chol_inv_inplace(float* S, int64_t b, float* P, DevState* st, 
   for (int k = 0; k < nblk; ++k) {
     const int64_t k0 = (int64_t)k * kNb;
     const int nbk = (int)((b - k0) < kNb ? (b - k0) : kNb);
-    const size_t lds = (size_t)nbk * kDP * sizeof(double);
-    if (k == 0) {
-      hipError_t a = hipFuncSetAttribute((const void*)diag_factor_kernel,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (a != hipSuccess) return a;
-    }
-    hipLaunchKernelGGL(diag_factor_kernel, dim3(1), dim3(1024), lds, s, S, b, k0, nbk, st);
+    hipLaunchKernelGGL(diag_factor_kernel, dim3(1), dim3(256), 0, s, S, b, k0, nbk, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nrow = nblk - k - 1;

@@ -33,16 +33,6 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kMP = kMaxBlock + 1;  // LDS pitch of M / N
 
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_wave_barrier();
-  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_wave_barrier();
-}
-
-__device__ __forceinline__ float bcast(float v, int lane) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
-}
-
 // Rank of entry e in its aligned group of m among scores sc[] (ties: lower column first).
 __device__ __forceinline__ bool nm_pruned(const float* sc, int e, int n, int m) {
   const int g0 = (e / m) * m;
@@ -68,8 +58,9 @@ __device__ __forceinline__ float gauss_jordan64(float (&reg)[64], float rhs, int
       scol[lane] = reg[j];
       wave_sync();
       const float p = bcast(reg[j], j);
+      const float pinv = 1.f / p;
       const float rj = bcast(rhs, j);
-      const float f = (lane == j) ? 0.f : reg[j] / p;
+      const float f = (lane == j) ? 0.f : reg[j] * pinv;
       if (lane == j) piv = p;
       rhs = fmaf(-f, rj, rhs);
 #pragma unroll
