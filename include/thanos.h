@@ -95,7 +95,7 @@ typedef struct {
  * [EXPL, "SparseGPT: Second-Order Reconstruction at Scale"]: H = 2XX^T (+ lambda I
  * later). X_chunk: [t, b] token-major, dtype xdt (TH_BF16: products are exact in
  * fp32 and accumulate in fp32 on the matrix cores; TH_F32: fp32 FMA). ldx >= b
- * and, for TH_BF16, ldx % 8 == 0 and a 16-byte aligned X. H: b x b fp32, zeroed by
+ * and, for TH_BF16, b % 8 == 0, ldx % 8 == 0 and a 16-byte aligned X. H: b x b fp32, zeroed by
  * the caller before the first chunk; the strict upper triangle is not touched.
  * workspace (optional, may be NULL with workspace_bytes 0) lets small b split the
  * token range over more workgroups; size from th_hessian_workspace_size. The

@@ -165,8 +165,8 @@ th_status th_hessian_accumulate(float* H, const void* X, th_dtype xdt, int64_t t
   if (!H || !X) return fail(TH_ERR_INVALID_ARG, "H and X must be non-NULL");
   if (t < 0 || b < 1 || ldx < b) return fail(TH_ERR_INVALID_ARG, "need t >= 0, b >= 1, ldx >= b");
   if (!dtype_ok(xdt)) return fail(TH_ERR_INVALID_ARG, "unknown dtype");
-  if (xdt == TH_BF16 && (ldx % 8 || ((uintptr_t)X & 15)))
-    return fail(TH_ERR_INVALID_ARG, "bf16 X needs ldx % 8 == 0 and 16-byte alignment");
+  if (xdt == TH_BF16 && (ldx % 8 || b % 8 || ((uintptr_t)X & 15)))
+    return fail(TH_ERR_INVALID_ARG, "bf16 X needs b % 8 == 0, ldx % 8 == 0 and 16-byte alignment");
   size_t need = 0;
   th_hessian_workspace_size(t, b, &need);
   float* part = nullptr;

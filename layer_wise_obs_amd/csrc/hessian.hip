@@ -6,13 +6,16 @@
 // Gram matrix, lambda*I is added for numerical stability.
 //
 // bf16 path: 256x256 output tiles of the lower triangle, 512 threads (8 waves as
-// 2 x 4, each wave 128x64 = 4x2 blocks of v_mfma_f32_32x32x16_bf16). Tokens are
-// the contraction dimension; X^T arrives token-major, so every thread loads an
-// 8-token x 8-feature brick (eight 16-byte loads), transposes it in registers
-// with v_perm_b32 and stores 8 feature rows of 8 tokens (16 bytes each) into LDS,
-// where the MFMA operands are then read as 16-byte K-contiguous vectors. The LDS
-// row pitch of 72 bf16 (36 dwords) makes both the stores and the operand reads
-// bank-conflict free.
+// 2 x 4, each wave 128x64 = 4x2 blocks of v_mfma_f32_32x32x16_bf16; two waves per
+// SIMD so one wave's loads, transposes and LDS traffic overlap the other's MFMAs).
+// Tokens are the contraction dimension; X^T arrives token-major, so every thread
+// loads an 8-token x 8-feature brick (eight 16-byte loads) of one panel,
+// transposes them in registers with v_perm_b32 and stores 8 feature rows of 8
+// tokens (16 bytes each) into LDS, where the MFMA operands are read as 16-byte
+// K-contiguous vectors. The LDS row pitch of 72 bf16 (36 dwords) makes both the
+// stores and the operand reads bank-conflict free. Two LDS stages (144 KB) and a
+// register stage give one barrier per 64 tokens, with each stage's global loads
+// in flight during a full stage of MFMA work.
 #include "common.h"
 
 namespace th {
@@ -24,78 +27,104 @@ constexpr int kBK = 64;
 constexpr int kPitch = 72;  // bf16 elements per LDS feature row (64 tokens + 8 pad)
 constexpr int kThreads = 512;
 
-__device__ __forceinline__ void load_brick(const unsigned short* __restrict__ X, int64_t ldx,
-                                           int64_t t_valid, int64_t b, int64_t tok0, int64_t f0,
-                                           u32x4_t (&v)[8]) {
-  const bool full_f = (f0 + 8 <= b);
+// 8 tokens x 8 features starting at (tok0, f0). b is a multiple of 8, so a
+// feature group is either fully inside or fully outside. Addresses are clamped
+// instead of branched on (loads stay branch-free and in bounds); the returned
+// bit mask marks the valid rows, and zeroing happens in transpose_store, so
+// nothing waits for the loads until the data is stored to LDS.
+__device__ __forceinline__ unsigned load_brick(const unsigned short* __restrict__ X, int64_t ldx,
+                                               int64_t t_valid, int64_t b, int64_t tok0,
+                                               int64_t f0, u32x4_t (&v)[8]) {
+  const bool fok = f0 < b;
+  const int64_t fc = fok ? f0 : 0;
+  unsigned ok = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t t = tok0 + i;
-    if (t < t_valid && full_f) {
-      v[i] = *(const u32x4_t*)(X + t * ldx + f0);
-    } else if (t < t_valid && f0 < b) {
-      unsigned int d[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        unsigned int lo = (f0 + 2 * p < b) ? X[t * ldx + f0 + 2 * p] : 0u;
-        unsigned int hi = (f0 + 2 * p + 1 < b) ? X[t * ldx + f0 + 2 * p + 1] : 0u;
-        d[p] = lo | (hi << 16);
-      }
-      v[i] = u32x4_t{d[0], d[1], d[2], d[3]};
-    } else {
-      v[i] = u32x4_t{0u, 0u, 0u, 0u};
-    }
+    const int64_t tc = (t < t_valid) ? t : (t_valid - 1);
+    v[i] = *(const u32x4_t*)(X + tc * ldx + fc);
+    ok |= (fok && t < t_valid) ? (1u << i) : 0u;
   }
+  return ok;
 }
 
-// 8 tokens x 8 features (v[token].dword[f/2]) -> 8 features x 8 tokens.
+// 8 tokens x 8 features (v[token].dword[f/2]) -> 8 features x 8 tokens; rows
+// whose bit is clear in `ok` are stored as zeros.
 __device__ __forceinline__ void transpose_store(unsigned short* __restrict__ s, int frow0, int oct,
-                                                const u32x4_t (&v)[8]) {
+                                                const u32x4_t (&v)[8], unsigned ok) {
+  u32x4_t w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = ((ok >> i) & 1u) ? v[i] : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     u32x4_t lo, hi;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      lo[p] = __builtin_amdgcn_perm(v[2 * p + 1][d], v[2 * p][d], 0x05040100u);
-      hi[p] = __builtin_amdgcn_perm(v[2 * p + 1][d], v[2 * p][d], 0x07060302u);
+      lo[p] = __builtin_amdgcn_perm(w[2 * p + 1][d], w[2 * p][d], 0x05040100u);
+      hi[p] = __builtin_amdgcn_perm(w[2 * p + 1][d], w[2 * p][d], 0x07060302u);
     }
     *(u32x4_t*)(s + (frow0 + 2 * d) * kPitch + oct * 8) = lo;
     *(u32x4_t*)(s + (frow0 + 2 * d + 1) * kPitch + oct * 8) = hi;
   }
 }
 
+// Tile order for L2 reuse: the lower triangle of nt x nt tiles is walked in
+// super-tiles of 4 tile rows x 8 tile columns (row-major inside each), super-
+// tiles row by row. Returns tile (ti, tj) of position lin.
+constexpr int kSupR = 4, kSupC = 8;
+__device__ __forceinline__ void tile_of(int lin, int nt, int& ti, int& tj) {
+  for (int sr = 0; sr * kSupR < nt; ++sr) {
+    const int r0 = sr * kSupR, r1 = min(nt, r0 + kSupR);
+    for (int sc = 0; sc * kSupC <= r1 - 1; ++sc) {
+      const int c0 = sc * kSupC, c1 = c0 + kSupC;
+      int cnt = 0;  // tiles (r, c) with r0 <= r < r1, c0 <= c < c1, c <= r
+      for (int r = r0; r < r1; ++r) cnt += max(0, min(c1, r + 1) - c0);
+      if (lin < cnt) {
+        for (int r = r0; r < r1; ++r) {
+          const int w = max(0, min(c1, r + 1) - c0);
+          if (lin < w) {
+            ti = r;
+            tj = c0 + lin;
+            return;
+          }
+          lin -= w;
+        }
+      }
+      lin -= cnt;
+    }
+  }
+  ti = tj = 0;  // not reached for lin < nt(nt+1)/2
+}
+
 __global__ __launch_bounds__(kThreads) void syrk_bf16_kernel(
     float* __restrict__ H, const unsigned short* __restrict__ X, int64_t t, int64_t b, int64_t ldx,
     int ntile_rows, int ntiles, int per_xcd, int splits, int64_t tok_per_split,
     float* __restrict__ partials) {
-  // XCD-aware order: consecutive workgroup ids go to different XCDs, so give each
-  // XCD a contiguous run of tiles (row-major over the lower triangle) to share
-  // row panels in its L2.
+  // XCD-aware order: consecutive workgroup ids go to different XCDs, so each XCD
+  // gets a contiguous run of the super-tile order below; the ~32 tiles an XCD
+  // runs at once then share 4 row panels and 8 column panels in its L2.
   const int wg = blockIdx.x;
   const int lin = (wg % 8) * per_xcd + wg / 8;
   const int split = blockIdx.y;
   if (lin >= ntiles) return;
-  int ti = 0, rem = lin;
-  while (rem > ti) { rem -= ti + 1; ++ti; }
-  const int tj = rem;
+  int ti, tj;
+  tile_of(lin, ntile_rows, ti, tj);
   const bool diag = (ti == tj);
   const int64_t I0 = (int64_t)ti * kTile, J0 = (int64_t)tj * kTile;
 
-  __shared__ __attribute__((aligned(16))) unsigned short sA[kTile * kPitch];
-  __shared__ __attribute__((aligned(16))) unsigned short sB[kTile * kPitch];
-  unsigned short* sBr = diag ? sA : sB;
-
+  // two pipeline stages x (A panel, B panel), each 256 features x 64 tokens
+  __shared__ __attribute__((aligned(16))) unsigned short smem[2 * 2 * kTile * kPitch];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int part = tid >> 8;           // 0: A panel, 1: B panel
+  const int part = tid >> 8;             // 0: A panel, 1: B panel
   const int q = tid & 255;
   const int oct = q & 7, fgrp = q >> 3;  // 8 token octets x 32 feature groups
   const bool loader = diag ? (part == 0) : true;
   const int64_t fbase = (part == 0 ? I0 : J0) + fgrp * 8;
-  unsigned short* sdst = (part == 0) ? sA : sB;
 
   const int64_t k_begin = (int64_t)split * tok_per_split;
   const int64_t k_end = (k_begin + tok_per_split < t) ? k_begin + tok_per_split : t;
+  const int nk = (int)cdiv(k_end - k_begin, kBK);
 
   f32x16_t acc[4][2];
 #pragma unroll
@@ -108,13 +137,19 @@ __global__ __launch_bounds__(kThreads) void syrk_bf16_kernel(
   const int wrow = wave >> 2, wcol = wave & 3;
   const int lr = lane & 31, lk = lane >> 5;
 
+  auto sbuf = [&](int stage, int panel) { return smem + (stage * 2 + panel) * (kTile * kPitch); };
   u32x4_t v[8];
-  if (loader) load_brick(X, ldx, k_end, b, k_begin + oct * 8, fbase, v);
-  for (int64_t kb = k_begin; kb < k_end; kb += kBK) {
-    __syncthreads();
-    if (loader) transpose_store(sdst, fgrp * 8, oct, v);
-    __syncthreads();
-    if (kb + kBK < k_end && loader) load_brick(X, ldx, k_end, b, kb + kBK + oct * 8, fbase, v);
+  unsigned ok = 0;
+  if (loader) {
+    ok = load_brick(X, ldx, k_end, b, k_begin + oct * 8, fbase, v);
+    transpose_store(sbuf(0, part), fgrp * 8, oct, v, ok);
+    if (nk > 1) ok = load_brick(X, ldx, k_end, b, k_begin + kBK + oct * 8, fbase, v);
+  }
+  __syncthreads();
+  for (int it = 0; it < nk; ++it) {
+    const int cur = it & 1;
+    const unsigned short* sA = sbuf(cur, 0);
+    const unsigned short* sB = diag ? sA : sbuf(cur, 1);
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       bf16x8_t af[4], bfr[2];
@@ -123,13 +158,19 @@ __global__ __launch_bounds__(kThreads) void syrk_bf16_kernel(
         af[a] = *(const bf16x8_t*)(sA + (wrow * 128 + a * 32 + lr) * kPitch + ks * 16 + lk * 8);
 #pragma unroll
       for (int c = 0; c < 2; ++c)
-        bfr[c] = *(const bf16x8_t*)(sBr + (wcol * 64 + c * 32 + lr) * kPitch + ks * 16 + lk * 8);
+        bfr[c] = *(const bf16x8_t*)(sB + (wcol * 64 + c * 32 + lr) * kPitch + ks * 16 + lk * 8);
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int c = 0; c < 2; ++c)
           acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[c], acc[a][c], 0, 0, 0);
     }
+    if (loader) {
+      if (it + 1 < nk) transpose_store(sbuf(cur ^ 1, part), fgrp * 8, oct, v, ok);
+      if (it + 2 < nk)
+        ok = load_brick(X, ldx, k_end, b, k_begin + (int64_t)(it + 2) * kBK + oct * 8, fbase, v);
+    }
+    __syncthreads();
   }
 
   if (splits == 1) {
@@ -162,9 +203,8 @@ __global__ __launch_bounds__(kThreads) void syrk_bf16_kernel(
 __global__ void syrk_reduce_kernel(float* __restrict__ H, const float* __restrict__ partials,
                                    int64_t b, int ntiles, int splits) {
   const int lin = blockIdx.x;
-  int ti = 0, rem = lin;
-  while (rem > ti) { rem -= ti + 1; ++ti; }
-  const int tj = rem;
+  int ti, tj;
+  tile_of(lin, (int)cdiv(b, kTile), ti, tj);
   const int64_t I0 = (int64_t)ti * kTile, J0 = (int64_t)tj * kTile;
   for (int e = threadIdx.x; e < kTile * kTile; e += blockDim.x) {
     const int r = e / kTile, c = e % kTile;
