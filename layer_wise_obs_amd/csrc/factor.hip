@@ -42,7 +42,8 @@ __device__ __forceinline__ int fresh_lane() {
 // diagonal). All steps are branch-free and fully unrolled so that the row
 // stays in registers.
 // Pass 1, right-looking Cholesky, lane i holds row i: step j needs column j of
-//   the (still symmetric) trailing block -- one LDS store per lane.
+//   the (still symmetric) trailing block -- lane c's register j, read with
+//   v_readlane.
 // Pass 2, forward substitution L X = I, lane j holds column j of X: row i of L
 //   is read as an LDS broadcast; no synchronisation inside the loop.
 __device__ __forceinline__ void wave_chol_inv64(const float* sm, float* sx, float* sl,
@@ -70,14 +71,12 @@ __device__ __forceinline__ void wave_chol_inv64(const float* sm, float* sx, floa
       lv = (ln > j) ? lv : 0.f;
       lv = (ln == j) ? sp : lv;
       sl[ln * kSP + j] = lv;
-      scol[ln] = rj;
-      wave_sync();
       static_for<j + 1, kHalf>([&](auto C) __attribute__((always_inline)) {
         constexpr int c = C;
-        reg[c] = fmaf(-f, scol[c], reg[c]);
+        reg[c] = fmaf(-f, bcast(rj, c), reg[c]);
       });
-      wave_sync();
     });
+    wave_sync();
   }
   {
     float x[kHalf];
@@ -190,7 +189,7 @@ __global__ __launch_bounds__(256) void diag_factor_kernel(float* __restrict__ S,
 
 // (2) Panel: blockIdx.x < nrow -> Lp for block row k+1+blockIdx.x;
 //            otherwise column tile (blockIdx.x - nrow) of row k: S[k,j] = X_kk S[k,j].
-__global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ S, int64_t b, int k,
+__global__ __launch_bounds__(256, 2) void panel_kernel(float* __restrict__ S, int64_t b, int k,
                                                     int nbk, int nrow, float* __restrict__ P) {
   __shared__ __attribute__((aligned(16))) float smem[kGemmLdsFloats];
   const int64_t k0 = (int64_t)k * kNb;
@@ -216,7 +215,7 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ S, int64
 }
 
 // (3) Trailing update over tiles (i, j), k < i < nblk, 0 <= j <= i.
-__global__ __launch_bounds__(256) void trailing_kernel(float* __restrict__ S, int64_t b, int k,
+__global__ __launch_bounds__(256, 2) void trailing_kernel(float* __restrict__ S, int64_t b, int k,
                                                        int nbk, int nblk,
                                                        const float* __restrict__ P) {
   __shared__ __attribute__((aligned(16))) float smem[kGemmLdsFloats];
@@ -228,21 +227,20 @@ __global__ __launch_bounds__(256) void trailing_kernel(float* __restrict__ S, in
   const int rows = (int)((b - i0) < kNb ? (b - i0) : kNb);
   const int cols = (int)((b - j0) < kNb ? (b - j0) : kNb);
   f32x16_t acc[2][2];
-  gemm_zero(acc);
+  float* C = S + i0 * b + j0;
+  // C = C - Lp_i B (column block k is overwritten: it starts from zero)
+  if (j == k) gemm_zero(acc);
+  else gemm_load_c(acc, C, b, rows, cols);
   const float* A = P + i0 * kNb;  // Lp_i, k-contig, ld kNb
   if (j <= k) {
     // B[kk][jj] = S[k0+kk][j0+jj]  (X row k for j < k, X_kk for j == k)
-    gemm_tile_f32<true, false>(A, kNb, rows, S + k0 * b + j0, b, cols, nbk, acc, smem);
+    gemm_tile_f32<true, false>(A, kNb, rows, S + k0 * b + j0, b, cols, nbk, acc, smem, true);
   } else {
     // B[kk][jj] = Lp_j[jj][kk]
-    gemm_tile_f32<true, true>(A, kNb, rows, P + j0 * kNb, kNb, cols, nbk, acc, smem);
+    gemm_tile_f32<true, true>(A, kNb, rows, P + j0 * kNb, kNb, cols, nbk, acc, smem, true);
   }
-  const bool overwrite = (j == k);
   gemm_foreach(acc, [&](int r, int c, float v) {
-    if (r < rows && c < cols) {
-      float* dst = S + (i0 + r) * b + j0 + c;
-      *dst = overwrite ? -v : (*dst - v);
-    }
+    if (r < rows && c < cols) C[(int64_t)r * b + c] = v;
   });
 }
 

@@ -31,7 +31,7 @@ __global__ void save_diag_blocks_kernel(const float* __restrict__ U, int64_t b, 
 }
 
 // One workgroup per (block J, 128-wide column tile of F).
-__global__ __launch_bounds__(256) void transform_rows_kernel(float* __restrict__ R, int64_t b,
+__global__ __launch_bounds__(256, 2) void transform_rows_kernel(float* __restrict__ R, int64_t b,
                                                              int64_t B, int nblk,
                                                              const float* __restrict__ Ublk) {
   __shared__ __attribute__((aligned(16))) float smem[kGemmLdsFloats];

@@ -47,16 +47,16 @@ __device__ __forceinline__ bool nm_pruned(const float* sc, int e, int n, int m) 
 }
 
 // Gauss-Jordan on 64 registers per lane: rows = lanes, steps j < nsys.
-// Returns x_lane = rhs_lane / pivot_lane for lanes < nsys.
+// Returns x_lane = rhs_lane / pivot_lane for lanes < nsys. The pivot row of step
+// j equals column j of the (still symmetric) trailing block, i.e. lane c's
+// register j, so it is broadcast with v_readlane: no LDS traffic and no waits.
 __device__ __forceinline__ float gauss_jordan64(float (&reg)[64], float rhs, int nsys,
-                                                float* scol) {
+                                                float* /*unused*/) {
   const int lane = threadIdx.x & 63;
   float piv = 1.f;
 #pragma unroll
   for (int j = 0; j < 64; ++j) {
     if (j < nsys) {
-      scol[lane] = reg[j];
-      wave_sync();
       const float p = bcast(reg[j], j);
       const float pinv = 1.f / p;
       const float rj = bcast(rhs, j);
@@ -64,8 +64,7 @@ __device__ __forceinline__ float gauss_jordan64(float (&reg)[64], float rhs, int
       if (lane == j) piv = p;
       rhs = fmaf(-f, rj, rhs);
 #pragma unroll
-      for (int c = j + 1; c < 64; ++c) reg[c] = fmaf(-f, scol[c], reg[c]);
-      wave_sync();
+      for (int c = j + 1; c < 64; ++c) reg[c] = fmaf(-f, bcast(reg[j], c), reg[c]);
     }
   }
   return rhs / piv;

@@ -16,7 +16,7 @@ namespace th {
 namespace {
 
 // W[row0:, col0:] -= Z[rows, 0:Bb] R[j0:j0+Bb, cols]; zero the pruned entries of J.
-__global__ __launch_bounds__(256) void update_kernel(float* __restrict__ W, int64_t c, int64_t b,
+__global__ __launch_bounds__(256, 2) void update_kernel(float* __restrict__ W, int64_t c, int64_t b,
                                                      int64_t j0, int Bb, int ldz,
                                                      int64_t col_end, int ncol_tiles,
                                                      const float* __restrict__ Z,
@@ -28,16 +28,16 @@ __global__ __launch_bounds__(256) void update_kernel(float* __restrict__ W, int6
   const int rows = (int)((c - row0) < 128 ? (c - row0) : 128);
   const int cols = (int)((col_end - col0) < 128 ? (col_end - col0) : 128);
   f32x16_t acc[2][2];
-  gemm_zero(acc);
-  gemm_tile_f32<true, false>(Z + row0 * ldz, ldz, rows, R + j0 * b + col0, b, cols, Bb, acc, smem);
+  float* C = W + row0 * b + col0;
+  gemm_load_c(acc, C, b, rows, cols);  // W tile, then W - Z R
+  gemm_tile_f32<true, false>(Z + row0 * ldz, ldz, rows, R + j0 * b + col0, b, cols, Bb, acc, smem,
+                             true);
   const int64_t jend = j0 + Bb;
   gemm_foreach(acc, [&](int r, int cc, float v) {
     if (r < rows && cc < cols) {
       const int64_t row = row0 + r, col = col0 + cc;
-      float* dst = W + row * b + col;
-      float nv = *dst - v;
-      if (col < jend && mask[row * b + col]) nv = 0.f;
-      *dst = nv;
+      if (col < jend && mask[row * b + col]) v = 0.f;
+      W[row * b + col] = v;
     }
   });
 }
@@ -81,7 +81,7 @@ __global__ void diff_kernel(const void* __restrict__ A, const void* __restrict__
 }
 
 // partial[tile] = sum over the tile of (D G) .* D   (G full symmetric, b x b)
-__global__ __launch_bounds__(256) void quadform_kernel(const float* __restrict__ D, int64_t c,
+__global__ __launch_bounds__(256, 2) void quadform_kernel(const float* __restrict__ D, int64_t c,
                                                        int64_t b, int ncol_tiles,
                                                        const float* __restrict__ G,
                                                        double* __restrict__ partials) {
