@@ -280,3 +280,28 @@ def test_reconstruction_error_from_activations():
     e, er = L.reconstruction_error(W.to(DEV), Wh.to(DEV), X=X.to(DEV))
     e_o, er_o = O.reconstruction_error(W, Wh, O.gram(X))
     assert abs(e - e_o) <= P.E_RTOL * e_o and abs(er - er_o) <= P.E_RTOL * er_o
+
+
+def test_prune_70b_like_unstructured_60():
+    _say("prune 60% unstructured, x100 outliers (70B-layer statistics, reduced size)")
+    W = synth.weights(256, 768, 0.015, 51, 100, torch.bfloat16)
+    X = synth.activations(4096, 768, 51, 1, 8, 100.0, False, torch.bfloat16)
+    _check_layer(W, X, sparsity=0.6, pattern=None, block=128)
+
+
+def test_prune_layers_sharing_one_hessian():
+    """q/k/v-like layers with one input: one H, three layers, each against the oracle."""
+    _say("three layers sharing one Hessian")
+    X = synth.activations(4096, 512, 52, 1, 5, 50.0, False, torch.bfloat16)
+    G = O.gram(X)
+    Hd = _gpu_hessian(X)
+    L.hessian_finalize(Hd, 0.01, True)
+    for li, c in enumerate((256, 256, 128)):
+        W = synth.weights(c, 512, 0.02, 52, 200 + li, torch.bfloat16)
+        trace = []
+        ora = O.prune_layer(W, G, sparsity=0.5, pattern=None, block=128, trace=trace)
+        _, Wg, mg, info = _run_gpu(W, H=Hd, sparsity=0.5, block=128)
+        rep = P.compare_pruned(Wg, mg, ora, 128, None, trace)
+        print(rep, flush=True)
+        assert rep["ok"], rep
+        assert info["pruned"] == ora["k_total"]
