@@ -50,6 +50,23 @@ def _ev_time(fn, reps, stream):
     return times
 
 
+def syrk_traffic():
+    """HBM-side bytes per syrk launch from the committed counter summary, or None
+    if the kernel source changed since the counters were taken."""
+    import hashlib
+    import re
+    prof = os.path.join(ROOT, "profiles", "syrk_bf16_down_proj_11008x262144_traffic.md")
+    try:
+        txt = open(prof).read()
+        d = json.loads(re.search(r"```json\n(.*?)\n```", txt, re.S).group(1))
+        src = open(os.path.join(ROOT, d["source"]), "rb").read()
+        if hashlib.sha256(src).hexdigest() != d["source_sha256"]:
+            return None
+        return float(d["traffic_bytes_per_launch"])
+    except Exception:
+        return None
+
+
 def cpu_baseline(X, W, c, b, n, pattern, block, lam_rel):
     """fp64 oracle on a bounded sample, scaled to seconds per layer.
 
@@ -215,7 +232,7 @@ def main():
                                f"lambda {lam_rel} relative"},
         "roofline": {"bound": "mfma", "kernel": "syrk_bf16_kernel", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": None, "launch_ms": syrk_avg,
+                     "traffic": syrk_traffic(), "launch_ms": syrk_avg,
                      "algorithmic": f"n*b*(b+1) = {syrk_flops:.4g} flop per launch"},
         "extra": {
             "hessian_tflops": achieved,
