@@ -13,9 +13,13 @@
 // transposes them in registers with v_perm_b32 and stores 8 feature rows of 8
 // tokens (16 bytes each) into LDS, where the MFMA operands are read as 16-byte
 // K-contiguous vectors. The LDS row pitch of 72 bf16 (36 dwords) makes both the
-// stores and the operand reads bank-conflict free. Two LDS stages (144 KB) and a
-// register stage give one barrier per 64 tokens, with each stage's global loads
-// in flight during a full stage of MFMA work.
+// stores and the operand reads bank-conflict free. Two LDS stages (144 KB) give one
+// barrier per 64 tokens; inside a stage the operand fragments are double-buffered
+// in registers and the next stage's transpose-store is split into four parts
+// interleaved with the four k-substeps of MFMAs. The loop body is branch-free
+// (clamped loads, stores into the idle buffer), so the compiler can interleave
+// LDS traffic, VALU transposes and MFMAs of one wave, and the two waves of a
+// SIMD no longer alternate between an MFMA phase and a store phase.
 #include "common.h"
 
 namespace th {
@@ -46,6 +50,22 @@ __device__ __forceinline__ unsigned load_brick(const unsigned short* __restrict_
     ok |= (fok && t < t_valid) ? (1u << i) : 0u;
   }
   return ok;
+}
+
+// Part d (0..3) of transpose_store: features 2d and 2d+1 of the brick.
+__device__ __forceinline__ void transpose_store_part(unsigned short* __restrict__ s, int frow0,
+                                                     int oct, const u32x4_t (&v)[8], unsigned ok,
+                                                     int d) {
+  u32x4_t lo, hi;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const unsigned a = ((ok >> (2 * p)) & 1u) ? v[2 * p][d] : 0u;
+    const unsigned c = ((ok >> (2 * p + 1)) & 1u) ? v[2 * p + 1][d] : 0u;
+    lo[p] = __builtin_amdgcn_perm(c, a, 0x05040100u);
+    hi[p] = __builtin_amdgcn_perm(c, a, 0x07060302u);
+  }
+  *(u32x4_t*)(s + (frow0 + 2 * d) * kPitch + oct * 8) = lo;
+  *(u32x4_t*)(s + (frow0 + 2 * d + 1) * kPitch + oct * 8) = hi;
 }
 
 // 8 tokens x 8 features (v[token].dword[f/2]) -> 8 features x 8 tokens; rows
@@ -119,7 +139,6 @@ __global__ __launch_bounds__(kThreads) void syrk_bf16_kernel(
   const int part = tid >> 8;             // 0: A panel, 1: B panel
   const int q = tid & 255;
   const int oct = q & 7, fgrp = q >> 3;  // 8 token octets x 32 feature groups
-  const bool loader = diag ? (part == 0) : true;
   const int64_t fbase = (part == 0 ? I0 : J0) + fgrp * 8;
 
   const int64_t k_begin = (int64_t)split * tok_per_split;
@@ -140,36 +159,51 @@ __global__ __launch_bounds__(kThreads) void syrk_bf16_kernel(
   auto sbuf = [&](int stage, int panel) { return smem + (stage * 2 + panel) * (kTile * kPitch); };
   u32x4_t v[8];
   unsigned ok = 0;
-  if (loader) {
-    ok = load_brick(X, ldx, k_end, b, k_begin + oct * 8, fbase, v);
-    transpose_store(sbuf(0, part), fgrp * 8, oct, v, ok);
-    if (nk > 1) ok = load_brick(X, ldx, k_end, b, k_begin + kBK + oct * 8, fbase, v);
-  }
+  ok = load_brick(X, ldx, k_end, b, k_begin + oct * 8, fbase, v);
+  transpose_store(sbuf(0, part), fgrp * 8, oct, v, ok);
+  ok = load_brick(X, ldx, k_end, b, k_begin + kBK + oct * 8, fbase, v);
   __syncthreads();
   for (int it = 0; it < nk; ++it) {
     const int cur = it & 1;
     const unsigned short* sA = sbuf(cur, 0);
     const unsigned short* sB = diag ? sA : sbuf(cur, 1);
+    // Every thread loads and stores every iteration (branch-free loop body): on
+    // diagonal tiles the second half of the threads fills the unused B buffer,
+    // and past the last stage the clamped loads and stores land in the buffer
+    // that is no longer read.
+    unsigned short* snext = sbuf(cur ^ 1, part);
+    // Operand fragments are double-buffered in registers: the reads for
+    // k-substep ks+1 are issued before the MFMAs of ks, and a quarter of the
+    // next stage's transpose-store follows each substep's MFMAs.
+    bf16x8_t af[2][4], bfr[2][2];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      af[0][a] = *(const bf16x8_t*)(sA + (wrow * 128 + a * 32 + lr) * kPitch + lk * 8);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      bfr[0][c] = *(const bf16x8_t*)(sB + (wcol * 64 + c * 32 + lr) * kPitch + lk * 8);
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
-      bf16x8_t af[4], bfr[2];
+      const int cb = ks & 1, nb = cb ^ 1;
+      if (ks + 1 < kBK / 16) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-        af[a] = *(const bf16x8_t*)(sA + (wrow * 128 + a * 32 + lr) * kPitch + ks * 16 + lk * 8);
+        for (int a = 0; a < 4; ++a)
+          af[nb][a] = *(const bf16x8_t*)(sA + (wrow * 128 + a * 32 + lr) * kPitch + (ks + 1) * 16 +
+                                         lk * 8);
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-        bfr[c] = *(const bf16x8_t*)(sB + (wcol * 64 + c * 32 + lr) * kPitch + ks * 16 + lk * 8);
+        for (int c = 0; c < 2; ++c)
+          bfr[nb][c] = *(const bf16x8_t*)(sB + (wcol * 64 + c * 32 + lr) * kPitch +
+                                          (ks + 1) * 16 + lk * 8);
+      }
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[c], acc[a][c], 0, 0, 0);
+          acc[a][c] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][a], bfr[cb][c], acc[a][c], 0, 0, 0);
+      transpose_store_part(snext, fgrp * 8, oct, v, ok, ks);
     }
-    if (loader) {
-      if (it + 1 < nk) transpose_store(sbuf(cur ^ 1, part), fgrp * 8, oct, v, ok);
-      if (it + 2 < nk)
-        ok = load_brick(X, ldx, k_end, b, k_begin + (int64_t)(it + 2) * kBK + oct * 8, fbase, v);
-    }
+    ok = load_brick(X, ldx, k_end, b, k_begin + (int64_t)(it + 2) * kBK + oct * 8, fbase, v);
     __syncthreads();
   }
 
