@@ -26,7 +26,10 @@ namespace th {
 namespace {
 
 constexpr int kNb = 128;
-constexpr int kHalf = 64;
+constexpr int kBase = 32;  // block-column width of the sweep inside the diagonal block
+constexpr int kBase16 = 16;  // register base case
+constexpr int kPP16 = kBase16 + 1;
+constexpr int kPP = kBase + 1;  // LDS pitch of a 32 x 32 panel tile
 constexpr int kSP = kNb + 1;  // LDS pitch (floats) of the 128 x 128 diagonal block
 
 // Copy of the lane id that the compiler cannot hoist or share across the
@@ -37,152 +40,265 @@ __device__ __forceinline__ int fresh_lane() {
   return l;
 }
 
-// One wave, 64 x 64 SPD block A (lower triangle read from sm, pitch kSP):
-// L = chol(A) into sl and X = L^-1 into sx (both pitch kSP, zeros above the
-// diagonal). All steps are branch-free and fully unrolled so that the row
-// stays in registers.
-// Pass 1, right-looking Cholesky, lane i holds row i: step j needs column j of
-//   the (still symmetric) trailing block -- lane c's register j, read with
-//   v_readlane.
-// Pass 2, forward substitution L X = I, lane j holds column j of X: row i of L
-//   is read as an LDS broadcast; no synchronisation inside the loop.
-__device__ __forceinline__ void wave_chol_inv64(const float* sm, float* sx, float* sl,
-                                                float* scol, int* bad) {
-  int flag = 0;
-  {
-    const int lane = threadIdx.x & 63;
-    float reg[kHalf];
-    static_for<0, kHalf>([&](auto C) __attribute__((always_inline)) {
-      constexpr int c = C;
-      reg[c] = (c <= lane) ? sm[lane * kSP + c] : sm[c * kSP + lane];
-    });
-    static_for<0, kHalf>([&](auto J) __attribute__((always_inline)) {
-      constexpr int j = J;
-      const int ln = fresh_lane();
-      const float p0 = bcast(reg[j], j);
-      const bool ok = (p0 > 0.f) && (p0 < 3.0e38f);
-      flag |= ok ? 0 : 1;
-      const float p = ok ? p0 : 1.f;
-      const float sp = __builtin_sqrtf(p);
-      const float rs = __builtin_amdgcn_rcpf(sp);
-      const float rj = reg[j];
-      const float f = (ln > j) ? rj * (rs * rs) : 0.f;
-      float lv = rj * rs;
-      lv = (ln > j) ? lv : 0.f;
-      lv = (ln == j) ? sp : lv;
-      sl[ln * kSP + j] = lv;
-      static_for<j + 1, kHalf>([&](auto C) __attribute__((always_inline)) {
-        constexpr int c = C;
-        reg[c] = fmaf(-f, bcast(rj, c), reg[c]);
-      });
-    });
-    wave_sync();
-  }
-  {
-    float x[kHalf];
-    static_for<0, kHalf>([&](auto I) __attribute__((always_inline)) {
-      constexpr int i = I;
-      const int ln = fresh_lane();
-      float acc = (ln == i) ? 1.f : 0.f;
-      static_for<0, i>([&](auto M) __attribute__((always_inline)) {
-        constexpr int m = M;
-        acc = fmaf(-sl[i * kSP + m], x[m], acc);
-      });
-      x[i] = acc * __builtin_amdgcn_rcpf(sl[i * kSP + i]);
-    });
-    const int lane = threadIdx.x & 63;
-    static_for<0, kHalf>([&](auto I) __attribute__((always_inline)) {
-      constexpr int i = I;
-      sx[i * kSP + lane] = (i >= lane) ? x[i] : 0.f;
-    });
-  }
-  if (flag && (threadIdx.x & 63) == 0) *bad = 1;
-}
-
-// 32 x 32 tile (this wave) of sum_m A(i, m) B(m, j), m < K, operands in LDS.
-template <class FA, class FB>
-__device__ __forceinline__ f32x16_t lds_mfma_tile(FA&& a, FB&& bop, int K) {
-  const int lane = threadIdx.x & 63;
-  const int i = lane & 31, kk = lane >> 5;
-  f32x16_t acc;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  for (int m = 0; m < K; m += 2)
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a(i, m + kk), bop(m + kk, i), acc, 0, 0, 0);
-  return acc;
-}
-
+// Accumulator layout of one 32x32 MFMA block (lane l, register q):
+// row 8*(q/4) + 4*(l/32) + (q%4), column l%32.
 template <class F>
 __device__ __forceinline__ void tile_foreach(const f32x16_t& acc, F&& f) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) f(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), lane & 31, acc[r]);
+  for (int q = 0; q < 16; ++q) f(8 * (q >> 2) + 4 * (lane >> 5) + (q & 3), lane & 31, acc[q]);
 }
 
-// (1) Diagonal block: X_kk = L_kk^-1 with A_kk = L_kk L_kk^T, fp32, 256 threads.
-// Split 2 x 2 into 64-blocks:  X11 = chol_inv(A11);  L21 = A21 X11^T;
-// A22 -= L21 L21^T;  X22 = chol_inv(A22);  X21 = -X22 (L21 X11).
+template <class F>
+__device__ __forceinline__ void tile_foreach_idx(f32x16_t& acc, F&& f) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) f(q, 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3), lane & 31);
+}
+
+// One wave, 16 x 16 SPD block `a` (lower triangle, pitch lda): X = L^-1 with
+// a = L L^T written to `x` (pitch ldx, zeros above the diagonal; x may be a).
+// Lanes 16..63 shadow lanes 0..15. Branch-free and fully unrolled:
+// Pass 1, right-looking Cholesky, lane i holds row i; step j reads column j of
+//   the (symmetric) trailing block from lane c's register j with v_readlane.
+//   Lane i keeps L[i][j] in Lc[j].
+// Pass 2, right-looking forward substitution L X = I, lane c holds column c of
+//   X; L[i][m] is lane i's Lc[m], read with v_readlane.
+__device__ __forceinline__ void wave_chol_inv16(const float* a, int lda, float* x, int ldx,
+                                                int& flag) {
+  float Lc[kBase16], rsv[kBase16];
+  {
+    const int row = threadIdx.x & 15;
+    float reg[kBase16];
+    static_for<0, kBase16>([&](auto C) __attribute__((always_inline)) {
+      constexpr int c = C;
+      reg[c] = (c <= row) ? a[row * lda + c] : a[c * lda + row];
+    });
+    static_for<0, kBase16>([&](auto J) __attribute__((always_inline)) {
+      constexpr int j = J;
+      const int ln = fresh_lane() & 15;
+      const float p0 = bcast(reg[j], j);
+      const bool ok = (p0 > 0.f) && (p0 < 3.0e38f);
+      flag |= ok ? 0 : 1;
+      const float p = ok ? p0 : 1.f;
+      const float rs = __builtin_amdgcn_rsqf(p);
+      const float sp = p * rs;
+      rsv[j] = rs;
+      const float rj = reg[j];
+      const float f = (ln > j) ? rj * (rs * rs) : 0.f;
+      float lv = rj * rs;
+      lv = (ln > j) ? lv : 0.f;
+      Lc[j] = (ln == j) ? sp : lv;
+      static_for<j + 1, kBase16>([&](auto C) __attribute__((always_inline)) {
+        constexpr int c = C;
+        reg[c] = fmaf(-f, bcast(rj, c), reg[c]);
+      });
+    });
+  }
+  const int col = fresh_lane() & 15;
+  float acc[kBase16];
+  static_for<0, kBase16>([&](auto I) __attribute__((always_inline)) {
+    constexpr int i = I;
+    acc[i] = (col == i) ? 1.f : 0.f;
+  });
+  static_for<0, kBase16>([&](auto M) __attribute__((always_inline)) {
+    constexpr int m = M;
+    const float xm = acc[m] * rsv[m];
+    acc[m] = xm;
+    static_for<m + 1, kBase16>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = I;
+      acc[i] = fmaf(-bcast(Lc[m], i), xm, acc[i]);
+    });
+  });
+  wave_sync();  // every lane has read `a` before `x` (possibly the same) is written
+  static_for<0, kBase16>([&](auto I) __attribute__((always_inline)) {
+    constexpr int i = I;
+    x[i * ldx + col] = (i >= col) ? acc[i] : 0.f;
+  });
+  wave_sync();
+}
+
+// 16 x 16 = acc + sum_k A(i, k) B(k, j), k < 16, on v_mfma_f32_16x16x4_f32
+// (A: lane l holds A[l%16][l/16]; B: B[l/16][l%16]; D register r of lane l is
+// D[4*(l/16) + r][l%16]).
+template <class FA, class FB>
+__device__ __forceinline__ f32x4_t mfma16(f32x4_t acc, FA&& a, FB&& bop) {
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15, kq = lane >> 4;
+#pragma unroll
+  for (int k0 = 0; k0 < kBase16; k0 += 4)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(i, k0 + kq), bop(k0 + kq, i), acc, 0, 0, 0);
+  return acc;
+}
+
+template <class F>
+__device__ __forceinline__ void foreach16(const f32x4_t& acc, F&& f) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) f(4 * (lane >> 4) + r, lane & 15, acc[r]);
+}
+
+// One wave, 32 x 32 SPD block d (lower triangle, pitch kSP) -> X = L^-1 in place
+// (zeros above the diagonal), split 2 x 2 into 16-blocks:
+//   X11 = chol_inv(A11);  L21 = A21 X11^T;  A22 -= L21 L21^T;  X22 = chol_inv(A22);
+//   X21 = -X22 (L21 X11).
+// tmp: 16 x kPP16 floats of LDS scratch.
+__device__ __forceinline__ void wave_chol_inv32(float* d, float* tmp, int* bad) {
+  int flag = 0;
+  float* A21 = d + 16 * kSP;
+  float* A22 = d + 16 * kSP + 16;
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  wave_chol_inv16(d, kSP, d, kSP, flag);
+  {  // L21 = A21 X11^T over A21
+    f32x4_t acc = mfma16(zero, [&](int i, int k) { return A21[i * kSP + k]; },
+                         [&](int k, int j) { return d[j * kSP + k]; });
+    wave_sync();
+    foreach16(acc, [&](int i, int j, float v) { A21[i * kSP + j] = v; });
+    wave_sync();
+  }
+  {  // A22 -= L21 L21^T
+    f32x4_t acc;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = -A22[(4 * (lane >> 4) + r) * kSP + (lane & 15)];
+    acc = mfma16(acc, [&](int i, int k) { return A21[i * kSP + k]; },
+                 [&](int k, int j) { return A21[j * kSP + k]; });
+    foreach16(acc, [&](int i, int j, float v) { A22[i * kSP + j] = -v; });
+    wave_sync();
+  }
+  wave_chol_inv16(A22, kSP, A22, kSP, flag);
+  {  // T = L21 X11 -> tmp
+    f32x4_t acc = mfma16(zero, [&](int i, int k) { return A21[i * kSP + k]; },
+                         [&](int k, int j) { return d[k * kSP + j]; });
+    foreach16(acc, [&](int i, int j, float v) { tmp[i * kPP16 + j] = v; });
+    wave_sync();
+  }
+  {  // X21 = -X22 T over A21; the upper-right block of X is zero
+    f32x4_t acc = mfma16(zero, [&](int i, int k) { return A22[i * kSP + k]; },
+                         [&](int k, int j) { return tmp[k * kPP16 + j]; });
+    foreach16(acc, [&](int i, int j, float v) {
+      A21[i * kSP + j] = -v;
+      d[i * kSP + 16 + j] = 0.f;
+    });
+    wave_sync();
+  }
+  if (flag && (threadIdx.x & 63) == 0) *bad = 1;
+}
+
+// 32 x 32 tile (this wave) of init - sum_m A(i, m) B(m, j), m < 32, operands in LDS.
+template <class FA, class FB>
+__device__ __forceinline__ f32x16_t lds_mfma_tile32(f32x16_t acc, FA&& a, FB&& bop) {
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 31, kk = lane >> 5;
+#pragma unroll
+  for (int m = 0; m < kBase; m += 2)
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(-a(i, m + kk), bop(m + kk, i), acc, 0, 0, 0);
+  return acc;
+}
+
+// (1) Diagonal block: X_kk = L_kk^-1 with A_kk = L_kk L_kk^T, fp32, 256 threads,
+// the whole block in LDS. The same right-looking in-place sweep as the layer's
+// factorisation, over four 32-wide block columns t = 0..3:
+//   base:     X_tt = chol_inv(A_tt)                       (one wave)
+//   panel:    Lp_i = A_it X_tt^T (i > t);  A_tj = X_tt A_tj (j < t)
+//   trailing: A_ij -= Lp_i [ A_tj | X_tt (overwrite) | Lp_j^T ]  (j < t | j = t | j > t)
+// The base case of step t + 1 needs only tile (t+1, t+1) of step t's trailing
+// update, so wave 0 updates that tile and factors it while the other waves
+// finish the step.
 // A block narrower than 128 (the last one) is padded with the identity.
 __global__ __launch_bounds__(256) void diag_factor_kernel(float* __restrict__ S, int64_t b,
                                                           int64_t k0, int nbk, DevState* st) {
-  __shared__ float sA[kNb * kSP];
-  __shared__ float sX[kNb * kSP];
-  __shared__ float scol[kHalf];
+  __shared__ float sS[kNb * kSP];
+  __shared__ float sP[3 * kBase * kPP];
+  __shared__ float sT[kBase16 * kPP16];
   __shared__ int bad;
   const int tid = threadIdx.x, wave = tid >> 6;
   if (tid == 0) bad = 0;
-  for (int e = tid; e < kNb * kNb; e += blockDim.x) {
-    const int i = e / kNb, j = e % kNb;
-    float v = (i == j) ? 1.f : 0.f;
-    if (i < nbk && j < nbk && j <= i) v = S[(k0 + i) * b + k0 + j];
-    sA[i * kSP + j] = v;
+  {  // all 64 loads of a thread in flight at once (addresses clamped into the block)
+    constexpr int kPer = kNb * kNb / 256;
+    float v[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int idx = e * 256 + tid, i = idx >> 7, j = idx & (kNb - 1);
+      const int ii = i < nbk ? i : nbk - 1, jj = j < nbk ? j : nbk - 1;
+      v[e] = S[(k0 + ii) * b + k0 + jj];
+    }
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int idx = e * 256 + tid, i = idx >> 7, j = idx & (kNb - 1);
+      const float pad = (i == j) ? 1.f : 0.f;
+      sS[i * kSP + j] = (i < nbk && j < nbk && j <= i) ? v[e] : pad;
+    }
   }
   __syncthreads();
-  // L11 scratch: the (not yet needed) rows 64.. of sX, columns 0..63
-  if (wave == 0) wave_chol_inv64(sA, sX, sX + kHalf * kSP, scol, &bad);
+  auto blk = [&](int i, int j) { return sS + (kBase * i) * kSP + kBase * j; };
+  // trailing tile q of step t: (i, j), t < i < 4, 0 <= j <= i, row-major order
+  auto trailing_tile = [&](int t, int q) {
+    int i = t + 1, rem = q;
+    while (rem > i) { rem -= i + 1; ++i; }
+    const int j = rem;
+    float* C = blk(i, j);
+    const float* Lpi = sP + (i - 1) * kBase * kPP;
+    f32x16_t acc;
+    tile_foreach_idx(acc, [&](int q2, int rr, int cc) {
+      acc[q2] = (j == t) ? 0.f : C[rr * kSP + cc];
+    });
+    if (j <= t) {
+      const float* Btj = blk(t, j);
+      acc = lds_mfma_tile32(
+          acc, [&](int ii, int m) { return Lpi[ii * kPP + m]; },
+          [&](int m, int jj) { return Btj[m * kSP + jj]; });
+    } else {
+      const float* Lpj = sP + (j - 1) * kBase * kPP;
+      acc = lds_mfma_tile32(
+          acc, [&](int ii, int m) { return Lpi[ii * kPP + m]; },
+          [&](int m, int jj) { return Lpj[jj * kPP + m]; });
+    }
+    tile_foreach(acc, [&](int rr, int cc, float x) { C[rr * kSP + cc] = x; });
+  };
+  if (wave == 0) wave_chol_inv32(blk(0, 0), sT, &bad);
   __syncthreads();
-  const int ti = wave >> 1, tj = wave & 1;
-  float* A21 = sA + kHalf * kSP;         // rows 64.., cols 0..63
-  float* A22 = sA + kHalf * kSP + kHalf;  // rows 64.., cols 64..
-  {  // L21 = A21 X11^T  (stored over A21)
-    f32x16_t acc = lds_mfma_tile(
-        [&](int i, int m) { return A21[(32 * ti + i) * kSP + m]; },
-        [&](int m, int j) { return sX[(32 * tj + j) * kSP + m]; }, kHalf);
+  for (int t = 0; t < 4; ++t) {
+    const float* Dtt = blk(t, t);
+    if (wave < 3) {  // 3 - t rows of Lp, t blocks of row t
+      f32x16_t acc;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+      if (wave < 3 - t) {
+        const int i = t + 1 + wave;
+        const float* Ait = blk(i, t);
+        acc = lds_mfma_tile32(
+            acc, [&](int ii, int m) { return -Ait[ii * kSP + m]; },
+            [&](int m, int jj) { return Dtt[jj * kSP + m]; });
+        float* P = sP + (i - 1) * kBase * kPP;
+        tile_foreach(acc, [&](int rr, int cc, float x) { P[rr * kPP + cc] = x; });
+      } else {
+        float* Atj = blk(t, wave - (3 - t));
+        acc = lds_mfma_tile32(
+            acc, [&](int ii, int m) { return -Dtt[ii * kSP + m]; },
+            [&](int m, int jj) { return Atj[m * kSP + jj]; });
+        tile_foreach(acc, [&](int rr, int cc, float x) { Atj[rr * kSP + cc] = x; });
+      }
+    }
     __syncthreads();
-    tile_foreach(acc, [&](int r, int c, float v) { A21[(32 * ti + r) * kSP + 32 * tj + c] = v; });
+    if (t == 3) break;
+    // Lookahead: wave 0 updates the next diagonal block (tile t + 1 of the
+    // step) and factors it while waves 1..3 update the other tiles.
+    const int ntile = (4 + t + 2) * (3 - t) / 2;
+    if (wave == 0) {
+      trailing_tile(t, t + 1);
+      wave_sync();
+      wave_chol_inv32(blk(t + 1, t + 1), sT, &bad);
+    } else {
+      for (int u = wave - 1; u < ntile - 1; u += 3) trailing_tile(t, u <= t ? u : u + 1);
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  {  // A22 -= L21 L21^T
-    f32x16_t acc = lds_mfma_tile(
-        [&](int i, int m) { return A21[(32 * ti + i) * kSP + m]; },
-        [&](int m, int j) { return A21[(32 * tj + j) * kSP + m]; }, kHalf);
-    tile_foreach(acc, [&](int r, int c, float v) { A22[(32 * ti + r) * kSP + 32 * tj + c] -= v; });
-  }
-  __syncthreads();
-  float* X22 = sX + kHalf * kSP + kHalf;
-  // L22 scratch: rows 64.. of sX, columns 0..63 (T is written after this)
-  if (wave == 0) wave_chol_inv64(A22, X22, sX + kHalf * kSP, scol, &bad);
-  __syncthreads();
-  float* T = sX + kHalf * kSP;  // rows 64.., cols 0..63 of sX: T = L21 X11
-  {
-    f32x16_t acc = lds_mfma_tile(
-        [&](int i, int m) { return A21[(32 * ti + i) * kSP + m]; },
-        [&](int m, int j) { return sX[m * kSP + 32 * tj + j]; }, kHalf);
-    tile_foreach(acc, [&](int r, int c, float v) { T[(32 * ti + r) * kSP + 32 * tj + c] = v; });
-  }
-  __syncthreads();
-  {  // X21 = -X22 T  (stored over A21)
-    f32x16_t acc = lds_mfma_tile(
-        [&](int i, int m) { return X22[(32 * ti + i) * kSP + m]; },
-        [&](int m, int j) { return T[m * kSP + 32 * tj + j]; }, kHalf);
-    tile_foreach(acc, [&](int r, int c, float v) { A21[(32 * ti + r) * kSP + 32 * tj + c] = -v; });
-  }
-  __syncthreads();
-  for (int e = tid; e < nbk * nbk; e += blockDim.x) {
-    const int i = e / nbk, j = e % nbk;
-    float v = 0.f;
-    if (j <= i) v = (i >= kHalf && j < kHalf) ? sA[i * kSP + j] : sX[i * kSP + j];
-    S[(k0 + i) * b + k0 + j] = v;
+#pragma unroll 16
+  for (int e = 0; e < kNb * kNb / 256; ++e) {
+    const int idx = e * 256 + tid, i = idx >> 7, j = idx & (kNb - 1);
+    const float v = (j <= i) ? sS[i * kSP + j] : 0.f;
+    if (i < nbk && j < nbk) S[(k0 + i) * b + k0 + j] = v;
   }
   if (tid == 0 && bad) st->not_spd = 1;
 }
