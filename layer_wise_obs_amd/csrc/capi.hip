@@ -7,7 +7,8 @@
 //   block loop (left to right, "Pruning LLMs with Thanos", section "The scaling
 //   problem, and what SparseGPT changes"):
 //       unstructured: threshold by radix select over F, solve, update W[:, F]
-//       N:M:          select + solve in one kernel, update W[:, F]
+//       N:M:          select + solve in one kernel, update W[:, J .. end of the
+//                     super-block]; the rest of F once per super-block
 //   output:             What cast back to the input dtype
 // The budget, the threshold and every count stay on the device; the host
 // synchronises once, at the end, to read the status flags.
@@ -72,6 +73,18 @@ struct PruneLayout {
   size_t bytes;
 };
 
+// N:M masks depend only on the block's own columns, so a block's compensation
+// of columns beyond its super-block (kSuperBlocks consecutive blocks) can wait:
+// it is applied once per super-block as one GEMM with K = kSuperBlocks * B.
+constexpr int64_t kSuperBlocks = 8;
+
+int64_t z_pitch(int64_t b, const th_prune_params* p) {
+  if (p->pattern.kind != TH_NM) return p->block;
+  const int64_t full = cdiv(b, p->block) * p->block;
+  const int64_t sb = kSuperBlocks * p->block;
+  return full < sb ? full : sb;
+}
+
 bool needs_complement(const th_prune_params* p) {
   if (p->block <= 64) return false;
   if (p->pattern.kind == TH_UNSTRUCTURED) return true;
@@ -94,7 +107,7 @@ PruneLayout layout_prune(void* ws, int64_t c, int64_t b, int64_t n, bool have_x,
   const bool unstr = p->pattern.kind == TH_UNSTRUCTURED;
   L.D = (unstr && p->score == TH_SCORE_OBS) ? cv.take<float>((size_t)nblk * b) : nullptr;
   L.gW = (p->score == TH_SCORE_WANDA) ? cv.take<float>((size_t)b) : nullptr;
-  L.Z = cv.take<float>((size_t)c * B);
+  L.Z = cv.take<float>((size_t)c * z_pitch(b, p));
   L.Wf = need_wf ? cv.take<float>((size_t)c * b) : nullptr;
   L.mask = need_mask ? cv.take<uint8_t>((size_t)c * b) : nullptr;
   L.syrk_part = nullptr;
@@ -268,11 +281,13 @@ th_status th_prune_layer(void* W, th_dtype wdt, int64_t c, int64_t b, const void
   if (L.Nblk) TH_HIP(launch_block_inverses(L.Ublk, b, B, L.Nblk, s), "block inverses");
   TH_HIP(launch_transform_rows(L.R, b, B, L.Ublk, s), "transform rows");
 
+  const int64_t ldz = z_pitch(b, p);
   for (int64_t blk = 0; blk < nblk; ++blk) {
     const int64_t j0 = blk * B;
     const int64_t Bb = (b - j0) < B ? (b - j0) : B;
     const float* Nb = L.Nblk ? L.Nblk + blk * B * B : nullptr;
     if (unstr) {
+      // the global selection scores every active column, so W[:, F] is updated in full
       const float* g = obs ? L.D + blk * b : L.gW;
       TH_HIP(launch_select_init(L.st, 0, blk == 0, (long long)(c * (b - j0)), s), "select init");
       for (int pass = 0; pass < 6; ++pass) {
@@ -282,12 +297,20 @@ th_status th_prune_layer(void* W, th_dtype wdt, int64_t c, int64_t b, const void
       TH_HIP(launch_solve_unstructured(Wf, c, b, j0, B, L.R, Nb, g, obs ? 1 : 0, L.Z, mask, L.st,
                                        L.counts + blk, s),
              "solve");
+      TH_HIP(launch_update(Wf, c, b, j0, Bb, B, j0, b, L.Z, L.R, mask, j0, Bb, s), "update");
     } else {
+      const int64_t per = ldz / B;  // blocks per super-block
+      const int64_t sb0 = (blk / per) * ldz;
+      const int64_t s1 = (sb0 + ldz) < b ? (sb0 + ldz) : b;
+      float* Zb = L.Z + (blk % per) * B;
       TH_HIP(launch_solve_nm(Wf, c, b, j0, B, p->pattern.n, p->pattern.m, L.R, obs ? nullptr : L.gW,
-                             Nb, L.Z, mask, L.st, L.counts + blk, s),
+                             Nb, Zb, ldz, mask, L.st, L.counts + blk, s),
              "solve");
+      TH_HIP(launch_update(Wf, c, b, j0, Bb, ldz, j0, s1, Zb, L.R, mask, j0, Bb, s), "update");
+      if (j0 + Bb == s1 && s1 < b)  // last block of the super-block: the deferred columns
+        TH_HIP(launch_update(Wf, c, b, sb0, s1 - sb0, ldz, s1, b, L.Z, L.R, mask, 0, 0, s),
+               "deferred update");
     }
-    TH_HIP(launch_update(Wf, c, b, j0, Bb, B, b, L.Z, L.R, mask, s), "update");
   }
   TH_HIP(launch_from_f32(Wf, c * b, wdt, W, s), "cast back");
 

@@ -127,7 +127,7 @@ hipError_t launch_select_pick(DevState* st, hipStream_t s);
 // solve.hip
 hipError_t launch_solve_nm(const float* W, int64_t c, int64_t b, int64_t j0, int64_t B, int n,
                            int m, const float* R, const float* gW, const float* Nblk, float* Z,
-                           uint8_t* mask, DevState* st, unsigned long long* blk_count,
+                           int64_t ldz, uint8_t* mask, DevState* st, unsigned long long* blk_count,
                            hipStream_t s);
 hipError_t launch_solve_unstructured(const float* W, int64_t c, int64_t b, int64_t j0, int64_t B,
                                      const float* R, const float* Nblk, const float* g, int obs,
@@ -141,9 +141,11 @@ hipError_t launch_debug_mask_from_scores(const float* scores, int64_t c, int64_t
                                          hipStream_t s);
 
 // update.hip
-hipError_t launch_update(float* W, int64_t c, int64_t b, int64_t j0, int64_t Bb, int64_t ldz,
-                         int64_t col_end, const float* Z, const float* R, const uint8_t* mask,
-                         hipStream_t s);
+// W[:, col0:col_end) -= Z[:, 0:K] R[r0:r0+K, col0:col_end) (Z pitch ldz); entries of
+// columns [mask_j0, mask_j0 + mask_w) with mask set are then zeroed.
+hipError_t launch_update(float* W, int64_t c, int64_t b, int64_t r0, int64_t K, int64_t ldz,
+                         int64_t col0, int64_t col_end, const float* Z, const float* R,
+                         const uint8_t* mask, int64_t mask_j0, int64_t mask_w, hipStream_t s);
 hipError_t launch_to_f32(const void* src, th_dtype dt, int64_t count, float* dst,
                          DevState* st, hipStream_t s);
 hipError_t launch_from_f32(const float* src, int64_t count, th_dtype dt, void* dst,

@@ -31,7 +31,10 @@ namespace th {
 namespace {
 
 constexpr int kWaves = 8;
-constexpr int kMP = kMaxBlock + 1;  // LDS pitch of M / N
+// M (or N) in LDS, 128 x 128 with an XOR swizzle: entry (r, q) sits at
+// r * 128 + (q ^ (r & 31)), so the per-lane row gathers of the solve (one
+// column, 64 different rows) hit distinct banks without padding the pitch.
+__device__ __forceinline__ int mat_idx(int r, int q) { return r * kMaxBlock + (q ^ (r & 31)); }
 
 // Rank of entry e in its aligned group of m among scores sc[] (ties: lower column first).
 __device__ __forceinline__ bool nm_pruned(const float* sc, int e, int n, int m) {
@@ -46,61 +49,83 @@ __device__ __forceinline__ bool nm_pruned(const float* sc, int e, int n, int m) 
   return rank < m - n;
 }
 
-// Gauss-Jordan on 64 registers per lane: rows = lanes, steps j < nsys.
-// Returns x_lane = rhs_lane / pivot_lane for lanes < nsys. The pivot row of step
-// j equals column j of the (still symmetric) trailing block, i.e. lane c's
-// register j, so it is broadcast with v_readlane: no LDS traffic and no waits.
-__device__ __forceinline__ float gauss_jordan64(float (&reg)[64], float rhs, int nsys,
-                                                float* /*unused*/) {
+// Gauss-Jordan on 64 registers per lane: rows = lanes, all 64 steps (rows and
+// columns past the system size hold the identity and a zero right-hand side, so
+// their steps change nothing). Returns x_lane = rhs_lane / pivot_lane. The pivot
+// row of step j equals column j of the (still symmetric) trailing block, i.e.
+// lane c's register j, broadcast with v_readlane; a step first reads all its
+// broadcasts into scalars and then issues the FMAs, so no FMA waits on the
+// readlane just before it. The pivot reciprocal is rcp plus one Newton step.
+__device__ __forceinline__ float gauss_jordan64(float (&reg)[64], float rhs) {
   const int lane = threadIdx.x & 63;
   float piv = 1.f;
-#pragma unroll
-  for (int j = 0; j < 64; ++j) {
-    if (j < nsys) {
-      const float p = bcast(reg[j], j);
-      const float pinv = 1.f / p;
-      const float rj = bcast(rhs, j);
-      const float f = (lane == j) ? 0.f : reg[j] * pinv;
-      if (lane == j) piv = p;
-      rhs = fmaf(-f, rj, rhs);
-#pragma unroll
-      for (int c = j + 1; c < 64; ++c) reg[c] = fmaf(-f, bcast(reg[j], c), reg[c]);
-    }
-  }
+  static_for<0, 64>([&](auto J) __attribute__((always_inline)) {
+    constexpr int j = J;
+    const float p = bcast(reg[j], j);
+    const float rj = bcast(rhs, j);
+    float row[64];
+    static_for<j + 1, 64>([&](auto C) __attribute__((always_inline)) {
+      constexpr int c = C;
+      row[c] = bcast(reg[j], c);
+    });
+    float pinv = __builtin_amdgcn_rcpf(p);
+    pinv = pinv * fmaf(-p, pinv, 2.f);
+    const float f = (lane == j) ? 0.f : reg[j] * pinv;
+    piv = (lane == j) ? p : piv;
+    rhs = fmaf(-f, rj, rhs);
+    static_for<j + 1, 64>([&](auto C) __attribute__((always_inline)) {
+      constexpr int c = C;
+      reg[c] = fmaf(-f, row[c], reg[c]);
+    });
+  });
   return rhs / piv;
 }
 
 struct SolveArgs {
   const float* W;      // working weights, c x b
   int64_t c, b, j0;
-  int Bb, B;           // block width, Z row pitch
+  int Bb, B;           // block width, N row pitch
+  int64_t ldz;         // Z row pitch
   int n, m;            // N:M (mode 0)
   const float* R;      // transformed rows: R[J, F] = [A_F]_{J,F}
   const float* Nblk;   // this block's N (route B), B x B
   const float* g;      // g_q source: mode 0 Wanda: gW; mode 1: D row (OBS) or gW
   int g_mode;          // 0: 1/M_qq (OBS, N:M), 1: 1/g[q] (OBS, unstructured), 2: g[q] (Wanda)
-  float* Z;            // c x B
+  float* Z;            // c rows, pitch ldz: this block's coefficients
   uint8_t* mask;       // c x b
   DevState* st;
   unsigned long long* blk_count;
 };
 
 template <int MODE, int ROUTE>
-__global__ __launch_bounds__(kWaves * 64) void solve_kernel(SolveArgs a) {
-  __shared__ float sM[kMaxBlock * kMP];
+__global__ __launch_bounds__(kWaves * 64, 4) void solve_kernel(SolveArgs a) {
+  __shared__ float sM[kMaxBlock * kMaxBlock];
   __shared__ float sg[kMaxBlock];
   __shared__ float sbuf[kWaves][kMaxBlock];
   __shared__ float su[kWaves][kMaxBlock];
   __shared__ int sQ[kWaves][kMaxBlock];
   __shared__ int sP[kWaves][64];
-  __shared__ float scol[kWaves][64];
+  __shared__ unsigned long long scount[kWaves];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Bb = a.Bb;
   const int64_t b = a.b, j0 = a.j0;
-  for (int e = tid; e < Bb * Bb; e += blockDim.x) {
-    const int r = e / Bb, q = e % Bb;
-    sM[r * kMP + q] = (ROUTE == 0) ? a.R[(j0 + r) * b + j0 + q] : a.Nblk[r * a.B + q];
+  {  // M (or N): all 32 loads of a thread in flight at once, addresses clamped
+    const float* src = (ROUTE == 0) ? a.R + j0 * b + j0 : a.Nblk;
+    const int64_t ld = (ROUTE == 0) ? b : a.B;
+    constexpr int kPer = kMaxBlock * kMaxBlock / (kWaves * 64);
+    float v[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int idx = e * kWaves * 64 + tid, r = idx >> 7, q = idx & (kMaxBlock - 1);
+      const int rr = r < Bb ? r : Bb - 1, qq = q < Bb ? q : Bb - 1;
+      v[e] = src[rr * ld + qq];
+    }
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int idx = e * kWaves * 64 + tid, r = idx >> 7, q = idx & (kMaxBlock - 1);
+      if (r < Bb && q < Bb) sM[mat_idx(r, q)] = v[e];
+    }
   }
   for (int q = tid; q < Bb; q += blockDim.x) {
     float gq;
@@ -112,6 +137,7 @@ __global__ __launch_bounds__(kWaves * 64) void solve_kernel(SolveArgs a) {
   __syncthreads();
   const unsigned long long tbound = (MODE == 1) ? a.st->tbound : 0ull;
   const unsigned long long lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+  unsigned long long count = 0;
 
   for (int64_t k = (int64_t)blockIdx.x * kWaves + wave; k < a.c; k += (int64_t)gridDim.x * kWaves) {
     const int e0 = lane, e1 = lane + 64;
@@ -139,7 +165,7 @@ __global__ __launch_bounds__(kWaves * 64) void solve_kernel(SolveArgs a) {
     uint8_t* mrow = a.mask + k * b + j0;
     if (v0) mrow[e0] = s0 ? 1 : 0;
     if (v1) mrow[e1] = s1 ? 1 : 0;
-    float* zrow = a.Z + k * a.B;
+    float* zrow = a.Z + k * a.ldz;
     if (v0 && !s0) zrow[e0] = 0.f;
     if (v1 && !s1) zrow[e1] = 0.f;
     const int pos0 = __popcll(m0 & lt), pos1 = __popcll(m0) + __popcll(m1 & lt);
@@ -157,32 +183,32 @@ __global__ __launch_bounds__(kWaves * 64) void solve_kernel(SolveArgs a) {
       if (ROUTE == 0) {
         const bool act = lane < s;
         const int qa = act ? sQ[wave][lane] : 0;
-        const float* mrowp = sM + qa * kMP;
 #pragma unroll
-        for (int c = 0; c < 64; ++c) {
-          float v = (c == lane) ? 1.f : 0.f;
-          if (c < s && act) v = mrowp[sQ[wave][c]];
-          reg[c] = v;
+        for (int c = 0; c < 64; ++c) {  // branch-free, so all 64 reads are in flight
+          const bool in = (c < s) && act;
+          const int qc = (c < s) ? sQ[wave][c] : 0;
+          const float v = sM[mat_idx(qa, qc)];
+          reg[c] = in ? v : ((c == lane) ? 1.f : 0.f);
         }
         const float u = act ? su[wave][lane] : 0.f;
-        const float z = gauss_jordan64(reg, u, s, scol[wave]);
+        const float z = gauss_jordan64(reg, u);
         if (act) zrow[qa] = z;
       } else {
         const int p = Bb - s;
         const bool act = lane < p;
         const int pb = act ? sP[wave][lane] : 0;
-        const float* nrowp = sM + pb * kMP;
 #pragma unroll
         for (int c = 0; c < 64; ++c) {
-          float v = (c == lane) ? 1.f : 0.f;
-          if (c < p && act) v = nrowp[sP[wave][c]];
-          reg[c] = v;
+          const bool in = (c < p) && act;
+          const int pc = (c < p) ? sP[wave][c] : 0;
+          const float v = sM[mat_idx(pb, pc)];
+          reg[c] = in ? v : ((c == lane) ? 1.f : 0.f);
         }
         float y = 0.f;
         if (act) {
-          for (int t = 0; t < s; ++t) y = fmaf(su[wave][t], sM[sQ[wave][t] * kMP + pb], y);
+          for (int t = 0; t < s; ++t) y = fmaf(su[wave][t], sM[mat_idx(sQ[wave][t], pb)], y);
         }
-        const float x = gauss_jordan64(reg, y, p, scol[wave]);
+        const float x = gauss_jordan64(reg, y);
         // v = [u on Q, -x on P], then z_q = (v N)_q for q in Q
         if (act) sbuf[wave][pb] = -x;
         if (s0) sbuf[wave][e0] = w0;
@@ -191,18 +217,26 @@ __global__ __launch_bounds__(kWaves * 64) void solve_kernel(SolveArgs a) {
         float z0 = 0.f, z1 = 0.f;
         for (int t = 0; t < Bb; ++t) {
           const float vt = sbuf[wave][t];
-          if (v0) z0 = fmaf(vt, sM[t * kMP + e0], z0);
-          if (v1) z1 = fmaf(vt, sM[t * kMP + e1], z1);
+          if (v0) z0 = fmaf(vt, sM[mat_idx(t, e0)], z0);
+          if (v1) z1 = fmaf(vt, sM[mat_idx(t, e1)], z1);
         }
         if (s0) zrow[e0] = z0;
         if (s1) zrow[e1] = z1;
       }
     }
-    if (lane == 0 && s > 0) {
-      atomicAdd((unsigned long long*)&a.st->pruned, (unsigned long long)s);
-      atomicAdd(a.blk_count, (unsigned long long)s);
-    }
+    count += (unsigned long long)s;
     wave_sync();
+  }
+  // one pair of atomics per workgroup (same-address atomics serialise in L2)
+  if (lane == 0) scount[wave] = count;
+  __syncthreads();
+  if (tid == 0) {
+    unsigned long long tot = 0;
+    for (int w = 0; w < kWaves; ++w) tot += scount[w];
+    if (tot) {
+      atomicAdd((unsigned long long*)&a.st->pruned, tot);
+      atomicAdd(a.blk_count, tot);
+    }
   }
 }
 
@@ -245,14 +279,14 @@ unsigned solve_grid(int64_t c) {
 
 hipError_t launch_solve_nm(const float* W, int64_t c, int64_t b, int64_t j0, int64_t B, int n,
                            int m, const float* R, const float* gW, const float* Nblk, float* Z,
-                           uint8_t* mask, DevState* st, unsigned long long* blk_count,
+                           int64_t ldz, uint8_t* mask, DevState* st, unsigned long long* blk_count,
                            hipStream_t s) {
   SolveArgs a;
   a.W = W; a.c = c; a.b = b; a.j0 = j0;
   a.Bb = (int)((b - j0) < B ? (b - j0) : B);
   a.B = (int)B; a.n = n; a.m = m; a.R = R; a.Nblk = Nblk;
   a.g = gW; a.g_mode = gW ? 2 : 0;
-  a.Z = Z; a.mask = mask; a.st = st; a.blk_count = blk_count;
+  a.Z = Z; a.ldz = ldz; a.mask = mask; a.st = st; a.blk_count = blk_count;
   const int sel = a.Bb / m * (m - n);
   if (sel <= 64)
     hipLaunchKernelGGL((solve_kernel<0, 0>), dim3(solve_grid(c)), dim3(kWaves * 64), 0, s, a);
@@ -270,7 +304,7 @@ hipError_t launch_solve_unstructured(const float* W, int64_t c, int64_t b, int64
   a.Bb = (int)((b - j0) < B ? (b - j0) : B);
   a.B = (int)B; a.n = 0; a.m = 1; a.R = R; a.Nblk = Nblk;
   a.g = g; a.g_mode = obs ? 1 : 2;
-  a.Z = Z; a.mask = mask; a.st = st; a.blk_count = blk_count;
+  a.Z = Z; a.ldz = B; a.mask = mask; a.st = st; a.blk_count = blk_count;
   hipLaunchKernelGGL((solve_kernel<1, 0>), dim3(solve_grid(c)), dim3(kWaves * 64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.Bb <= 64) return e;

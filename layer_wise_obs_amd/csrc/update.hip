@@ -1,10 +1,12 @@
 // Compensation update, dtype conversions and the reconstruction error.
 //
 // Update ("Pruning LLMs with Thanos", sections "Contribution one" and "The scaling
-// problem, and what SparseGPT changes": compensation goes only into columns that
-// are still active): W[:, F] -= Z [A_F]_{J,F}, a rank-B update on the fp32 matrix
-// cores, followed by W[k, Q_k] = 0 exactly ("makes every coordinate in Q exactly
-// zero").
+// problem, and what SparseGPT changes": only still-active columns receive
+// compensation): W[:, F] -= Z [A_F]_{J,F}, a rank-B update on the fp32 matrix
+// cores, after which the pruned entries of block J are set to exactly zero.
+// The kernel takes any column range and any K, so the driver can split one
+// block's update into the columns it needs now and a deferred part that is
+// applied for several blocks at once (K = several blocks).
 //
 // Error ("The layer-reconstruction lens"): E = ||(W - What) X||_F^2 =
 // sum_k D_k G D_k^T, computed as T = D G per 128x128 tile (fp32 MFMA) with the
@@ -15,28 +17,30 @@ namespace th {
 
 namespace {
 
-// W[row0:, col0:] -= Z[rows, 0:Bb] R[j0:j0+Bb, cols]; zero the pruned entries of J.
+// W[row0:, col0:] -= Z[rows, 0:K] R[r0:r0+K, cols]; zero the pruned entries of
+// columns [mask_j0, mask_jend).
 __global__ __launch_bounds__(256, 2) void update_kernel(float* __restrict__ W, int64_t c, int64_t b,
-                                                     int64_t j0, int Bb, int ldz,
-                                                     int64_t col_end, int ncol_tiles,
-                                                     const float* __restrict__ Z,
+                                                     int64_t r0, int K, int64_t ldz,
+                                                     int64_t col_begin, int64_t col_end,
+                                                     int ncol_tiles, const float* __restrict__ Z,
                                                      const float* __restrict__ R,
-                                                     const uint8_t* __restrict__ mask) {
+                                                     const uint8_t* __restrict__ mask,
+                                                     int64_t mask_j0, int64_t mask_jend) {
   __shared__ __attribute__((aligned(16))) float smem[kGemmLdsFloats];
   const int64_t row0 = (int64_t)(blockIdx.x / ncol_tiles) * 128;
-  const int64_t col0 = j0 + (int64_t)(blockIdx.x % ncol_tiles) * 128;
+  const int64_t col0 = col_begin + (int64_t)(blockIdx.x % ncol_tiles) * 128;
   const int rows = (int)((c - row0) < 128 ? (c - row0) : 128);
   const int cols = (int)((col_end - col0) < 128 ? (col_end - col0) : 128);
   f32x16_t acc[2][2];
   float* C = W + row0 * b + col0;
   gemm_load_c(acc, C, b, rows, cols);  // W tile, then W - Z R
-  gemm_tile_f32<true, false>(Z + row0 * ldz, ldz, rows, R + j0 * b + col0, b, cols, Bb, acc, smem,
+  gemm_tile_f32<true, false>(Z + row0 * ldz, ldz, rows, R + r0 * b + col0, b, cols, K, acc, smem,
                              true);
-  const int64_t jend = j0 + Bb;
+  const bool masked = col0 < mask_jend && col0 + 128 > mask_j0;
   gemm_foreach(acc, [&](int r, int cc, float v) {
     if (r < rows && cc < cols) {
       const int64_t row = row0 + r, col = col0 + cc;
-      if (col < jend && mask[row * b + col]) v = 0.f;
+      if (masked && col >= mask_j0 && col < mask_jend && mask[row * b + col]) v = 0.f;
       W[row * b + col] = v;
     }
   });
@@ -129,14 +133,14 @@ unsigned ew_grid(int64_t n) {
 
 }  // namespace
 
-hipError_t launch_update(float* W, int64_t c, int64_t b, int64_t j0, int64_t Bb, int64_t ldz,
-                         int64_t col_end, const float* Z, const float* R, const uint8_t* mask,
-                         hipStream_t s) {
-  if (col_end <= j0) return hipSuccess;
-  const int nct = (int)cdiv(col_end - j0, 128);
+hipError_t launch_update(float* W, int64_t c, int64_t b, int64_t r0, int64_t K, int64_t ldz,
+                         int64_t col0, int64_t col_end, const float* Z, const float* R,
+                         const uint8_t* mask, int64_t mask_j0, int64_t mask_w, hipStream_t s) {
+  if (col_end <= col0 || K <= 0) return hipSuccess;
+  const int nct = (int)cdiv(col_end - col0, 128);
   const int nrt = (int)cdiv(c, 128);
-  hipLaunchKernelGGL(update_kernel, dim3((unsigned)(nct * nrt)), dim3(256), 0, s, W, c, b, j0,
-                     (int)Bb, (int)ldz, col_end, nct, Z, R, mask);
+  hipLaunchKernelGGL(update_kernel, dim3((unsigned)(nct * nrt)), dim3(256), 0, s, W, c, b, r0,
+                     (int)K, ldz, col0, col_end, nct, Z, R, mask, mask_j0, mask_j0 + mask_w);
   return hipGetLastError();
 }
 

@@ -212,6 +212,15 @@ def test_prune_nm_several_tiles(pattern):
     _check_layer(W, X, pattern=pattern, block=128)
 
 
+@pytest.mark.parametrize("pattern,block,c,b", [((2, 4), 32, 200, 1096), ((4, 8), 64, 160, 1624)])
+def test_prune_nm_across_super_blocks(pattern, block, c, b):
+    """N:M over several groups of eight blocks (the columns beyond a group are
+    compensated once per group) and a ragged last block."""
+    _say(f"prune N:M {pattern} B={block} c={c} b={b} (several block groups)")
+    W, X = _inputs(c, b, 4096, 35, relu=True)
+    _check_layer(W, X, pattern=pattern, block=block)
+
+
 def test_prune_unstructured_ragged_last_block():
     _say("prune unstructured c=200 b=392 ragged")
     W, X = _inputs(200, 392, 3000, 32)
