@@ -5,21 +5,18 @@
 // Thanos", section "One deletion with compensation: the OBS view": G = XX^T is the
 // Gram matrix, lambda*I is added for numerical stability.
 //
-// bf16 path: 256x256 output tiles of the lower triangle, 512 threads (8 waves as
-// 2 x 4, each wave 128x64 = 4x2 blocks of v_mfma_f32_32x32x16_bf16; two waves per
-// SIMD so one wave's loads, transposes and LDS traffic overlap the other's MFMAs).
-// Tokens are the contraction dimension; X^T arrives token-major, so every thread
-// loads an 8-token x 8-feature brick (eight 16-byte loads) of one panel,
-// transposes them in registers with v_perm_b32 and stores 8 feature rows of 8
-// tokens (16 bytes each) into LDS, where the MFMA operands are read as 16-byte
-// K-contiguous vectors. The LDS row pitch of 72 bf16 (36 dwords) makes both the
-// stores and the operand reads bank-conflict free. Two LDS stages (144 KB) give one
-// barrier per 64 tokens; inside a stage the operand fragments are double-buffered
-// in registers and the next stage's transpose-store is split into four parts
-// interleaved with the four k-substeps of MFMAs. The loop body is branch-free
-// (clamped loads, stores into the idle buffer), so the compiler can interleave
-// LDS traffic, VALU transposes and MFMAs of one wave, and the two waves of a
-// SIMD no longer alternate between an MFMA phase and a store phase.
+// bf16 path: 256x256 output tiles of the lower triangle, 256 threads (4 waves as
+// 2 x 2, each wave 128x128 = 4x4 blocks of v_mfma_f32_32x32x16_bf16 with the
+// accumulators in AGPRs). Tokens are the contraction dimension and X^T arrives
+// token-major, so the tiles are staged in LDS as they are in memory (token rows
+// of 256 features) with direct global->LDS loads (global_load_lds_dwordx4, no
+// register staging), and the MFMA operands -- 8 consecutive tokens of one feature
+// per lane -- are formed by the gfx950 transposing LDS read ds_read_b64_tr_b16.
+// The 16-byte pieces of a token row are XOR-swizzled by (token & 3) so that those
+// reads spread over all banks. Four LDS stages of 32 tokens (128 KB) keep the
+// loads three stages ahead; operand fragments are double-buffered in registers
+// across the 16-token substeps, so the reads for the next substep overlap the
+// current substep's 16 MFMAs.
 #include "common.h"
 
 namespace th {
@@ -27,66 +24,7 @@ namespace th {
 namespace {
 
 constexpr int kTile = 256;
-constexpr int kBK = 64;
-constexpr int kPitch = 72;  // bf16 elements per LDS feature row (64 tokens + 8 pad)
-constexpr int kThreads = 512;
-
-// 8 tokens x 8 features starting at (tok0, f0). b is a multiple of 8, so a
-// feature group is either fully inside or fully outside. Addresses are clamped
-// instead of branched on (loads stay branch-free and in bounds); the returned
-// bit mask marks the valid rows, and zeroing happens in transpose_store, so
-// nothing waits for the loads until the data is stored to LDS.
-__device__ __forceinline__ unsigned load_brick(const unsigned short* __restrict__ X, int64_t ldx,
-                                               int64_t t_valid, int64_t b, int64_t tok0,
-                                               int64_t f0, u32x4_t (&v)[8]) {
-  const bool fok = f0 < b;
-  const int64_t fc = fok ? f0 : 0;
-  unsigned ok = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t t = tok0 + i;
-    const int64_t tc = (t < t_valid) ? t : (t_valid - 1);
-    v[i] = *(const u32x4_t*)(X + tc * ldx + fc);
-    ok |= (fok && t < t_valid) ? (1u << i) : 0u;
-  }
-  return ok;
-}
-
-// Part d (0..3) of transpose_store: features 2d and 2d+1 of the brick.
-__device__ __forceinline__ void transpose_store_part(unsigned short* __restrict__ s, int frow0,
-                                                     int oct, const u32x4_t (&v)[8], unsigned ok,
-                                                     int d) {
-  u32x4_t lo, hi;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const unsigned a = ((ok >> (2 * p)) & 1u) ? v[2 * p][d] : 0u;
-    const unsigned c = ((ok >> (2 * p + 1)) & 1u) ? v[2 * p + 1][d] : 0u;
-    lo[p] = __builtin_amdgcn_perm(c, a, 0x05040100u);
-    hi[p] = __builtin_amdgcn_perm(c, a, 0x07060302u);
-  }
-  *(u32x4_t*)(s + (frow0 + 2 * d) * kPitch + oct * 8) = lo;
-  *(u32x4_t*)(s + (frow0 + 2 * d + 1) * kPitch + oct * 8) = hi;
-}
-
-// 8 tokens x 8 features (v[token].dword[f/2]) -> 8 features x 8 tokens; rows
-// whose bit is clear in `ok` are stored as zeros.
-__device__ __forceinline__ void transpose_store(unsigned short* __restrict__ s, int frow0, int oct,
-                                                const u32x4_t (&v)[8], unsigned ok) {
-  u32x4_t w[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) w[i] = ((ok >> i) & 1u) ? v[i] : u32x4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    u32x4_t lo, hi;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      lo[p] = __builtin_amdgcn_perm(w[2 * p + 1][d], w[2 * p][d], 0x05040100u);
-      hi[p] = __builtin_amdgcn_perm(w[2 * p + 1][d], w[2 * p][d], 0x07060302u);
-    }
-    *(u32x4_t*)(s + (frow0 + 2 * d) * kPitch + oct * 8) = lo;
-    *(u32x4_t*)(s + (frow0 + 2 * d + 1) * kPitch + oct * 8) = hi;
-  }
-}
+constexpr int kBK = 64;  // token granularity of the split ranges
 
 // Tile order for L2 reuse: the lower triangle of nt x nt tiles is walked in
 // super-tiles of 4 tile rows x 8 tile columns (row-major inside each), super-
@@ -116,13 +54,57 @@ __device__ __forceinline__ void tile_of(int lin, int nt, int& ti, int& tj) {
   ti = tj = 0;  // not reached for lin < nt(nt+1)/2
 }
 
-__global__ __launch_bounds__(kThreads) void syrk_bf16_kernel(
+constexpr int kDBK = 32;       // tokens per LDS stage
+constexpr int kDStages = 4;    // LDS stages (loads run three stages ahead)
+constexpr int kDThreads = 256; // 4 waves, 2 x 2, each 128 x 128
+constexpr int kRowBytes = kTile * 2;                  // one token row of a panel
+constexpr int kPanelBytes = kDBK * kRowBytes;         // 16 KB
+constexpr int kStageBytes = 2 * kPanelBytes;          // A and B panels
+
+// Byte offset of (token t, 8-feature piece fg) inside a panel: token-major rows of
+// 512 bytes, pieces XOR-swizzled by (t & 3) so that the transposing operand reads
+// of 8 tokens x 32 features spread over all banks.
+__device__ __forceinline__ int piece_off(int t, int fg) { return t * kRowBytes + ((fg ^ ((t & 3) << 2)) << 4); }
+
+// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
+// (global_load_lds_dwordx4, LDS base in M0). Written as asm so that the compiler
+// does not order LDS reads of other buffers after these loads; completion is
+// tracked by the explicit vmcnt waits before each barrier. The instruction has
+// no result register.
+__device__ __forceinline__ void lds_dma16(const void* gptr, const void* lds) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)lds);
+  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                   :
+                   : "v"(gptr), "s"(m0)
+                   : "m0");
+}
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// MFMA operand (32 features x 16 tokens, k-substep at token ks16) from a panel:
+// lane L gets feature f0 + L%32, tokens ks16 + 8*(L/32) + 0..7. Each
+// ds_read_b64_tr_b16 transposes, per 16-lane group, 4 tokens x 16 features: slot
+// s reads token tb + s/4, features fb + 4*(s%4) .. +3; lane s then holds feature
+// fb + s of the 4 tokens.
+__device__ __forceinline__ bf16x8_t tr_frag(const unsigned char* panel, int f0, int ks16, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int fb = f0 + ((g & 1) << 4) + ((s & 3) << 2);  // first feature this slot reads
+  const int tb = ks16 + ((g >> 1) << 3) + (s >> 2);
+  const int fg = fb >> 3, within = (fb & 7) << 1;
+  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16_t*)(panel + piece_off(tb, fg) + within));
+  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16_t*)(panel + piece_off(tb + 4, fg) + within));
+  typedef short v8i16_t __attribute__((ext_vector_type(8)));
+  const v8i16_t r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
+__global__ __launch_bounds__(kDThreads) void syrk_bf16_kernel(
     float* __restrict__ H, const unsigned short* __restrict__ X, int64_t t, int64_t b, int64_t ldx,
     int ntile_rows, int ntiles, int per_xcd, int splits, int64_t tok_per_split,
     float* __restrict__ partials) {
-  // XCD-aware order: consecutive workgroup ids go to different XCDs, so each XCD
-  // gets a contiguous run of the super-tile order below; the ~32 tiles an XCD
-  // runs at once then share 4 row panels and 8 column panels in its L2.
   const int wg = blockIdx.x;
   const int lin = (wg % 8) * per_xcd + wg / 8;
   const int split = blockIdx.y;
@@ -132,90 +114,133 @@ __global__ __launch_bounds__(kThreads) void syrk_bf16_kernel(
   const bool diag = (ti == tj);
   const int64_t I0 = (int64_t)ti * kTile, J0 = (int64_t)tj * kTile;
 
-  // two pipeline stages x (A panel, B panel), each 256 features x 64 tokens
-  __shared__ __attribute__((aligned(16))) unsigned short smem[2 * 2 * kTile * kPitch];
+  // One LDS array per stage: with the stage index a compile-time constant the
+  // compiler can tell the buffers apart and does not make operand reads wait for
+  // the direct-to-LDS loads that are in flight into the other buffers.
+  __shared__ __attribute__((aligned(1024))) unsigned char sm0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char sm1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char sm2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char sm3[kStageBytes];
+  auto buf = [&](auto S) -> unsigned char* {
+    constexpr int s = decltype(S)::value;
+    if constexpr (s == 0) return sm0;
+    else if constexpr (s == 1) return sm1;
+    else if constexpr (s == 2) return sm2;
+    else return sm3;
+  };
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int part = tid >> 8;             // 0: A panel, 1: B panel
-  const int q = tid & 255;
-  const int oct = q & 7, fgrp = q >> 3;  // 8 token octets x 32 feature groups
-  const int64_t fbase = (part == 0 ? I0 : J0) + fgrp * 8;
-
   const int64_t k_begin = (int64_t)split * tok_per_split;
   const int64_t k_end = (k_begin + tok_per_split < t) ? k_begin + tok_per_split : t;
-  const int nk = (int)cdiv(k_end - k_begin, kBK);
+  const int nk = (int)cdiv(k_end - k_begin, kDBK);
 
-  f32x16_t acc[4][2];
+  // Loader: per stage and panel, 16 wave instructions of 1 KB (token rows 2i,
+  // 2i+1); wave w issues i = w, w+4, w+8, w+12 for both panels. Lane l writes
+  // bytes [16 l, 16 l + 16) of the chunk: row 2i + l/32, swizzled position l%32.
+  const int lrow = lane >> 5, lpos = lane & 31;
+  auto issue_stage = [&](int st, unsigned char* sbase) {
+    const int64_t tok0 = k_begin + (int64_t)st * kDBK;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int i = wave + 4 * m;
+      const int tr = 2 * i + lrow;  // token row inside the stage
+      const int fg = lpos ^ ((tr & 3) << 2);
+      int64_t tok = tok0 + tr;
+      tok = tok < k_end ? tok : k_end - 1;  // rows past the end are zeroed after the wait
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        int64_t f = (p == 0 ? I0 : J0) + fg * 8;
+        f = f < b ? f : 0;  // features past b only feed outputs that are never stored
+        lds_dma16(X + tok * ldx + f, sbase + p * kPanelBytes + i * 1024);
+      }
+    }
+  };
+  // zero this wave's rows of stage st that lie past k_end (its own loads have landed)
+  auto zero_tail = [&](int st, unsigned char* sbase) {
+    const int64_t tok0 = k_begin + (int64_t)st * kDBK;
+    if (tok0 + kDBK <= k_end) return;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int i = wave + 4 * m;
+      const int tr = 2 * i + lrow;
+      if (tok0 + tr >= k_end) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          *(u32x4_t*)(sbase + p * kPanelBytes + i * 1024 + lane * 16) = u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+
+  f32x16_t acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][c][r] = 0.f;
-
-  const int wrow = wave >> 2, wcol = wave & 3;
+  const int wrow = wave >> 1, wcol = wave & 1;
   const int lr = lane & 31, lk = lane >> 5;
 
-  auto sbuf = [&](int stage, int panel) { return smem + (stage * 2 + panel) * (kTile * kPitch); };
-  u32x4_t v[8];
-  unsigned ok = 0;
-  ok = load_brick(X, ldx, k_end, b, k_begin + oct * 8, fbase, v);
-  transpose_store(sbuf(0, part), fgrp * 8, oct, v, ok);
-  ok = load_brick(X, ldx, k_end, b, k_begin + kBK + oct * 8, fbase, v);
-  __syncthreads();
-  for (int it = 0; it < nk; ++it) {
-    const int cur = it & 1;
-    const unsigned short* sA = sbuf(cur, 0);
-    const unsigned short* sB = diag ? sA : sbuf(cur, 1);
-    // Every thread loads and stores every iteration (branch-free loop body): on
-    // diagonal tiles the second half of the threads fills the unused B buffer,
-    // and past the last stage the clamped loads and stores land in the buffer
-    // that is no longer read.
-    unsigned short* snext = sbuf(cur ^ 1, part);
-    // Operand fragments are double-buffered in registers: the reads for
-    // k-substep ks+1 are issued before the MFMAs of ks, and a quarter of the
-    // next stage's transpose-store follows each substep's MFMAs.
-    bf16x8_t af[2][4], bfr[2][2];
+  bf16x8_t af0[4], bf0[4], af1[4], bf1[4];
+  auto read_frags = [&](const unsigned char* pA, int ks, bf16x8_t (&af)[4], bf16x8_t (&bf)[4]) {
+    const unsigned char* pB = diag ? pA : pA + kPanelBytes;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) af[a] = tr_frag(pA, wrow * 128 + a * 32, ks * 16, lane);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) bf[c] = tr_frag(pB, wcol * 128 + c * 32, ks * 16, lane);
+  };
+  auto mfmas = [&](const bf16x8_t (&af)[4], const bf16x8_t (&bf)[4]) {
 #pragma unroll
     for (int a = 0; a < 4; ++a)
-      af[0][a] = *(const bf16x8_t*)(sA + (wrow * 128 + a * 32 + lr) * kPitch + lk * 8);
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-      bfr[0][c] = *(const bf16x8_t*)(sB + (wcol * 64 + c * 32 + lr) * kPitch + lk * 8);
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int cb = ks & 1, nb = cb ^ 1;
-      if (ks + 1 < kBK / 16) {
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-          af[nb][a] = *(const bf16x8_t*)(sA + (wrow * 128 + a * 32 + lr) * kPitch + (ks + 1) * 16 +
-                                         lk * 8);
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          bfr[nb][c] = *(const bf16x8_t*)(sB + (wcol * 64 + c * 32 + lr) * kPitch +
-                                          (ks + 1) * 16 + lk * 8);
+      for (int c = 0; c < 4; ++c)
+        acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bf[c], acc[a][c], 0, 0, 0);
+  };
+
+  // prologue: stages 0, 1, 2 in flight; wait for stage 0
+  issue_stage(0, sm0);
+  issue_stage(1, sm1);
+  issue_stage(2, sm2);
+  __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  zero_tail(0, sm0);
+  __syncthreads();
+  read_frags(sm0, 0, af0, bf0);
+  // Fragments are double-buffered across the two 16-token substeps of a stage:
+  // the reads for the next substep (or the next stage's first, right after the
+  // barrier) are in flight while the current substep's 16 MFMAs run. Unrolled by
+  // the number of stages so that every buffer index is a constant.
+  for (int it0 = 0; it0 < nk; it0 += kDStages) {
+    static_for<0, kDStages>([&](auto U) __attribute__((always_inline)) {
+      constexpr int u = U;
+      const int it = it0 + u;
+      if (it < nk) {
+        // buffer (u+3)%4 was last read before the barrier of iteration it-1
+        issue_stage(it + 3, buf(std::integral_constant<int, (u + 3) % kDStages>{}));
+        read_frags(buf(std::integral_constant<int, u>{}), 1, af1, bf1);
+        mfmas(af0, bf0);
+        // stage it+1 complete for this wave (stages it+2, it+3 may still be in flight)
+        __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        unsigned char* nb = buf(std::integral_constant<int, (u + 1) % kDStages>{});
+        zero_tail(it + 1, nb);
+        __syncthreads();
+        read_frags(nb, 0, af0, bf0);
+        mfmas(af1, bf1);
       }
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          acc[a][c] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][a], bfr[cb][c], acc[a][c], 0, 0, 0);
-      transpose_store_part(snext, fgrp * 8, oct, v, ok, ks);
-    }
-    ok = load_brick(X, ldx, k_end, b, k_begin + (int64_t)(it + 2) * kBK + oct * 8, fbase, v);
-    __syncthreads();
+    });
   }
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  (void)lr;
+  (void)lk;
 
   if (splits == 1) {
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t row = I0 + wrow * 128 + a * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
-          const int64_t col = J0 + wcol * 64 + c * 32 + lr;
+          const int64_t col = J0 + wcol * 128 + c * 32 + lr;
           if (row < b && col < b && col <= row) H[row * b + col] += 2.0f * acc[a][c][r];
         }
   } else {
@@ -223,11 +248,11 @@ __global__ __launch_bounds__(kThreads) void syrk_bf16_kernel(
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = wrow * 128 + a * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
-          const int col = wcol * 64 + c * 32 + lr;
+          const int col = wcol * 128 + c * 32 + lr;
           dst[row * kTile + col] = acc[a][c][r];
         }
   }
@@ -401,7 +426,7 @@ hipError_t launch_syrk_bf16(float* H, const unsigned short* X, int64_t t, int64_
   int64_t tps = cdiv(cdiv(t, splits), kBK) * kBK;
   splits = (int)cdiv(t, tps);
   dim3 grid(per_xcd * 8, splits);
-  hipLaunchKernelGGL(syrk_bf16_kernel, grid, dim3(kThreads), 0, s, H, X, t, b, ldx, nt, ntiles,
+  hipLaunchKernelGGL(syrk_bf16_kernel, grid, dim3(kDThreads), 0, s, H, X, t, b, ldx, nt, ntiles,
                      per_xcd, splits, tps, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
