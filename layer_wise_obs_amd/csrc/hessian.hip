@@ -66,18 +66,33 @@ constexpr int kStageBytes = 2 * kPanelBytes;          // A and B panels
 // of 8 tokens x 32 features spread over all banks.
 __device__ __forceinline__ int piece_off(int t, int fg) { return t * kRowBytes + ((fg ^ ((t & 3) << 2)) << 4); }
 
-// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
-// (global_load_lds_dwordx4, LDS base in M0). Written as asm so that the compiler
-// does not order LDS reads of other buffers after these loads; completion is
-// tracked by the explicit vmcnt waits before each barrier. The instruction has
-// no result register.
-__device__ __forceinline__ void lds_dma16(const void* gptr, const void* lds) {
-  const unsigned m0 = __builtin_amdgcn_readfirstlane(
+// One stage's share of a wave: eight loads of 16 bytes per lane from global
+// memory straight into LDS (global_load_lds_dwordx4; lane l writes LDS bytes
+// [M0 + 16 l, M0 + 16 l + 16)). The LDS destinations are lds + the offsets
+// below (m = 0..3 four KB apart, the B panel 16 KB after the A panel). Written as
+// one asm block so that the compiler does not make LDS reads of other buffers
+// wait for these loads -- completion is tracked by the explicit vmcnt waits
+// before each barrier -- and so that M0 is restored before the compiler sees it
+// again. The loads have no result registers.
+__device__ __forceinline__ void lds_dma_stage(const void* const (&g)[8], const void* lds) {
+  const unsigned base = __builtin_amdgcn_readfirstlane(
       (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)lds);
-  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                   :
-                   : "v"(gptr), "s"(m0)
-                   : "m0");
+  unsigned saved;
+  __asm__ volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %9, off\n\t"
+      "s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %10, off\n\t"
+      "s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %11, off\n\t"
+      "s_mov_b32 m0, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %12, off\n\t"
+      "s_mov_b32 m0, %5\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %13, off\n\t"
+      "s_mov_b32 m0, %6\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %14, off\n\t"
+      "s_mov_b32 m0, %7\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %15, off\n\t"
+      "s_mov_b32 m0, %8\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %16, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(base), "s"(base + 16384u), "s"(base + 4096u), "s"(base + 20480u),
+        "s"(base + 8192u), "s"(base + 24576u), "s"(base + 12288u), "s"(base + 28672u),
+        "v"(g[0]), "v"(g[1]), "v"(g[2]), "v"(g[3]), "v"(g[4]), "v"(g[5]), "v"(g[6]), "v"(g[7]));
 }
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -140,6 +155,7 @@ __global__ __launch_bounds__(kDThreads) void syrk_bf16_kernel(
   const int lrow = lane >> 5, lpos = lane & 31;
   auto issue_stage = [&](int st, unsigned char* sbase) {
     const int64_t tok0 = k_begin + (int64_t)st * kDBK;
+    const void* g[8];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int i = wave + 4 * m;
@@ -151,9 +167,11 @@ __global__ __launch_bounds__(kDThreads) void syrk_bf16_kernel(
       for (int p = 0; p < 2; ++p) {
         int64_t f = (p == 0 ? I0 : J0) + fg * 8;
         f = f < b ? f : 0;  // features past b only feed outputs that are never stored
-        lds_dma16(X + tok * ldx + f, sbase + p * kPanelBytes + i * 1024);
+        g[2 * m + p] = X + tok * ldx + f;  // to sbase + p * kPanelBytes + i * 1024
       }
     }
+    static_assert(kPanelBytes == 16384, "LDS offsets in lds_dma_stage");
+    lds_dma_stage(g, sbase + wave * 1024);
   };
   // zero this wave's rows of stage st that lie past k_end (its own loads have landed)
   auto zero_tail = [&](int st, unsigned char* sbase) {
