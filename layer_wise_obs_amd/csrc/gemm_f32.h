@@ -171,3 +171,119 @@ __device__ __forceinline__ void gemm_tile_f32(const float* __restrict__ A, int64
 }
 
 }  // namespace th
+
+namespace th {
+
+// ---- 64x64 variant: 256 threads = 4 waves, each wave one 32x32 MFMA block.
+// For short GEMMs with few output tiles (block-local updates, panels), where
+// more and smaller workgroups finish sooner than a few 128x128 ones.
+constexpr int kG64Pitch = 68;  // floats per staged k-row (64 + 4)
+constexpr int kG64LdsFloats = 2 * kGemmBK * kG64Pitch;
+
+template <bool KC>
+__device__ __forceinline__ void g64_load_part(const float* __restrict__ P, int64_t ld, int nvalid,
+                                              int K, int kb, int tid, float (&r)[8]) {
+  if (KC) {  // thread: row i, 8 consecutive k
+    const int i = tid >> 2, k0 = kb + (tid & 3) * 8;
+    const float* src = P + (int64_t)i * ld + k0;
+    if (i < nvalid && k0 + 8 <= K && ((((uintptr_t)src) & 15) == 0)) {
+      const f32x4_t v0 = *(const f32x4_t*)src, v1 = *(const f32x4_t*)(src + 4);
+      r[0] = v0[0]; r[1] = v0[1]; r[2] = v0[2]; r[3] = v0[3];
+      r[4] = v1[0]; r[5] = v1[1]; r[6] = v1[2]; r[7] = v1[3];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r[e] = (i < nvalid && k0 + e < K) ? src[e] : 0.f;
+    }
+  } else {  // thread: k row, 8 consecutive i
+    const int k = kb + (tid >> 3), i0 = (tid & 7) * 8;
+    const float* src = P + (int64_t)k * ld + i0;
+    if (k < K && i0 + 8 <= nvalid && ((((uintptr_t)src) & 15) == 0)) {
+      const f32x4_t v0 = *(const f32x4_t*)src, v1 = *(const f32x4_t*)(src + 4);
+      r[0] = v0[0]; r[1] = v0[1]; r[2] = v0[2]; r[3] = v0[3];
+      r[4] = v1[0]; r[5] = v1[1]; r[6] = v1[2]; r[7] = v1[3];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r[e] = (k < K && i0 + e < nvalid) ? src[e] : 0.f;
+    }
+  }
+}
+
+template <bool KC>
+__device__ __forceinline__ void g64_store_part(float* __restrict__ sm, int tid, const float (&r)[8],
+                                               float sign) {
+  if (KC) {
+    const int i = tid >> 2, k0 = (tid & 3) * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sm[(k0 + e) * kG64Pitch + i] = sign * r[e];
+  } else {
+    const int k = tid >> 3, i0 = (tid & 7) * 8;
+    *(f32x4_t*)(sm + k * kG64Pitch + i0) = f32x4_t{sign * r[0], sign * r[1], sign * r[2], sign * r[3]};
+    *(f32x4_t*)(sm + k * kG64Pitch + i0 + 4) =
+        f32x4_t{sign * r[4], sign * r[5], sign * r[6], sign * r[7]};
+  }
+}
+
+// Visit every accumulator element of the 64x64 tile with its tile-local (row, col).
+template <class F>
+__device__ __forceinline__ void g64_foreach(const f32x16_t& acc, F&& f) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wi = (wave >> 1) * 32, wj = (wave & 1) * 32;
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    f(wi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), wj + (lane & 31), acc[r]);
+}
+
+__device__ __forceinline__ void g64_load_c(f32x16_t& acc, const float* __restrict__ C, int64_t ldc,
+                                           int rows, int cols) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wi = (wave >> 1) * 32, wj = (wave & 1) * 32;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = wi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    const int col = wj + (lane & 31);
+    acc[r] = (row < rows && col < cols) ? C[(int64_t)row * ldc + col] : 0.f;
+  }
+}
+
+// acc += (negA ? -A : A) (64 x K) * B (K x 64). All 256 threads must call it.
+template <bool A_KC, bool B_KC>
+__device__ __forceinline__ void g64_tile_f32(const float* __restrict__ A, int64_t lda, int a_rows,
+                                             const float* __restrict__ B, int64_t ldb, int b_cols,
+                                             int K, f32x16_t& acc, float* smem,
+                                             bool negA = false) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wi = (wave >> 1) * 32, wj = (wave & 1) * 32;
+  float* sA = smem;
+  float* sB = smem + kGemmBK * kG64Pitch;
+  const float sign = negA ? -1.f : 1.f;
+  float ra[8], rb[8];
+  g64_load_part<A_KC>(A, lda, a_rows, K, 0, tid, ra);
+  g64_load_part<B_KC>(B, ldb, b_cols, K, 0, tid, rb);
+  const int lr = lane & 31, lk = lane >> 5;
+  for (int kb = 0; kb < K; kb += kGemmBK) {
+    __syncthreads();
+    g64_store_part<A_KC>(sA, tid, ra, sign);
+    g64_store_part<B_KC>(sB, tid, rb, 1.f);
+    __syncthreads();
+    if (kb + kGemmBK < K) {
+      g64_load_part<A_KC>(A, lda, a_rows, K, kb + kGemmBK, tid, ra);
+      g64_load_part<B_KC>(B, ldb, b_cols, K, kb + kGemmBK, tid, rb);
+    }
+    const int kmax = (K - kb) < kGemmBK ? (K - kb) : kGemmBK;
+    if (kmax == kGemmBK) {
+#pragma unroll
+      for (int kk = 0; kk < kGemmBK; kk += 2)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sA[(kk + lk) * kG64Pitch + wi + lr],
+                                                   sB[(kk + lk) * kG64Pitch + wj + lr], acc, 0, 0, 0);
+    } else {
+      for (int kk = 0; kk < kmax; kk += 2)  // zero-padded rows past K
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sA[(kk + lk) * kG64Pitch + wi + lr],
+                                                   sB[(kk + lk) * kG64Pitch + wj + lr], acc, 0, 0, 0);
+    }
+  }
+}
+
+}  // namespace th

@@ -46,6 +46,34 @@ __global__ __launch_bounds__(256, 2) void update_kernel(float* __restrict__ W, i
   });
 }
 
+// The same update on 64 x 64 tiles, for launches with few 128 x 128 tiles.
+__global__ __launch_bounds__(256, 2) void update64_kernel(float* __restrict__ W, int64_t c,
+                                                       int64_t b, int64_t r0, int K, int64_t ldz,
+                                                       int64_t col_begin, int64_t col_end,
+                                                       int ncol_tiles, const float* __restrict__ Z,
+                                                       const float* __restrict__ R,
+                                                       const uint8_t* __restrict__ mask,
+                                                       int64_t mask_j0, int64_t mask_jend) {
+  __shared__ __attribute__((aligned(16))) float smem[kG64LdsFloats];
+  const int64_t row0 = (int64_t)(blockIdx.x / ncol_tiles) * 64;
+  const int64_t col0 = col_begin + (int64_t)(blockIdx.x % ncol_tiles) * 64;
+  const int rows = (int)((c - row0) < 64 ? (c - row0) : 64);
+  const int cols = (int)((col_end - col0) < 64 ? (col_end - col0) : 64);
+  f32x16_t acc;
+  float* C = W + row0 * b + col0;
+  g64_load_c(acc, C, b, rows, cols);
+  g64_tile_f32<true, false>(Z + row0 * ldz, ldz, rows, R + r0 * b + col0, b, cols, K, acc, smem,
+                            true);
+  const bool masked = col0 < mask_jend && col0 + 64 > mask_j0;
+  g64_foreach(acc, [&](int r, int cc, float v) {
+    if (r < rows && cc < cols) {
+      const int64_t row = row0 + r, col = col0 + cc;
+      if (masked && col >= mask_j0 && col < mask_jend && mask[row * b + col]) v = 0.f;
+      W[row * b + col] = v;
+    }
+  });
+}
+
 __global__ void to_f32_kernel(const void* __restrict__ src, int dt, int64_t n,
                               float* __restrict__ dst, DevState* st) {
   int bad = 0;
@@ -139,6 +167,14 @@ hipError_t launch_update(float* W, int64_t c, int64_t b, int64_t r0, int64_t K, 
   if (col_end <= col0 || K <= 0) return hipSuccess;
   const int nct = (int)cdiv(col_end - col0, 128);
   const int nrt = (int)cdiv(c, 128);
+  if ((int64_t)nct * nrt < 1024) {  // under ~4 tiles per CU: smaller tiles finish sooner
+    const int nct64 = (int)cdiv(col_end - col0, 64);
+    const int nrt64 = (int)cdiv(c, 64);
+    hipLaunchKernelGGL(update64_kernel, dim3((unsigned)(nct64 * nrt64)), dim3(256), 0, s, W, c, b,
+                       r0, (int)K, ldz, col0, col_end, nct64, Z, R, mask, mask_j0,
+                       mask_j0 + mask_w);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(update_kernel, dim3((unsigned)(nct * nrt)), dim3(256), 0, s, W, c, b, r0,
                      (int)K, ldz, col0, col_end, nct, Z, R, mask, mask_j0, mask_j0 + mask_w);
   return hipGetLastError();
