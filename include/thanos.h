@@ -173,8 +173,9 @@ th_status th_debug_select_global(const float* scores, int64_t c, int64_t f, int6
 
 /* U = upper-triangular factor with H^-1 = U^T U (U = chol_upper(H^-1), the factor
  * [EXPL, "SparseGPT"] computes once per layer), from a damped, full symmetric H
- * [b,b] fp32. U [b,b] fp32 (strict lower triangle zero). workspace: >= 2*b*b*4 +
- * b*128*4 + 4096 bytes. Returns TH_ERR_NOT_SPD on a non-positive pivot.
+ * [b,b] fp32. U [b,b] fp32 (strict lower triangle zero). workspace: >= b*b*4 +
+ * ceil(b/128)*128*256*4 + 65536 bytes (TH_ERR_WORKSPACE if smaller). Returns
+ * TH_ERR_NOT_SPD on a non-positive pivot.
  * Synchronises. */
 th_status th_debug_factor(const float* H, int64_t b, float* U, void* workspace,
                           size_t workspace_bytes, th_stream_t stream);

@@ -18,6 +18,9 @@
 //            (3) trailing, one fp32 MFMA GEMM over all tiles (i > k, j <= i):
 //                S[i,j] -= Lp_i [ X row k | -/X_kk | Lp_j^T ]  (j < k | j = k | j > k),
 //                where column block k is overwritten with -Lp_i X_kk.
+//   Steps run in pairs: step k updates only block row and column k+1, block k+1
+//   is factored, and then one K = 256 GEMM applies both steps to everything else
+//   (half the C traffic per flop of two K = 128 updates).
 // At the end S holds L^-1 (lower); U is the element-wise reversal of S.
 #include "gemm_f32.h"
 
@@ -303,6 +306,11 @@ __global__ __launch_bounds__(256) void diag_factor_kernel(float* __restrict__ S,
   if (tid == 0 && bad) st->not_spd = 1;
 }
 
+// Panel rows Lp_i live in a buffer of pitch kPP2 = 256: the panel of an even step
+// in columns 0..127, of an odd step in 128..255, so the two panels of a pair of
+// steps form one K = 256 operand.
+constexpr int kPP2 = 2 * kNb;
+
 // (2) Panel: blockIdx.x < nrow -> Lp for block row k+1+blockIdx.x;
 //            otherwise column tile (blockIdx.x - nrow) of row k: S[k,j] = X_kk S[k,j].
 __global__ __launch_bounds__(256, 2) void panel_kernel(float* __restrict__ S, int64_t b, int k,
@@ -315,10 +323,11 @@ __global__ __launch_bounds__(256, 2) void panel_kernel(float* __restrict__ S, in
   if ((int)blockIdx.x < nrow) {
     const int64_t i0 = k0 + kNb + (int64_t)blockIdx.x * kNb;
     const int rows = (int)((b - i0) < kNb ? (b - i0) : kNb);
+    float* Pk = P + (k & 1) * kNb;
     // A[i][kk] = S[i0+i][k0+kk]; B[kk][jj] = X_kk[jj][kk]
     gemm_tile_f32<true, true>(S + i0 * b + k0, b, rows, Xkk, b, nbk, nbk, acc, smem);
     gemm_foreach(acc, [&](int r, int c, float v) {
-      if (r < rows && c < nbk) P[(i0 + r) * kNb + c] = v;
+      if (r < rows && c < nbk) Pk[(i0 + r) * kPP2 + c] = v;
     });
   } else {
     const int64_t j0 = (int64_t)(blockIdx.x - nrow) * kNb;
@@ -330,30 +339,86 @@ __global__ __launch_bounds__(256, 2) void panel_kernel(float* __restrict__ S, in
   }
 }
 
-// (3) Trailing update over tiles (i, j), k < i < nblk, 0 <= j <= i.
+// One tile (i, j), i > k, j <= i, of step k's trailing update:
+//   C = S[i,j] - Lp_i [ X row k | X_kk | Lp_j^T ]   (j < k | j = k, C from zero | j > k)
+__device__ __forceinline__ void trailing_tile(float* __restrict__ S, int64_t b, int k, int nbk,
+                                              int i, int j, const float* __restrict__ P,
+                                              float* smem) {
+  const int64_t k0 = (int64_t)k * kNb, i0 = (int64_t)i * kNb, j0 = (int64_t)j * kNb;
+  const int rows = (int)((b - i0) < kNb ? (b - i0) : kNb);
+  const int cols = (int)((b - j0) < kNb ? (b - j0) : kNb);
+  const float* Pk = P + (k & 1) * kNb;
+  f32x16_t acc[2][2];
+  float* C = S + i0 * b + j0;
+  if (j == k) gemm_zero(acc);
+  else gemm_load_c(acc, C, b, rows, cols);
+  const float* A = Pk + i0 * kPP2;  // Lp_i, k-contig
+  if (j <= k) {
+    // B[kk][jj] = S[k0+kk][j0+jj]  (X row k for j < k, X_kk for j == k)
+    gemm_tile_f32<true, false>(A, kPP2, rows, S + k0 * b + j0, b, cols, nbk, acc, smem, true);
+  } else {
+    // B[kk][jj] = Lp_j[jj][kk]
+    gemm_tile_f32<true, true>(A, kPP2, rows, Pk + j0 * kPP2, kPP2, cols, nbk, acc, smem, true);
+  }
+  gemm_foreach(acc, [&](int r, int c, float v) {
+    if (r < rows && c < cols) C[(int64_t)r * b + c] = v;
+  });
+}
+
+// (3) Trailing update of one step over tiles (i, j), k < i < nblk, 0 <= j <= i.
 __global__ __launch_bounds__(256, 2) void trailing_kernel(float* __restrict__ S, int64_t b, int k,
                                                        int nbk, int nblk,
                                                        const float* __restrict__ P) {
   __shared__ __attribute__((aligned(16))) float smem[kGemmLdsFloats];
   int rem = blockIdx.x, i = k + 1;
   while (rem > i) { rem -= i + 1; ++i; }
-  const int j = rem;
   if (i >= nblk) return;
+  trailing_tile(S, b, k, nbk, i, rem, P, smem);
+}
+
+// (3a) First part of an even step k of a pair: only block row k+1 (tiles
+// (k+1, j), j <= k+1) and block column k+1 (tiles (i, k+1), i > k+1), which the
+// factorisation of block k+1 needs. Tile q < k+2 is (k+1, q), else (q, k+1).
+__global__ __launch_bounds__(256, 2) void trailing_next_kernel(float* __restrict__ S, int64_t b,
+                                                            int k, int nblk,
+                                                            const float* __restrict__ P) {
+  __shared__ __attribute__((aligned(16))) float smem[kGemmLdsFloats];
+  const int q = blockIdx.x;
+  if (q >= nblk) return;
+  const int i = q <= k + 1 ? k + 1 : q, j = q <= k + 1 ? q : k + 1;
+  trailing_tile(S, b, k, kNb, i, j, P, smem);
+}
+
+// (3b) The rest of steps k and k+1 together (k even, both blocks full), tiles
+// (i, j), i > k+1, j <= i, with K = 256 from the two panels [Lp_i(k) | Lp_i(k+1)]:
+//   j <  k  : S[i,j] -= [Lp_i(k) Lp_i(k+1)] [S[k,j] ; S[k+1,j]]   (the final X rows)
+//   j == k  : S[i,k]  = -[Lp_i(k) Lp_i(k+1)] [X_kk ; S[k+1,k]]
+//   j == k+1: S[i,k+1] = -Lp_i(k+1) X_{k+1,k+1}                    (K = 128)
+//   j >  k+1: S[i,j] -= [Lp_i(k) Lp_i(k+1)] [Lp_j(k)^T ; Lp_j(k+1)^T]
+// Rows k and k+1 of S are adjacent, so every B operand is one contiguous slab.
+__global__ __launch_bounds__(256, 3) void trailing_pair_kernel(float* __restrict__ S, int64_t b,
+                                                            int k, int nblk,
+                                                            const float* __restrict__ P) {
+  __shared__ __attribute__((aligned(16))) float smem[kGemmLdsFloats];
+  int rem = blockIdx.x, i = k + 2;
+  while (rem > i) { rem -= i + 1; ++i; }
+  if (i >= nblk) return;
+  const int j = rem;
   const int64_t k0 = (int64_t)k * kNb, i0 = (int64_t)i * kNb, j0 = (int64_t)j * kNb;
   const int rows = (int)((b - i0) < kNb ? (b - i0) : kNb);
   const int cols = (int)((b - j0) < kNb ? (b - j0) : kNb);
   f32x16_t acc[2][2];
   float* C = S + i0 * b + j0;
-  // C = C - Lp_i B (column block k is overwritten: it starts from zero)
-  if (j == k) gemm_zero(acc);
+  if (j == k || j == k + 1) gemm_zero(acc);
   else gemm_load_c(acc, C, b, rows, cols);
-  const float* A = P + i0 * kNb;  // Lp_i, k-contig, ld kNb
-  if (j <= k) {
-    // B[kk][jj] = S[k0+kk][j0+jj]  (X row k for j < k, X_kk for j == k)
-    gemm_tile_f32<true, false>(A, kNb, rows, S + k0 * b + j0, b, cols, nbk, acc, smem, true);
+  const float* A = P + i0 * kPP2;
+  if (j == k + 1) {
+    gemm_tile_f32<true, false>(A + kNb, kPP2, rows, S + (k0 + kNb) * b + j0, b, cols, kNb, acc,
+                               smem, true);
+  } else if (j <= k) {
+    gemm_tile_f32<true, false>(A, kPP2, rows, S + k0 * b + j0, b, cols, 2 * kNb, acc, smem, true);
   } else {
-    // B[kk][jj] = Lp_j[jj][kk]
-    gemm_tile_f32<true, true>(A, kNb, rows, P + j0 * kNb, kNb, cols, nbk, acc, smem, true);
+    gemm_tile_f32<true, true>(A, kPP2, rows, P + j0 * kPP2, kPP2, cols, 2 * kNb, acc, smem, true);
   }
   gemm_foreach(acc, [&](int r, int c, float v) {
     if (r < rows && c < cols) C[(int64_t)r * b + c] = v;
@@ -374,7 +439,7 @@ __global__ void reverse_kernel(const float* __restrict__ S, float* __restrict__ 
 
 hipError_t launch_chol_inv_inplace(float* S, int64_t b, float* P, DevState* st, hipStream_t s) {
   const int nblk = (int)cdiv(b, kNb);
-  for (int k = 0; k < nblk; ++k) {
+  auto factor_and_panel = [&](int k) -> hipError_t {
     const int64_t k0 = (int64_t)k * kNb;
     const int nbk = (int)((b - k0) < kNb ? (b - k0) : kNb);
     hipLaunchKernelGGL(diag_factor_kernel, dim3(1), dim3(256), 0, s, S, b, k0, nbk, st);
@@ -383,12 +448,25 @@ hipError_t launch_chol_inv_inplace(float* S, int64_t b, float* P, DevState* st, 
     const int nrow = nblk - k - 1;
     if (nrow + k > 0) {
       hipLaunchKernelGGL(panel_kernel, dim3(nrow + k), dim3(256), 0, s, S, b, k, nbk, nrow, P);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
+      e = hipGetLastError();
     }
+    return e;
+  };
+  // Steps in pairs (k, k+1): block row and column k+1 first, then one K = 256
+  // update of everything else. An odd last block is a single step.
+  for (int k = 0; k < nblk; k += 2) {
+    hipError_t e = factor_and_panel(k);
+    if (e != hipSuccess) return e;
+    if (k + 1 >= nblk) break;
+    hipLaunchKernelGGL(trailing_next_kernel, dim3((unsigned)nblk), dim3(256), 0, s, S, b, k, nblk,
+                       P);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = factor_and_panel(k + 1)) != hipSuccess) return e;
+    const int nrow = nblk - k - 2;
     if (nrow > 0) {
-      // tiles: sum_{i=k+1}^{nblk-1} (i+1)
-      const int64_t ntiles = (int64_t)(nblk + k + 2) * nrow / 2;
-      hipLaunchKernelGGL(trailing_kernel, dim3((unsigned)ntiles), dim3(256), 0, s, S, b, k, nbk,
+      // tiles: sum_{i=k+2}^{nblk-1} (i+1)
+      const int64_t ntiles = (int64_t)(nblk + k + 3) * nrow / 2;
+      hipLaunchKernelGGL(trailing_pair_kernel, dim3((unsigned)ntiles), dim3(256), 0, s, S, b, k,
                          nblk, P);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }

@@ -19,6 +19,15 @@
 
 namespace th {
 
+// threadIdx.x through an empty asm: index math derived from it cannot be shared
+// with (and kept alive from) an earlier use, e.g. the C-tile addresses of the
+// load before the K loop and of the stores after it.
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  __asm__ volatile("" : "+v"(t));
+  return t;
+}
+
 constexpr int kGemmBK = 32;
 constexpr int kGemmLdsPitch = 132;  // floats per staged k-row (128 + 4)
 constexpr int kGemmLdsFloats = 2 * kGemmBK * kGemmLdsPitch;
@@ -84,7 +93,7 @@ __device__ __forceinline__ void gemm_zero(f32x16_t (&acc)[2][2]) {
 // Visit every accumulator element with its tile-local (row, col).
 template <class F>
 __device__ __forceinline__ void gemm_foreach(const f32x16_t (&acc)[2][2], F&& f) {
-  const int tid = threadIdx.x;
+  const int tid = opaque_tid();
   const int lane = tid & 63, wave = tid >> 6;
   const int wi = (wave >> 1) * 64, wj = (wave & 1) * 64;
 #pragma unroll
@@ -102,7 +111,7 @@ __device__ __forceinline__ void gemm_foreach(const f32x16_t (&acc)[2][2], F&& f)
 // acc = C (row-major, ldc) on the valid rows x cols, 0 elsewhere.
 __device__ __forceinline__ void gemm_load_c(f32x16_t (&acc)[2][2], const float* __restrict__ C,
                                             int64_t ldc, int rows, int cols) {
-  const int tid = threadIdx.x;
+  const int tid = opaque_tid();
   const int lane = tid & 63, wave = tid >> 6;
   const int wi = (wave >> 1) * 64, wj = (wave & 1) * 64;
 #pragma unroll
@@ -226,7 +235,7 @@ __device__ __forceinline__ void g64_store_part(float* __restrict__ sm, int tid, 
 // Visit every accumulator element of the 64x64 tile with its tile-local (row, col).
 template <class F>
 __device__ __forceinline__ void g64_foreach(const f32x16_t& acc, F&& f) {
-  const int tid = threadIdx.x;
+  const int tid = opaque_tid();
   const int lane = tid & 63, wave = tid >> 6;
   const int wi = (wave >> 1) * 32, wj = (wave & 1) * 32;
 #pragma unroll
@@ -236,7 +245,7 @@ __device__ __forceinline__ void g64_foreach(const f32x16_t& acc, F&& f) {
 
 __device__ __forceinline__ void g64_load_c(f32x16_t& acc, const float* __restrict__ C, int64_t ldc,
                                            int rows, int cols) {
-  const int tid = threadIdx.x;
+  const int tid = opaque_tid();
   const int lane = tid & 63, wave = tid >> 6;
   const int wi = (wave >> 1) * 32, wj = (wave & 1) * 32;
 #pragma unroll
