@@ -13,7 +13,9 @@ Prints one JSON line. `roofline` is for the dominant kernel (the bf16 syrk),
 timed with HIP events on the stream it runs on; `cpu_baseline` is the fp64
 oracle on a bounded sample of the same workload, scaled to seconds per layer.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--pattern 2:4]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--pattern 2:4|4:8|unstructured]
+                       [--sparsity 0.5] [--no-cpu-baseline]
+(the headline line is the default 2:4; the other patterns are extra measurements)
 """
 from __future__ import annotations
 
@@ -67,7 +69,7 @@ def syrk_traffic():
         return None
 
 
-def cpu_baseline(X, W, c, b, n, pattern, block, lam_rel):
+def cpu_baseline(X, W, c, b, n, pattern, block, lam_rel, sparsity=0.5):
     """fp64 oracle on a bounded sample, scaled to seconds per layer.
 
     Sample: G from the first 1024 tokens (scaled by n/1024); the Cholesky check
@@ -90,7 +92,8 @@ def cpu_baseline(X, W, c, b, n, pattern, block, lam_rel):
     Wn = W.float().cpu().numpy()
     k_s = 3
     t0 = time.perf_counter()
-    O.prune_layer(Wn, G, pattern=pattern, block=block, lam=lam_rel, max_blocks=k_s)
+    O.prune_layer(Wn, G, sparsity=sparsity, pattern=pattern, block=block, lam=lam_rel,
+                  max_blocks=k_s)
     t_rest = time.perf_counter() - t0
     # split t_rest into the (unscaled) inverse and the sampled blocks
     H = O.hessian(G, O.damping(G, lam_rel))
@@ -99,7 +102,7 @@ def cpu_baseline(X, W, c, b, n, pattern, block, lam_rel):
     np.linalg.inv(H)
     t_inv = time.perf_counter() - t0
     t_blocks_s = max(t_rest - t_inv, 0.0)
-    s = block * (pattern[1] - pattern[0]) // pattern[1]
+    s = (block * (pattern[1] - pattern[0]) // pattern[1]) if pattern else round(block * sparsity)
 
     def cost(j0):
         f = b - j0
@@ -122,7 +125,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--pattern", default="2:4")
+    ap.add_argument("--pattern", default="2:4", help="N:M such as 2:4 or 4:8, or unstructured")
+    ap.add_argument("--sparsity", type=float, default=0.5, help="unstructured sparsity")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -141,7 +145,10 @@ def main():
     layer = cfg.layers[0]
     st = cfg.streams[layer.hessian]
     c, b, n = layer.c, layer.b, st.n
-    pn, pm = (int(v) for v in args.pattern.split(":"))
+    unstructured = args.pattern == "unstructured"
+    pn, pm = (0, 1) if unstructured else (int(v) for v in args.pattern.split(":"))
+    pattern = None if unstructured else (pn, pm)
+    pat_name = f"{args.sparsity:g} unstructured" if unstructured else f"{pn}:{pm}"
     block, lam_rel = cfg.block, cfg.lambda_rel
 
     _log(f"generating X [{n} x {b}] bf16 and W [{c} x {b}] on the GPU")
@@ -151,7 +158,8 @@ def main():
     W = torch.empty_like(W0)
     torch.cuda.synchronize()
 
-    params = L.make_params(pattern=(pn, pm), block=block, lam=lam_rel, relative=True)
+    params = L.make_params(sparsity=args.sparsity, pattern=pattern, block=block, lam=lam_rel,
+                           relative=True)
     ws = L.workspace(L.prune_layer_workspace_size(c, b, n, True, params), dev)
     Wout = torch.empty((c, b), dtype=torch.float32, device=dev)
     mask = torch.empty((c, b), dtype=torch.uint8, device=dev)
@@ -212,10 +220,13 @@ def main():
     floor_ms = (syrk_flops / (PEAK_BF16_TFLOPS * 1e12)
                 + (fact_flops + upd_flops) / (PEAK_FP32_TFLOPS * 1e12)) * 1e3
     m = mask.bool()
-    nm_ok = bool((m.view(c, -1, pm).sum(dim=2) == pm - pn).all().item())
+    if unstructured:  # the global budget is met exactly
+        count_ok = int(m.sum().item()) == info["pruned"] == round(args.sparsity * c * b)
+    else:  # exactly m - n pruned in every group of m
+        count_ok = bool((m.view(c, -1, pm).sum(dim=2) == pm - pn).all().item())
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.pattern == "2:4" else METRIC.replace("2:4", pat_name),
         "value": ms_step / 1000.0,
         "unit": "s",
         "n_gpus": 1,
@@ -227,7 +238,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16/fp32",
         "data": "synthetic",
-        "config": {"workload": f"down_proj {c}x{b}, {pn}:{pm}, block {block}, X {n} tokens bf16 "
+        "config": {"workload": f"down_proj {c}x{b}, {pat_name}, block {block}, X {n} tokens bf16 "
                                f"(ReLU-like, {st.outlier_count} channels x{st.outlier_scale:g}), "
                                f"lambda {lam_rel} relative"},
         "roofline": {"bound": "mfma", "kernel": "syrk_bf16_kernel", "achieved": achieved,
@@ -239,7 +250,7 @@ def main():
             "ms_per_layer_given_H": ms_given_h,
             "pruned_weights_per_s": info["pruned"] / (ms_step / 1000.0),
             "pruned": info["pruned"],
-            "nm_exact": nm_ok,
+            "counts_exact": count_ok,
             "at_peak_floor_ms": floor_ms,
             "mfma_utilisation_e2e": floor_ms / ms_step,
             "recon_error_rel": E_rel,
@@ -248,7 +259,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         _log("timing the fp64 oracle on a bounded sample (CPU)")
-        out["cpu_baseline"] = cpu_baseline(X, W0, c, b, n, (pn, pm), block, lam_rel)
+        out["cpu_baseline"] = cpu_baseline(X, W0, c, b, n, pattern, block, lam_rel, args.sparsity)
     print(json.dumps(out), flush=True)
 
 

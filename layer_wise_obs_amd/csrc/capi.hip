@@ -277,7 +277,10 @@ th_status th_prune_layer(void* W, th_dtype wdt, int64_t c, int64_t b, const void
   TH_HIP(launch_chol_inv_inplace(L.S, b, L.P, L.st, s), "cholesky/inverse");
   TH_HIP(launch_reverse(L.S, L.R, b, s), "reverse");
   TH_HIP(launch_save_diag_blocks(L.R, b, B, L.Ublk, s), "diag blocks");
-  if (L.D) TH_HIP(launch_colnorm_downdate(L.R, b, B, L.D, s), "column norms");
+  // S is free once reversed into R: it holds the fp64 partial sums
+  if (L.D)
+    TH_HIP(launch_colnorm_downdate(L.R, b, B, L.D, (double*)L.S, (size_t)b * b / 2, s),
+           "column norms");
   if (L.Nblk) TH_HIP(launch_block_inverses(L.Ublk, b, B, L.Nblk, s), "block inverses");
   TH_HIP(launch_transform_rows(L.R, b, B, L.Ublk, s), "transform rows");
 
@@ -291,10 +294,10 @@ th_status th_prune_layer(void* W, th_dtype wdt, int64_t c, int64_t b, const void
       const float* g = obs ? L.D + blk * b : L.gW;
       TH_HIP(launch_select_init(L.st, 0, blk == 0, (long long)(c * (b - j0)), s), "select init");
       for (int pass = 0; pass < 6; ++pass) {
-        TH_HIP(launch_select_pass(Wf, c, b, j0, g, obs ? 1 : 0, L.st, s), "select pass");
+        TH_HIP(launch_select_pass(Wf, c, b, j0, g, L.st, s), "select pass");
         TH_HIP(launch_select_pick(L.st, s), "select pick");
       }
-      TH_HIP(launch_solve_unstructured(Wf, c, b, j0, B, L.R, Nb, g, obs ? 1 : 0, L.Z, mask, L.st,
+      TH_HIP(launch_solve_unstructured(Wf, c, b, j0, B, L.R, Nb, g, L.Z, mask, L.st,
                                        L.counts + blk, s),
              "solve");
       TH_HIP(launch_update(Wf, c, b, j0, Bb, B, j0, b, L.Z, L.R, mask, j0, Bb, s), "update");

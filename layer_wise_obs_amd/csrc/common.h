@@ -110,19 +110,22 @@ hipError_t launch_save_diag_blocks(const float* U, int64_t b, int64_t B, float* 
                                    hipStream_t s);
 hipError_t launch_transform_rows(float* R, int64_t b, int64_t B, const float* Ublk,
                                  hipStream_t s);
+// D[r][q] = sum_{i = rB .. q} U_iq^2 (fp64 sums); scratch (optional, e.g. the free
+// S buffer) of at least ceil(b/B)*b doubles selects the two-pass coalesced version.
 hipError_t launch_colnorm_downdate(const float* U, int64_t b, int64_t B, float* D,
-                                   hipStream_t s);
+                                   double* scratch, size_t scratch_doubles, hipStream_t s);
 hipError_t launch_block_inverses(const float* Ublk, int64_t b, int64_t B, float* Nblk,
                                  hipStream_t s);
 
 // select.hip
 hipError_t launch_select_init(DevState* st, long long unused, int first, long long ncand,
                               hipStream_t s);
+// One radix pass over the keys of W[:, j0:] with score weights g, then the pick.
 hipError_t launch_select_pass(const float* W, int64_t c, int64_t b, int64_t j0,
-                              const float* g, int invert_g, DevState* st, hipStream_t s);
+                              const float* g, DevState* st, hipStream_t s);
+hipError_t launch_select_pick(DevState* st, hipStream_t s);
 hipError_t launch_select_scores_pass(const float* scores, int64_t c, int64_t f,
                                      int64_t b_full, int64_t j0, DevState* st, hipStream_t s);
-hipError_t launch_select_pick(DevState* st, hipStream_t s);
 
 // solve.hip
 hipError_t launch_solve_nm(const float* W, int64_t c, int64_t b, int64_t j0, int64_t B, int n,
@@ -130,7 +133,7 @@ hipError_t launch_solve_nm(const float* W, int64_t c, int64_t b, int64_t j0, int
                            int64_t ldz, uint8_t* mask, DevState* st, unsigned long long* blk_count,
                            hipStream_t s);
 hipError_t launch_solve_unstructured(const float* W, int64_t c, int64_t b, int64_t j0, int64_t B,
-                                     const float* R, const float* Nblk, const float* g, int obs,
+                                     const float* R, const float* Nblk, const float* g,
                                      float* Z, uint8_t* mask, DevState* st,
                                      unsigned long long* blk_count, hipStream_t s);
 hipError_t launch_debug_select_nm(const float* scores, int64_t c, int64_t blk, int n, int m,

@@ -9,7 +9,7 @@
 //
 //   save_diag_blocks : Ublk[J] = U_JJ                        (B x B, zero padded)
 //   transform_rows   : R[J, F] = U_JJ^T U[J, F] in place      (fp32 MFMA)
-//   colnorm_downdate : D[J][q] = [A_F]_qq for q in F          (OBS score over F)
+//   colnorm_downdate : D[J][q] = 1/[A_F]_qq for q in F        (OBS score weight over F)
 //   block_inverses   : N[J] = (A_F[J,J])^-1 = V_JJ V_JJ^T, V_JJ = U_JJ^-1
 //                      (used when a row selects more than half of a block)
 #include "gemm_f32.h"
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256, 2) void transform_rows_kernel(float* __restric
 }
 
 // One thread per column q: walk up the column of U accumulating squares and
-// record the partial sums at every block start j0 <= q.
+// record 1/(partial sum) at every block start j0 <= q (fallback for tiny B).
 __global__ void colnorm_kernel(const float* __restrict__ U, int64_t b, int64_t B,
                                float* __restrict__ D) {
   const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -71,9 +71,39 @@ __global__ void colnorm_kernel(const float* __restrict__ U, int64_t b, int64_t B
     const double u = U[i * b + q];
     s += u * u;
     if (i == blk * B) {
-      D[blk * b + q] = (float)s;
+      D[blk * b + q] = __fdiv_rn(1.0f, (float)s);
       --blk;
     }
+  }
+}
+
+// The same sums in two coalesced passes: P[r][q] = sum over rows i of block r
+// with i <= q of U_iq^2 (one workgroup per block row and 256 columns), then per
+// column a suffix sum over the blocks, stored as its reciprocal:
+// D[r][q] = 1 / sum_{r' >= r} P[r'][q], q >= r B.
+__global__ void colnorm_partial_kernel(const float* __restrict__ U, int64_t b, int64_t B,
+                                       double* __restrict__ P) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t r = blockIdx.y;
+  if (q >= b) return;
+  const int64_t j0 = r * B;
+  const int64_t j1 = (j0 + B) < b ? (j0 + B) : b;
+  double s = 0.0;
+  for (int64_t i = j0; i < j1; ++i) {
+    const double u = (i <= q) ? (double)U[i * b + q] : 0.0;
+    s += u * u;
+  }
+  P[r * b + q] = s;
+}
+
+__global__ void colnorm_scan_kernel(const double* __restrict__ P, int64_t b, int64_t B, int nblk,
+                                    float* __restrict__ D) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= b) return;
+  double s = 0.0;
+  for (int r = nblk - 1; r >= 0; --r) {
+    s += P[(int64_t)r * b + q];
+    if (q >= (int64_t)r * B) D[(int64_t)r * b + q] = __fdiv_rn(1.0f, (float)s);
   }
 }
 
@@ -145,7 +175,17 @@ hipError_t launch_transform_rows(float* R, int64_t b, int64_t B, const float* Ub
 }
 
 hipError_t launch_colnorm_downdate(const float* U, int64_t b, int64_t B, float* D,
-                                   hipStream_t s) {
+                                   double* scratch, size_t scratch_doubles, hipStream_t s) {
+  const int64_t nblk = cdiv(b, B);
+  if (scratch && (size_t)(nblk * b) <= scratch_doubles) {
+    hipLaunchKernelGGL(colnorm_partial_kernel, dim3((unsigned)cdiv(b, 256), (unsigned)nblk),
+                       dim3(256), 0, s, U, b, B, scratch);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(colnorm_scan_kernel, dim3((unsigned)cdiv(b, 256)), dim3(256), 0, s, scratch,
+                       b, B, (int)nblk, D);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(colnorm_kernel, dim3((unsigned)cdiv(b, 256)), dim3(256), 0, s, U, b, B, D);
   return hipGetLastError();
 }

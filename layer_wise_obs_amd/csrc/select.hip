@@ -11,9 +11,11 @@
 // candidate set is exactly { key < tbound } and ties in the score go to the
 // lower flat index. Each pass histograms one 11-bit digit (LDS histogram per
 // workgroup, integer atomics into the global one, so counts are exact and
-// order-independent); a one-workgroup pick kernel narrows the prefix. Budget,
-// prefix and threshold stay on the device: the host launches a fixed number of
-// passes and finished passes exit at once.
+// order-independent); a one-workgroup pick kernel narrows the prefix (a kernel
+// boundary orders the counts of all XCDs for it far more cheaply than a device-
+// scope fence in every workgroup would). Budget, prefix and threshold stay on
+// the device: the host launches a fixed number of passes and finished passes
+// exit at once.
 #include "common.h"
 
 namespace th {
@@ -45,62 +47,20 @@ __global__ void select_init_kernel(DevState* st, long long ncand) {
   }
 }
 
-template <class KeyF>
-__device__ __forceinline__ void hist_body(DevState* st, int64_t total, KeyF&& keyf) {
-  __shared__ unsigned int sh[kSelBins];
-  const int shift = st->shift;
-  int width;
-  digit_of(shift, width);
-  const int top = shift + width;
-  const unsigned long long prefix = st->prefix;
-  for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) sh[i] = 0u;
-  __syncthreads();
-  const unsigned long long dmask = (1ull << width) - 1ull;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const unsigned long long key = keyf(e);
-    const bool match = (top >= 64) || ((key >> top) == (prefix >> top));
-    if (match) atomicAdd(&sh[(key >> shift) & dmask], 1u);
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < kSelBins; i += blockDim.x)
-    if (sh[i]) atomicAdd(&st->hist[i], sh[i]);
-}
-
-// Keys recomputed from the current weights: S = W^2 * g, g = 1/D (OBS) or G_qq.
-__global__ __launch_bounds__(256) void select_pass_kernel(const float* __restrict__ W, int64_t c,
-                                                          int64_t b, int64_t j0,
-                                                          const float* __restrict__ g,
-                                                          int invert_g, DevState* st) {
+// Narrow the prefix by the digit whose bucket holds the rrem-th smallest key
+// (one workgroup of 256 threads), then clear the histogram for the next pass.
+__global__ __launch_bounds__(256) void select_pick_kernel(DevState* st) {
   if (st->done) return;
-  const int64_t f = b - j0;
-  hist_body(st, c * f, [&](int64_t e) {
-    const int64_t k = e / f, q = j0 + (e - k * f);
-    const float gq = invert_g ? __fdiv_rn(1.0f, g[q]) : g[q];
-    const float s = score_of(W[k * b + q], gq);
-    return make_key(s, (unsigned int)(k * b + q));
-  });
-}
-
-// Keys from given scores [c, f] (parity entry point).
-__global__ __launch_bounds__(256) void select_scores_pass_kernel(const float* __restrict__ S,
-                                                                 int64_t c, int64_t f,
-                                                                 int64_t b_full, int64_t j0,
-                                                                 DevState* st) {
-  if (st->done) return;
-  hist_body(st, c * f, [&](int64_t e) {
-    const int64_t k = e / f, q = e - k * f;
-    return make_key(S[e], (unsigned int)(k * b_full + j0 + q));
-  });
-}
-
-__global__ void select_pick_kernel(DevState* st) {
   __shared__ unsigned int part[256];
-  if (st->done) return;
+  __shared__ unsigned int hcopy[kSelBins];
   const int tid = threadIdx.x;
   const int per = kSelBins / 256;  // 8 bins per thread
   unsigned int local = 0;
-  for (int i = 0; i < per; ++i) local += st->hist[tid * per + i];
+  for (int i = 0; i < per; ++i) {
+    const unsigned int h = st->hist[tid * per + i];
+    hcopy[tid * per + i] = h;
+    local += h;
+  }
   part[tid] = local;
   __syncthreads();
   if (tid == 0) {
@@ -110,7 +70,7 @@ __global__ void select_pick_kernel(DevState* st) {
     for (int t = 0; t < 256 && d < 0; ++t) {
       if (cum + (long long)part[t] >= r) {
         for (int i = 0; i < per; ++i) {
-          const long long h = st->hist[t * per + i];
+          const long long h = hcopy[t * per + i];
           if (cum + h >= r) {
             d = t * per + i;
             break;
@@ -126,7 +86,7 @@ __global__ void select_pick_kernel(DevState* st) {
       st->tbound = st->prefix;
       st->done = 1;
     } else {
-      const long long inb = st->hist[d];
+      const long long inb = hcopy[d];
       const long long rnew = r - cum;
       st->prefix |= ((unsigned long long)d) << shift;
       st->rrem = rnew;
@@ -139,8 +99,57 @@ __global__ void select_pick_kernel(DevState* st) {
       }
     }
   }
-  __syncthreads();
   for (int i = tid; i < kSelBins; i += blockDim.x) st->hist[i] = 0u;
+}
+
+// Histogram of the current digit over the keys of rows k = blockIdx.x + m gridDim.x,
+// columns 0..f-1 (keyf(k, q)).
+template <class KeyF>
+__device__ __forceinline__ void pass_body(DevState* st, int64_t rows, int64_t f, KeyF&& keyf) {
+  __shared__ unsigned int sh[kSelBins];
+  const int shift = st->shift;
+  int width;
+  digit_of(shift, width);
+  const int top = shift + width;
+  const unsigned long long prefix = st->prefix;
+  for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) sh[i] = 0u;
+  __syncthreads();
+  const unsigned long long dmask = (1ull << width) - 1ull;
+  for (int64_t k = blockIdx.x; k < rows; k += gridDim.x) {
+    for (int64_t q = threadIdx.x; q < f; q += blockDim.x) {
+      const unsigned long long key = keyf(k, q);
+      const bool match = (top >= 64) || ((key >> top) == (prefix >> top));
+      if (match) atomicAdd(&sh[(key >> shift) & dmask], 1u);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kSelBins; i += blockDim.x)
+    if (sh[i]) atomicAdd(&st->hist[i], sh[i]);
+}
+
+// Keys recomputed from the current weights: S = W^2 * g with g the per-column
+// score weight (1/[A_F]_qq for OBS, G_qq for Wanda).
+__global__ __launch_bounds__(256) void select_pass_kernel(const float* __restrict__ W, int64_t c,
+                                                          int64_t b, int64_t j0,
+                                                          const float* __restrict__ g,
+                                                          DevState* st) {
+  if (st->done) return;
+  pass_body(st, c, b - j0, [&](int64_t k, int64_t q) {
+    const int64_t col = j0 + q;
+    const float s = score_of(W[k * b + col], g[col]);
+    return make_key(s, (unsigned int)(k * b + col));
+  });
+}
+
+// Keys from given scores [c, f] (parity entry point).
+__global__ __launch_bounds__(256) void select_scores_pass_kernel(const float* __restrict__ S,
+                                                                 int64_t c, int64_t f,
+                                                                 int64_t b_full, int64_t j0,
+                                                                 DevState* st) {
+  if (st->done) return;
+  pass_body(st, c, f, [&](int64_t k, int64_t q) {
+    return make_key(S[k * f + q], (unsigned int)(k * b_full + j0 + q));
+  });
 }
 
 }  // namespace
@@ -151,24 +160,21 @@ hipError_t launch_select_init(DevState* st, long long /*unused*/, int /*first*/,
   return hipGetLastError();
 }
 
-static unsigned hist_grid(int64_t total) {
-  int64_t g = cdiv(total, 256 * 8);
-  if (g > 2048) g = 2048;
-  if (g < 1) g = 1;
-  return (unsigned)g;
+static unsigned pass_grid(int64_t rows) {
+  int64_t g = rows < 1024 ? rows : 1024;
+  return (unsigned)(g < 1 ? 1 : g);
 }
 
 hipError_t launch_select_pass(const float* W, int64_t c, int64_t b, int64_t j0, const float* g,
-                              int invert_g, DevState* st, hipStream_t s) {
-  hipLaunchKernelGGL(select_pass_kernel, dim3(hist_grid(c * (b - j0))), dim3(256), 0, s, W, c, b,
-                     j0, g, invert_g, st);
+                              DevState* st, hipStream_t s) {
+  hipLaunchKernelGGL(select_pass_kernel, dim3(pass_grid(c)), dim3(256), 0, s, W, c, b, j0, g, st);
   return hipGetLastError();
 }
 
 hipError_t launch_select_scores_pass(const float* scores, int64_t c, int64_t f, int64_t b_full,
                                      int64_t j0, DevState* st, hipStream_t s) {
-  hipLaunchKernelGGL(select_scores_pass_kernel, dim3(hist_grid(c * f)), dim3(256), 0, s, scores,
-                     c, f, b_full, j0, st);
+  hipLaunchKernelGGL(select_scores_pass_kernel, dim3(pass_grid(c)), dim3(256), 0, s, scores, c, f,
+                     b_full, j0, st);
   return hipGetLastError();
 }
 

@@ -90,7 +90,7 @@ struct SolveArgs {
   const float* R;      // transformed rows: R[J, F] = [A_F]_{J,F}
   const float* Nblk;   // this block's N (route B), B x B
   const float* g;      // g_q source: mode 0 Wanda: gW; mode 1: D row (OBS) or gW
-  int g_mode;          // 0: 1/M_qq (OBS, N:M), 1: 1/g[q] (OBS, unstructured), 2: g[q] (Wanda)
+  int g_mode;          // 0: 1/M_qq (OBS, N:M), 2: g[q] given (OBS unstructured, Wanda)
   float* Z;            // c rows, pitch ldz: this block's coefficients
   uint8_t* mask;       // c x b
   DevState* st;
@@ -130,7 +130,6 @@ __global__ __launch_bounds__(kWaves * 64, 4) void solve_kernel(SolveArgs a) {
   for (int q = tid; q < Bb; q += blockDim.x) {
     float gq;
     if (a.g_mode == 0) gq = __fdiv_rn(1.0f, a.R[(j0 + q) * b + j0 + q]);
-    else if (a.g_mode == 1) gq = __fdiv_rn(1.0f, a.g[j0 + q]);
     else gq = a.g[j0 + q];
     sg[q] = gq;
   }
@@ -296,14 +295,14 @@ hipError_t launch_solve_nm(const float* W, int64_t c, int64_t b, int64_t j0, int
 }
 
 hipError_t launch_solve_unstructured(const float* W, int64_t c, int64_t b, int64_t j0, int64_t B,
-                                     const float* R, const float* Nblk, const float* g, int obs,
+                                     const float* R, const float* Nblk, const float* g,
                                      float* Z, uint8_t* mask, DevState* st,
                                      unsigned long long* blk_count, hipStream_t s) {
   SolveArgs a;
   a.W = W; a.c = c; a.b = b; a.j0 = j0;
   a.Bb = (int)((b - j0) < B ? (b - j0) : B);
   a.B = (int)B; a.n = 0; a.m = 1; a.R = R; a.Nblk = Nblk;
-  a.g = g; a.g_mode = obs ? 1 : 2;
+  a.g = g; a.g_mode = 2;  // per-column score weight given (1/[A_F]_qq or G_qq)
   a.Z = Z; a.ldz = B; a.mask = mask; a.st = st; a.blk_count = blk_count;
   hipLaunchKernelGGL((solve_kernel<1, 0>), dim3(solve_grid(c)), dim3(kWaves * 64), 0, s, a);
   hipError_t e = hipGetLastError();
