@@ -53,21 +53,21 @@ __device__ __forceinline__ bool nm_pruned(const float* sc, int e, int n, int m) 
 // columns past the system size hold the identity and a zero right-hand side, so
 // their steps change nothing). Returns x_lane = rhs_lane / pivot_lane. The pivot
 // row of step j equals column j of the (still symmetric) trailing block, i.e.
-// lane c's register j, broadcast with v_readlane; a step first reads all its
-// broadcasts into scalars and then issues the FMAs, so no FMA waits on the
-// readlane just before it. The pivot reciprocal is rcp plus one Newton step.
-__device__ __forceinline__ float gauss_jordan64(float (&reg)[64], float rhs) {
+// lane c's register j. Entries c < kLdsFrom are broadcast with v_readlane (a
+// VALU op each); for c >= kLdsFrom every lane stores its register j into a
+// per-wave LDS row and the entries are read back as wave-uniform 128-bit loads,
+// which moves part of the broadcast work from the VALU to the LDS pipe. The
+// pivot reciprocal is rcp plus one Newton step.
+constexpr int kLdsFrom = 32;
+
+__device__ __forceinline__ float gauss_jordan64(float (&reg)[64], float rhs, float* row) {
   const int lane = threadIdx.x & 63;
   float piv = 1.f;
   static_for<0, 64>([&](auto J) __attribute__((always_inline)) {
     constexpr int j = J;
+    if constexpr (j + 1 < 64) row[lane] = reg[j];
     const float p = bcast(reg[j], j);
     const float rj = bcast(rhs, j);
-    float row[64];
-    static_for<j + 1, 64>([&](auto C) __attribute__((always_inline)) {
-      constexpr int c = C;
-      row[c] = bcast(reg[j], c);
-    });
     float pinv = __builtin_amdgcn_rcpf(p);
     pinv = pinv * fmaf(-p, pinv, 2.f);
     const float f = (lane == j) ? 0.f : reg[j] * pinv;
@@ -75,7 +75,8 @@ __device__ __forceinline__ float gauss_jordan64(float (&reg)[64], float rhs) {
     rhs = fmaf(-f, rj, rhs);
     static_for<j + 1, 64>([&](auto C) __attribute__((always_inline)) {
       constexpr int c = C;
-      reg[c] = fmaf(-f, row[c], reg[c]);
+      const float v = (c >= kLdsFrom) ? row[c] : bcast(reg[j], c);
+      reg[c] = fmaf(-f, v, reg[c]);
     });
   });
   return rhs / piv;
@@ -104,7 +105,9 @@ __global__ __launch_bounds__(kWaves * 64, 4) void solve_kernel(SolveArgs a) {
   __shared__ float sbuf[kWaves][kMaxBlock];
   __shared__ float su[kWaves][kMaxBlock];
   __shared__ int sQ[kWaves][kMaxBlock];
-  __shared__ int sP[kWaves][64];
+  // sP (route B's complement list) is read only by the gather before the
+  // elimination, which then reuses the same words as its LDS pivot row.
+  __shared__ __attribute__((aligned(16))) int sP[kWaves][64];
   __shared__ unsigned long long scount[kWaves];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -190,7 +193,8 @@ __global__ __launch_bounds__(kWaves * 64, 4) void solve_kernel(SolveArgs a) {
           reg[c] = in ? v : ((c == lane) ? 1.f : 0.f);
         }
         const float u = act ? su[wave][lane] : 0.f;
-        const float z = gauss_jordan64(reg, u);
+        wave_sync();  // the gather's reads are done before the pivot row is written
+        const float z = gauss_jordan64(reg, u, (float*)sP[wave]);
         if (act) zrow[qa] = z;
       } else {
         const int p = Bb - s;
@@ -207,7 +211,8 @@ __global__ __launch_bounds__(kWaves * 64, 4) void solve_kernel(SolveArgs a) {
         if (act) {
           for (int t = 0; t < s; ++t) y = fmaf(su[wave][t], sM[mat_idx(sQ[wave][t], pb)], y);
         }
-        const float x = gauss_jordan64(reg, y);
+        wave_sync();  // the gather's reads of sP are done before it becomes the pivot row
+        const float x = gauss_jordan64(reg, y, (float*)sP[wave]);
         // v = [u on Q, -x on P], then z_q = (v N)_q for q in Q
         if (act) sbuf[wave][pb] = -x;
         if (s0) sbuf[wave][e0] = w0;
