@@ -221,6 +221,22 @@ def test_prune_nm_across_super_blocks(pattern, block, c, b):
     _check_layer(W, X, pattern=pattern, block=block)
 
 
+@pytest.mark.parametrize("c,b,n,block,pattern,sparsity,dtype", [
+    (1, 64, 256, 16, None, 0.5, torch.bfloat16),      # a single output row
+    (7, 40, 300, 8, (2, 4), 0.5, torch.float32),      # fp32 W and X, tiny blocks
+    (33, 136, 512, 1, None, 0.3, torch.float32),      # B = 1: one column per block
+    (64, 8, 64, 8, (4, 8), 0.5, torch.bfloat16),      # b = 8, fewer tokens than a stage
+    (20, 200, 1000, 128, None, 0.9, torch.bfloat16),  # 90%, ragged 72-column last block
+])
+def test_prune_degenerate_shapes(c, b, n, block, pattern, sparsity, dtype):
+    """Edge shapes against the oracle. With a handful of rows one near-tie flip is
+    a large fraction, so any number of rows may differ -- each only at an fp32
+    near-tie (the comparison checks that)."""
+    _say(f"prune degenerate c={c} b={b} n={n} B={block} {pattern or sparsity} {dtype}")
+    W, X = _inputs(c, b, n, 40, wdtype=dtype, xdtype=dtype, outliers=2)
+    _check_layer(W, X, sparsity=sparsity, pattern=pattern, block=block, max_flip_frac=1.0)
+
+
 def test_prune_unstructured_ragged_last_block():
     _say("prune unstructured c=200 b=392 ragged")
     W, X = _inputs(200, 392, 3000, 32)
