@@ -15,14 +15,17 @@
 //                LDS): X_kk = L_kk^-1, written back over the block;
 //            (2) panel:  Lp_i = S[i,k] X_kk^T for block rows i > k (to a buffer),
 //                        S[k,:k] = X_kk S[k,:k] (row k of L^-1 is now final);
-//            (3) trailing, one fp32 MFMA GEMM over all tiles (i > k, j <= i):
+//            (3) trailing, one GEMM over all tiles (i > k, j <= i):
 //                S[i,j] -= Lp_i [ X row k | -/X_kk | Lp_j^T ]  (j < k | j = k | j > k),
 //                where column block k is overwritten with -Lp_i X_kk.
 //   Steps run in pairs: step k updates only block row and column k+1, block k+1
 //   is factored, and then one K = 256 GEMM applies both steps to everything else
 //   (half the C traffic per flop of two K = 128 updates).
+// The panel and trailing GEMMs run on the bf16 matrix cores with three-way split
+// fp32 operands (gemm_x3.h: errors of the order of fp32 accumulation, at about a
+// third of the fp32 matrix-core time); the diagonal blocks stay in fp32.
 // At the end S holds L^-1 (lower); U is the element-wise reversal of S.
-#include "gemm_f32.h"
+#include "gemm_x3.h"
 
 namespace th {
 
@@ -315,7 +318,7 @@ constexpr int kPP2 = 2 * kNb;
 //            otherwise column tile (blockIdx.x - nrow) of row k: S[k,j] = X_kk S[k,j].
 __global__ __launch_bounds__(256, 2) void panel_kernel(float* __restrict__ S, int64_t b, int k,
                                                     int nbk, int nrow, float* __restrict__ P) {
-  __shared__ __attribute__((aligned(16))) float smem[kGemmLdsFloats];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kX3LdsBytes];
   const int64_t k0 = (int64_t)k * kNb;
   f32x16_t acc[2][2];
   gemm_zero(acc);
@@ -325,14 +328,14 @@ __global__ __launch_bounds__(256, 2) void panel_kernel(float* __restrict__ S, in
     const int rows = (int)((b - i0) < kNb ? (b - i0) : kNb);
     float* Pk = P + (k & 1) * kNb;
     // A[i][kk] = S[i0+i][k0+kk]; B[kk][jj] = X_kk[jj][kk]
-    gemm_tile_f32<true, true>(S + i0 * b + k0, b, rows, Xkk, b, nbk, nbk, acc, smem);
+    gemm_tile_x3<true>(S + i0 * b + k0, b, rows, Xkk, b, nbk, nbk, acc, smem);
     gemm_foreach(acc, [&](int r, int c, float v) {
       if (r < rows && c < nbk) Pk[(i0 + r) * kPP2 + c] = v;
     });
   } else {
     const int64_t j0 = (int64_t)(blockIdx.x - nrow) * kNb;
     // A = X_kk (k-contig), B[kk][jj] = S[k0+kk][j0+jj]
-    gemm_tile_f32<true, false>(Xkk, b, nbk, S + k0 * b + j0, b, kNb, nbk, acc, smem);
+    gemm_tile_x3<false>(Xkk, b, nbk, S + k0 * b + j0, b, kNb, nbk, acc, smem);
     gemm_foreach(acc, [&](int r, int c, float v) {
       if (r < nbk) S[(k0 + r) * b + j0 + c] = v;
     });
@@ -343,7 +346,7 @@ __global__ __launch_bounds__(256, 2) void panel_kernel(float* __restrict__ S, in
 //   C = S[i,j] - Lp_i [ X row k | X_kk | Lp_j^T ]   (j < k | j = k, C from zero | j > k)
 __device__ __forceinline__ void trailing_tile(float* __restrict__ S, int64_t b, int k, int nbk,
                                               int i, int j, const float* __restrict__ P,
-                                              float* smem) {
+                                              unsigned char* smem) {
   const int64_t k0 = (int64_t)k * kNb, i0 = (int64_t)i * kNb, j0 = (int64_t)j * kNb;
   const int rows = (int)((b - i0) < kNb ? (b - i0) : kNb);
   const int cols = (int)((b - j0) < kNb ? (b - j0) : kNb);
@@ -355,25 +358,14 @@ __device__ __forceinline__ void trailing_tile(float* __restrict__ S, int64_t b, 
   const float* A = Pk + i0 * kPP2;  // Lp_i, k-contig
   if (j <= k) {
     // B[kk][jj] = S[k0+kk][j0+jj]  (X row k for j < k, X_kk for j == k)
-    gemm_tile_f32<true, false>(A, kPP2, rows, S + k0 * b + j0, b, cols, nbk, acc, smem, true);
+    gemm_tile_x3<false>(A, kPP2, rows, S + k0 * b + j0, b, cols, nbk, acc, smem, true);
   } else {
     // B[kk][jj] = Lp_j[jj][kk]
-    gemm_tile_f32<true, true>(A, kPP2, rows, Pk + j0 * kPP2, kPP2, cols, nbk, acc, smem, true);
+    gemm_tile_x3<true>(A, kPP2, rows, Pk + j0 * kPP2, kPP2, cols, nbk, acc, smem, true);
   }
   gemm_foreach(acc, [&](int r, int c, float v) {
     if (r < rows && c < cols) C[(int64_t)r * b + c] = v;
   });
-}
-
-// (3) Trailing update of one step over tiles (i, j), k < i < nblk, 0 <= j <= i.
-__global__ __launch_bounds__(256, 2) void trailing_kernel(float* __restrict__ S, int64_t b, int k,
-                                                       int nbk, int nblk,
-                                                       const float* __restrict__ P) {
-  __shared__ __attribute__((aligned(16))) float smem[kGemmLdsFloats];
-  int rem = blockIdx.x, i = k + 1;
-  while (rem > i) { rem -= i + 1; ++i; }
-  if (i >= nblk) return;
-  trailing_tile(S, b, k, nbk, i, rem, P, smem);
 }
 
 // (3a) First part of an even step k of a pair: only block row k+1 (tiles
@@ -382,7 +374,7 @@ __global__ __launch_bounds__(256, 2) void trailing_kernel(float* __restrict__ S,
 __global__ __launch_bounds__(256, 2) void trailing_next_kernel(float* __restrict__ S, int64_t b,
                                                             int k, int nblk,
                                                             const float* __restrict__ P) {
-  __shared__ __attribute__((aligned(16))) float smem[kGemmLdsFloats];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kX3LdsBytes];
   const int q = blockIdx.x;
   if (q >= nblk) return;
   const int i = q <= k + 1 ? k + 1 : q, j = q <= k + 1 ? q : k + 1;
@@ -396,10 +388,10 @@ __global__ __launch_bounds__(256, 2) void trailing_next_kernel(float* __restrict
 //   j == k+1: S[i,k+1] = -Lp_i(k+1) X_{k+1,k+1}                    (K = 128)
 //   j >  k+1: S[i,j] -= [Lp_i(k) Lp_i(k+1)] [Lp_j(k)^T ; Lp_j(k+1)^T]
 // Rows k and k+1 of S are adjacent, so every B operand is one contiguous slab.
-__global__ __launch_bounds__(256, 3) void trailing_pair_kernel(float* __restrict__ S, int64_t b,
+__global__ __launch_bounds__(256, 2) void trailing_pair_kernel(float* __restrict__ S, int64_t b,
                                                             int k, int nblk,
                                                             const float* __restrict__ P) {
-  __shared__ __attribute__((aligned(16))) float smem[kGemmLdsFloats];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kX3LdsBytes];
   int rem = blockIdx.x, i = k + 2;
   while (rem > i) { rem -= i + 1; ++i; }
   if (i >= nblk) return;
@@ -413,12 +405,12 @@ __global__ __launch_bounds__(256, 3) void trailing_pair_kernel(float* __restrict
   else gemm_load_c(acc, C, b, rows, cols);
   const float* A = P + i0 * kPP2;
   if (j == k + 1) {
-    gemm_tile_f32<true, false>(A + kNb, kPP2, rows, S + (k0 + kNb) * b + j0, b, cols, kNb, acc,
+    gemm_tile_x3<false>(A + kNb, kPP2, rows, S + (k0 + kNb) * b + j0, b, cols, kNb, acc,
                                smem, true);
   } else if (j <= k) {
-    gemm_tile_f32<true, false>(A, kPP2, rows, S + k0 * b + j0, b, cols, 2 * kNb, acc, smem, true);
+    gemm_tile_x3<false>(A, kPP2, rows, S + k0 * b + j0, b, cols, 2 * kNb, acc, smem, true);
   } else {
-    gemm_tile_f32<true, true>(A, kPP2, rows, P + j0 * kPP2, kPP2, cols, 2 * kNb, acc, smem, true);
+    gemm_tile_x3<true>(A, kPP2, rows, P + j0 * kPP2, kPP2, cols, 2 * kNb, acc, smem, true);
   }
   gemm_foreach(acc, [&](int r, int c, float v) {
     if (r < rows && c < cols) C[(int64_t)r * b + c] = v;

@@ -2,8 +2,10 @@
 //
 // Update ("Pruning LLMs with Thanos", sections "Contribution one" and "The scaling
 // problem, and what SparseGPT changes": only still-active columns receive
-// compensation): W[:, F] -= Z [A_F]_{J,F}, a rank-B update on the fp32 matrix
-// cores, after which the pruned entries of block J are set to exactly zero.
+// compensation): W[:, F] -= Z [A_F]_{J,F}, a rank-B update (128 x 128 tiles on
+// the bf16 matrix cores with three-way split fp32 operands, gemm_x3.h; 64 x 64
+// tiles on the fp32 matrix cores for launches with few tiles), after which the
+// pruned entries of block J are set to exactly zero.
 // The kernel takes any column range and any K, so the driver can split one
 // block's update into the columns it needs now and a deferred part that is
 // applied for several blocks at once (K = several blocks).
@@ -11,7 +13,7 @@
 // Error ("The layer-reconstruction lens"): E = ||(W - What) X||_F^2 =
 // sum_k D_k G D_k^T, computed as T = D G per 128x128 tile (fp32 MFMA) with the
 // tile's sum of T .* D in fp64; partial sums are reduced in a fixed order.
-#include "gemm_f32.h"
+#include "gemm_x3.h"
 
 namespace th {
 
@@ -26,7 +28,7 @@ __global__ __launch_bounds__(256, 2) void update_kernel(float* __restrict__ W, i
                                                      const float* __restrict__ R,
                                                      const uint8_t* __restrict__ mask,
                                                      int64_t mask_j0, int64_t mask_jend) {
-  __shared__ __attribute__((aligned(16))) float smem[kGemmLdsFloats];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kX3LdsBytes];
   const int64_t row0 = (int64_t)(blockIdx.x / ncol_tiles) * 128;
   const int64_t col0 = col_begin + (int64_t)(blockIdx.x % ncol_tiles) * 128;
   const int rows = (int)((c - row0) < 128 ? (c - row0) : 128);
@@ -34,7 +36,7 @@ __global__ __launch_bounds__(256, 2) void update_kernel(float* __restrict__ W, i
   f32x16_t acc[2][2];
   float* C = W + row0 * b + col0;
   gemm_load_c(acc, C, b, rows, cols);  // W tile, then W - Z R
-  gemm_tile_f32<true, false>(Z + row0 * ldz, ldz, rows, R + r0 * b + col0, b, cols, K, acc, smem,
+  gemm_tile_x3<false>(Z + row0 * ldz, ldz, rows, R + r0 * b + col0, b, cols, K, acc, smem,
                              true);
   const bool masked = col0 < mask_jend && col0 + 128 > mask_j0;
   gemm_foreach(acc, [&](int r, int cc, float v) {
