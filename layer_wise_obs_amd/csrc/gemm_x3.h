@@ -32,24 +32,25 @@ constexpr int kX3LdsBytes = 6 * kX3Plane;              // A: 3 planes, B: 3 plan
 typedef short x3_v4i16 __attribute__((ext_vector_type(4)));
 typedef short x3_v8i16 __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ unsigned short x3_bits(__bf16 v) {
-  return __builtin_bit_cast(unsigned short, v);
+typedef float x3_f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 x3_b2 __attribute__((ext_vector_type(2)));
+
+// bf16 pair (round to nearest even, one v_cvt_pk_bf16_f32) and its exact fp32 value.
+__device__ __forceinline__ unsigned x3_round2(x3_f2 v, x3_f2& back) {
+  const unsigned p = __builtin_bit_cast(unsigned, __builtin_convertvector(v, x3_b2));
+  back = x3_f2{__builtin_bit_cast(float, p << 16), __builtin_bit_cast(float, p & 0xffff0000u)};
+  return p;
 }
 
-// x = h + m + l (+ |e| <= 2^-24 |x|), each part bf16, rounded to nearest even.
-__device__ __forceinline__ void x3_split(float x, unsigned short& h, unsigned short& m,
-                                         unsigned short& l) {
-  const __bf16 bh = (__bf16)x;
-  const float r1 = x - (float)bh;
-  const __bf16 bm = (__bf16)r1;
-  const float r2 = r1 - (float)bm;
-  h = x3_bits(bh);
-  m = x3_bits(bm);
-  l = x3_bits((__bf16)r2);
-}
-
-__device__ __forceinline__ unsigned x3_pack(unsigned short lo, unsigned short hi) {
-  return (unsigned)lo | ((unsigned)hi << 16);
+// Two values split at once: x = h + m + l (+ |e| <= 2^-24 |x|), each part bf16;
+// h, m and l are packed pairs (element 0 in the low half).
+__device__ __forceinline__ void x3_split2(x3_f2 x, unsigned& h, unsigned& m, unsigned& l) {
+  x3_f2 back;
+  h = x3_round2(x, back);
+  const x3_f2 r1 = x - back;
+  m = x3_round2(r1, back);
+  const x3_f2 r2 = r1 - back;
+  l = __builtin_bit_cast(unsigned, __builtin_convertvector(r2, x3_b2));
 }
 
 // Store one thread's 16 staged values, split into the three planes.
@@ -58,17 +59,15 @@ __device__ __forceinline__ unsigned x3_pack(unsigned short lo, unsigned short hi
 template <bool KC>
 __device__ __forceinline__ void x3_store_part(unsigned char* planes, int tid, const float (&r)[16],
                                               float sign) {
-  unsigned short h[16], m[16], l[16];
+  unsigned part[3][8];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) x3_split(sign * r[e], h[e], m[e], l[e]);
-  unsigned short* part[3] = {h, m, l};
+  for (int e = 0; e < 8; ++e)
+    x3_split2(x3_f2{sign * r[2 * e], sign * r[2 * e + 1]}, part[0][e], part[1][e], part[2][e]);
 #pragma unroll
   for (int p = 0; p < 3; ++p) {
-    const unsigned short* v = part[p];
-    const u32x4_t w0 = {x3_pack(v[0], v[1]), x3_pack(v[2], v[3]), x3_pack(v[4], v[5]),
-                        x3_pack(v[6], v[7])};
-    const u32x4_t w1 = {x3_pack(v[8], v[9]), x3_pack(v[10], v[11]), x3_pack(v[12], v[13]),
-                        x3_pack(v[14], v[15])};
+    const unsigned* v = part[p];
+    const u32x4_t w0 = {v[0], v[1], v[2], v[3]};
+    const u32x4_t w1 = {v[4], v[5], v[6], v[7]};
     unsigned char* base = planes + p * kX3Plane;
     if (KC) {
       const int i = tid >> 1, k0 = (tid & 1) * 16;
