@@ -26,6 +26,10 @@
  *   - The caller owns every buffer, including the workspace. The library never
  *     allocates device memory.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ *     The factorisation of the Hessian also runs part of its work on a stream
+ *     the library creates once per device and host thread (default priority);
+ *     that work is joined back into `stream` with events, so everything the
+ *     caller enqueues on `stream` afterwards sees the results.
  *     Entry points that return host values or a status that depends on device
  *     results synchronise that stream before returning.
  *   - Argument errors are reported before anything is launched. No C++
@@ -174,7 +178,7 @@ th_status th_debug_select_global(const float* scores, int64_t c, int64_t f, int6
 /* U = upper-triangular factor with H^-1 = U^T U (U = chol_upper(H^-1), the factor
  * [EXPL, "SparseGPT"] computes once per layer), from a damped, full symmetric H
  * [b,b] fp32. U [b,b] fp32 (strict lower triangle zero). workspace: >= b*b*4 +
- * ceil(b/128)*128*256*4 + 65536 bytes (TH_ERR_WORKSPACE if smaller). Returns
+ * 2*ceil(b/128)*128*256*4 + 65536 bytes (TH_ERR_WORKSPACE if smaller). Returns
  * TH_ERR_NOT_SPD on a non-positive pivot.
  * Synchronises. */
 th_status th_debug_factor(const float* H, int64_t b, float* U, void* workspace,

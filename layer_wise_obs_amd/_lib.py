@@ -237,7 +237,7 @@ def debug_factor(H):
     _require_cuda(H)
     b = H.shape[0]
     U = torch.empty_like(H)
-    nbytes = 4 * b * b + 4 * (-(-b // 128)) * 128 * 256 + (1 << 16)
+    nbytes = 4 * b * b + 2 * 4 * (-(-b // 128)) * 128 * 256 + (1 << 16)
     ws = workspace(nbytes, H.device)
     _check(lib().th_debug_factor(_ptr(H), b, _ptr(U), _ptr(ws), ws.numel(), _stream(H.device)))
     return U

@@ -101,7 +101,7 @@ PruneLayout layout_prune(void* ws, int64_t c, int64_t b, int64_t n, bool have_x,
   L.counts = cv.take<unsigned long long>(nblk);
   L.S = cv.take<float>((size_t)b * b);
   L.R = cv.take<float>((size_t)b * b);
-  L.P = cv.take<float>((size_t)cdiv(b, 128) * 128 * 256);
+  L.P = cv.take<float>(chol_panel_floats(b));
   L.Ublk = cv.take<float>((size_t)nblk * B * B);
   L.Nblk = needs_complement(p) ? cv.take<float>((size_t)nblk * B * B) : nullptr;
   const bool unstr = p->pattern.kind == TH_UNSTRUCTURED;
@@ -432,7 +432,7 @@ th_status th_debug_factor(const float* H, int64_t b, float* U, void* workspace,
   Carve cv(workspace);
   DevState* st = cv.take<DevState>(1);
   float* S = cv.take<float>((size_t)b * b);
-  float* P = cv.take<float>((size_t)cdiv(b, 128) * 128 * 256);
+  float* P = cv.take<float>(chol_panel_floats(b));
   if (workspace_bytes < cv.off) return fail(TH_ERR_WORKSPACE, "workspace too small");
   hipStream_t s = (hipStream_t)stream;
   TH_HIP(hipMemsetAsync(st, 0, sizeof(DevState), s), "memset");

@@ -101,6 +101,9 @@ hipError_t launch_wanda_diag(const float* H, int64_t b, const DevState* st, int 
                              float* gdiag, hipStream_t s);
 
 // factor.hip
+// panel: chol_panel_floats(b) floats. Part of the work runs on a library-owned
+// stream of the current device, joined back into s before the call returns.
+size_t chol_panel_floats(int64_t b);
 hipError_t launch_chol_inv_inplace(float* S, int64_t b, float* panel, DevState* st,
                                    hipStream_t s);
 hipError_t launch_reverse(const float* S, float* U, int64_t b, hipStream_t s);

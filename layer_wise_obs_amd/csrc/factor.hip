@@ -20,7 +20,12 @@
 //                where column block k is overwritten with -Lp_i X_kk.
 //   Steps run in pairs: step k updates only block row and column k+1, block k+1
 //   is factored, and then one K = 256 GEMM applies both steps to everything else
-//   (half the C traffic per flop of two K = 128 updates).
+//   (half the C traffic per flop of two K = 128 updates). That GEMM is split in
+//   two: the tiles the next pair's factorisation reads first (block rows and
+//   columns k+2, k+3) run on the caller's stream, the rest on a second stream as
+//   a persistent kernel of one workgroup per compute unit, so that the next
+//   pair's diagonal blocks, panels and row/column update (a chain of small,
+//   latency-bound kernels) run beside the bulk of the update.
 // The panel and trailing GEMMs run on the bf16 matrix cores with three-way split
 // fp32 operands (gemm_x3.h: errors of the order of fp32 accumulation, at about a
 // third of the fp32 matrix-core time); the diagonal blocks stay in fp32.
@@ -214,6 +219,9 @@ __device__ __forceinline__ f32x16_t lds_mfma_tile32(f32x16_t acc, FA&& a, FB&& b
 // A block narrower than 128 (the last one) is padded with the identity.
 __global__ __launch_bounds__(256) void diag_factor_kernel(float* __restrict__ S, int64_t b,
                                                           int64_t k0, int nbk, DevState* st) {
+  // This kernel and the panel and row/column updates form the serial chain that
+  // runs beside the rest set of the previous pair: their waves issue first.
+  __builtin_amdgcn_s_setprio(3);
   __shared__ float sS[kNb * kSP];
   __shared__ float sP[3 * kBase * kPP];
   __shared__ float sT[kBase16 * kPP16];
@@ -318,6 +326,8 @@ constexpr int kPP2 = 2 * kNb;
 //            otherwise column tile (blockIdx.x - nrow) of row k: S[k,j] = X_kk S[k,j].
 __global__ __launch_bounds__(256, 2) void panel_kernel(float* __restrict__ S, int64_t b, int k,
                                                     int nbk, int nrow, float* __restrict__ P) {
+  // on the serial chain (see diag_factor_kernel)
+  __builtin_amdgcn_s_setprio(2);
   __shared__ __attribute__((aligned(16))) unsigned char smem[kX3LdsBytes];
   const int64_t k0 = (int64_t)k * kNb;
   f32x16_t acc[2][2];
@@ -374,6 +384,8 @@ __device__ __forceinline__ void trailing_tile(float* __restrict__ S, int64_t b, 
 __global__ __launch_bounds__(256, 2) void trailing_next_kernel(float* __restrict__ S, int64_t b,
                                                             int k, int nblk,
                                                             const float* __restrict__ P) {
+  // on the serial chain (see diag_factor_kernel)
+  __builtin_amdgcn_s_setprio(2);
   __shared__ __attribute__((aligned(16))) unsigned char smem[kX3LdsBytes];
   const int q = blockIdx.x;
   if (q >= nblk) return;
@@ -381,21 +393,15 @@ __global__ __launch_bounds__(256, 2) void trailing_next_kernel(float* __restrict
   trailing_tile(S, b, k, kNb, i, j, P, smem);
 }
 
-// (3b) The rest of steps k and k+1 together (k even, both blocks full), tiles
+// (3b) The rest of steps k and k+1 together (k even, both blocks full): tile
 // (i, j), i > k+1, j <= i, with K = 256 from the two panels [Lp_i(k) | Lp_i(k+1)]:
 //   j <  k  : S[i,j] -= [Lp_i(k) Lp_i(k+1)] [S[k,j] ; S[k+1,j]]   (the final X rows)
 //   j == k  : S[i,k]  = -[Lp_i(k) Lp_i(k+1)] [X_kk ; S[k+1,k]]
 //   j == k+1: S[i,k+1] = -Lp_i(k+1) X_{k+1,k+1}                    (K = 128)
 //   j >  k+1: S[i,j] -= [Lp_i(k) Lp_i(k+1)] [Lp_j(k)^T ; Lp_j(k+1)^T]
 // Rows k and k+1 of S are adjacent, so every B operand is one contiguous slab.
-__global__ __launch_bounds__(256, 2) void trailing_pair_kernel(float* __restrict__ S, int64_t b,
-                                                            int k, int nblk,
-                                                            const float* __restrict__ P) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kX3LdsBytes];
-  int rem = blockIdx.x, i = k + 2;
-  while (rem > i) { rem -= i + 1; ++i; }
-  if (i >= nblk) return;
-  const int j = rem;
+__device__ __forceinline__ void pair_tile(float* __restrict__ S, int64_t b, int k, int i, int j,
+                                          const float* __restrict__ P, unsigned char* smem) {
   const int64_t k0 = (int64_t)k * kNb, i0 = (int64_t)i * kNb, j0 = (int64_t)j * kNb;
   const int rows = (int)((b - i0) < kNb ? (b - i0) : kNb);
   const int cols = (int)((b - j0) < kNb ? (b - j0) : kNb);
@@ -417,6 +423,63 @@ __global__ __launch_bounds__(256, 2) void trailing_pair_kernel(float* __restrict
   });
 }
 
+// The pair's tiles split in two sets. "Look-ahead": block rows k+2 and k+3
+// (every j <= i) and block columns k+2, k+3 below them -- everything the
+// factorisation of blocks k+2 and k+3 reads. "Rest": all other tiles (i >= k+4,
+// j not in {k+2, k+3}), which the next pair's trailing update is the first to
+// read. The rest runs on a second stream while the next pair's diagonal blocks
+// and panels run behind the look-ahead set.
+__host__ __device__ inline int64_t look_tiles(int k, int nblk) {
+  const int kk = k + 2;
+  if (kk >= nblk) return 0;
+  int64_t n = kk + 1;                                   // row kk
+  if (kk + 1 < nblk) n += kk + 2;                       // row kk+1
+  if (kk + 2 < nblk) n += 2 * (int64_t)(nblk - kk - 2); // columns kk, kk+1 below
+  return n;
+}
+__host__ __device__ inline int64_t rest_tiles(int k, int nblk) {
+  const int64_t lo = k + 4, hi = nblk - 1;  // rows i in [k+4, nblk-1], i-1 tiles each
+  if (lo > hi) return 0;
+  return (hi + lo - 2) * (hi - lo + 1) / 2;
+}
+
+__global__ __launch_bounds__(256, 2) void trailing_look_kernel(float* __restrict__ S, int64_t b,
+                                                            int k, int nblk,
+                                                            const float* __restrict__ P) {
+  // on the serial chain (see diag_factor_kernel)
+  __builtin_amdgcn_s_setprio(2);
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kX3LdsBytes];
+  const int kk = k + 2;
+  int q = blockIdx.x, i, j;
+  if (q <= kk) {
+    i = kk; j = q;
+  } else if (kk + 1 < nblk && q <= 2 * kk + 2) {
+    i = kk + 1; j = q - (kk + 1);
+  } else {
+    q -= (kk + 1) + (kk + 1 < nblk ? kk + 2 : 0);
+    i = kk + 2 + (q >> 1); j = kk + (q & 1);
+    if (i >= nblk) return;
+  }
+  pair_tile(S, b, k, i, j, P, smem);
+}
+
+// Persistent over the rest set: workgroup w takes tiles w, w + gridDim.x, ...
+// (row-major over rows i >= k+4, skipping columns k+2 and k+3).
+__global__ __launch_bounds__(256, 2) void trailing_rest_kernel(float* __restrict__ S, int64_t b,
+                                                            int k, int nblk, int64_t ntiles,
+                                                            const float* __restrict__ P) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kX3LdsBytes];
+  const int kk = k + 2;
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    int64_t rem = t;
+    int i = kk + 2;
+    while (rem >= i - 1) { rem -= i - 1; ++i; }
+    const int j = (int)rem < kk ? (int)rem : (int)rem + 2;
+    pair_tile(S, b, k, i, j, P, smem);
+    __syncthreads();  // the next tile's staging reuses the LDS planes
+  }
+}
+
 // U[a][c] = S[b-1-a][b-1-c] for c >= a, 0 below the diagonal (a flat reversal).
 __global__ void reverse_kernel(const float* __restrict__ S, float* __restrict__ U, int64_t b) {
   const int64_t n = b * b;
@@ -429,41 +492,104 @@ __global__ void reverse_kernel(const float* __restrict__ S, float* __restrict__ 
 
 }  // namespace
 
+namespace {
+
+// A second stream and two events per device and host thread (created on first
+// use, kept until the process ends). Default priority, non-blocking. `slots` is
+// the rest set's persistent grid: one workgroup per compute unit, so that every
+// unit keeps room (LDS and registers) for one workgroup of the next pair's
+// diagonal factor, panels and row/column update, which run beside it.
+struct SideStream {
+  hipStream_t s2 = nullptr;
+  hipEvent_t chain = nullptr, rest = nullptr;
+  int slots = 0;
+};
+
+hipError_t side_stream(SideStream*& out) {
+  constexpr int kMaxDev = 64;
+  thread_local SideStream tab[kMaxDev];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  SideStream& t = tab[dev];
+  if (!t.s2) {
+    int ncu = 0;
+    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+      return e;
+    if ((e = hipEventCreateWithFlags(&t.chain, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&t.rest, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipStreamCreateWithFlags(&t.s2, hipStreamNonBlocking)) != hipSuccess) return e;
+    t.slots = ncu > 0 ? ncu : 1;
+  }
+  out = &t;
+  return hipSuccess;
+}
+
+}  // namespace
+
+size_t chol_panel_floats(int64_t b) { return 2 * (size_t)cdiv(b, kNb) * kNb * kPP2; }
+
 hipError_t launch_chol_inv_inplace(float* S, int64_t b, float* P, DevState* st, hipStream_t s) {
   const int nblk = (int)cdiv(b, kNb);
-  auto factor_and_panel = [&](int k) -> hipError_t {
+  SideStream* side = nullptr;
+  hipError_t e = side_stream(side);
+  if (e != hipSuccess) return e;
+  // Two panel buffers: pair p writes buffer p % 2 while the rest set of pair
+  // p - 1 may still read the other one.
+  const size_t pbuf = (size_t)cdiv(b, kNb) * kNb * kPP2;
+  auto factor_and_panel = [&](int k, float* Pp) -> hipError_t {
     const int64_t k0 = (int64_t)k * kNb;
     const int nbk = (int)((b - k0) < kNb ? (b - k0) : kNb);
     hipLaunchKernelGGL(diag_factor_kernel, dim3(1), dim3(256), 0, s, S, b, k0, nbk, st);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e2 = hipGetLastError();
+    if (e2 != hipSuccess) return e2;
     const int nrow = nblk - k - 1;
     if (nrow + k > 0) {
-      hipLaunchKernelGGL(panel_kernel, dim3(nrow + k), dim3(256), 0, s, S, b, k, nbk, nrow, P);
-      e = hipGetLastError();
+      hipLaunchKernelGGL(panel_kernel, dim3(nrow + k), dim3(256), 0, s, S, b, k, nbk, nrow, Pp);
+      e2 = hipGetLastError();
     }
-    return e;
+    return e2;
   };
   // Steps in pairs (k, k+1): block row and column k+1 first, then one K = 256
-  // update of everything else. An odd last block is a single step.
-  for (int k = 0; k < nblk; k += 2) {
-    hipError_t e = factor_and_panel(k);
-    if (e != hipSuccess) return e;
+  // update of everything else, split into the look-ahead set (stream s) and the
+  // rest set (side stream). The next pair's diagonal blocks and panels wait only
+  // for the look-ahead set; the next pair's update waits for the rest set.
+  // An odd last block is a single step.
+  bool rest_pending = false;
+  for (int k = 0, pair = 0; k < nblk; k += 2, ++pair) {
+    float* Pp = P + (size_t)(pair & 1) * pbuf;
+    if ((e = factor_and_panel(k, Pp)) != hipSuccess) return e;
     if (k + 1 >= nblk) break;
     hipLaunchKernelGGL(trailing_next_kernel, dim3((unsigned)nblk), dim3(256), 0, s, S, b, k, nblk,
-                       P);
+                       Pp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = factor_and_panel(k + 1)) != hipSuccess) return e;
-    const int nrow = nblk - k - 2;
-    if (nrow > 0) {
-      // tiles: sum_{i=k+2}^{nblk-1} (i+1)
-      const int64_t ntiles = (int64_t)(nblk + k + 3) * nrow / 2;
-      hipLaunchKernelGGL(trailing_pair_kernel, dim3((unsigned)ntiles), dim3(256), 0, s, S, b, k,
-                         nblk, P);
+    if ((e = factor_and_panel(k + 1, Pp)) != hipSuccess) return e;
+    // the previous pair's rest set covers tiles of this pair's look-ahead set
+    if (rest_pending) {
+      if ((e = hipStreamWaitEvent(s, side->rest, 0)) != hipSuccess) return e;
+      rest_pending = false;
+    }
+    const int64_t nrest = rest_tiles(k, nblk);
+    if (nrest > 0) {
+      if ((e = hipEventRecord(side->chain, s)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(side->s2, side->chain, 0)) != hipSuccess) return e;
+      const int64_t grid = nrest < side->slots ? nrest : side->slots;
+      hipLaunchKernelGGL(trailing_rest_kernel, dim3((unsigned)grid), dim3(256), 0, side->s2, S, b,
+                         k, nblk, nrest, Pp);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = hipEventRecord(side->rest, side->s2)) != hipSuccess) return e;
+      rest_pending = true;
+    }
+    const int64_t nlook = look_tiles(k, nblk);
+    if (nlook > 0) {
+      hipLaunchKernelGGL(trailing_look_kernel, dim3((unsigned)nlook), dim3(256), 0, s, S, b, k,
+                         nblk, Pp);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
-  return hipSuccess;
+  if (rest_pending) e = hipStreamWaitEvent(s, side->rest, 0);
+  return e;
 }
 
 hipError_t launch_reverse(const float* S, float* U, int64_t b, hipStream_t s) {

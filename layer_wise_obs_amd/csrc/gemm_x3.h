@@ -12,22 +12,35 @@
 // of eight fp32 ones (8 x 64 cycles).
 //
 // Operands are split once, when a K step of 32 is staged in LDS, into three
-// bf16 planes:
-//   k-contiguous operands (A always; B when B_KC): rows of 32 k (pitch 40 bf16),
-//     MFMA fragments are 16-byte reads;
+// bf16 planes, laid out so that every LDS access below is free of bank conflicts
+// (64 banks of 4 bytes; a 16-byte access serves 16 lanes per cycle, an 8-byte
+// access 32):
+//   k-contiguous operands (A always; B when B_KC): one 64-byte row of 32 k per
+//     output row, its four 16-byte units XOR-swizzled by (row >> 2) & 3; MFMA
+//     fragments are 16-byte reads;
 //   B with k as the row index (B_KC false): rows of 128 values (256 bytes) with
-//     16-byte pieces XOR-swizzled by (k & 3), fragments by ds_read_b64_tr_b16.
+//     16-byte pieces XOR-swizzled by 4 (k & 3) + (k & 1), fragments by
+//     ds_read_b64_tr_b16.
 #pragma once
 
 #include "gemm_f32.h"
 
 namespace th {
 
-constexpr int kX3KPitch = 40;                          // bf16 per k-contiguous plane row
-constexpr int kX3KPlane = 128 * kX3KPitch * 2;         // bytes of a k-contiguous plane
+constexpr int kX3KRow = 64;                            // bytes per row of a k-contiguous plane
 constexpr int kX3NRow = 256;                           // bytes per k row of an n-contiguous plane
-constexpr int kX3Plane = kX3KPlane;                    // plane slot (the larger layout)
+constexpr int kX3Plane = 128 * kX3KRow;                // bytes of a plane (either layout)
+static_assert(kX3Plane == 32 * kX3NRow, "both plane layouts hold 128 x 32 values");
 constexpr int kX3LdsBytes = 6 * kX3Plane;              // A: 3 planes, B: 3 planes
+
+// Byte offset of 16-byte unit u (k = 8u .. 8u+7) of row r in a k-contiguous plane.
+__device__ __forceinline__ int x3_kc_off(int r, int u) {
+  return r * kX3KRow + ((u ^ ((r >> 2) & 3)) << 4);
+}
+// Byte offset of piece fg (values 8 fg .. 8 fg + 7) of k row k in an n-contiguous plane.
+__device__ __forceinline__ int x3_n_off(int k, int fg) {
+  return k * kX3NRow + ((fg ^ ((k & 3) << 2) ^ (k & 1)) << 4);
+}
 
 typedef short x3_v4i16 __attribute__((ext_vector_type(4)));
 typedef short x3_v8i16 __attribute__((ext_vector_type(8)));
@@ -70,15 +83,13 @@ __device__ __forceinline__ void x3_store_part(unsigned char* planes, int tid, co
     const u32x4_t w1 = {v[4], v[5], v[6], v[7]};
     unsigned char* base = planes + p * kX3Plane;
     if (KC) {
-      const int i = tid >> 1, k0 = (tid & 1) * 16;
-      unsigned char* row = base + i * (kX3KPitch * 2) + k0 * 2;
-      *(u32x4_t*)row = w0;
-      *(u32x4_t*)(row + 16) = w1;
+      const int i = tid >> 1, u0 = (tid & 1) * 2;
+      *(u32x4_t*)(base + x3_kc_off(i, u0)) = w0;
+      *(u32x4_t*)(base + x3_kc_off(i, u0 + 1)) = w1;
     } else {
       const int k = tid >> 3, fg0 = (tid & 7) * 2;  // 8-value pieces fg0, fg0+1
-      unsigned char* row = base + k * kX3NRow;
-      *(u32x4_t*)(row + ((fg0 ^ ((k & 3) << 2)) << 4)) = w0;
-      *(u32x4_t*)(row + (((fg0 + 1) ^ ((k & 3) << 2)) << 4)) = w1;
+      *(u32x4_t*)(base + x3_n_off(k, fg0)) = w0;
+      *(u32x4_t*)(base + x3_n_off(k, fg0 + 1)) = w1;
     }
   }
 }
@@ -87,8 +98,8 @@ __device__ __forceinline__ void x3_store_part(unsigned char* planes, int tid, co
 // lane l holds row r0 + l%32, k0 + 8*(l/32) .. +7.
 __device__ __forceinline__ bf16x8_t x3_frag_kc(const unsigned char* plane, int r0, int k0,
                                                int lane) {
-  const unsigned char* p =
-      plane + (r0 + (lane & 31)) * (kX3KPitch * 2) + (k0 + 8 * (lane >> 5)) * 2;
+  const int r = r0 + (lane & 31);
+  const unsigned char* p = plane + x3_kc_off(r, (k0 >> 3) + (lane >> 5));
   return __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)p);
 }
 
@@ -101,13 +112,10 @@ __device__ __forceinline__ bf16x8_t x3_frag_tr(const unsigned char* plane, int n
   const int fb = n0 + ((g & 1) << 4) + ((s & 3) << 2);
   const int tb = k0 + ((g >> 1) << 3) + (s >> 2);
   const int fg = fb >> 3, within = (fb & 7) << 1;
-  const int t2 = tb + 4;
   const x3_v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) x3_v4i16*)(plane + tb * kX3NRow +
-                                                     ((fg ^ ((tb & 3) << 2)) << 4) + within));
+      (__attribute__((address_space(3))) x3_v4i16*)(plane + x3_n_off(tb, fg) + within));
   const x3_v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) x3_v4i16*)(plane + t2 * kX3NRow +
-                                                     ((fg ^ ((t2 & 3) << 2)) << 4) + within));
+      (__attribute__((address_space(3))) x3_v4i16*)(plane + x3_n_off(tb + 4, fg) + within));
   const x3_v8i16 r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8_t, r);
 }
