@@ -92,7 +92,7 @@ def test_hessian_accumulates_over_chunks():
 
 # ------------------------------------------------------------ factorisation
 
-@pytest.mark.parametrize("b", [130, 300, 512])
+@pytest.mark.parametrize("b", [130, 300, 512, 1500, 1664])
 def test_factor_matches_inverse_cholesky(b):
     _say(f"factor b={b}")
     _, X = _inputs(4, b, 4 * b, 21, xdtype=torch.float32)
@@ -105,6 +105,22 @@ def test_factor_matches_inverse_cholesky(b):
     # U H U^T = I
     R = U.astype(np.float64) @ H @ U.astype(np.float64).T
     assert np.max(np.abs(R - np.eye(b))) <= 1e-3
+
+
+def test_factor_same_on_a_side_stream():
+    """Part of the factorisation runs on a library stream joined back into the
+    caller's; the result must not depend on which stream the caller uses."""
+    _say("factor on a non-default stream")
+    b = 1664  # 13 blocks: several pairs with a rest set, odd last step
+    _, X = _inputs(4, b, 2 * b, 23, xdtype=torch.float32)
+    G = O.gram(X)
+    H = torch.tensor(O.hessian(G, O.damping(G)), dtype=torch.float32, device=DEV)
+    U0 = L.debug_factor(H)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        U1 = L.debug_factor(H)
+    s.synchronize()
+    assert torch.equal(U0, U1)
 
 
 def test_factor_reports_not_spd():
