@@ -175,6 +175,36 @@ th_status th_debug_select_global(const float* scores, int64_t c, int64_t f, int6
                                  int32_t* s_k, void* workspace, size_t workspace_bytes,
                                  th_stream_t stream);
 
+/* ---- Comparators without compensation ------------------------------------
+ * [EXPL, "Wanda: Pruning by Weights and Activations"]: score |W_kq| * ||X_q||_2,
+ * thresholds computed per output row, no update of the remaining weights.
+ * [EXPL, "The Failure of Magnitude Pruning in Large Transformers"]: rank by
+ * |W_kq| and remove the smallest (compared here per output row, like Wanda).
+ * [BLOG, "Why magnitude alone misses important weights"]: W_kq^2 G_qq (G = X X^T)
+ * orders like the Wanda score. [EXPL, "N:M Semi-Structured Sparsity (2:4
+ * Pattern)"]: both enforce the pattern within every aligned group of m. */
+typedef enum { TH_BASE_MAGNITUDE = 0, TH_BASE_WANDA = 1 } th_baseline;
+
+/* gdiag[q] = G_qq = sum_t X_tq^2 (fp64 accumulation in a fixed order, rounded to
+ * fp32). X token-major [n, b] (row pitch ldx >= b), bf16 or fp32; gdiag: b floats.
+ * workspace (device) >= th_column_sq_norms_workspace_size bytes. Asynchronous. */
+th_status th_column_sq_norms_workspace_size(int64_t n, int64_t b, size_t* bytes /* host */);
+th_status th_column_sq_norms(const void* X, th_dtype xdt, int64_t n, int64_t b, int64_t ldx,
+                             float* gdiag, void* workspace, size_t workspace_bytes,
+                             th_stream_t stream);
+
+/* Prune W (c x b, bf16 or fp32) in place: the pruned entries become exactly 0,
+ * every other entry is left unchanged. Key of (k, q): w^2 rounded to fp32, times
+ * gdiag[q] (Wanda; gdiag required, device, b floats) or times 1 (magnitude;
+ * gdiag ignored), rounded to fp32; among equal keys the lower column is pruned
+ * first. Unstructured (p->pattern.kind): every row loses its round-half-even(
+ * p->sparsity * b) smallest keys. N:M: in every aligned group of m along a row,
+ * the m-n smallest (1 <= m <= 128, m | b). p->block, lambda and score are not
+ * used. mask_out (optional, device, c x b uint8): 1 = pruned. Asynchronous. */
+th_status th_prune_baseline(void* W, th_dtype wdt, int64_t c, int64_t b, th_baseline method,
+                            const float* gdiag, const th_prune_params* p, uint8_t* mask_out,
+                            th_stream_t stream);
+
 /* U = upper-triangular factor with H^-1 = U^T U (U = chol_upper(H^-1), the factor
  * [EXPL, "SparseGPT"] computes once per layer), from a damped, full symmetric H
  * [b,b] fp32. U [b,b] fp32 (strict lower triangle zero). workspace: >= b*b*4 +

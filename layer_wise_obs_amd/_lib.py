@@ -16,6 +16,7 @@ TH_OK, TH_ERR_INVALID_ARG, TH_ERR_NOT_SPD, TH_ERR_NONFINITE, TH_ERR_WORKSPACE, T
 TH_F32, TH_BF16 = 0, 1
 TH_UNSTRUCTURED, TH_NM = 0, 1
 TH_SCORE_OBS, TH_SCORE_WANDA = 0, 1
+TH_BASE_MAGNITUDE, TH_BASE_WANDA = 0, 1
 STATUS_NAMES = {0: "TH_OK", 1: "TH_ERR_INVALID_ARG", 2: "TH_ERR_NOT_SPD", 3: "TH_ERR_NONFINITE",
                 4: "TH_ERR_WORKSPACE", 5: "TH_ERR_HIP"}
 
@@ -60,6 +61,9 @@ _SIG = {
     "th_debug_select_global": [_P, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P,
                                ctypes.c_size_t, _P],
     "th_debug_factor": [_P, _I64, _P, _P, ctypes.c_size_t, _P],
+    "th_column_sq_norms_workspace_size": [_I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
+    "th_column_sq_norms": [_P, _I32, _I64, _I64, _I64, _P, _P, ctypes.c_size_t, _P],
+    "th_prune_baseline": [_P, _I32, _I64, _I64, _I32, _P, ctypes.POINTER(PruneParams), _P, _P],
 }
 
 _lib = None
@@ -241,3 +245,28 @@ def debug_factor(H):
     ws = workspace(nbytes, H.device)
     _check(lib().th_debug_factor(_ptr(H), b, _ptr(U), _ptr(ws), ws.numel(), _stream(H.device)))
     return U
+
+
+def column_sq_norms(X):
+    """G_qq = sum_t X_tq^2 (fp32, b values) for token-major X [n, b]."""
+    torch = _torch()
+    _require_cuda(X)
+    n, b = X.shape
+    out = ctypes.c_size_t(0)
+    _check(lib().th_column_sq_norms_workspace_size(n, b, ctypes.byref(out)))
+    ws = workspace(out.value, X.device)
+    g = torch.empty((b,), dtype=torch.float32, device=X.device)
+    _check(lib().th_column_sq_norms(_ptr(X), _dtype_code(X), n, b, X.stride(0), _ptr(g), _ptr(ws),
+                                    ws.numel(), _stream(X.device)))
+    return g
+
+
+def prune_baseline(W, method: str, gdiag=None, params: PruneParams | None = None, mask_out=None):
+    """Magnitude or Wanda pruning of W (c x b, bf16/fp32) in place, no compensation."""
+    _require_cuda(W, gdiag, mask_out)
+    if params is None:
+        params = make_params()
+    c, b = W.shape
+    code = {"magnitude": TH_BASE_MAGNITUDE, "wanda": TH_BASE_WANDA}[method]
+    _check(lib().th_prune_baseline(_ptr(W), _dtype_code(W), c, b, code, _ptr(gdiag),
+                                   ctypes.byref(params), _ptr(mask_out), _stream(W.device)))

@@ -426,6 +426,55 @@ th_status th_debug_select_global(const float* scores, int64_t c, int64_t f, int6
   return TH_OK;
 }
 
+th_status th_column_sq_norms_workspace_size(int64_t n, int64_t b, size_t* bytes) {
+  if (!bytes || n < 1 || b < 1) return fail(TH_ERR_INVALID_ARG, "bad arguments");
+  *bytes = (size_t)colsq_splits(n) * (size_t)b * sizeof(double);
+  return TH_OK;
+}
+
+th_status th_column_sq_norms(const void* X, th_dtype xdt, int64_t n, int64_t b, int64_t ldx,
+                             float* gdiag, void* workspace, size_t workspace_bytes,
+                             th_stream_t stream) {
+  if (!X || !gdiag || n < 1 || b < 1 || ldx < b || !dtype_ok(xdt))
+    return fail(TH_ERR_INVALID_ARG, "bad arguments");
+  size_t need = 0;
+  th_column_sq_norms_workspace_size(n, b, &need);
+  if (!workspace || workspace_bytes < need) return fail(TH_ERR_WORKSPACE, "workspace too small");
+  TH_HIP(launch_column_sq_norms(X, xdt, n, b, ldx, (double*)workspace, gdiag, (hipStream_t)stream),
+         "column norms");
+  return TH_OK;
+}
+
+th_status th_prune_baseline(void* W, th_dtype wdt, int64_t c, int64_t b, th_baseline method,
+                            const float* gdiag, const th_prune_params* p, uint8_t* mask_out,
+                            th_stream_t stream) {
+  if (!W || !p || !dtype_ok(wdt)) return fail(TH_ERR_INVALID_ARG, "bad arguments");
+  if (c < 1 || b < 1) return fail(TH_ERR_INVALID_ARG, "c and b must be >= 1");
+  if (c * b >= (int64_t)1 << 32) return fail(TH_ERR_INVALID_ARG, "c*b must be < 2^32");
+  if (method != TH_BASE_MAGNITUDE && method != TH_BASE_WANDA)
+    return fail(TH_ERR_INVALID_ARG, "unknown baseline method");
+  if (method == TH_BASE_WANDA && !gdiag)
+    return fail(TH_ERR_INVALID_ARG, "Wanda needs the squared column norms gdiag");
+  const float* g = method == TH_BASE_WANDA ? gdiag : nullptr;
+  hipStream_t s = (hipStream_t)stream;
+  if (p->pattern.kind == TH_UNSTRUCTURED) {
+    if (!(p->sparsity >= 0.0 && p->sparsity <= 1.0))
+      return fail(TH_ERR_INVALID_ARG, "sparsity must be in [0, 1]");
+    // every row loses round-half-even(p * b) weights
+    const int64_t krow = (int64_t)std::nearbyint(p->sparsity * (double)b);
+    TH_HIP(launch_baseline_rows(W, wdt, c, b, g, krow, mask_out, s), "baseline rows");
+  } else if (p->pattern.kind == TH_NM) {
+    const int n = p->pattern.n, m = p->pattern.m;
+    if (m < 1 || m > kMaxBlock || n < 0 || n > m)
+      return fail(TH_ERR_INVALID_ARG, "N:M needs 0 <= n <= m, 1 <= m <= 128");
+    if (b % m) return fail(TH_ERR_INVALID_ARG, "N:M needs m | b");
+    TH_HIP(launch_baseline_nm(W, wdt, c, b, g, n, m, mask_out, s), "baseline N:M");
+  } else {
+    return fail(TH_ERR_INVALID_ARG, "unknown pattern kind");
+  }
+  return TH_OK;
+}
+
 th_status th_debug_factor(const float* H, int64_t b, float* U, void* workspace,
                           size_t workspace_bytes, th_stream_t stream) {
   if (!H || !U || !workspace || b < 1) return fail(TH_ERR_INVALID_ARG, "bad arguments");

@@ -100,6 +100,15 @@ hipError_t launch_flip_lower(const float* H, float* S, int64_t b, const DevState
 hipError_t launch_wanda_diag(const float* H, int64_t b, const DevState* st, int h_is_damped,
                              float* gdiag, hipStream_t s);
 
+// baseline.hip
+int colsq_splits(int64_t n);
+hipError_t launch_column_sq_norms(const void* X, th_dtype xdt, int64_t n, int64_t b, int64_t ldx,
+                                  double* part, float* g, hipStream_t s);
+hipError_t launch_baseline_rows(void* W, th_dtype wdt, int64_t c, int64_t b, const float* g,
+                                int64_t krow, uint8_t* mask, hipStream_t s);
+hipError_t launch_baseline_nm(void* W, th_dtype wdt, int64_t c, int64_t b, const float* g, int n,
+                              int m, uint8_t* mask, hipStream_t s);
+
 // factor.hip
 // panel: chol_panel_floats(b) floats. Part of the work runs on a library-owned
 // stream of the current device, joined back into s before the call returns.

@@ -43,7 +43,7 @@ import numpy as np
 __all__ = [
     "NotSPDError", "gram", "damping", "hessian", "k_total", "obs_scores",
     "select_unstructured", "select_nm", "solve_rows", "schur_downdate",
-    "prune_layer", "reconstruction_error",
+    "prune_layer", "reconstruction_error", "column_sq_norms", "baseline_keys", "prune_baseline",
 ]
 
 
@@ -273,3 +273,56 @@ def reconstruction_error(W, W_hat, G: np.ndarray):
     E = float(np.sum((D @ G) * D))
     base = float(np.sum((W0 @ G) * W0))
     return E, (E / base if base > 0 else 0.0)
+
+
+def column_sq_norms(X_tok) -> np.ndarray:
+    """G_qq = sum_t X_tq^2 in fp64, rounded to fp32 (the squared input-feature norms
+    of the explainer's section "Wanda: Pruning by Weights and Activations")."""
+    X = _f64(X_tok)
+    return np.sum(X * X, axis=0).astype(np.float32)
+
+
+def baseline_keys(W, gdiag=None) -> np.ndarray:
+    """Comparator keys in fp32: w^2 (rounded) times g_q (rounded), g = 1 without gdiag.
+
+    "Pruning LLMs with Thanos", section "Why magnitude alone misses important
+    weights": W_kq^2 G_qq orders like Wanda's |W_kq| ||X_q||_2; with g = 1 the key
+    orders like |W_kq|. The keys are computed in fp32 (the precision in which the
+    selection is decided), so both implementations see the same keys.
+    """
+    w = _f64(W).astype(np.float32)
+    k = np.multiply(w, w, dtype=np.float32)
+    if gdiag is not None:
+        k = np.multiply(k, np.asarray(gdiag, dtype=np.float32)[None, :], dtype=np.float32)
+    return k
+
+
+def prune_baseline(W, method: str, gdiag=None, sparsity: float = 0.5, pattern=None) -> dict:
+    """Magnitude or Wanda pruning: zero the lowest keys, no other weight changes.
+
+    The explainer's section "Wanda: Pruning by Weights and Activations": each output
+    row loses its lowest fraction of scores and the remaining weights are not
+    updated; section "The Failure of Magnitude Pruning in Large Transformers":
+    magnitude ranks by |W| (compared per output row here, like Wanda). Section
+    "N:M Semi-Structured Sparsity (2:4 Pattern)": with a pattern, the m-n lowest of
+    every aligned group of m. Unstructured: round-half-even(p*b) per row. Ties: the
+    lower column is pruned first (stable sort).
+    """
+    W0 = _f64(W)
+    c, b = W0.shape
+    if method not in ("magnitude", "wanda"):
+        raise ValueError(method)
+    keys = baseline_keys(W, gdiag if method == "wanda" else None)
+    if pattern is None:
+        krow = int(np.round(np.float64(sparsity) * b))
+        order = np.argsort(keys, axis=1, kind="stable")
+        mask = np.zeros((c, b), dtype=bool)
+        np.put_along_axis(mask, order[:, :krow], True, axis=1)
+    else:
+        n_keep, m = pattern
+        if not (0 <= n_keep <= m) or b % m:
+            raise ValueError("N:M needs 0<=n<=m and m | b")
+        mask = select_nm(keys, n_keep, m)
+    W_hat = W0.copy()
+    W_hat[mask] = 0.0
+    return {"W_hat": W_hat, "mask": mask}

@@ -20,7 +20,8 @@ def test_header_declares_the_path():
     names = _declared()
     for must in ("th_hessian_accumulate", "th_hessian_finalize", "th_prune_layer",
                  "th_prune_layer_workspace_size", "th_reconstruction_error", "th_debug_select_nm",
-                 "th_debug_select_global", "th_debug_factor", "th_last_error"):
+                 "th_debug_select_global", "th_debug_factor", "th_last_error",
+                 "th_column_sq_norms", "th_column_sq_norms_workspace_size", "th_prune_baseline"):
         assert must in names
 
 
@@ -85,3 +86,30 @@ def test_workspace_size_queries():
     assert out.value > 0  # 136 tiles: token split with a fixed-order reduction
     assert L.th_reconstruction_error_workspace_size(4096, 11008, 0, ctypes.byref(out)) == 0
     assert out.value >= 2 * 4096 * 11008 * 4
+
+
+def test_baseline_arguments_are_rejected_before_any_launch():
+    L = _lib.lib()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its checks first
+    ok = _lib.make_params(sparsity=0.5)
+    cases = [
+        (None, _lib.TH_BF16, 4, 16, _lib.TH_BASE_MAGNITUDE, None, ok),          # W is NULL
+        (fake, 7, 4, 16, _lib.TH_BASE_MAGNITUDE, None, ok),                      # bad dtype
+        (fake, _lib.TH_BF16, 0, 16, _lib.TH_BASE_MAGNITUDE, None, ok),           # c = 0
+        (fake, _lib.TH_BF16, 4, 16, 5, None, ok),                                # bad method
+        (fake, _lib.TH_BF16, 4, 16, _lib.TH_BASE_WANDA, None, ok),               # Wanda without G
+        (fake, _lib.TH_BF16, 4, 16, _lib.TH_BASE_MAGNITUDE, None, _lib.make_params(sparsity=1.5)),
+        (fake, _lib.TH_BF16, 4, 18, _lib.TH_BASE_MAGNITUDE, None,
+         _lib.make_params(pattern=(2, 4), block=16)),                            # m does not divide b
+        (fake, _lib.TH_BF16, 4, 16, _lib.TH_BASE_MAGNITUDE, None,
+         _lib.make_params(pattern=(5, 4), block=16)),                            # n > m
+    ]
+    for W, dt, c, b, method, g, p in cases:
+        st = L.th_prune_baseline(W, dt, c, b, method, g, ctypes.byref(p), None, None)
+        assert st == _lib.TH_ERR_INVALID_ARG, (dt, c, b, method)
+    out = ctypes.c_size_t(0)
+    assert L.th_column_sq_norms_workspace_size(262144, 11008, ctypes.byref(out)) == 0
+    assert out.value == 128 * 11008 * 8
+    assert L.th_column_sq_norms(None, _lib.TH_BF16, 10, 8, 8, fake, fake, 1 << 20, None) == 1
+    assert L.th_column_sq_norms(fake, _lib.TH_BF16, 10, 8, 8, fake, fake, 8, None) == \
+        _lib.TH_ERR_WORKSPACE

@@ -495,6 +495,88 @@ def test_k_total_round_half_even():
     assert O.k_total(0.6, 8192, 28672) == 140928614
 
 
+# ------------------------------------------- comparators (magnitude, Wanda)
+# The explainer's section "Wanda: Pruning by Weights and Activations" (score
+# |W_kq| ||X_q||_2, thresholds per output row, no update of the other weights);
+# "Pruning LLMs with Thanos", section "Why magnitude alone misses important
+# weights" (magnitude ranks by |W_kq|; the squared Wanda score has the same order).
+
+def test_p16_baseline_hand_example():
+    # rows [3, -1, 2, 0.5] and [1, 1, -1, 2]; 50% per row; Wanda with G_qq = [1, 100, 1, 1]
+    W = np.array([[3.0, -1.0, 2.0, 0.5], [1.0, 1.0, -1.0, 2.0]])
+    mag = O.prune_baseline(W, "magnitude", sparsity=0.5)
+    # |W| row 0: 0.5 and 1 are the smallest; row 1: three entries of magnitude 1,
+    # the two lowest columns go first
+    assert mag["mask"].astype(int).tolist() == [[0, 1, 0, 1], [1, 1, 0, 0]]
+    g = np.array([1.0, 100.0, 1.0, 1.0])
+    wan = O.prune_baseline(W, "wanda", gdiag=g, sparsity=0.5)
+    # |W| sqrt(G): row 0 [3, 10, 2, 0.5] -> columns 3, 2; row 1 [1, 10, 1, 2] -> columns 0, 2
+    assert wan["mask"].astype(int).tolist() == [[0, 0, 1, 1], [1, 0, 1, 0]]
+    # no compensation: kept entries unchanged, pruned entries exactly zero
+    for r in (mag, wan):
+        assert np.all(r["W_hat"][~r["mask"]] == W[~r["mask"]])
+        assert np.all(r["W_hat"][r["mask"]] == 0.0)
+
+
+@pytest.mark.parametrize("p", [0.0, 0.3, 0.5, 0.77, 1.0])
+def test_p17_baseline_per_row_budget_and_wanda_order(p):
+    rng = np.random.default_rng(41)
+    c, b = 7, 53
+    W = rng.standard_normal((c, b))
+    X = rng.standard_normal((300, b)) * rng.uniform(0.1, 10.0, size=b)
+    g = O.column_sq_norms(X)
+    res = O.prune_baseline(W, "wanda", gdiag=g, sparsity=p)
+    k = int(np.round(p * b))
+    assert np.all(res["mask"].sum(axis=1) == k)
+    # the same rows' lowest |W| * ||X_q||_2 in fp64 (a different formula: norms,
+    # not squares; tie-free data)
+    s = np.abs(W) * np.sqrt(np.sum(X * X, axis=0))[None, :]
+    ref = np.zeros_like(res["mask"])
+    np.put_along_axis(ref, np.argsort(s, axis=1)[:, :k], True, axis=1)
+    assert np.array_equal(res["mask"], ref)
+    # magnitude is Wanda with equal feature norms
+    mag = O.prune_baseline(W, "magnitude", sparsity=p)
+    eq = O.prune_baseline(W, "wanda", gdiag=np.full(b, 4.0), sparsity=p)
+    assert np.array_equal(mag["mask"], eq["mask"])
+
+
+def test_p18_baseline_error_closed_form_and_nm_counts():
+    rng = np.random.default_rng(43)
+    c, b = 5, 24
+    W = rng.standard_normal((c, b))
+    d = rng.uniform(0.5, 3.0, size=b)
+    G = np.diag(d)  # independent features: E = sum over pruned of W^2 G_qq
+    res = O.prune_baseline(W, "wanda", gdiag=d, pattern=(2, 4))
+    E, _ = O.reconstruction_error(W, res["W_hat"], G)
+    assert np.isclose(E, np.sum((W ** 2 * d[None, :])[res["mask"]]), rtol=1e-12)
+    groups = res["mask"].reshape(c, b // 4, 4).sum(axis=2)
+    assert np.all(groups == 2)
+    # within every group the two pruned keys are the two smallest
+    keys = (W ** 2 * d[None, :]).reshape(c, b // 4, 4)
+    m = res["mask"].reshape(c, b // 4, 4)
+    assert np.all(keys[m].reshape(c, b // 4, 2).max(axis=2) <= keys[~m].reshape(c, b // 4, 2).min(axis=2))
+
+
+def test_p19_compensation_never_hurts_on_the_same_mask():
+    """The joint solve is the exact constrained minimiser ("Pruning LLMs with
+    Thanos", section "Contribution one"): with the comparator's mask fixed, the
+    compensated weights reach an error no larger than the uncompensated ones."""
+    rng = np.random.default_rng(44)
+    c, b = 4, 12
+    W, X = _problem(c, b, 200, 45)
+    G = O.gram(X)
+    res = O.prune_baseline(W, "wanda", gdiag=O.column_sq_norms(X), sparsity=0.5)
+    H = 2 * G + 1e-9 * np.mean(np.diag(2 * G)) * np.eye(b)
+    E_plain, _ = O.reconstruction_error(W, res["W_hat"], G)
+    for k in range(c):
+        Q = np.flatnonzero(res["mask"][k])
+        best, cost = _constrained_min(W[k], H, np.array([], dtype=int), Q)
+        assert np.all(best[Q] == 0.0) or np.allclose(best[Q], 0.0, atol=1e-12)
+        d_plain = res["W_hat"][k] - W[k]
+        assert cost <= float(d_plain @ H @ d_plain) * (1 + 1e-9)
+    assert E_plain > 0
+
+
 # ------------------------------------------------------- planted mistakes
 
 def _pins_pass():
@@ -507,6 +589,9 @@ def _pins_pass():
         test_select_nm_ties_break_by_column()
         test_select_unstructured_ties_break_by_flat_index()
         test_p11_wanda_ordering_and_diagonal_gram()
+        test_p16_baseline_hand_example()
+        test_p17_baseline_per_row_budget_and_wanda_order(0.5)
+        test_p18_baseline_error_closed_form_and_nm_counts()
     except AssertionError:
         return False
     return True
@@ -525,7 +610,16 @@ def _bad_nm(S_J, n, m):
     return sel[:, :, ::-1].reshape(c, blk)
 
 
-@pytest.mark.parametrize("mutation", ["downdate", "sign", "nm_ties", "score_diag_H"])
+def _bad_keys_abs_times_g(W, gdiag=None):
+    w = O.thanos_oracle._f64(W).astype(np.float32)
+    k = np.abs(w)
+    if gdiag is not None:
+        k = np.multiply(k, np.asarray(gdiag, dtype=np.float32)[None, :], dtype=np.float32)
+    return k  # |W| G instead of W^2 G: a wrong power of the feature norm
+
+
+@pytest.mark.parametrize("mutation", ["downdate", "sign", "nm_ties", "score_diag_H",
+                                      "baseline_power", "baseline_layer_budget"])
 def test_planted_mistakes_are_caught(monkeypatch, mutation):
     assert _pins_pass()
     T = O.thanos_oracle
@@ -545,4 +639,21 @@ def test_planted_mistakes_are_caught(monkeypatch, mutation):
                 kw = dict(kw, score="wanda")
             return orig_prune(W, G, **kw)
         monkeypatch.setattr(O, "prune_layer", wrong)
+    elif mutation == "baseline_power":
+        monkeypatch.setattr(T, "baseline_keys", _bad_keys_abs_times_g)
+    elif mutation == "baseline_layer_budget":
+        orig_b = T.prune_baseline
+
+        def layer_wide(W, method, gdiag=None, sparsity=0.5, pattern=None):
+            if pattern is not None:
+                return orig_b(W, method, gdiag=gdiag, sparsity=sparsity, pattern=pattern)
+            keys = T.baseline_keys(W, gdiag if method == "wanda" else None)
+            k = int(np.round(sparsity * keys.size))  # one threshold for the whole layer
+            flat = np.zeros(keys.size, dtype=bool)
+            flat[np.argsort(keys.ravel(), kind="stable")[:k]] = True
+            mask = flat.reshape(keys.shape)
+            W_hat = T._f64(W).copy()
+            W_hat[mask] = 0.0
+            return {"W_hat": W_hat, "mask": mask}
+        monkeypatch.setattr(O, "prune_baseline", layer_wide)
     assert not _pins_pass()
