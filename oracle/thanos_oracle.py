@@ -10,13 +10,14 @@ Sources (titles of the pages and their sections):
   layer-reconstruction lens", "Why magnitude alone misses important weights",
   "One deletion with compensation: the OBS view", "Contribution one: solve a
   selected set directly", "Contribution two: keep the budget global and the
-  execution local", "Making irregular row masks batchable".
+  execution local", "Making irregular row masks batchable", and "The scaling
+  problem, and what SparseGPT changes" for the column-sequential comparator.
 * "Weight Pruning in Large Language Models: How SparseGPT, Wanda, and
   Semi-Structured 2:4 Sparsity ..." (explainer) -- section "SparseGPT:
-  Second-Order Reconstruction at Scale" for the damped Hessian H = 2XX^T + lambda*I
-  and the reconstruction objective; section "Wanda: Pruning by Weights and
-  Activations" for the |W|*||X_q|| score; section "N:M Semi-Structured Sparsity
-  (2:4 Pattern)" for the group constraint.
+  Second-Order Reconstruction at Scale" for the damped Hessian H = 2XX^T + lambda*I,
+  the reconstruction objective and the comparator's per-column update; section
+  "Wanda: Pruning by Weights and Activations" for the |W|*||X_q|| score; section
+  "N:M Semi-Structured Sparsity (2:4 Pattern)" for the group constraint.
 
 Every value here is fp64. Inputs are decoded exactly from bf16 or fp32. The
 route deliberately differs from the GPU's: the inverse Hessian comes from an LU
@@ -44,6 +45,7 @@ __all__ = [
     "NotSPDError", "gram", "damping", "hessian", "k_total", "obs_scores",
     "select_unstructured", "select_nm", "solve_rows", "schur_downdate",
     "prune_layer", "reconstruction_error", "column_sq_norms", "baseline_keys", "prune_baseline",
+    "trailing_inverse_rows", "sparsegpt_column", "prune_sparsegpt",
 ]
 
 
@@ -326,3 +328,95 @@ def prune_baseline(W, method: str, gdiag=None, sparsity: float = 0.5, pattern=No
     W_hat = W0.copy()
     W_hat[mask] = 0.0
     return {"W_hat": W_hat, "mask": mask}
+
+
+def trailing_inverse_rows(H: np.ndarray) -> np.ndarray:
+    """T[q, q:] = row q of inv(H restricted to columns q, q+1, ..., b-1); zero below.
+
+    The explainer's section "SparseGPT: Second-Order Reconstruction at Scale": when
+    column q is processed the inverse Hessian is that of the columns still active,
+    q and everything right of it ("Pruning LLMs with Thanos", section "The scaling
+    problem, and what SparseGPT changes": finished columns are frozen). Computed
+    from an LU inverse of H by one single-column Schur downdate per column.
+    """
+    b = H.shape[0]
+    A = np.linalg.inv(H)
+    T = np.zeros((b, b), dtype=np.float64)
+    for q in range(b):
+        T[q, q:] = A[0]
+        if q + 1 < b:
+            A = schur_downdate(A, 1)
+    return T
+
+
+def sparsegpt_column(Wc: np.ndarray, q: int, pruned: np.ndarray, t_row: np.ndarray) -> None:
+    """Process column q for every row at once (in place on Wc).
+
+    The explainer's section "SparseGPT: Second-Order Reconstruction at Scale": a
+    pruned w_kq (W_hat = 0) has error w_kq / [H^-1]_qq, and that error times row q of
+    H^-1 (over the active columns, t_row = [H^-1]_{q, q:}) is subtracted from row k
+    at columns q and after; a kept weight has no error and changes nothing. Column q
+    is then exactly zero where pruned.
+    """
+    err = np.where(pruned, Wc[:, q], 0.0) / t_row[0]
+    Wc[:, q:] -= np.outer(err, t_row)
+    Wc[pruned, q] = 0.0
+
+
+def prune_sparsegpt(W, G: np.ndarray, sparsity: float = 0.5, pattern=None, block: int = 128,
+                    lam: float = 0.01, lam_relative: bool = True, trace: list | None = None) -> dict:
+    """Column-sequential pruning on a schedule shared by all rows (the SparseGPT comparator).
+
+    "Pruning LLMs with Thanos", section "The scaling problem, and what SparseGPT
+    changes": columns are processed left to right, every row at once; a finished
+    column is frozen; compensation goes only into columns still active; pruning
+    decisions are refreshed block by block. The explainer's section "SparseGPT:
+    Second-Order Reconstruction at Scale" gives the update for column j:
+    the error (W_j - W_hat_j) / [H^-1]_jj times row j of H^-1 is subtracted from the
+    columns after j, with H^-1 the inverse over the active columns.
+
+    Readings (the pages leave these open):
+    * score of w_kq: the OBS cost w_kq^2 / [inv(H_{q:})]_qq of deleting it when
+      column q is processed, from the weights at the start of the block;
+    * unstructured: every block loses exactly round-half-even(p * c * |J|) weights,
+      the lowest (score, flat index) of the block (the equal per-block quota that
+      "Contribution two: keep the budget global and the execution local" contrasts
+      with the dynamic budget); N:M: the m-n lowest (score, column) of every group;
+    * pruned entries are set to exactly 0.0.
+    """
+    W0 = _f64(W)
+    G = np.asarray(G, dtype=np.float64)
+    c, b = W0.shape
+    if block < 1:
+        raise ValueError("block must be >= 1")
+    if pattern is not None:
+        n_keep, m = pattern
+        if not (0 <= n_keep <= m) or block % m or b % m:
+            raise ValueError("N:M needs 0<=n<=m, m | block and m | b")
+    lam_abs = damping(G, lam, lam_relative)
+    H = hessian(G, lam_abs)
+    try:
+        np.linalg.cholesky(H)
+    except np.linalg.LinAlgError as exc:
+        raise NotSPDError("damped Hessian is not positive definite") from exc
+    T = trailing_inverse_rows(H)
+    d = np.diag(T).copy()
+    Wc = W0.copy()
+    mask = np.zeros((c, b), dtype=bool)
+    counts = []
+    for j0 in range(0, b, block):
+        blk = min(block, b - j0)
+        S = Wc[:, j0:j0 + blk] ** 2 / d[None, j0:j0 + blk]
+        if pattern is None:
+            sel = select_unstructured(S, k_total(sparsity, c, blk), blk)
+        else:
+            sel = select_nm(S, pattern[0], pattern[1])
+        if trace is not None:
+            trace.append({"j0": j0, "S": S.copy()})
+        for t in range(blk):
+            sparsegpt_column(Wc, j0 + t, sel[:, t], T[j0 + t, j0 + t:])
+        mask[:, j0:j0 + blk] = sel
+        counts.append(int(sel.sum()))
+    return {"W_hat": Wc, "mask": mask, "counts": counts, "lam": lam_abs,
+            "pruned": int(sum(counts))}
+

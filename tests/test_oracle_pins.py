@@ -577,6 +577,99 @@ def test_p19_compensation_never_hurts_on_the_same_mask():
     assert E_plain > 0
 
 
+# ------------------------------------------- SparseGPT comparator (P20-P23)
+
+def test_p20_sparsegpt_is_sequential_least_squares():
+    """Every pruned weight, in column order, is deleted by the least-squares optimum
+    with the columns before it frozen (explainer, "SparseGPT: Second-Order
+    Reconstruction at Scale"; "Pruning LLMs with Thanos", "The scaling problem, and
+    what SparseGPT changes"), replayed for the oracle's own mask with least squares
+    on C^T (C C^T = H); and no sequential schedule beats the least-squares
+    reconstruction of the same final mask."""
+    c, b = 4, 12
+    W, X = _problem(c, b, 120, RNG_SEED + 20)
+    G = O.gram(X)
+    for pattern in (None, (2, 4)):
+        out = O.prune_sparsegpt(W, G, sparsity=0.5, pattern=pattern, block=4)
+        H = O.hessian(G, out["lam"])
+        for k in range(c):
+            w = W[k].copy()
+            for q in range(b):
+                if out["mask"][k, q]:
+                    w, _ = _constrained_min(w, H, np.arange(q), [q])
+            np.testing.assert_allclose(out["W_hat"][k], w, rtol=1e-7, atol=1e-12)
+            _, best = _constrained_min(W[k], H, [], np.flatnonzero(out["mask"][k]))
+            d = out["W_hat"][k] - W[k]
+            assert float(d @ H @ d) >= best * (1 - 1e-9)
+
+
+def test_p21_sparsegpt_score_is_obs_cost_with_earlier_columns_frozen():
+    """The score the block's mask is chosen from is the cost of deleting w_kq alone
+    at the moment column q is processed: min d H d^T with d_q = -w_kq and the
+    columns before q frozen (least squares), from the block-start weights."""
+    c, b, B = 3, 12, 4
+    W, X = _problem(c, b, 120, RNG_SEED + 21)
+    G = O.gram(X)
+    trace = []
+    out = O.prune_sparsegpt(W, G, sparsity=0.5, block=B, trace=trace)
+    H = O.hessian(G, out["lam"])
+    Wc = W.copy()
+    for ent in trace:
+        j0 = ent["j0"]
+        for k in range(c):
+            for t in range(B):
+                _, cost = _constrained_min(Wc[k], H, np.arange(j0 + t), [j0 + t])
+                assert ent["S"][k, t] == pytest.approx(cost, rel=1e-8, abs=1e-15)
+        for k in range(c):  # advance to the next block start with the oracle's mask
+            for q in range(j0, j0 + B):
+                if out["mask"][k, q]:
+                    Wc[k], _ = _constrained_min(Wc[k], H, np.arange(q), [q])
+
+
+def test_p22_sparsegpt_diagonal_gram_is_blockwise_threshold():
+    """Independent features: nothing to compensate, so W_hat is W with the mask
+    zeroed, and each block's mask is its lowest w^2 (2 G_qq + lambda) by (score,
+    flat index), exactly round(p c B) of them."""
+    c, b, B = 5, 16, 8
+    rng = np.random.default_rng(RNG_SEED + 22)
+    W = rng.standard_normal((c, b))
+    W[1, 3] = -W[0, 3]  # equal scores in one column: the lower row goes first
+    W[2, 9] = W[4, 9]
+    gd = rng.uniform(0.5, 3.0, b)
+    G = np.diag(gd)
+    out = O.prune_sparsegpt(W, G, sparsity=0.5, block=B)
+    h = 2.0 * gd + out["lam"]
+    for j0 in (0, 8):
+        score = W[:, j0:j0 + B] ** 2 * h[None, j0:j0 + B]
+        flat = (np.arange(c)[:, None] * b + np.arange(j0, j0 + B)[None, :]).ravel()
+        order = np.lexsort((flat, score.ravel()))
+        expect = np.zeros(c * B, dtype=bool)
+        expect[order[:20]] = True
+        np.testing.assert_array_equal(out["mask"][:, j0:j0 + B], expect.reshape(c, B))
+    ref = W.copy()
+    ref[out["mask"]] = 0.0
+    np.testing.assert_array_equal(out["W_hat"], ref)
+
+
+@pytest.mark.parametrize("p,counts", [(0.0, [0, 0, 0]), (0.3, [12, 12, 6]),
+                                      (0.5, [20, 20, 10]), (1.0, [40, 40, 20])])
+def test_p23_sparsegpt_per_block_quota_and_limits(p, counts):
+    """Blocks of 8, 8 and a ragged 4 columns over 5 rows: each block loses exactly
+    round(p * 5 * |J|); p = 0 changes nothing, p = 1 zeroes everything; N:M counts
+    are exact in every group."""
+    W, X = _problem(5, 20, 100, RNG_SEED + 23)
+    G = O.gram(X)
+    out = O.prune_sparsegpt(W, G, sparsity=p, block=8)
+    assert out["counts"] == counts
+    assert np.all(out["W_hat"][out["mask"]] == 0.0)
+    if p == 0.0:
+        np.testing.assert_array_equal(out["W_hat"], W)
+    if p == 1.0:
+        assert np.all(out["W_hat"] == 0.0)
+    nm = O.prune_sparsegpt(W, G, pattern=(1, 4), block=8)
+    assert np.all(nm["mask"].reshape(5, 5, 4).sum(axis=2) == 3)
+
+
 # ------------------------------------------------------- planted mistakes
 
 def _pins_pass():
@@ -592,6 +685,10 @@ def _pins_pass():
         test_p16_baseline_hand_example()
         test_p17_baseline_per_row_budget_and_wanda_order(0.5)
         test_p18_baseline_error_closed_form_and_nm_counts()
+        test_p20_sparsegpt_is_sequential_least_squares()
+        test_p21_sparsegpt_score_is_obs_cost_with_earlier_columns_frozen()
+        test_p22_sparsegpt_diagonal_gram_is_blockwise_threshold()
+        test_p23_sparsegpt_per_block_quota_and_limits(0.3, [12, 12, 6])
     except AssertionError:
         return False
     return True
@@ -619,7 +716,8 @@ def _bad_keys_abs_times_g(W, gdiag=None):
 
 
 @pytest.mark.parametrize("mutation", ["downdate", "sign", "nm_ties", "score_diag_H",
-                                      "baseline_power", "baseline_layer_budget"])
+                                      "baseline_power", "baseline_layer_budget",
+                                      "sgpt_full_inverse", "sgpt_sign", "sgpt_row_quota"])
 def test_planted_mistakes_are_caught(monkeypatch, mutation):
     assert _pins_pass()
     T = O.thanos_oracle
@@ -656,4 +754,21 @@ def test_planted_mistakes_are_caught(monkeypatch, mutation):
             W_hat[mask] = 0.0
             return {"W_hat": W_hat, "mask": mask}
         monkeypatch.setattr(O, "prune_baseline", layer_wide)
+    elif mutation == "sgpt_full_inverse":
+        # rows of the full inverse instead of the inverse over the active columns
+        monkeypatch.setattr(T, "trailing_inverse_rows", lambda H: np.triu(np.linalg.inv(H)))
+    elif mutation == "sgpt_sign":
+        def added(Wc, q, pruned, t_row):
+            err = np.where(pruned, Wc[:, q], 0.0) / t_row[0]
+            Wc[:, q + 1:] += np.outer(err, t_row[1:])
+            Wc[pruned, q] = 0.0
+        monkeypatch.setattr(T, "sparsegpt_column", added)
+    elif mutation == "sgpt_row_quota":
+        orig_sel = T.select_unstructured
+
+        def per_row(S_F, r, blk):
+            c = S_F.shape[0]
+            return np.concatenate([orig_sel(S_F[k:k + 1], int(np.round(r / c)), blk)
+                                   for k in range(c)])
+        monkeypatch.setattr(T, "select_unstructured", per_row)
     assert not _pins_pass()
