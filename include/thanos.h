@@ -144,6 +144,29 @@ th_status th_prune_layer(void* W, th_dtype wdt, int64_t c, int64_t b, const void
 th_status th_prune_layer_workspace_size(int64_t c, int64_t b, int64_t n, int32_t have_x,
                                         const th_prune_params* p, size_t* bytes /* host */);
 
+/* Comparator: the column-sequential schedule of SparseGPT on the same Hessian and
+ * factor [BLOG, "The scaling problem, and what SparseGPT changes": left to right,
+ * every row at once, finished columns frozen, compensation only into active
+ * columns, masks refreshed per block; EXPL, "SparseGPT: Second-Order
+ * Reconstruction at Scale": pruning w_kq subtracts (w_kq/[H^-1]_qq) times row q
+ * of H^-1 over the active columns from the rest of row k]. With H^-1 = U^T U that
+ * update is (w_kq/U_qq) U_{q,q:}. Mask of block J chosen at block start from the
+ * score w_kq^2/U_qq^2 (the cost of deleting w_kq alone when column q is
+ * processed): unstructured, the block's round-half-even(p*c*|J|) lowest
+ * (score, flat index k*b+q) — an equal quota per block, unlike th_prune_layer's
+ * global budget; N:M, the m-n lowest (score, column) of every aligned group.
+ * Arguments, layout, ownership, synchronisation and errors as th_prune_layer;
+ * p->score must be TH_SCORE_OBS (else TH_ERR_INVALID_ARG). workspace: >=
+ * th_prune_sparsegpt_workspace_size bytes, 256-byte aligned. block_counts get
+ * the weights pruned in each block. */
+th_status th_prune_sparsegpt(void* W, th_dtype wdt, int64_t c, int64_t b, const void* X,
+                             th_dtype xdt, int64_t n, const float* H, const th_prune_params* p,
+                             float* W_out_f32, uint8_t* mask_out, void* workspace,
+                             size_t workspace_bytes, th_stats* stats_out,
+                             int64_t* block_counts, th_stream_t stream);
+th_status th_prune_sparsegpt_workspace_size(int64_t c, int64_t b, int64_t n, int32_t have_x,
+                                            const th_prune_params* p, size_t* bytes /* host */);
+
 /* E = ||(W - What) X||_F^2 = sum_k D_k G D_k^T and E / ||W X||_F^2
  * [BLOG, "The layer-reconstruction lens"]. W and What: [c,b] dtype wdt. Exactly
  * one of X ([n,b] token-major, dtype xdt) or G ([b,b] fp32, full symmetric,

@@ -53,6 +53,11 @@ _SIG = {
                        _P, _P, ctypes.c_size_t, ctypes.POINTER(Stats), ctypes.POINTER(_I64), _P],
     "th_prune_layer_workspace_size": [_I64, _I64, _I64, _I32, ctypes.POINTER(PruneParams),
                                       ctypes.POINTER(ctypes.c_size_t)],
+    "th_prune_sparsegpt": [_P, _I32, _I64, _I64, _P, _I32, _I64, _P, ctypes.POINTER(PruneParams),
+                           _P, _P, _P, ctypes.c_size_t, ctypes.POINTER(Stats),
+                           ctypes.POINTER(_I64), _P],
+    "th_prune_sparsegpt_workspace_size": [_I64, _I64, _I64, _I32, ctypes.POINTER(PruneParams),
+                                          ctypes.POINTER(ctypes.c_size_t)],
     "th_reconstruction_error": [_P, _P, _I32, _I64, _I64, _P, _I32, _I64, _P, _P, ctypes.c_size_t,
                                 ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
                                 _P],
@@ -176,25 +181,46 @@ def prune_layer_workspace_size(c, b, n, have_x, params: PruneParams) -> int:
     return out.value
 
 
-def prune_layer(W, X=None, H=None, params: PruneParams | None = None, W_out=None, mask_out=None,
-                ws=None) -> dict:
-    """Prune W (c x b, bf16/fp32) in place; returns stats and per-block counts."""
+def _layer_call(entry, size_entry, W, X, H, params, W_out, mask_out, ws) -> dict:
     _require_cuda(W, X, H, W_out, mask_out)
     if params is None:
         params = make_params()
     c, b = W.shape
     n = X.shape[0] if X is not None else 0
     if ws is None:
-        ws = workspace(prune_layer_workspace_size(c, b, n, X is not None, params), W.device)
+        out = ctypes.c_size_t(0)
+        _check(size_entry(c, b, n, 1 if X is not None else 0, ctypes.byref(params),
+                          ctypes.byref(out)))
+        ws = workspace(out.value, W.device)
     stats = Stats()
     nblk = -(-b // params.block)
     counts = (_I64 * nblk)()
-    _check(lib().th_prune_layer(_ptr(W), _dtype_code(W), c, b, _ptr(X),
-                                _dtype_code(X) if X is not None else 0, n, _ptr(H),
-                                ctypes.byref(params), _ptr(W_out), _ptr(mask_out), _ptr(ws),
-                                ws.numel(), ctypes.byref(stats), counts, _stream(W.device)))
+    _check(entry(_ptr(W), _dtype_code(W), c, b, _ptr(X), _dtype_code(X) if X is not None else 0,
+                 n, _ptr(H), ctypes.byref(params), _ptr(W_out), _ptr(mask_out), _ptr(ws),
+                 ws.numel(), ctypes.byref(stats), counts, _stream(W.device)))
     return {"lambda": stats.lambda_used, "pruned": stats.total_pruned, "nblocks": stats.nblocks,
             "counts": list(counts)}
+
+
+def prune_layer(W, X=None, H=None, params: PruneParams | None = None, W_out=None, mask_out=None,
+                ws=None) -> dict:
+    """Prune W (c x b, bf16/fp32) in place; returns stats and per-block counts."""
+    return _layer_call(lib().th_prune_layer, lib().th_prune_layer_workspace_size, W, X, H,
+                       params, W_out, mask_out, ws)
+
+
+def prune_sparsegpt_workspace_size(c, b, n, have_x, params: PruneParams) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().th_prune_sparsegpt_workspace_size(c, b, n, 1 if have_x else 0,
+                                                   ctypes.byref(params), ctypes.byref(out)))
+    return out.value
+
+
+def prune_sparsegpt(W, X=None, H=None, params: PruneParams | None = None, W_out=None,
+                    mask_out=None, ws=None) -> dict:
+    """The column-sequential comparator on W (c x b) in place; same arguments as prune_layer."""
+    return _layer_call(lib().th_prune_sparsegpt, lib().th_prune_sparsegpt_workspace_size, W, X,
+                       H, params, W_out, mask_out, ws)
 
 
 def reconstruction_error(W, W_hat, X=None, G=None, ws=None):

@@ -1,12 +1,14 @@
-"""Reconstruction error of the joint-compensation method against the two comparators
-(Wanda and magnitude pruning, no compensation) on the synthetic workloads.
+"""Reconstruction error of the joint-compensation method against its comparators
+(SparseGPT's column-sequential schedule; Wanda and magnitude pruning, no
+compensation) on the synthetic workloads.
 
 Usage: python -m layer_wise_obs_amd.compare [--configs 1 2 3 4 5]
 
 For every layer and pattern of a workload: H from the layer's synthetic input
 stream (th_hessian_accumulate, th_hessian_finalize), then th_prune_layer (the
-method), th_prune_baseline with G_qq from th_column_sq_norms (Wanda) and without
-(magnitude), and th_reconstruction_error against G = (H - lambda I) / 2. Every step
+method), th_prune_sparsegpt, th_prune_baseline with G_qq from th_column_sq_norms
+(Wanda) and without (magnitude), and th_reconstruction_error against
+G = (H - lambda I) / 2. Every step
 runs in the HIP library; this file only moves tensors and prints one JSON line per
 (workload, layer, pattern).
 """
@@ -60,13 +62,14 @@ def run_config(cid: int):
             params = L.make_params(block=cfg.block, lam=cfg.lambda_rel, **kw)
             out = {"config": cid, "layer": layer.name, "c": layer.c, "b": layer.b,
                    "pattern": name, "E_rel": {}, "ms": {}}
-            W = W0.clone()
-            Wout = torch.empty(W.shape, dtype=torch.float32, device=DEV)
-            t0 = time.perf_counter()
-            L.prune_layer(W, H=H, params=params, W_out=Wout)
-            out["ms"]["thanos"] = round(_ms(t0), 3)
-            out["E_rel"]["thanos"] = L.reconstruction_error(W0.float(), Wout, G=G)[1]
-            del W, Wout
+            for name, fn in (("thanos", L.prune_layer), ("sparsegpt", L.prune_sparsegpt)):
+                W = W0.clone()
+                Wout = torch.empty(W.shape, dtype=torch.float32, device=DEV)
+                t0 = time.perf_counter()
+                fn(W, H=H, params=params, W_out=Wout)
+                out["ms"][name] = round(_ms(t0), 3)
+                out["E_rel"][name] = L.reconstruction_error(W0.float(), Wout, G=G)[1]
+                del W, Wout
             for method in ("wanda", "magnitude"):
                 W = W0.clone()
                 t0 = time.perf_counter()

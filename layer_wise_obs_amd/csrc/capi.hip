@@ -10,6 +10,9 @@
 //       N:M:          select + solve in one kernel, update W[:, J .. end of the
 //                     super-block]; the rest of F once per super-block
 //   output:             What cast back to the input dtype
+// th_prune_sparsegpt (comparator) shares the Hessian and the factor, then runs the
+// column-sequential schedule: per block a block-local mask, the per-row error
+// recurrence, and the same update GEMM with U in place of the slices.
 // The budget, the threshold and every count stay on the device; the host
 // synchronises once, at the end, to read the status flags.
 #include <cmath>
@@ -78,11 +81,15 @@ struct PruneLayout {
 // it is applied once per super-block as one GEMM with K = kSuperBlocks * B.
 constexpr int64_t kSuperBlocks = 8;
 
+int64_t super_pitch(int64_t b, int64_t B) {
+  const int64_t full = cdiv(b, B) * B;
+  const int64_t sb = kSuperBlocks * B;
+  return full < sb ? full : sb;
+}
+
 int64_t z_pitch(int64_t b, const th_prune_params* p) {
   if (p->pattern.kind != TH_NM) return p->block;
-  const int64_t full = cdiv(b, p->block) * p->block;
-  const int64_t sb = kSuperBlocks * p->block;
-  return full < sb ? full : sb;
+  return super_pitch(b, p->block);
 }
 
 bool needs_complement(const th_prune_params* p) {
@@ -91,8 +98,11 @@ bool needs_complement(const th_prune_params* p) {
   return (p->block / p->pattern.m) * (p->pattern.m - p->pattern.n) > 64;
 }
 
+// sgpt: the column-sequential comparator's layout (U only, no slices; gW holds the
+// score weights 1/U_qq^2; E in Z with the super-block pitch for both patterns).
 PruneLayout layout_prune(void* ws, int64_t c, int64_t b, int64_t n, bool have_x,
-                         const th_prune_params* p, bool need_wf, bool need_mask, th_dtype xdt) {
+                         const th_prune_params* p, bool need_wf, bool need_mask, th_dtype xdt,
+                         bool sgpt = false) {
   Carve cv(ws);
   PruneLayout L;
   const int64_t B = p->block;
@@ -102,12 +112,12 @@ PruneLayout layout_prune(void* ws, int64_t c, int64_t b, int64_t n, bool have_x,
   L.S = cv.take<float>((size_t)b * b);
   L.R = cv.take<float>((size_t)b * b);
   L.P = cv.take<float>(chol_panel_floats(b));
-  L.Ublk = cv.take<float>((size_t)nblk * B * B);
-  L.Nblk = needs_complement(p) ? cv.take<float>((size_t)nblk * B * B) : nullptr;
+  L.Ublk = sgpt ? nullptr : cv.take<float>((size_t)nblk * B * B);
+  L.Nblk = (!sgpt && needs_complement(p)) ? cv.take<float>((size_t)nblk * B * B) : nullptr;
   const bool unstr = p->pattern.kind == TH_UNSTRUCTURED;
-  L.D = (unstr && p->score == TH_SCORE_OBS) ? cv.take<float>((size_t)nblk * b) : nullptr;
-  L.gW = (p->score == TH_SCORE_WANDA) ? cv.take<float>((size_t)b) : nullptr;
-  L.Z = cv.take<float>((size_t)c * z_pitch(b, p));
+  L.D = (!sgpt && unstr && p->score == TH_SCORE_OBS) ? cv.take<float>((size_t)nblk * b) : nullptr;
+  L.gW = (sgpt || p->score == TH_SCORE_WANDA) ? cv.take<float>((size_t)b) : nullptr;
+  L.Z = cv.take<float>((size_t)c * (sgpt ? super_pitch(b, B) : z_pitch(b, p)));
   L.Wf = need_wf ? cv.take<float>((size_t)c * b) : nullptr;
   L.mask = need_mask ? cv.take<uint8_t>((size_t)c * b) : nullptr;
   L.syrk_part = nullptr;
@@ -147,6 +157,23 @@ th_status check_params(int64_t c, int64_t b, const th_prune_params* p) {
 
 bool dtype_ok(th_dtype d) { return d == TH_F32 || d == TH_BF16; }
 
+// Checks shared by the layer entry points (before anything is enqueued).
+th_status check_layer_args(const void* W, th_dtype wdt, int64_t c, int64_t b, const void* X,
+                           th_dtype xdt, int64_t n, const float* H, const th_prune_params* p,
+                           const void* workspace) {
+  th_status chk = check_params(c, b, p);
+  if (chk != TH_OK) return chk;
+  if (!W) return fail(TH_ERR_INVALID_ARG, "W is NULL");
+  if ((X == nullptr) == (H == nullptr)) return fail(TH_ERR_INVALID_ARG, "pass exactly one of X, H");
+  if (!dtype_ok(wdt) || (X && !dtype_ok(xdt))) return fail(TH_ERR_INVALID_ARG, "unknown dtype");
+  if (X && n < 1) return fail(TH_ERR_INVALID_ARG, "n must be >= 1");
+  if (X && xdt == TH_BF16 && (b % 8 || ((uintptr_t)X & 15)))
+    return fail(TH_ERR_INVALID_ARG, "bf16 X needs b % 8 == 0 and 16-byte alignment");
+  if (!workspace) return fail(TH_ERR_INVALID_ARG, "workspace is NULL");
+  if ((uintptr_t)workspace & 255) return fail(TH_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return TH_OK;
+}
+
 th_status accumulate_into(float* H, const void* X, th_dtype xdt, int64_t t, int64_t b,
                           int64_t ldx, float* part, hipStream_t s) {
   if (xdt == TH_BF16) {
@@ -155,6 +182,53 @@ th_status accumulate_into(float* H, const void* X, th_dtype xdt, int64_t t, int6
   } else {
     TH_HIP(launch_syrk_f32(H, (const float*)X, t, b, ldx, s), "syrk_f32");
   }
+  return TH_OK;
+}
+
+// Damped H (from X through the syrk, or given), its flipped lower triangle in S,
+// then U with H^-1 = U^T U in R (in-place Cholesky and inverse of S, reversed).
+// Wanda's G_qq goes to L.gW when the score asks for it.
+th_status inverse_factor(const void* X, th_dtype xdt, int64_t n, const float* H, int64_t b,
+                         const th_prune_params* p, const PruneLayout& L, hipStream_t s) {
+  const bool obs = p->score == TH_SCORE_OBS;
+  if (X) {
+    float* Hb = L.R;  // R is free until the factor is reversed into it
+    TH_HIP(hipMemsetAsync(Hb, 0, (size_t)b * b * sizeof(float), s), "memset H");
+    th_status a = accumulate_into(Hb, X, xdt, n, b, b, L.syrk_part, s);
+    if (a != TH_OK) return a;
+    TH_HIP(launch_lambda(Hb, b, p->lambda, p->lambda_is_relative, 0, L.st, s), "lambda");
+    if (!obs) TH_HIP(launch_wanda_diag(Hb, b, L.st, 0, L.gW, s), "wanda diag");
+    TH_HIP(launch_flip_lower(Hb, L.S, b, L.st, 1, s), "flip");
+  } else {
+    TH_HIP(launch_lambda(H, b, p->lambda, p->lambda_is_relative, 1, L.st, s), "lambda");
+    if (!obs) TH_HIP(launch_wanda_diag(H, b, L.st, 1, L.gW, s), "wanda diag");
+    TH_HIP(launch_flip_lower(H, L.S, b, L.st, 0, s), "flip");
+  }
+  TH_HIP(launch_chol_inv_inplace(L.S, b, L.P, L.st, s), "cholesky/inverse");
+  TH_HIP(launch_reverse(L.S, L.R, b, s), "reverse");
+  return TH_OK;
+}
+
+// The one synchronisation of a layer call: device state and per-block counts to
+// the host, then the status flags.
+th_status finish_layer(const PruneLayout& L, int64_t nblk, th_stats* stats_out,
+                       int64_t* block_counts, hipStream_t s) {
+  DevState host;
+  TH_HIP(hipMemcpyAsync(&host, L.st, offsetof(DevState, hist), hipMemcpyDeviceToHost, s), "state");
+  std::vector<unsigned long long> counts((size_t)nblk);
+  TH_HIP(hipMemcpyAsync(counts.data(), L.counts, nblk * sizeof(unsigned long long),
+                        hipMemcpyDeviceToHost, s),
+         "counts");
+  TH_HIP(hipStreamSynchronize(s), "sync");
+  if (stats_out) {
+    stats_out->lambda_used = host.lambda;
+    stats_out->total_pruned = host.pruned;
+    stats_out->nblocks = nblk;
+  }
+  if (block_counts)
+    for (int64_t i = 0; i < nblk; ++i) block_counts[i] = (int64_t)counts[i];
+  if (host.nonfinite) return fail(TH_ERR_NONFINITE, "non-finite value in W or diag(H)");
+  if (host.not_spd) return fail(TH_ERR_NOT_SPD, "damped Hessian is not positive definite");
   return TH_OK;
 }
 
@@ -227,16 +301,8 @@ th_status th_prune_layer(void* W, th_dtype wdt, int64_t c, int64_t b, const void
                          int64_t n, const float* H, const th_prune_params* p, float* W_out_f32,
                          uint8_t* mask_out, void* workspace, size_t workspace_bytes,
                          th_stats* stats_out, int64_t* block_counts, th_stream_t stream) {
-  th_status chk = check_params(c, b, p);
+  th_status chk = check_layer_args(W, wdt, c, b, X, xdt, n, H, p, workspace);
   if (chk != TH_OK) return chk;
-  if (!W) return fail(TH_ERR_INVALID_ARG, "W is NULL");
-  if ((X == nullptr) == (H == nullptr)) return fail(TH_ERR_INVALID_ARG, "pass exactly one of X, H");
-  if (!dtype_ok(wdt) || (X && !dtype_ok(xdt))) return fail(TH_ERR_INVALID_ARG, "unknown dtype");
-  if (X && n < 1) return fail(TH_ERR_INVALID_ARG, "n must be >= 1");
-  if (X && xdt == TH_BF16 && (b % 8 || ((uintptr_t)X & 15)))
-    return fail(TH_ERR_INVALID_ARG, "bf16 X needs b % 8 == 0 and 16-byte alignment");
-  if (!workspace) return fail(TH_ERR_INVALID_ARG, "workspace is NULL");
-  if ((uintptr_t)workspace & 255) return fail(TH_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   PruneLayout L = layout_prune(workspace, c, b, n, X != nullptr, p, W_out_f32 == nullptr,
                                mask_out == nullptr, xdt);
   if (workspace_bytes < L.bytes) return fail(TH_ERR_WORKSPACE, "workspace too small");
@@ -258,24 +324,10 @@ th_status th_prune_layer(void* W, th_dtype wdt, int64_t c, int64_t b, const void
   }
   TH_HIP(launch_to_f32(W, wdt, c * b, Wf, L.st, s), "W to fp32");
 
-  // Hessian and its flipped, damped lower triangle.
-  if (X) {
-    float* Hb = L.R;  // R is free until the factor is reversed into it
-    TH_HIP(hipMemsetAsync(Hb, 0, (size_t)b * b * sizeof(float), s), "memset H");
-    th_status a = accumulate_into(Hb, X, xdt, n, b, b, L.syrk_part, s);
-    if (a != TH_OK) return a;
-    TH_HIP(launch_lambda(Hb, b, p->lambda, p->lambda_is_relative, 0, L.st, s), "lambda");
-    if (!obs) TH_HIP(launch_wanda_diag(Hb, b, L.st, 0, L.gW, s), "wanda diag");
-    TH_HIP(launch_flip_lower(Hb, L.S, b, L.st, 1, s), "flip");
-  } else {
-    TH_HIP(launch_lambda(H, b, p->lambda, p->lambda_is_relative, 1, L.st, s), "lambda");
-    if (!obs) TH_HIP(launch_wanda_diag(H, b, L.st, 1, L.gW, s), "wanda diag");
-    TH_HIP(launch_flip_lower(H, L.S, b, L.st, 0, s), "flip");
-  }
+  th_status pre = inverse_factor(X, xdt, n, H, b, p, L, s);
+  if (pre != TH_OK) return pre;
 
-  // U with H^-1 = U^T U, then the per-block slices.
-  TH_HIP(launch_chol_inv_inplace(L.S, b, L.P, L.st, s), "cholesky/inverse");
-  TH_HIP(launch_reverse(L.S, L.R, b, s), "reverse");
+  // the per-block slices
   TH_HIP(launch_save_diag_blocks(L.R, b, B, L.Ublk, s), "diag blocks");
   // S is free once reversed into R: it holds the fp64 partial sums
   if (L.D)
@@ -292,9 +344,9 @@ th_status th_prune_layer(void* W, th_dtype wdt, int64_t c, int64_t b, const void
     if (unstr) {
       // the global selection scores every active column, so W[:, F] is updated in full
       const float* g = obs ? L.D + blk * b : L.gW;
-      TH_HIP(launch_select_init(L.st, 0, blk == 0, (long long)(c * (b - j0)), s), "select init");
+      TH_HIP(launch_select_init(L.st, 0, (long long)(c * (b - j0)), s), "select init");
       for (int pass = 0; pass < 6; ++pass) {
-        TH_HIP(launch_select_pass(Wf, c, b, j0, g, L.st, s), "select pass");
+        TH_HIP(launch_select_pass(Wf, c, b, j0, b, g, L.st, s), "select pass");
         TH_HIP(launch_select_pick(L.st, s), "select pick");
       }
       TH_HIP(launch_solve_unstructured(Wf, c, b, j0, B, L.R, Nb, g, L.Z, mask, L.st,
@@ -316,24 +368,73 @@ th_status th_prune_layer(void* W, th_dtype wdt, int64_t c, int64_t b, const void
     }
   }
   TH_HIP(launch_from_f32(Wf, c * b, wdt, W, s), "cast back");
+  return finish_layer(L, nblk, stats_out, block_counts, s);
+}
 
-  DevState host;
-  TH_HIP(hipMemcpyAsync(&host, L.st, offsetof(DevState, hist), hipMemcpyDeviceToHost, s), "state");
-  std::vector<unsigned long long> counts((size_t)nblk);
-  TH_HIP(hipMemcpyAsync(counts.data(), L.counts, nblk * sizeof(unsigned long long),
-                        hipMemcpyDeviceToHost, s),
-         "counts");
-  TH_HIP(hipStreamSynchronize(s), "sync");
-  if (stats_out) {
-    stats_out->lambda_used = host.lambda;
-    stats_out->total_pruned = host.pruned;
-    stats_out->nblocks = nblk;
-  }
-  if (block_counts)
-    for (int64_t i = 0; i < nblk; ++i) block_counts[i] = (int64_t)counts[i];
-  if (host.nonfinite) return fail(TH_ERR_NONFINITE, "non-finite value in W or diag(H)");
-  if (host.not_spd) return fail(TH_ERR_NOT_SPD, "damped Hessian is not positive definite");
+th_status th_prune_sparsegpt_workspace_size(int64_t c, int64_t b, int64_t n, int32_t have_x,
+                                            const th_prune_params* p, size_t* bytes) {
+  if (!bytes) return fail(TH_ERR_INVALID_ARG, "bytes is NULL");
+  th_status st = check_params(c, b, p);
+  if (st != TH_OK) return st;
+  PruneLayout L = layout_prune(nullptr, c, b, n, have_x != 0, p, true, true, TH_BF16, true);
+  *bytes = L.bytes;
   return TH_OK;
+}
+
+th_status th_prune_sparsegpt(void* W, th_dtype wdt, int64_t c, int64_t b, const void* X,
+                             th_dtype xdt, int64_t n, const float* H, const th_prune_params* p,
+                             float* W_out_f32, uint8_t* mask_out, void* workspace,
+                             size_t workspace_bytes, th_stats* stats_out, int64_t* block_counts,
+                             th_stream_t stream) {
+  th_status chk = check_layer_args(W, wdt, c, b, X, xdt, n, H, p, workspace);
+  if (chk != TH_OK) return chk;
+  if (p->score != TH_SCORE_OBS)
+    return fail(TH_ERR_INVALID_ARG, "the column-sequential comparator takes the OBS score only");
+  PruneLayout L = layout_prune(workspace, c, b, n, X != nullptr, p, W_out_f32 == nullptr,
+                               mask_out == nullptr, xdt, true);
+  if (workspace_bytes < L.bytes) return fail(TH_ERR_WORKSPACE, "workspace too small");
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t B = p->block;
+  const int64_t nblk = cdiv(b, B);
+  float* Wf = W_out_f32 ? W_out_f32 : L.Wf;
+  uint8_t* mask = mask_out ? mask_out : L.mask;
+  const bool unstr = p->pattern.kind == TH_UNSTRUCTURED;
+
+  TH_HIP(hipMemsetAsync(L.st, 0, sizeof(DevState), s), "memset state");
+  TH_HIP(hipMemsetAsync(L.counts, 0, nblk * sizeof(unsigned long long), s), "memset counts");
+  TH_HIP(launch_to_f32(W, wdt, c * b, Wf, L.st, s), "W to fp32");
+  th_status pre = inverse_factor(X, xdt, n, H, b, p, L, s);
+  if (pre != TH_OK) return pre;
+  TH_HIP(launch_sgpt_gdiag(L.R, b, L.gW, s), "score weights");
+
+  // Both masks depend only on the block's own columns, so compensation beyond the
+  // super-block waits and is applied once per super-block (K = its width).
+  const int64_t ldz = super_pitch(b, B);
+  const int64_t per = ldz / B;
+  for (int64_t blk = 0; blk < nblk; ++blk) {
+    const int64_t j0 = blk * B;
+    const int64_t Bb = (b - j0) < B ? (b - j0) : B;
+    const int64_t sb0 = (blk / per) * ldz;
+    const int64_t s1 = (sb0 + ldz) < b ? (sb0 + ldz) : b;
+    float* Eb = L.Z + (blk % per) * B;
+    if (unstr) {  // the block's quota: round-half-even(p * c * |J|)
+      const long long quota = (long long)std::nearbyint(p->sparsity * (double)c * (double)Bb);
+      TH_HIP(launch_select_init(L.st, quota, (long long)(c * Bb), s), "select init");
+      for (int pass = 0; pass < 6; ++pass) {
+        TH_HIP(launch_select_pass(Wf, c, b, j0, j0 + Bb, L.gW, L.st, s), "select pass");
+        TH_HIP(launch_select_pick(L.st, s), "select pick");
+      }
+    }
+    TH_HIP(launch_sgpt_errors(Wf, c, b, j0, B, p->pattern.n, p->pattern.m, unstr ? 1 : 0, L.R,
+                              L.gW, Eb, ldz, mask, L.st, L.counts + blk, s),
+           "errors");
+    TH_HIP(launch_update(Wf, c, b, j0, Bb, ldz, j0, s1, Eb, L.R, mask, j0, Bb, s), "update");
+    if (j0 + Bb == s1 && s1 < b)
+      TH_HIP(launch_update(Wf, c, b, sb0, s1 - sb0, ldz, s1, b, L.Z, L.R, mask, 0, 0, s),
+             "deferred update");
+  }
+  TH_HIP(launch_from_f32(Wf, c * b, wdt, W, s), "cast back");
+  return finish_layer(L, nblk, stats_out, block_counts, s);
 }
 
 th_status th_reconstruction_error_workspace_size(int64_t c, int64_t b, int32_t have_x,
@@ -416,7 +517,7 @@ th_status th_debug_select_global(const float* scores, int64_t c, int64_t f, int6
   TH_HIP(hipMemsetAsync(st, 0, sizeof(DevState), s), "memset");
   long long budget = r;
   TH_HIP(hipMemcpyAsync(&st->budget, &budget, sizeof(budget), hipMemcpyHostToDevice, s), "budget");
-  TH_HIP(launch_select_init(st, 0, 1, (long long)(c * f), s), "init");
+  TH_HIP(launch_select_init(st, 0, (long long)(c * f), s), "init");
   for (int pass = 0; pass < 6; ++pass) {
     TH_HIP(launch_select_scores_pass(scores, c, f, b_full, j0, st, s), "pass");
     TH_HIP(launch_select_pick(st, s), "pick");

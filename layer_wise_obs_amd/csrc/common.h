@@ -43,6 +43,20 @@ __device__ __forceinline__ float score_of(float w, float g) {
   return __fmul_rn(w2, g);
 }
 
+// N:M selection: whether entry e is among the m-n lowest (score, column) of its
+// aligned group of m in sc[] (ties: the lower column is pruned first).
+__device__ __forceinline__ bool nm_pruned(const float* sc, int e, int n, int m) {
+  const int g0 = (e / m) * m;
+  const float se = sc[e];
+  int rank = 0;
+  for (int t = 0; t < m; ++t) {
+    const int q = g0 + t;
+    const float sq = sc[q];
+    rank += (q != e) && ((sq < se) || (sq == se && q < e));
+  }
+  return rank < m - n;
+}
+
 __device__ __forceinline__ unsigned long long make_key(float s, unsigned int flat) {
   return ((unsigned long long)__float_as_uint(s) << 32) | (unsigned long long)flat;
 }
@@ -130,10 +144,11 @@ hipError_t launch_block_inverses(const float* Ublk, int64_t b, int64_t B, float*
                                  hipStream_t s);
 
 // select.hip
-hipError_t launch_select_init(DevState* st, long long unused, int first, long long ncand,
+// budget += add_budget, then r = budget - pruned keys are to be found among ncand.
+hipError_t launch_select_init(DevState* st, long long add_budget, long long ncand,
                               hipStream_t s);
-// One radix pass over the keys of W[:, j0:] with score weights g, then the pick.
-hipError_t launch_select_pass(const float* W, int64_t c, int64_t b, int64_t j0,
+// One radix pass over the keys of W[:, j0:j1) with score weights g, then the pick.
+hipError_t launch_select_pass(const float* W, int64_t c, int64_t b, int64_t j0, int64_t j1,
                               const float* g, DevState* st, hipStream_t s);
 hipError_t launch_select_pick(DevState* st, hipStream_t s);
 hipError_t launch_select_scores_pass(const float* scores, int64_t c, int64_t f,
@@ -154,6 +169,13 @@ hipError_t launch_debug_mask_from_scores(const float* scores, int64_t c, int64_t
                                          int64_t b_full, int64_t j0, int64_t blk,
                                          const DevState* st, uint8_t* mask, int32_t* s_k,
                                          hipStream_t s);
+
+// sparsegpt.hip
+hipError_t launch_sgpt_gdiag(const float* U, int64_t b, float* g, hipStream_t s);
+hipError_t launch_sgpt_errors(const float* W, int64_t c, int64_t b, int64_t j0, int64_t B, int n,
+                              int m, int unstructured, const float* U, const float* g, float* E,
+                              int64_t lde, uint8_t* mask, DevState* st,
+                              unsigned long long* blk_count, hipStream_t s);
 
 // update.hip
 // W[:, col0:col_end) -= Z[:, 0:K] R[r0:r0+K, col0:col_end) (Z pitch ldz); entries of

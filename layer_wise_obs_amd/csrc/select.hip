@@ -27,10 +27,12 @@ __device__ __forceinline__ void digit_of(int shift, int& width) {
   width = (shift == 0) ? 9 : 11;
 }
 
-__global__ void select_init_kernel(DevState* st, long long ncand) {
+__global__ void select_init_kernel(DevState* st, long long add_budget, long long ncand) {
   for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) st->hist[i] = 0u;
   if (threadIdx.x == 0) {
-    const long long r = st->budget - st->pruned;
+    const long long budget = st->budget + add_budget;
+    st->budget = budget;
+    const long long r = budget - st->pruned;
     st->rrem = r;
     st->prefix = 0ull;
     st->shift = 53;
@@ -130,11 +132,11 @@ __device__ __forceinline__ void pass_body(DevState* st, int64_t rows, int64_t f,
 // Keys recomputed from the current weights: S = W^2 * g with g the per-column
 // score weight (1/[A_F]_qq for OBS, G_qq for Wanda).
 __global__ __launch_bounds__(256) void select_pass_kernel(const float* __restrict__ W, int64_t c,
-                                                          int64_t b, int64_t j0,
+                                                          int64_t b, int64_t j0, int64_t j1,
                                                           const float* __restrict__ g,
                                                           DevState* st) {
   if (st->done) return;
-  pass_body(st, c, b - j0, [&](int64_t k, int64_t q) {
+  pass_body(st, c, j1 - j0, [&](int64_t k, int64_t q) {
     const int64_t col = j0 + q;
     const float s = score_of(W[k * b + col], g[col]);
     return make_key(s, (unsigned int)(k * b + col));
@@ -154,9 +156,9 @@ __global__ __launch_bounds__(256) void select_scores_pass_kernel(const float* __
 
 }  // namespace
 
-hipError_t launch_select_init(DevState* st, long long /*unused*/, int /*first*/, long long ncand,
+hipError_t launch_select_init(DevState* st, long long add_budget, long long ncand,
                               hipStream_t s) {
-  hipLaunchKernelGGL(select_init_kernel, dim3(1), dim3(256), 0, s, st, ncand);
+  hipLaunchKernelGGL(select_init_kernel, dim3(1), dim3(256), 0, s, st, add_budget, ncand);
   return hipGetLastError();
 }
 
@@ -165,9 +167,10 @@ static unsigned pass_grid(int64_t rows) {
   return (unsigned)(g < 1 ? 1 : g);
 }
 
-hipError_t launch_select_pass(const float* W, int64_t c, int64_t b, int64_t j0, const float* g,
-                              DevState* st, hipStream_t s) {
-  hipLaunchKernelGGL(select_pass_kernel, dim3(pass_grid(c)), dim3(256), 0, s, W, c, b, j0, g, st);
+hipError_t launch_select_pass(const float* W, int64_t c, int64_t b, int64_t j0, int64_t j1,
+                              const float* g, DevState* st, hipStream_t s) {
+  hipLaunchKernelGGL(select_pass_kernel, dim3(pass_grid(c)), dim3(256), 0, s, W, c, b, j0, j1, g,
+                     st);
   return hipGetLastError();
 }
 

@@ -36,19 +36,6 @@ constexpr int kWaves = 8;
 // column, 64 different rows) hit distinct banks without padding the pitch.
 __device__ __forceinline__ int mat_idx(int r, int q) { return r * kMaxBlock + (q ^ (r & 31)); }
 
-// Rank of entry e in its aligned group of m among scores sc[] (ties: lower column first).
-__device__ __forceinline__ bool nm_pruned(const float* sc, int e, int n, int m) {
-  const int g0 = (e / m) * m;
-  const float se = sc[e];
-  int rank = 0;
-  for (int t = 0; t < m; ++t) {
-    const int q = g0 + t;
-    const float sq = sc[q];
-    rank += (q != e) && ((sq < se) || (sq == se && q < e));
-  }
-  return rank < m - n;
-}
-
 // Gauss-Jordan on 64 registers per lane: rows = lanes, all 64 steps (rows and
 // columns past the system size hold the identity and a zero right-hand side, so
 // their steps change nothing). Returns x_lane = rhs_lane / pivot_lane. The pivot

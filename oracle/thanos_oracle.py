@@ -407,12 +407,13 @@ def prune_sparsegpt(W, G: np.ndarray, sparsity: float = 0.5, pattern=None, block
     for j0 in range(0, b, block):
         blk = min(block, b - j0)
         S = Wc[:, j0:j0 + blk] ** 2 / d[None, j0:j0 + blk]
+        r = k_total(sparsity, c, blk) if pattern is None else None
         if pattern is None:
-            sel = select_unstructured(S, k_total(sparsity, c, blk), blk)
+            sel = select_unstructured(S, r, blk)
         else:
             sel = select_nm(S, pattern[0], pattern[1])
         if trace is not None:
-            trace.append({"j0": j0, "S": S.copy()})
+            trace.append({"j0": j0, "S": S.copy(), "r": r})
         for t in range(blk):
             sparsegpt_column(Wc, j0 + t, sel[:, t], T[j0 + t, j0 + t:])
         mask[:, j0:j0 + blk] = sel

@@ -21,7 +21,8 @@ def test_header_declares_the_path():
     for must in ("th_hessian_accumulate", "th_hessian_finalize", "th_prune_layer",
                  "th_prune_layer_workspace_size", "th_reconstruction_error", "th_debug_select_nm",
                  "th_debug_select_global", "th_debug_factor", "th_last_error",
-                 "th_column_sq_norms", "th_column_sq_norms_workspace_size", "th_prune_baseline"):
+                 "th_column_sq_norms", "th_column_sq_norms_workspace_size", "th_prune_baseline",
+                 "th_prune_sparsegpt", "th_prune_sparsegpt_workspace_size"):
         assert must in names
 
 
@@ -113,3 +114,30 @@ def test_baseline_arguments_are_rejected_before_any_launch():
     assert L.th_column_sq_norms(None, _lib.TH_BF16, 10, 8, 8, fake, fake, 1 << 20, None) == 1
     assert L.th_column_sq_norms(fake, _lib.TH_BF16, 10, 8, 8, fake, fake, 8, None) == \
         _lib.TH_ERR_WORKSPACE
+
+
+def test_sparsegpt_arguments_are_rejected_before_any_launch():
+    L = _lib.lib()
+    out = ctypes.c_size_t(0)
+    ok = _lib.make_params(pattern=(2, 4), block=128)
+    assert L.th_prune_sparsegpt_workspace_size(4096, 11008, 262144, 1, ctypes.byref(ok),
+                                               ctypes.byref(out)) == 0
+    full = ctypes.c_size_t(0)
+    L.th_prune_layer_workspace_size(4096, 11008, 262144, 1, ctypes.byref(ok), ctypes.byref(full))
+    assert 2 * 11008 * 11008 * 4 < out.value <= full.value  # no slices beside U
+    bad = _lib.make_params(pattern=(2, 4), block=126)
+    assert L.th_prune_sparsegpt_workspace_size(64, 128, 10, 1, ctypes.byref(bad),
+                                               ctypes.byref(out)) == 1
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its checks first
+    wanda = _lib.make_params(score="wanda")
+    args = [fake, _lib.TH_BF16, 8, 8, fake, _lib.TH_BF16, 8, None, ctypes.byref(wanda), None, None,
+            ctypes.c_void_p(0x1000), 1 << 20, None, None, None]
+    assert L.th_prune_sparsegpt(*args) == 1  # the comparator takes the OBS score only
+    assert "OBS" in L.th_last_error().decode()
+    p = _lib.make_params()
+    args[8] = ctypes.byref(p)
+    args[7] = fake  # both X and H
+    assert L.th_prune_sparsegpt(*args) == 1
+    args[7] = None
+    args[11] = ctypes.c_void_p(0x1010)  # workspace not 256-byte aligned
+    assert L.th_prune_sparsegpt(*args) == 1
