@@ -45,7 +45,8 @@ __all__ = [
     "NotSPDError", "gram", "damping", "hessian", "k_total", "obs_scores",
     "select_unstructured", "select_nm", "solve_rows", "schur_downdate",
     "prune_layer", "reconstruction_error", "column_sq_norms", "baseline_keys", "prune_baseline",
-    "trailing_inverse_rows", "sparsegpt_column", "prune_sparsegpt",
+    "trailing_inverse_rows", "sparsegpt_column", "prune_sparsegpt", "silu", "gated_ffn_input",
+    "prune_mlp_sequential",
 ]
 
 
@@ -420,4 +421,53 @@ def prune_sparsegpt(W, G: np.ndarray, sparsity: float = 0.5, pattern=None, block
         counts.append(int(sel.sum()))
     return {"W_hat": Wc, "mask": mask, "counts": counts, "lam": lam_abs,
             "pruned": int(sum(counts))}
+
+
+def silu(z):
+    """silu(z) = z * sigmoid(z), with sigmoid(z) = (1 + tanh(z/2)) / 2 (no overflow)."""
+    z = np.asarray(z, dtype=np.float64)
+    return z * (0.5 * (1.0 + np.tanh(0.5 * z)))
+
+
+def gated_ffn_input(X_tok, W_gate, W_up) -> np.ndarray:
+    """Input of down_proj: Y = silu(X W_gate^T) * (X W_up^T), fp64, token-major [n, f].
+
+    "Pruning LLMs with Thanos", section "The compression target: linear layers": a
+    block's feed-forward projections are joined by a nonlinearity. The layer names
+    gate_proj / up_proj / down_proj are LLaMA's gated feed-forward, read here as
+    down_proj(silu(gate_proj(x)) * up_proj(x)).
+    """
+    X = _f64(X_tok)
+    return silu(X @ _f64(W_gate).T) * (X @ _f64(W_up).T)
+
+
+def _bf16_round(a: np.ndarray) -> np.ndarray:
+    """Round fp64 values to bf16 (through fp32, each step to nearest even), as fp64."""
+    f = np.asarray(a, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    finite = np.isfinite(f)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    out = np.where(finite, r, u).astype(np.uint32).view(np.float32)
+    return out.astype(np.float64)
+
+
+def prune_mlp_sequential(X_mlp, W_gate, W_up, W_down, sparsity: float = 0.5, pattern=None,
+                         block: int = 128, lam: float = 0.01) -> dict:
+    """The feed-forward half of a block pruned in order, with propagated activations.
+
+    gate_proj and up_proj share the input X_mlp and so one Hessian; they are pruned
+    first. down_proj's calibration input is then produced by the pruned gate and up
+    (gated_ffn_input), stored like every other activation in bf16 (rounded to
+    nearest even), and down_proj is pruned on its own Hessian ("Pruning LLMs with
+    Thanos", section "The layer-reconstruction lens": each linear layer is
+    reconstructed from its own inputs).
+    """
+    G_mlp = gram(X_mlp)
+    gate = prune_layer(W_gate, G_mlp, sparsity=sparsity, pattern=pattern, block=block, lam=lam)
+    up = prune_layer(W_up, G_mlp, sparsity=sparsity, pattern=pattern, block=block, lam=lam)
+    X_down = _bf16_round(gated_ffn_input(X_mlp, gate["W_hat"], up["W_hat"]))
+    G_down = gram(X_down)
+    down = prune_layer(W_down, G_down, sparsity=sparsity, pattern=pattern, block=block, lam=lam)
+    return {"gate": gate, "up": up, "down": down, "X_down": X_down, "G_mlp": G_mlp,
+            "G_down": G_down}
 

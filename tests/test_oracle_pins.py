@@ -670,6 +670,61 @@ def test_p23_sparsegpt_per_block_quota_and_limits(p, counts):
     assert np.all(nm["mask"].reshape(5, 5, 4).sum(axis=2) == 3)
 
 
+# ------------------------------- gated feed-forward and sequential block (P24-P25)
+
+def test_p24_silu_and_gated_ffn_input():
+    """silu(z) = z / (1 + e^-z) (hand values from math.exp, the odd-part identity
+    silu(z) - silu(-z) = z, saturation) and Y = silu(X Wg^T) * (X Wu^T) against
+    torch's fp64 silu and matmul; the bf16 rounding against torch's cast."""
+    import math
+
+    import torch
+    np.testing.assert_allclose(O.silu(np.array([0.0, 1.0, 2.0, -1.0])),
+                               [0.0, 1.0 / (1.0 + math.exp(-1.0)), 2.0 / (1.0 + math.exp(-2.0)),
+                                -1.0 / (1.0 + math.exp(1.0))], rtol=1e-15, atol=0)
+    z = np.random.default_rng(RNG_SEED + 24).standard_normal(1000) * 30
+    np.testing.assert_allclose(O.silu(z) - O.silu(-z), z, rtol=1e-12, atol=1e-12)
+    assert O.silu(np.array([800.0]))[0] == 800.0 and O.silu(np.array([-800.0]))[0] == 0.0
+    # hand example: X = [1, 2], gate rows e1, e2 -> (1, 2); up rows -> (3, 2)
+    Y = O.gated_ffn_input(np.array([[1.0, 2.0]]), np.eye(2), np.array([[1.0, 1.0], [2.0, 0.0]]))
+    np.testing.assert_allclose(Y, [[3.0 / (1.0 + math.exp(-1.0)), 4.0 / (1.0 + math.exp(-2.0))]],
+                               rtol=1e-15)
+    rng = np.random.default_rng(RNG_SEED + 25)
+    X, Wg, Wu = rng.standard_normal((40, 16)), rng.standard_normal((24, 16)), rng.standard_normal((24, 16))
+    Xt, Wgt, Wut = (torch.tensor(a, dtype=torch.float64) for a in (X, Wg, Wu))
+    ref = (torch.nn.functional.silu(Xt @ Wgt.T) * (Xt @ Wut.T)).numpy()
+    np.testing.assert_allclose(O.gated_ffn_input(X, Wg, Wu), ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(O.gated_ffn_input(X, Wg, 3.0 * Wu), 3.0 * ref, rtol=1e-12, atol=1e-12)
+    v = rng.standard_normal(5000) * 10.0 ** rng.integers(-6, 6, 5000)
+    bt = torch.tensor(v.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(O.thanos_oracle._bf16_round(v), bt)
+
+
+def test_p25_sequential_mlp_block():
+    """gate and up are pruned on the Hessian of their shared input; down on the
+    Hessian of the input its pruned predecessors produce. At p = 0 nothing is
+    pruned, so down's input is the bf16 rounding of the dense block's (torch fp64
+    silu); at p = 0.5 down's input differs from the dense one and down is the
+    layer step on it."""
+    import torch
+    rng = np.random.default_rng(RNG_SEED + 26)
+    X = rng.standard_normal((300, 16))
+    Wg, Wu, Wd = (0.3 * rng.standard_normal(s) for s in ((24, 16), (24, 16), (16, 24)))
+    dense = O.prune_mlp_sequential(X, Wg, Wu, Wd, sparsity=0.0, block=8)
+    Xt = torch.tensor(X)
+    Yd = torch.nn.functional.silu(Xt @ torch.tensor(Wg).T) * (Xt @ torch.tensor(Wu).T)
+    np.testing.assert_array_equal(dense["X_down"], Yd.float().to(torch.bfloat16).double().numpy())
+    np.testing.assert_array_equal(dense["down"]["W_hat"], Wd)
+    sp = O.prune_mlp_sequential(X, Wg, Wu, Wd, sparsity=0.5, block=8)
+    for name, W in (("gate", Wg), ("up", Wu)):
+        alone = O.prune_layer(W, O.gram(X), sparsity=0.5, block=8)
+        np.testing.assert_array_equal(sp[name]["W_hat"], alone["W_hat"])
+    assert not np.array_equal(sp["X_down"], dense["X_down"])
+    down = O.prune_layer(Wd, O.gram(sp["X_down"]), sparsity=0.5, block=8)
+    np.testing.assert_array_equal(sp["down"]["W_hat"], down["W_hat"])
+    assert sp["down"]["pruned"] == O.k_total(0.5, 16, 24)
+
+
 # ------------------------------------------------------- planted mistakes
 
 def _pins_pass():
@@ -689,6 +744,7 @@ def _pins_pass():
         test_p21_sparsegpt_score_is_obs_cost_with_earlier_columns_frozen()
         test_p22_sparsegpt_diagonal_gram_is_blockwise_threshold()
         test_p23_sparsegpt_per_block_quota_and_limits(0.3, [12, 12, 6])
+        test_p24_silu_and_gated_ffn_input()
     except AssertionError:
         return False
     return True
@@ -717,7 +773,8 @@ def _bad_keys_abs_times_g(W, gdiag=None):
 
 @pytest.mark.parametrize("mutation", ["downdate", "sign", "nm_ties", "score_diag_H",
                                       "baseline_power", "baseline_layer_budget",
-                                      "sgpt_full_inverse", "sgpt_sign", "sgpt_row_quota"])
+                                      "sgpt_full_inverse", "sgpt_sign", "sgpt_row_quota",
+                                      "silu_mirrored"])
 def test_planted_mistakes_are_caught(monkeypatch, mutation):
     assert _pins_pass()
     T = O.thanos_oracle
@@ -771,4 +828,8 @@ def test_planted_mistakes_are_caught(monkeypatch, mutation):
             return np.concatenate([orig_sel(S_F[k:k + 1], int(np.round(r / c)), blk)
                                    for k in range(c)])
         monkeypatch.setattr(T, "select_unstructured", per_row)
+    elif mutation == "silu_mirrored":
+        # z * sigmoid(-z): the same odd part, the wrong function
+        monkeypatch.setattr(T, "silu", lambda z: np.asarray(z, np.float64)
+                            * (0.5 * (1.0 - np.tanh(0.5 * np.asarray(z, np.float64)))))
     assert not _pins_pass()
