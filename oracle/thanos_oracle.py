@@ -457,15 +457,22 @@ def prune_mlp_sequential(X_mlp, W_gate, W_up, W_down, sparsity: float = 0.5, pat
 
     gate_proj and up_proj share the input X_mlp and so one Hessian; they are pruned
     first. down_proj's calibration input is then produced by the pruned gate and up
-    (gated_ffn_input), stored like every other activation in bf16 (rounded to
-    nearest even), and down_proj is pruned on its own Hessian ("Pruning LLMs with
-    Thanos", section "The layer-reconstruction lens": each linear layer is
-    reconstructed from its own inputs).
+    as the layers store them (in their own dtype: bf16 weights rounded to nearest
+    even) through gated_ffn_input, kept like every other activation in bf16, and
+    down_proj is pruned on its own Hessian ("Pruning LLMs with Thanos", section
+    "The layer-reconstruction lens": each linear layer is reconstructed from its
+    own inputs).
     """
     G_mlp = gram(X_mlp)
     gate = prune_layer(W_gate, G_mlp, sparsity=sparsity, pattern=pattern, block=block, lam=lam)
     up = prune_layer(W_up, G_mlp, sparsity=sparsity, pattern=pattern, block=block, lam=lam)
-    X_down = _bf16_round(gated_ffn_input(X_mlp, gate["W_hat"], up["W_hat"]))
+
+    def stored(W, W_hat):
+        bf16 = hasattr(W, "dtype") and str(W.dtype) == "torch.bfloat16"
+        return _bf16_round(W_hat) if bf16 else W_hat
+
+    X_down = _bf16_round(gated_ffn_input(X_mlp, stored(W_gate, gate["W_hat"]),
+                                         stored(W_up, up["W_hat"])))
     G_down = gram(X_down)
     down = prune_layer(W_down, G_down, sparsity=sparsity, pattern=pattern, block=block, lam=lam)
     return {"gate": gate, "up": up, "down": down, "X_down": X_down, "G_mlp": G_mlp,
