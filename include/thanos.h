@@ -144,6 +144,47 @@ th_status th_prune_layer(void* W, th_dtype wdt, int64_t c, int64_t b, const void
 th_status th_prune_layer_workspace_size(int64_t c, int64_t b, int64_t n, int32_t have_x,
                                         const th_prune_params* p, size_t* bytes /* host */);
 
+/* Inverse factor of a damped Hessian, for layers that share one input (q/k/v,
+ * gate/up): H^-1 = U^T U with U upper [EXPL, "SparseGPT: Second-Order
+ * Reconstruction at Scale": one factorisation of the inverse Hessian per layer;
+ * here per shared input]. Exactly one of X ([n,b] token-major, dtype xdt: H =
+ * 2XX^T + lambda*I is built inside) / H ([b,b] fp32, full symmetric, already
+ * damped) is non-NULL; lambda and lambda_is_relative as in th_prune_params.
+ * U [b,b] fp32 (device, caller-owned): receives U, zero below the diagonal (with
+ * X it also serves as the Hessian's scratch). *lambda_out (host, optional): the
+ * absolute lambda, added (X given) or taken to be in a given H (lambda when
+ * absolute, lambda/(1+lambda) * mean(diag H) when relative). workspace: >=
+ * th_factor_workspace_size bytes, 256-byte aligned. Synchronises once.
+ * TH_ERR_NOT_SPD / TH_ERR_NONFINITE as th_prune_layer. */
+th_status th_factor(const void* X, th_dtype xdt, int64_t n, const float* H, int64_t b,
+                    double lambda, int32_t lambda_is_relative, float* U, double* lambda_out,
+                    void* workspace, size_t workspace_bytes, th_stream_t stream);
+th_status th_factor_workspace_size(int64_t b, int64_t n, int32_t have_x, size_t* bytes /* host */);
+
+/* th_prune_layer from a given factor U (th_factor's output; read only, copied
+ * into the workspace): the same block loop, so the result is identical to
+ * th_prune_layer on the H that U came from [BLOG, "Contribution one" and
+ * "Contribution two"]. p->score must be TH_SCORE_OBS (the Wanda score needs
+ * diag(H)); p->lambda is not used and stats_out->lambda_used is 0. Other
+ * arguments, synchronisation and errors as th_prune_layer. workspace: >=
+ * th_prune_layer_factored_workspace_size bytes. */
+th_status th_prune_layer_factored(void* W, th_dtype wdt, int64_t c, int64_t b, const float* U,
+                                  const th_prune_params* p, float* W_out_f32, uint8_t* mask_out,
+                                  void* workspace, size_t workspace_bytes, th_stats* stats_out,
+                                  int64_t* block_counts, th_stream_t stream);
+th_status th_prune_layer_factored_workspace_size(int64_t c, int64_t b, const th_prune_params* p,
+                                                 size_t* bytes /* host */);
+
+/* Input of down_proj from a gated feed-forward: Y = silu(X W_gate^T) * (X W_up^T)
+ * with silu(z) = z/(1+e^-z) [BLOG, "The compression target: linear layers":
+ * feed-forward projections joined by a nonlinearity; gate/up/down as in LLaMA].
+ * X [n,d] token-major, W_gate and W_up [f,d] row-major, Y [n,f]; all bf16 (dt
+ * must be TH_BF16), device, caller-owned. Products on the bf16 matrix cores with
+ * fp32 sums, silu and the product in fp32, Y rounded to nearest even. Needs
+ * d % 8 == 0 and 16-byte aligned X, W_gate, W_up. Asynchronous on the stream. */
+th_status th_gated_ffn_input(const void* X, const void* W_gate, const void* W_up, th_dtype dt,
+                             int64_t n, int64_t d, int64_t f, void* Y, th_stream_t stream);
+
 /* Comparator: the column-sequential schedule of SparseGPT on the same Hessian and
  * factor [BLOG, "The scaling problem, and what SparseGPT changes": left to right,
  * every row at once, finished columns frozen, compensation only into active

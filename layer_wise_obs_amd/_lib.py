@@ -53,6 +53,14 @@ _SIG = {
                        _P, _P, ctypes.c_size_t, ctypes.POINTER(Stats), ctypes.POINTER(_I64), _P],
     "th_prune_layer_workspace_size": [_I64, _I64, _I64, _I32, ctypes.POINTER(PruneParams),
                                       ctypes.POINTER(ctypes.c_size_t)],
+    "th_factor": [_P, _I32, _I64, _P, _I64, ctypes.c_double, _I32, _P,
+                  ctypes.POINTER(ctypes.c_double), _P, ctypes.c_size_t, _P],
+    "th_factor_workspace_size": [_I64, _I64, _I32, ctypes.POINTER(ctypes.c_size_t)],
+    "th_prune_layer_factored": [_P, _I32, _I64, _I64, _P, ctypes.POINTER(PruneParams), _P, _P, _P,
+                                ctypes.c_size_t, ctypes.POINTER(Stats), ctypes.POINTER(_I64), _P],
+    "th_prune_layer_factored_workspace_size": [_I64, _I64, ctypes.POINTER(PruneParams),
+                                               ctypes.POINTER(ctypes.c_size_t)],
+    "th_gated_ffn_input": [_P, _P, _P, _I32, _I64, _I64, _I64, _P, _P],
     "th_prune_sparsegpt": [_P, _I32, _I64, _I64, _P, _I32, _I64, _P, ctypes.POINTER(PruneParams),
                            _P, _P, _P, ctypes.c_size_t, ctypes.POINTER(Stats),
                            ctypes.POINTER(_I64), _P],
@@ -207,6 +215,61 @@ def prune_layer(W, X=None, H=None, params: PruneParams | None = None, W_out=None
     """Prune W (c x b, bf16/fp32) in place; returns stats and per-block counts."""
     return _layer_call(lib().th_prune_layer, lib().th_prune_layer_workspace_size, W, X, H,
                        params, W_out, mask_out, ws)
+
+
+def factor(X=None, H=None, lam=0.01, relative=True, U=None, ws=None):
+    """U (b x b fp32, upper) with H^-1 = U^T U from X [n, b] or a damped H; returns (U, lambda)."""
+    torch = _torch()
+    _require_cuda(X, H, U)
+    b = X.shape[1] if X is not None else H.shape[0]
+    dev = (X if X is not None else H).device
+    n = X.shape[0] if X is not None else 0
+    if U is None:
+        U = torch.empty((b, b), dtype=torch.float32, device=dev)
+    if ws is None:
+        out = ctypes.c_size_t(0)
+        _check(lib().th_factor_workspace_size(b, n, 1 if X is not None else 0, ctypes.byref(out)))
+        ws = workspace(out.value, dev)
+    lam_out = ctypes.c_double(0.0)
+    _check(lib().th_factor(_ptr(X), _dtype_code(X) if X is not None else 0, n, _ptr(H), b,
+                           float(lam), 1 if relative else 0, _ptr(U), ctypes.byref(lam_out),
+                           _ptr(ws), ws.numel(), _stream(dev)))
+    return U, lam_out.value
+
+
+def prune_layer_factored(W, U, params: PruneParams | None = None, W_out=None, mask_out=None,
+                         ws=None) -> dict:
+    """prune_layer from a factor U that layers sharing one input reuse."""
+    _require_cuda(W, U, W_out, mask_out)
+    if params is None:
+        params = make_params()
+    c, b = W.shape
+    if ws is None:
+        out = ctypes.c_size_t(0)
+        _check(lib().th_prune_layer_factored_workspace_size(c, b, ctypes.byref(params),
+                                                            ctypes.byref(out)))
+        ws = workspace(out.value, W.device)
+    stats = Stats()
+    counts = (_I64 * (-(-b // params.block)))()
+    _check(lib().th_prune_layer_factored(_ptr(W), _dtype_code(W), c, b, _ptr(U),
+                                         ctypes.byref(params), _ptr(W_out), _ptr(mask_out),
+                                         _ptr(ws), ws.numel(), ctypes.byref(stats), counts,
+                                         _stream(W.device)))
+    return {"lambda": stats.lambda_used, "pruned": stats.total_pruned, "nblocks": stats.nblocks,
+            "counts": list(counts)}
+
+
+def gated_ffn_input(X, W_gate, W_up, Y=None):
+    """Y = silu(X W_gate^T) * (X W_up^T) in bf16 for X [n, d], W [f, d] (bf16)."""
+    torch = _torch()
+    _require_cuda(X, W_gate, W_up, Y)
+    n, d = X.shape
+    f = W_gate.shape[0]
+    if Y is None:
+        Y = torch.empty((n, f), dtype=torch.bfloat16, device=X.device)
+    _check(lib().th_gated_ffn_input(_ptr(X), _ptr(W_gate), _ptr(W_up), _dtype_code(X), n, d, f,
+                                    _ptr(Y), _stream(X.device)))
+    return Y
 
 
 def prune_sparsegpt_workspace_size(c, b, n, have_x, params: PruneParams) -> int:

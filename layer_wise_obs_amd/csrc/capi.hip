@@ -100,9 +100,10 @@ bool needs_complement(const th_prune_params* p) {
 
 // sgpt: the column-sequential comparator's layout (U only, no slices; gW holds the
 // score weights 1/U_qq^2; E in Z with the super-block pitch for both patterns).
+// factor: false when U is given (no panel buffer).
 PruneLayout layout_prune(void* ws, int64_t c, int64_t b, int64_t n, bool have_x,
                          const th_prune_params* p, bool need_wf, bool need_mask, th_dtype xdt,
-                         bool sgpt = false) {
+                         bool sgpt = false, bool factor = true) {
   Carve cv(ws);
   PruneLayout L;
   const int64_t B = p->block;
@@ -111,7 +112,7 @@ PruneLayout layout_prune(void* ws, int64_t c, int64_t b, int64_t n, bool have_x,
   L.counts = cv.take<unsigned long long>(nblk);
   L.S = cv.take<float>((size_t)b * b);
   L.R = cv.take<float>((size_t)b * b);
-  L.P = cv.take<float>(chol_panel_floats(b));
+  L.P = factor ? cv.take<float>(chol_panel_floats(b)) : nullptr;
   L.Ublk = sgpt ? nullptr : cv.take<float>((size_t)nblk * B * B);
   L.Nblk = (!sgpt && needs_complement(p)) ? cv.take<float>((size_t)nblk * B * B) : nullptr;
   const bool unstr = p->pattern.kind == TH_UNSTRUCTURED;
@@ -232,6 +233,69 @@ th_status finish_layer(const PruneLayout& L, int64_t nblk, th_stats* stats_out,
   return TH_OK;
 }
 
+// Cleared device state (budget 0) and counts, W in fp32.
+th_status begin_layer(const PruneLayout& L, const void* W, th_dtype wdt, int64_t c, int64_t b,
+                      const th_prune_params* p, float* Wf, hipStream_t s) {
+  const int64_t nblk = cdiv(b, p->block);
+  TH_HIP(hipMemsetAsync(L.st, 0, sizeof(DevState), s), "memset state");
+  TH_HIP(hipMemsetAsync(L.counts, 0, nblk * sizeof(unsigned long long), s), "memset counts");
+  TH_HIP(launch_to_f32(W, wdt, c * b, Wf, L.st, s), "W to fp32");
+  return TH_OK;
+}
+
+// The per-block slices of U (in L.R) and the block loop: What in Wf, the mask,
+// per-block counts and the pruned total in the device state.
+th_status prune_blocks(const PruneLayout& L, int64_t c, int64_t b, const th_prune_params* p,
+                       float* Wf, uint8_t* mask, hipStream_t s) {
+  const int64_t B = p->block;
+  const int64_t nblk = cdiv(b, B);
+  const bool unstr = p->pattern.kind == TH_UNSTRUCTURED;
+  const bool obs = p->score == TH_SCORE_OBS;
+  TH_HIP(launch_save_diag_blocks(L.R, b, B, L.Ublk, s), "diag blocks");
+  // S is free once reversed into R: it holds the fp64 partial sums
+  if (L.D)
+    TH_HIP(launch_colnorm_downdate(L.R, b, B, L.D, (double*)L.S, (size_t)b * b / 2, s),
+           "column norms");
+  if (L.Nblk) TH_HIP(launch_block_inverses(L.Ublk, b, B, L.Nblk, s), "block inverses");
+  TH_HIP(launch_transform_rows(L.R, b, B, L.Ublk, s), "transform rows");
+
+  const int64_t ldz = z_pitch(b, p);
+  // the layer's budget k_total = round-half-even(p c b) joins at the first block
+  const long long k_total = unstr ? (long long)std::nearbyint(p->sparsity * (double)c * (double)b) : 0;
+  for (int64_t blk = 0; blk < nblk; ++blk) {
+    const int64_t j0 = blk * B;
+    const int64_t Bb = (b - j0) < B ? (b - j0) : B;
+    const float* Nb = L.Nblk ? L.Nblk + blk * B * B : nullptr;
+    if (unstr) {
+      // the global selection scores every active column, so W[:, F] is updated in full
+      const float* g = obs ? L.D + blk * b : L.gW;
+      TH_HIP(launch_select_init(L.st, blk == 0 ? k_total : 0, (long long)(c * (b - j0)), s),
+             "select init");
+      for (int pass = 0; pass < 6; ++pass) {
+        TH_HIP(launch_select_pass(Wf, c, b, j0, b, g, L.st, s), "select pass");
+        TH_HIP(launch_select_pick(L.st, s), "select pick");
+      }
+      TH_HIP(launch_solve_unstructured(Wf, c, b, j0, B, L.R, Nb, g, L.Z, mask, L.st,
+                                       L.counts + blk, s),
+             "solve");
+      TH_HIP(launch_update(Wf, c, b, j0, Bb, B, j0, b, L.Z, L.R, mask, j0, Bb, s), "update");
+    } else {
+      const int64_t per = ldz / B;  // blocks per super-block
+      const int64_t sb0 = (blk / per) * ldz;
+      const int64_t s1 = (sb0 + ldz) < b ? (sb0 + ldz) : b;
+      float* Zb = L.Z + (blk % per) * B;
+      TH_HIP(launch_solve_nm(Wf, c, b, j0, B, p->pattern.n, p->pattern.m, L.R, obs ? nullptr : L.gW,
+                             Nb, Zb, ldz, mask, L.st, L.counts + blk, s),
+             "solve");
+      TH_HIP(launch_update(Wf, c, b, j0, Bb, ldz, j0, s1, Zb, L.R, mask, j0, Bb, s), "update");
+      if (j0 + Bb == s1 && s1 < b)  // last block of the super-block: the deferred columns
+        TH_HIP(launch_update(Wf, c, b, sb0, s1 - sb0, ldz, s1, b, L.Z, L.R, mask, 0, 0, s),
+               "deferred update");
+    }
+  }
+  return TH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -311,62 +375,14 @@ th_status th_prune_layer(void* W, th_dtype wdt, int64_t c, int64_t b, const void
   const int64_t nblk = cdiv(b, B);
   float* Wf = W_out_f32 ? W_out_f32 : L.Wf;
   uint8_t* mask = mask_out ? mask_out : L.mask;
-  const bool unstr = p->pattern.kind == TH_UNSTRUCTURED;
-  const bool obs = p->score == TH_SCORE_OBS;
 
-  TH_HIP(hipMemsetAsync(L.st, 0, sizeof(DevState), s), "memset state");
-  TH_HIP(hipMemsetAsync(L.counts, 0, nblk * sizeof(unsigned long long), s), "memset counts");
-  long long k_total = 0;
-  if (unstr) {
-    k_total = (long long)std::nearbyint(p->sparsity * (double)c * (double)b);
-    TH_HIP(hipMemcpyAsync(&L.st->budget, &k_total, sizeof(k_total), hipMemcpyHostToDevice, s),
-           "budget");
-  }
-  TH_HIP(launch_to_f32(W, wdt, c * b, Wf, L.st, s), "W to fp32");
-
+  th_status st0 = begin_layer(L, W, wdt, c, b, p, Wf, s);
+  if (st0 != TH_OK) return st0;
   th_status pre = inverse_factor(X, xdt, n, H, b, p, L, s);
   if (pre != TH_OK) return pre;
 
-  // the per-block slices
-  TH_HIP(launch_save_diag_blocks(L.R, b, B, L.Ublk, s), "diag blocks");
-  // S is free once reversed into R: it holds the fp64 partial sums
-  if (L.D)
-    TH_HIP(launch_colnorm_downdate(L.R, b, B, L.D, (double*)L.S, (size_t)b * b / 2, s),
-           "column norms");
-  if (L.Nblk) TH_HIP(launch_block_inverses(L.Ublk, b, B, L.Nblk, s), "block inverses");
-  TH_HIP(launch_transform_rows(L.R, b, B, L.Ublk, s), "transform rows");
-
-  const int64_t ldz = z_pitch(b, p);
-  for (int64_t blk = 0; blk < nblk; ++blk) {
-    const int64_t j0 = blk * B;
-    const int64_t Bb = (b - j0) < B ? (b - j0) : B;
-    const float* Nb = L.Nblk ? L.Nblk + blk * B * B : nullptr;
-    if (unstr) {
-      // the global selection scores every active column, so W[:, F] is updated in full
-      const float* g = obs ? L.D + blk * b : L.gW;
-      TH_HIP(launch_select_init(L.st, 0, (long long)(c * (b - j0)), s), "select init");
-      for (int pass = 0; pass < 6; ++pass) {
-        TH_HIP(launch_select_pass(Wf, c, b, j0, b, g, L.st, s), "select pass");
-        TH_HIP(launch_select_pick(L.st, s), "select pick");
-      }
-      TH_HIP(launch_solve_unstructured(Wf, c, b, j0, B, L.R, Nb, g, L.Z, mask, L.st,
-                                       L.counts + blk, s),
-             "solve");
-      TH_HIP(launch_update(Wf, c, b, j0, Bb, B, j0, b, L.Z, L.R, mask, j0, Bb, s), "update");
-    } else {
-      const int64_t per = ldz / B;  // blocks per super-block
-      const int64_t sb0 = (blk / per) * ldz;
-      const int64_t s1 = (sb0 + ldz) < b ? (sb0 + ldz) : b;
-      float* Zb = L.Z + (blk % per) * B;
-      TH_HIP(launch_solve_nm(Wf, c, b, j0, B, p->pattern.n, p->pattern.m, L.R, obs ? nullptr : L.gW,
-                             Nb, Zb, ldz, mask, L.st, L.counts + blk, s),
-             "solve");
-      TH_HIP(launch_update(Wf, c, b, j0, Bb, ldz, j0, s1, Zb, L.R, mask, j0, Bb, s), "update");
-      if (j0 + Bb == s1 && s1 < b)  // last block of the super-block: the deferred columns
-        TH_HIP(launch_update(Wf, c, b, sb0, s1 - sb0, ldz, s1, b, L.Z, L.R, mask, 0, 0, s),
-               "deferred update");
-    }
-  }
+  th_status blocks = prune_blocks(L, c, b, p, Wf, mask, s);
+  if (blocks != TH_OK) return blocks;
   TH_HIP(launch_from_f32(Wf, c * b, wdt, W, s), "cast back");
   return finish_layer(L, nblk, stats_out, block_counts, s);
 }
@@ -400,9 +416,8 @@ th_status th_prune_sparsegpt(void* W, th_dtype wdt, int64_t c, int64_t b, const 
   uint8_t* mask = mask_out ? mask_out : L.mask;
   const bool unstr = p->pattern.kind == TH_UNSTRUCTURED;
 
-  TH_HIP(hipMemsetAsync(L.st, 0, sizeof(DevState), s), "memset state");
-  TH_HIP(hipMemsetAsync(L.counts, 0, nblk * sizeof(unsigned long long), s), "memset counts");
-  TH_HIP(launch_to_f32(W, wdt, c * b, Wf, L.st, s), "W to fp32");
+  th_status st0 = begin_layer(L, W, wdt, c, b, p, Wf, s);  // the budget grows block by block
+  if (st0 != TH_OK) return st0;
   th_status pre = inverse_factor(X, xdt, n, H, b, p, L, s);
   if (pre != TH_OK) return pre;
   TH_HIP(launch_sgpt_gdiag(L.R, b, L.gW, s), "score weights");
@@ -435,6 +450,131 @@ th_status th_prune_sparsegpt(void* W, th_dtype wdt, int64_t c, int64_t b, const 
   }
   TH_HIP(launch_from_f32(Wf, c * b, wdt, W, s), "cast back");
   return finish_layer(L, nblk, stats_out, block_counts, s);
+}
+
+// ----------------------------------------------------------- shared factor
+
+namespace {
+struct FactorLayout {
+  DevState* st;
+  float* S;
+  float* P;
+  float* syrk_part;
+  size_t bytes;
+};
+
+FactorLayout layout_factor(void* ws, int64_t b, int64_t n, bool have_x, th_dtype xdt) {
+  Carve cv(ws);
+  FactorLayout F;
+  F.st = cv.take<DevState>(1);
+  F.S = cv.take<float>((size_t)b * b);
+  F.P = cv.take<float>(chol_panel_floats(b));
+  F.syrk_part = nullptr;
+  if (have_x && xdt == TH_BF16) {
+    const int splits = syrk_bf16_splits(n, b);
+    if (splits > 1) {
+      const int64_t nt = cdiv(b, 256);
+      F.syrk_part = cv.take<float>((size_t)splits * (nt * (nt + 1) / 2) * 256 * 256);
+    }
+  }
+  F.bytes = cv.off;
+  return F;
+}
+}  // namespace
+
+th_status th_factor_workspace_size(int64_t b, int64_t n, int32_t have_x, size_t* bytes) {
+  if (!bytes || b < 1) return fail(TH_ERR_INVALID_ARG, "bad arguments");
+  *bytes = layout_factor(nullptr, b, n, have_x != 0, TH_BF16).bytes;
+  return TH_OK;
+}
+
+th_status th_factor(const void* X, th_dtype xdt, int64_t n, const float* H, int64_t b,
+                    double lambda, int32_t lambda_is_relative, float* U, double* lambda_out,
+                    void* workspace, size_t workspace_bytes, th_stream_t stream) {
+  if (!U || b < 1) return fail(TH_ERR_INVALID_ARG, "U is NULL or b < 1");
+  if ((X == nullptr) == (H == nullptr)) return fail(TH_ERR_INVALID_ARG, "pass exactly one of X, H");
+  if (X && (!dtype_ok(xdt) || n < 1)) return fail(TH_ERR_INVALID_ARG, "bad X");
+  if (X && xdt == TH_BF16 && (b % 8 || ((uintptr_t)X & 15)))
+    return fail(TH_ERR_INVALID_ARG, "bf16 X needs b % 8 == 0 and 16-byte alignment");
+  if (!(lambda >= 0.0) || !std::isfinite(lambda))
+    return fail(TH_ERR_INVALID_ARG, "lambda must be finite and >= 0");
+  if (!workspace || ((uintptr_t)workspace & 255))
+    return fail(TH_ERR_INVALID_ARG, "workspace must be non-NULL and 256-byte aligned");
+  FactorLayout F = layout_factor(workspace, b, n, X != nullptr, xdt);
+  if (workspace_bytes < F.bytes) return fail(TH_ERR_WORKSPACE, "workspace too small");
+  hipStream_t s = (hipStream_t)stream;
+  th_prune_params p{};
+  p.lambda = lambda;
+  p.lambda_is_relative = lambda_is_relative;
+  p.score = TH_SCORE_OBS;
+  PruneLayout L{};
+  L.st = F.st;
+  L.S = F.S;
+  L.R = U;  // H from X accumulates in U, which then receives the factor
+  L.P = F.P;
+  L.syrk_part = F.syrk_part;
+  TH_HIP(hipMemsetAsync(F.st, 0, sizeof(DevState), s), "memset state");
+  th_status pre = inverse_factor(X, xdt, n, H, b, &p, L, s);
+  if (pre != TH_OK) return pre;
+  DevState host;
+  TH_HIP(hipMemcpyAsync(&host, F.st, offsetof(DevState, hist), hipMemcpyDeviceToHost, s), "state");
+  TH_HIP(hipStreamSynchronize(s), "sync");
+  if (lambda_out) *lambda_out = host.lambda;
+  if (host.nonfinite) return fail(TH_ERR_NONFINITE, "non-finite value in diag(H)");
+  if (host.not_spd) return fail(TH_ERR_NOT_SPD, "damped Hessian is not positive definite");
+  return TH_OK;
+}
+
+th_status th_prune_layer_factored_workspace_size(int64_t c, int64_t b, const th_prune_params* p,
+                                                 size_t* bytes) {
+  if (!bytes) return fail(TH_ERR_INVALID_ARG, "bytes is NULL");
+  th_status st = check_params(c, b, p);
+  if (st != TH_OK) return st;
+  *bytes = layout_prune(nullptr, c, b, 0, false, p, true, true, TH_BF16, false, false).bytes;
+  return TH_OK;
+}
+
+th_status th_prune_layer_factored(void* W, th_dtype wdt, int64_t c, int64_t b, const float* U,
+                                  const th_prune_params* p, float* W_out_f32, uint8_t* mask_out,
+                                  void* workspace, size_t workspace_bytes, th_stats* stats_out,
+                                  int64_t* block_counts, th_stream_t stream) {
+  // U stands in for H in the shared checks (exactly one of X and H)
+  th_status chk = check_layer_args(W, wdt, c, b, nullptr, TH_BF16, 0, U, p, workspace);
+  if (chk != TH_OK) return chk;
+  if (p->score != TH_SCORE_OBS)
+    return fail(TH_ERR_INVALID_ARG, "a given factor takes the OBS score only");
+  PruneLayout L = layout_prune(workspace, c, b, 0, false, p, W_out_f32 == nullptr,
+                               mask_out == nullptr, TH_BF16, false, false);
+  if (workspace_bytes < L.bytes) return fail(TH_ERR_WORKSPACE, "workspace too small");
+  hipStream_t s = (hipStream_t)stream;
+  float* Wf = W_out_f32 ? W_out_f32 : L.Wf;
+  uint8_t* mask = mask_out ? mask_out : L.mask;
+  th_status st0 = begin_layer(L, W, wdt, c, b, p, Wf, s);
+  if (st0 != TH_OK) return st0;
+  // the slices are formed in place, so the caller's factor is copied first
+  TH_HIP(hipMemcpyAsync(L.R, U, (size_t)b * b * sizeof(float), hipMemcpyDeviceToDevice, s), "U");
+  th_status blocks = prune_blocks(L, c, b, p, Wf, mask, s);
+  if (blocks != TH_OK) return blocks;
+  TH_HIP(launch_from_f32(Wf, c * b, wdt, W, s), "cast back");
+  return finish_layer(L, cdiv(b, p->block), stats_out, block_counts, s);
+}
+
+// ------------------------------------------------------ gated feed-forward
+
+th_status th_gated_ffn_input(const void* X, const void* W_gate, const void* W_up, th_dtype dt,
+                             int64_t n, int64_t d, int64_t f, void* Y, th_stream_t stream) {
+  if (!X || !W_gate || !W_up || !Y) return fail(TH_ERR_INVALID_ARG, "NULL argument");
+  if (dt != TH_BF16) return fail(TH_ERR_INVALID_ARG, "bf16 only");
+  if (n < 1 || d < 8 || f < 1 || d % 8) return fail(TH_ERR_INVALID_ARG, "needs n, f >= 1, d % 8 == 0");
+  if (cdiv(n, 256) * cdiv(f, 128) >= ((int64_t)1 << 30))
+    return fail(TH_ERR_INVALID_ARG, "n * f too large for one launch");
+  if (((uintptr_t)X | (uintptr_t)W_gate | (uintptr_t)W_up) & 15)
+    return fail(TH_ERR_INVALID_ARG, "X, W_gate and W_up must be 16-byte aligned");
+  TH_HIP(launch_gated_ffn((const unsigned short*)X, (const unsigned short*)W_gate,
+                          (const unsigned short*)W_up, (unsigned short*)Y, n, d, f,
+                          (hipStream_t)stream),
+         "gated ffn");
+  return TH_OK;
 }
 
 th_status th_reconstruction_error_workspace_size(int64_t c, int64_t b, int32_t have_x,
@@ -515,9 +655,7 @@ th_status th_debug_select_global(const float* scores, int64_t c, int64_t f, int6
   hipStream_t s = (hipStream_t)stream;
   DevState* st = (DevState*)workspace;
   TH_HIP(hipMemsetAsync(st, 0, sizeof(DevState), s), "memset");
-  long long budget = r;
-  TH_HIP(hipMemcpyAsync(&st->budget, &budget, sizeof(budget), hipMemcpyHostToDevice, s), "budget");
-  TH_HIP(launch_select_init(st, 0, (long long)(c * f), s), "init");
+  TH_HIP(launch_select_init(st, (long long)r, (long long)(c * f), s), "init");  // budget = r
   for (int pass = 0; pass < 6; ++pass) {
     TH_HIP(launch_select_scores_pass(scores, c, f, b_full, j0, st, s), "pass");
     TH_HIP(launch_select_pick(st, s), "pick");

@@ -177,6 +177,11 @@ hipError_t launch_sgpt_errors(const float* W, int64_t c, int64_t b, int64_t j0, 
                               int64_t lde, uint8_t* mask, DevState* st,
                               unsigned long long* blk_count, hipStream_t s);
 
+// ffn.hip
+hipError_t launch_gated_ffn(const unsigned short* X, const unsigned short* Wg,
+                            const unsigned short* Wu, unsigned short* Y, int64_t n, int64_t d,
+                            int64_t f, hipStream_t s);
+
 // update.hip
 // W[:, col0:col_end) -= Z[:, 0:K] R[r0:r0+K, col0:col_end) (Z pitch ldz); entries of
 // columns [mask_j0, mask_j0 + mask_w) with mask set are then zeroed.

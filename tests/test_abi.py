@@ -22,7 +22,9 @@ def test_header_declares_the_path():
                  "th_prune_layer_workspace_size", "th_reconstruction_error", "th_debug_select_nm",
                  "th_debug_select_global", "th_debug_factor", "th_last_error",
                  "th_column_sq_norms", "th_column_sq_norms_workspace_size", "th_prune_baseline",
-                 "th_prune_sparsegpt", "th_prune_sparsegpt_workspace_size"):
+                 "th_prune_sparsegpt", "th_prune_sparsegpt_workspace_size", "th_factor",
+                 "th_factor_workspace_size", "th_prune_layer_factored",
+                 "th_prune_layer_factored_workspace_size", "th_gated_ffn_input"):
         assert must in names
 
 
@@ -141,3 +143,39 @@ def test_sparsegpt_arguments_are_rejected_before_any_launch():
     args[7] = None
     args[11] = ctypes.c_void_p(0x1010)  # workspace not 256-byte aligned
     assert L.th_prune_sparsegpt(*args) == 1
+
+
+def test_factor_and_ffn_arguments_are_rejected_before_any_launch():
+    L = _lib.lib()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its checks first
+    ws = ctypes.c_void_p(0x1000)
+    lam = ctypes.c_double(0.0)
+    # th_factor: both / neither of X and H, negative lambda, misaligned workspace
+    assert L.th_factor(fake, _lib.TH_BF16, 8, fake, 8, 0.01, 1, fake, ctypes.byref(lam), ws,
+                       1 << 30, None) == 1
+    assert L.th_factor(None, _lib.TH_BF16, 8, None, 8, 0.01, 1, fake, ctypes.byref(lam), ws,
+                       1 << 30, None) == 1
+    assert L.th_factor(None, _lib.TH_BF16, 0, fake, 8, -1.0, 1, fake, ctypes.byref(lam), ws,
+                       1 << 30, None) == 1
+    assert L.th_factor(None, _lib.TH_BF16, 0, fake, 8, 0.01, 1, fake, ctypes.byref(lam),
+                       ctypes.c_void_p(0x1010), 1 << 30, None) == 1
+    out = ctypes.c_size_t(0)
+    assert L.th_factor(None, _lib.TH_BF16, 0, fake, 8, 0.01, 1, fake, ctypes.byref(lam), ws, 0,
+                       None) == 4  # TH_ERR_WORKSPACE
+    assert L.th_factor_workspace_size(11008, 262144, 1, ctypes.byref(out)) == 0
+    assert out.value >= 11008 * 11008 * 4
+    # factored prune: Wanda score rejected; workspace query smaller than the full layer's
+    p = _lib.make_params(pattern=(2, 4))
+    full = ctypes.c_size_t(0)
+    assert L.th_prune_layer_factored_workspace_size(4096, 11008, ctypes.byref(p), ctypes.byref(out)) == 0
+    L.th_prune_layer_workspace_size(4096, 11008, 0, 0, ctypes.byref(p), ctypes.byref(full))
+    assert out.value < full.value
+    wanda = _lib.make_params(score="wanda")
+    assert L.th_prune_layer_factored(fake, _lib.TH_BF16, 8, 8, fake, ctypes.byref(wanda), None,
+                                     None, ws, 1 << 30, None, None, None) == 1
+    assert "OBS" in L.th_last_error().decode()
+    # gated ffn: fp32, d % 8, misaligned
+    assert L.th_gated_ffn_input(fake, fake, fake, _lib.TH_F32, 4, 8, 4, fake, None) == 1
+    assert L.th_gated_ffn_input(fake, fake, fake, _lib.TH_BF16, 4, 12, 4, fake, None) == 1
+    assert L.th_gated_ffn_input(ctypes.c_void_p(0x1002), fake, fake, _lib.TH_BF16, 4, 8, 4, fake,
+                                None) == 1
