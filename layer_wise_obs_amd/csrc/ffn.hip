@@ -14,13 +14,17 @@
 // accumulators in AGPRs), so the epilogue has g and u of every output at hand.
 // The contraction dimension d is contiguous in both operands, so an MFMA operand
 // (8 consecutive k of one row per lane) is one 16-byte LDS read. K stages of 32
-// (64-byte rows, 32 KB per stage) are double-buffered and filled through
-// registers; the 16-byte pieces of a row are XOR-swizzled by (row / 4) & 3 so
-// that the operand reads (16 rows at one piece per 16 lanes) and the fills (4
-// rows x 4 pieces) use all 64 banks. Tiles are walked in groups of 8 token tiles
-// per feature-tile column, and each XCD takes a contiguous range of that order,
-// so the 32 workgroups an XCD runs at once share their X and W slices in its L2.
+// (64-byte rows: X 16 KB, W_gate and W_up 8 KB each) are filled by direct
+// global->LDS loads, four stages deep with the loads three stages ahead, and the
+// operand fragments are double-buffered across the two 16-wide substeps of a
+// stage. The 16-byte pieces of a row are XOR-swizzled by (row / 4) & 3, so the
+// operand reads (16 rows at one piece per 16 lanes) use all 64 banks; a load lane
+// fetches whichever piece its fixed LDS slot holds. Tiles are walked in groups
+// of 8 token tiles per feature-tile column, and each XCD takes a contiguous range
+// of that order, so the 32 workgroups an XCD runs at once share their X and W
+// slices in its L2.
 #include "common.h"
+#include "lds_dma.h"
 
 namespace th {
 
@@ -30,6 +34,7 @@ constexpr int kFM = 256;     // tokens per tile
 constexpr int kFN = 128;     // features per tile
 constexpr int kFK = 32;      // contraction per stage
 constexpr int kFThreads = 256;
+constexpr int kFStages = 4;
 constexpr int kFGroup = 8;   // token tiles per group in the walk order
 constexpr int kRow = kFK * 2;                 // bytes per staged row
 constexpr int kABytes = kFM * kRow;           // 16 KB
@@ -64,58 +69,62 @@ __global__ __launch_bounds__(kFThreads) void gated_ffn_kernel(
   ffn_tile(lin, ntm, ntn, tm, tn);
   const int64_t M0 = (int64_t)tm * kFM, N0 = (int64_t)tn * kFN;
 
-  __shared__ __attribute__((aligned(1024))) unsigned char sm[2][kStage];
+  __shared__ __attribute__((aligned(1024))) unsigned char sm0[kStage];
+  __shared__ __attribute__((aligned(1024))) unsigned char sm1[kStage];
+  __shared__ __attribute__((aligned(1024))) unsigned char sm2[kStage];
+  __shared__ __attribute__((aligned(1024))) unsigned char sm3[kStage];
+  auto buf = [&](auto S) -> unsigned char* {
+    constexpr int s = decltype(S)::value;
+    if constexpr (s == 0) return sm0;
+    else if constexpr (s == 1) return sm1;
+    else if constexpr (s == 2) return sm2;
+    else return sm3;
+  };
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;  // wave tile: tokens wm*128.., features wn*64..
 
-  // Fill assignment: thread tid moves piece (tid & 3) of rows (tid >> 2) + 64 i:
-  // A rows i = 0..3, gate rows i = 0..1, up rows i = 0..1.
-  const int prow = tid >> 2, piece = tid & 3;
-  const unsigned short* srcA[4];
-  const unsigned short* srcG[2];
-  const unsigned short* srcU[2];
+  // Loader: a stage is 32 chunks of 1 KB (16 rows of 64 bytes): X chunks 0..15,
+  // W_gate 16..23, W_up 24..31. Wave w loads X chunks w + 4m (m = 0..3) and gate
+  // and up chunks w + 4m (m = 0, 1); with lds_dma_stage's slots (lds + 4096 i in
+  // the order 0, 4, 1, 5, 2, 6, 3, 7 for i = 0..7) from base = stage + 1024 w, the
+  // sources are ordered X0, G0, X1, G1, X2, U0, X3, U1. Lane l fills row
+  // 16 chunk + l/4 at physical piece l%4, i.e. logical piece lp below.
+  const int lrow = lane >> 2;
+  const int64_t nk = cdiv(d, kFK);
+  const unsigned short* src[8];
+  int lp[8];
+  {
+    const int chunk[8] = {wave, 16 + wave, wave + 4, 16 + wave + 4, wave + 8, 24 + wave,
+                          wave + 12, 24 + wave + 4};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int64_t r = M0 + prow + 64 * i;
-    r = r < n ? r : n - 1;
-    srcA[i] = X + r * d + piece * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    int64_t r = N0 + prow + 64 * i;
-    r = r < f ? r : f - 1;
-    srcG[i] = Wg + r * d + piece * 8;
-    srcU[i] = Wu + r * d + piece * 8;
-  }
-  u32x4_t rA[4], rG[2], rU[2];
-  const int nk = (int)cdiv(d, kFK);
-  auto load = [&](int ks) {
-    const int64_t k0 = (int64_t)ks * kFK;
-    const bool in = k0 + piece * 8 < d;  // d % 8 == 0: a piece is wholly in or out
-    const int64_t off = in ? k0 : 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      rA[i] = *(const u32x4_t*)(srcA[i] + off);
-      if (!in) rA[i] = u32x4_t{0u, 0u, 0u, 0u};
+    for (int i = 0; i < 8; ++i) {
+      const int c = chunk[i];
+      const int mat = c < 16 ? 0 : (c < 24 ? 1 : 2);
+      const int row = (c - (mat == 0 ? 0 : (mat == 1 ? 16 : 24))) * 16 + lrow;
+      lp[i] = (lane & 3) ^ ((row >> 2) & 3);
+      int64_t r = (mat == 0 ? M0 : N0) + row;
+      const int64_t lim = mat == 0 ? n : f;
+      r = r < lim ? r : lim - 1;  // rows past the end feed outputs that are never stored
+      const unsigned short* base = mat == 0 ? X : (mat == 1 ? Wg : Wu);
+      src[i] = base + r * d + lp[i] * 8;
     }
+  }
+  auto issue_stage = [&](int64_t st, unsigned char* sbase) {
+    const int64_t k0 = st * kFK;
+    const void* g[8];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      rG[i] = *(const u32x4_t*)(srcG[i] + off);
-      rU[i] = *(const u32x4_t*)(srcU[i] + off);
-      if (!in) {
-        rG[i] = u32x4_t{0u, 0u, 0u, 0u};
-        rU[i] = u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
+    for (int i = 0; i < 8; ++i) g[i] = src[i] + ((k0 + lp[i] * 8 < d) ? k0 : 0);
+    lds_dma_stage(g, sbase + wave * 1024);
   };
-  auto store = [&](unsigned char* st) {
+  // zero this wave's pieces of stage st that lie past d (its own loads have landed)
+  auto zero_tail = [&](int64_t st, unsigned char* sbase) {
+    const int64_t k0 = st * kFK;
+    if (k0 + kFK <= d) return;
+    constexpr int slot[8] = {0, 4, 1, 5, 2, 6, 3, 7};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *(u32x4_t*)(st + sw_off(prow + 64 * i, piece)) = rA[i];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *(u32x4_t*)(st + kABytes + sw_off(prow + 64 * i, piece)) = rG[i];
-      *(u32x4_t*)(st + kABytes + kBBytes + sw_off(prow + 64 * i, piece)) = rU[i];
-    }
+    for (int i = 0; i < 8; ++i)
+      if (k0 + lp[i] * 8 >= d)
+        *(u32x4_t*)(sbase + wave * 1024 + slot[i] * 4096 + lane * 16) = u32x4_t{0u, 0u, 0u, 0u};
   };
 
   f32x16_t accG[4][2], accU[4][2];
@@ -128,39 +137,57 @@ __global__ __launch_bounds__(kFThreads) void gated_ffn_kernel(
         accG[i][j][e] = 0.f;
         accU[i][j][e] = 0.f;
       }
-
-  load(0);
-  store(sm[0]);
-  __syncthreads();
   const int r32 = lane & 31, half = lane >> 5;
-  for (int ks = 0; ks < nk; ++ks) {
-    const unsigned char* cur = sm[ks & 1];
-    if (ks + 1 < nk) load(ks + 1);
+  bf16x8_t a0[4], g0[2], u0[2], a1[4], g1[2], u1[2];
+  auto read_frags = [&](const unsigned char* st, int sub, bf16x8_t (&a)[4], bf16x8_t (&g)[2],
+                        bf16x8_t (&u)[2]) {
+    const int pc = sub * 2 + half;  // piece of this lane's 8 k values
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int pc = sub * 2 + half;  // piece of this lane's 8 k values
-      bf16x8_t a[4], g[2], u[2];
+    for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8_t*)(st + sw_off(wm * 128 + i * 32 + r32, pc));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *(const bf16x8_t*)(cur + sw_off(wm * 128 + i * 32 + r32, pc));
+    for (int j = 0; j < 2; ++j) {
+      g[j] = *(const bf16x8_t*)(st + kABytes + sw_off(wn * 64 + j * 32 + r32, pc));
+      u[j] = *(const bf16x8_t*)(st + kABytes + kBBytes + sw_off(wn * 64 + j * 32 + r32, pc));
+    }
+  };
+  auto mfmas = [&](const bf16x8_t (&a)[4], const bf16x8_t (&g)[2], const bf16x8_t (&u)[2]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        g[j] = *(const bf16x8_t*)(cur + kABytes + sw_off(wn * 64 + j * 32 + r32, pc));
-        u[j] = *(const bf16x8_t*)(cur + kABytes + kBBytes + sw_off(wn * 64 + j * 32 + r32, pc));
+        accG[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], g[j], accG[i][j], 0, 0, 0);
+        accU[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], u[j], accU[i][j], 0, 0, 0);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          accG[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], g[j], accG[i][j], 0, 0, 0);
-          accU[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], u[j], accU[i][j], 0, 0, 0);
-        }
-    }
-    if (ks + 1 < nk) {
-      store(sm[(ks + 1) & 1]);  // the other buffer: its last reads ended at the barrier below
-    }
-    __syncthreads();
+  };
+
+  // prologue: stages 0, 1, 2 in flight; wait for stage 0
+  issue_stage(0, sm0);
+  issue_stage(1, sm1);
+  issue_stage(2, sm2);
+  __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  zero_tail(0, sm0);
+  __syncthreads();
+  read_frags(sm0, 0, a0, g0, u0);
+  for (int64_t it0 = 0; it0 < nk; it0 += kFStages) {
+    static_for<0, kFStages>([&](auto U) __attribute__((always_inline)) {
+      constexpr int uu = U;
+      const int64_t it = it0 + uu;
+      if (it < nk) {
+        // buffer (uu+3)%4 was last read before the barrier of iteration it-1
+        issue_stage(it + 3, buf(std::integral_constant<int, (uu + 3) % kFStages>{}));
+        read_frags(buf(std::integral_constant<int, uu>{}), 1, a1, g1, u1);
+        mfmas(a0, g0, u0);
+        // stage it+1 complete for this wave (stages it+2, it+3 may still be in flight)
+        __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        unsigned char* nb = buf(std::integral_constant<int, (uu + 1) % kFStages>{});
+        zero_tail(it + 1, nb);
+        __syncthreads();
+        read_frags(nb, 0, a0, g0, u0);
+        mfmas(a1, g1, u1);
+      }
+    });
   }
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // Epilogue: lane holds feature column r32 of each 32 x 32 block and rows
   // 8 (e / 4) + 4 half + (e % 4).

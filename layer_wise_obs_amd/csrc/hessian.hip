@@ -18,6 +18,7 @@
 // across the 16-token substeps, so the reads for the next substep overlap the
 // current substep's 16 MFMAs.
 #include "common.h"
+#include "lds_dma.h"
 
 namespace th {
 
@@ -65,35 +66,6 @@ constexpr int kStageBytes = 2 * kPanelBytes;          // A and B panels
 // 512 bytes, pieces XOR-swizzled by (t & 3) so that the transposing operand reads
 // of 8 tokens x 32 features spread over all banks.
 __device__ __forceinline__ int piece_off(int t, int fg) { return t * kRowBytes + ((fg ^ ((t & 3) << 2)) << 4); }
-
-// One stage's share of a wave: eight loads of 16 bytes per lane from global
-// memory straight into LDS (global_load_lds_dwordx4; lane l writes LDS bytes
-// [M0 + 16 l, M0 + 16 l + 16)). The LDS destinations are lds + the offsets
-// below (m = 0..3 four KB apart, the B panel 16 KB after the A panel). Written as
-// one asm block so that the compiler does not make LDS reads of other buffers
-// wait for these loads -- completion is tracked by the explicit vmcnt waits
-// before each barrier -- and so that M0 is restored before the compiler sees it
-// again. The loads have no result registers.
-__device__ __forceinline__ void lds_dma_stage(const void* const (&g)[8], const void* lds) {
-  const unsigned base = __builtin_amdgcn_readfirstlane(
-      (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)lds);
-  unsigned saved;
-  __asm__ volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %9, off\n\t"
-      "s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %10, off\n\t"
-      "s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %11, off\n\t"
-      "s_mov_b32 m0, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %12, off\n\t"
-      "s_mov_b32 m0, %5\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %13, off\n\t"
-      "s_mov_b32 m0, %6\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %14, off\n\t"
-      "s_mov_b32 m0, %7\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %15, off\n\t"
-      "s_mov_b32 m0, %8\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %16, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(base), "s"(base + 16384u), "s"(base + 4096u), "s"(base + 20480u),
-        "s"(base + 8192u), "s"(base + 24576u), "s"(base + 12288u), "s"(base + 28672u),
-        "v"(g[0]), "v"(g[1]), "v"(g[2]), "v"(g[3]), "v"(g[4]), "v"(g[5]), "v"(g[6]), "v"(g[7]));
-}
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
