@@ -46,7 +46,7 @@ __all__ = [
     "select_unstructured", "select_nm", "solve_rows", "schur_downdate",
     "prune_layer", "reconstruction_error", "column_sq_norms", "baseline_keys", "prune_baseline",
     "trailing_inverse_rows", "sparsegpt_column", "prune_sparsegpt", "silu", "gated_ffn_input",
-    "prune_mlp_sequential",
+    "prune_mlp_sequential", "outlier_rows", "prune_layer_alpha",
 ]
 
 
@@ -477,4 +477,52 @@ def prune_mlp_sequential(X_mlp, W_gate, W_up, W_down, sparsity: float = 0.5, pat
     down = prune_layer(W_down, G_down, sparsity=sparsity, pattern=pattern, block=block, lam=lam)
     return {"gate": gate, "up": up, "down": down, "X_down": X_down, "G_mlp": G_mlp,
             "G_down": G_down}
+
+
+def outlier_rows(W, gdiag, alpha: float) -> np.ndarray:
+    """Rows kept dense by the alpha variant (True = dense).
+
+    "Pruning LLMs with Thanos", section "What the experiments show": the alpha = 0.1
+    variant keeps 10% of the rows as outliers (50% sparsity becomes 45%). Which rows
+    is not stated; read here as the rows with the largest output energy
+    s_k = sum_q W_kq^2 G_qq (the diagonal part of ||W_k X||^2, the error of deleting
+    the whole row with every column independent), round-half-even(alpha * c) of
+    them. s_k is summed in fp64 from G_qq given in fp32 and ranked by its fp32
+    value, ties to the higher row index (rows ordered by (s_k, k); the last ones
+    stay dense).
+    """
+    W0 = _f64(W)
+    c = W0.shape[0]
+    g = np.asarray(gdiag, dtype=np.float32).astype(np.float64)
+    s32 = ((W0 * W0) @ g).astype(np.float32)
+    r = int(np.round(np.float64(alpha) * c))
+    order = np.lexsort((np.arange(c), s32))
+    dense = np.zeros(c, dtype=bool)
+    if r > 0:
+        dense[order[c - r:]] = True
+    return dense
+
+
+def prune_layer_alpha(W, G: np.ndarray, alpha: float, gdiag=None, **kw) -> dict:
+    """The layer step on the rows that are not kept dense (outlier_rows), which form
+    a layer of their own: its budget, blocks and solves see only those rows (rows
+    are independent given H, "The layer-reconstruction lens"). Dense rows are
+    returned unchanged with an all-zero mask. gdiag defaults to diag(G) in fp32."""
+    W0 = _f64(W)
+    c, b = W0.shape
+    if gdiag is None:
+        gdiag = np.diag(np.asarray(G, dtype=np.float64)).astype(np.float32)
+    dense = outlier_rows(W, gdiag, alpha)
+    W_hat = W0.copy()
+    mask = np.zeros((c, b), dtype=bool)
+    rest = np.flatnonzero(~dense)
+    out = {"dense": dense, "counts": [], "pruned": 0, "lam": damping(np.asarray(G), kw.get("lam", 0.01),
+                                                                   kw.get("lam_relative", True))}
+    if len(rest):
+        sub = prune_layer(W0[rest], G, **kw)
+        W_hat[rest] = sub["W_hat"]
+        mask[rest] = sub["mask"]
+        out.update({k: sub[k] for k in ("counts", "pruned", "lam", "k_total")})
+    out.update({"W_hat": W_hat, "mask": mask})
+    return out
 

@@ -725,6 +725,41 @@ def test_p25_sequential_mlp_block():
     assert sp["down"]["pruned"] == O.k_total(0.5, 16, 24)
 
 
+# ---------------------------------------------------- alpha outlier rows (P26)
+
+def test_p26_alpha_outlier_rows():
+    """Hand example (energies 1, 36, 20, 1.25 -> the two largest rows stay dense;
+    equal energies -> the higher row index); with orthogonal input features the
+    energy is ||W_k X||^2 computed from X; alpha = 0 is the plain layer step,
+    alpha = 1 prunes nothing; the other rows are pruned as a layer of their own
+    (2:4 at alpha = 0.1 leaves 45% zeros)."""
+    W = np.array([[1.0, 0.0], [0.0, 3.0], [2.0, 2.0], [0.5, 0.5]])
+    np.testing.assert_array_equal(O.outlier_rows(W, [1.0, 4.0], 0.5), [False, True, True, False])
+    Wt = np.array([[1.0, 0.0], [1.0, 0.0], [0.0, 0.5]])
+    np.testing.assert_array_equal(O.outlier_rows(Wt, [1.0, 4.0], 1.0 / 3.0), [False, False, True])
+    rng = np.random.default_rng(RNG_SEED + 27)
+    Q, _ = np.linalg.qr(rng.standard_normal((200, 12)))
+    X = Q * rng.uniform(0.5, 5.0, 12)[None, :]  # orthogonal columns: G is diagonal
+    Wr = rng.standard_normal((30, 12))
+    energy = np.sum((Wr @ X.T) ** 2, axis=1)
+    dense = O.outlier_rows(Wr, np.diag(X.T @ X), 0.2)
+    np.testing.assert_array_equal(np.flatnonzero(dense), np.sort(np.argsort(energy)[-6:]))
+    W2, X2 = _problem(40, 16, 200, RNG_SEED + 28)
+    G = O.gram(X2)
+    base = O.prune_layer(W2, G, pattern=(2, 4), block=8)
+    a0 = O.prune_layer_alpha(W2, G, 0.0, pattern=(2, 4), block=8)
+    np.testing.assert_array_equal(a0["W_hat"], base["W_hat"])
+    a1 = O.prune_layer_alpha(W2, G, 1.0, pattern=(2, 4), block=8)
+    assert not a1["mask"].any() and np.array_equal(a1["W_hat"], W2)
+    a = O.prune_layer_alpha(W2, G, 0.1, pattern=(2, 4), block=8)
+    assert a["dense"].sum() == 4 and a["mask"].sum() == 36 * 8
+    assert a["mask"].mean() == pytest.approx(0.45)
+    rest = np.flatnonzero(~a["dense"])
+    sub = O.prune_layer(W2[rest], G, pattern=(2, 4), block=8)
+    np.testing.assert_array_equal(a["W_hat"][rest], sub["W_hat"])
+    np.testing.assert_array_equal(a["W_hat"][a["dense"]], W2[a["dense"]])
+
+
 # ------------------------------------------------------- planted mistakes
 
 def _pins_pass():
@@ -745,6 +780,7 @@ def _pins_pass():
         test_p22_sparsegpt_diagonal_gram_is_blockwise_threshold()
         test_p23_sparsegpt_per_block_quota_and_limits(0.3, [12, 12, 6])
         test_p24_silu_and_gated_ffn_input()
+        test_p26_alpha_outlier_rows()
     except AssertionError:
         return False
     return True
@@ -774,7 +810,7 @@ def _bad_keys_abs_times_g(W, gdiag=None):
 @pytest.mark.parametrize("mutation", ["downdate", "sign", "nm_ties", "score_diag_H",
                                       "baseline_power", "baseline_layer_budget",
                                       "sgpt_full_inverse", "sgpt_sign", "sgpt_row_quota",
-                                      "silu_mirrored"])
+                                      "silu_mirrored", "alpha_smallest_rows"])
 def test_planted_mistakes_are_caught(monkeypatch, mutation):
     assert _pins_pass()
     T = O.thanos_oracle
@@ -828,6 +864,15 @@ def test_planted_mistakes_are_caught(monkeypatch, mutation):
             return np.concatenate([orig_sel(S_F[k:k + 1], int(np.round(r / c)), blk)
                                    for k in range(c)])
         monkeypatch.setattr(T, "select_unstructured", per_row)
+    elif mutation == "alpha_smallest_rows":
+        orig_rows = T.outlier_rows
+
+        def smallest(W, gdiag, alpha):
+            W0 = T._f64(W)
+            g = np.asarray(gdiag, dtype=np.float32).astype(np.float64)
+            return orig_rows(-W0, g, 0.0) if alpha == 0 else ~orig_rows(W0, g, 1.0 - alpha)
+        monkeypatch.setattr(T, "outlier_rows", smallest)
+        monkeypatch.setattr(O, "outlier_rows", smallest)
     elif mutation == "silu_mirrored":
         # z * sigmoid(-z): the same odd part, the wrong function
         monkeypatch.setattr(T, "silu", lambda z: np.asarray(z, np.float64)
