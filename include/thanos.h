@@ -175,6 +175,27 @@ th_status th_prune_layer_factored(void* W, th_dtype wdt, int64_t c, int64_t b, c
 th_status th_prune_layer_factored_workspace_size(int64_t c, int64_t b, const th_prune_params* p,
                                                  size_t* bytes /* host */);
 
+/* The alpha variant: round-half-even(alpha*c) rows of W stay dense, the other
+ * rows are pruned as a layer of their own [BLOG, "What the experiments show":
+ * the alpha = 0.1 variant keeps 10% of the rows as outliers, so 50% becomes 45%].
+ * Which rows is not on the pages; here the rows of largest output energy
+ * s_k = sum_q W_kq^2 G_qq (fp64 sums, ranked by their fp32 value, ties to the
+ * higher row index), with G_qq from X's column norms (th_column_sq_norms) or
+ * from a given damped H as (H_qq - lambda)/2. Arguments as th_prune_layer, plus
+ * alpha in [0, 1] and dense_rows_out [c] uint8 (device, optional): 1 = kept
+ * dense. Dense rows are left unchanged (mask 0); block_counts and stats count
+ * the pruned rows only. workspace: >= th_prune_layer_alpha_workspace_size
+ * bytes. Synchronisation and errors as th_prune_layer (a non-finite weight in
+ * any row gives TH_ERR_NONFINITE). */
+th_status th_prune_layer_alpha(void* W, th_dtype wdt, int64_t c, int64_t b, const void* X,
+                               th_dtype xdt, int64_t n, const float* H, const th_prune_params* p,
+                               double alpha, float* W_out_f32, uint8_t* mask_out,
+                               uint8_t* dense_rows_out, void* workspace, size_t workspace_bytes,
+                               th_stats* stats_out, int64_t* block_counts, th_stream_t stream);
+th_status th_prune_layer_alpha_workspace_size(int64_t c, int64_t b, int64_t n, int32_t have_x,
+                                              const th_prune_params* p, double alpha,
+                                              size_t* bytes /* host */);
+
 /* Input of down_proj from a gated feed-forward: Y = silu(X W_gate^T) * (X W_up^T)
  * with silu(z) = z/(1+e^-z) [BLOG, "The compression target: linear layers":
  * feed-forward projections joined by a nonlinearity; gate/up/down as in LLaMA].

@@ -60,6 +60,11 @@ _SIG = {
                                 ctypes.c_size_t, ctypes.POINTER(Stats), ctypes.POINTER(_I64), _P],
     "th_prune_layer_factored_workspace_size": [_I64, _I64, ctypes.POINTER(PruneParams),
                                                ctypes.POINTER(ctypes.c_size_t)],
+    "th_prune_layer_alpha": [_P, _I32, _I64, _I64, _P, _I32, _I64, _P, ctypes.POINTER(PruneParams),
+                             ctypes.c_double, _P, _P, _P, _P, ctypes.c_size_t, ctypes.POINTER(Stats),
+                             ctypes.POINTER(_I64), _P],
+    "th_prune_layer_alpha_workspace_size": [_I64, _I64, _I64, _I32, ctypes.POINTER(PruneParams),
+                                            ctypes.c_double, ctypes.POINTER(ctypes.c_size_t)],
     "th_gated_ffn_input": [_P, _P, _P, _I32, _I64, _I64, _I64, _P, _P],
     "th_prune_sparsegpt": [_P, _I32, _I64, _I64, _P, _I32, _I64, _P, ctypes.POINTER(PruneParams),
                            _P, _P, _P, ctypes.c_size_t, ctypes.POINTER(Stats),
@@ -255,6 +260,31 @@ def prune_layer_factored(W, U, params: PruneParams | None = None, W_out=None, ma
                                          ctypes.byref(params), _ptr(W_out), _ptr(mask_out),
                                          _ptr(ws), ws.numel(), ctypes.byref(stats), counts,
                                          _stream(W.device)))
+    return {"lambda": stats.lambda_used, "pruned": stats.total_pruned, "nblocks": stats.nblocks,
+            "counts": list(counts)}
+
+
+def prune_layer_alpha(W, alpha: float, X=None, H=None, params: PruneParams | None = None,
+                      W_out=None, mask_out=None, dense_out=None, ws=None) -> dict:
+    """prune_layer with round(alpha c) rows of largest output energy kept dense."""
+    _require_cuda(W, X, H, W_out, mask_out, dense_out)
+    if params is None:
+        params = make_params()
+    c, b = W.shape
+    n = X.shape[0] if X is not None else 0
+    if ws is None:
+        out = ctypes.c_size_t(0)
+        _check(lib().th_prune_layer_alpha_workspace_size(c, b, n, 1 if X is not None else 0,
+                                                         ctypes.byref(params), float(alpha),
+                                                         ctypes.byref(out)))
+        ws = workspace(out.value, W.device)
+    stats = Stats()
+    counts = (_I64 * (-(-b // params.block)))()
+    _check(lib().th_prune_layer_alpha(_ptr(W), _dtype_code(W), c, b, _ptr(X),
+                                      _dtype_code(X) if X is not None else 0, n, _ptr(H),
+                                      ctypes.byref(params), float(alpha), _ptr(W_out),
+                                      _ptr(mask_out), _ptr(dense_out), _ptr(ws), ws.numel(),
+                                      ctypes.byref(stats), counts, _stream(W.device)))
     return {"lambda": stats.lambda_used, "pruned": stats.total_pruned, "nblocks": stats.nblocks,
             "counts": list(counts)}
 

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libthanos.so")
 SOURCES = ["hessian.hip", "factor.hip", "prep.hip", "select.hip", "solve.hip", "update.hip",
-           "baseline.hip", "sparsegpt.hip", "ffn.hip", "capi.hip"]
+           "baseline.hip", "sparsegpt.hip", "ffn.hip", "rows.hip", "capi.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",

@@ -559,6 +559,100 @@ th_status th_prune_layer_factored(void* W, th_dtype wdt, int64_t c, int64_t b, c
   return finish_layer(L, cdiv(b, p->block), stats_out, block_counts, s);
 }
 
+// ------------------------------------------------------- alpha outlier rows
+
+namespace {
+struct AlphaLayout {
+  PruneLayout L;  // the compact layer (c - r rows), with its own fp32 W and mask
+  DevState* sel;  // state of the row selection (the layer keeps L.st)
+  float* scores;
+  int32_t* idx;
+  int32_t* rowmap;
+  float* gdiag;
+  double* colsq;
+  size_t bytes;
+};
+
+AlphaLayout layout_alpha(void* ws, int64_t c, int64_t cp, int64_t b, int64_t n, bool have_x,
+                         const th_prune_params* p, th_dtype xdt) {
+  AlphaLayout A;
+  A.L = layout_prune(ws, cp < 1 ? 1 : cp, b, n, have_x, p, true, true, xdt);
+  Carve cv(ws);
+  cv.off = A.L.bytes;
+  A.sel = cv.take<DevState>(1);
+  A.scores = cv.take<float>((size_t)c);
+  A.idx = cv.take<int32_t>((size_t)c);
+  A.rowmap = cv.take<int32_t>((size_t)c);
+  A.gdiag = cv.take<float>((size_t)b);
+  A.colsq = have_x ? cv.take<double>((size_t)colsq_splits(n) * b) : nullptr;
+  A.bytes = cv.off;
+  return A;
+}
+}  // namespace
+
+th_status th_prune_layer_alpha_workspace_size(int64_t c, int64_t b, int64_t n, int32_t have_x,
+                                              const th_prune_params* p, double alpha,
+                                              size_t* bytes) {
+  if (!bytes) return fail(TH_ERR_INVALID_ARG, "bytes is NULL");
+  th_status st = check_params(c, b, p);
+  if (st != TH_OK) return st;
+  if (!(alpha >= 0.0 && alpha <= 1.0)) return fail(TH_ERR_INVALID_ARG, "alpha must be in [0, 1]");
+  const int64_t cp = c - (int64_t)std::nearbyint(alpha * (double)c);
+  *bytes = layout_alpha(nullptr, c, cp, b, n, have_x != 0, p, TH_BF16).bytes;
+  return TH_OK;
+}
+
+th_status th_prune_layer_alpha(void* W, th_dtype wdt, int64_t c, int64_t b, const void* X,
+                               th_dtype xdt, int64_t n, const float* H, const th_prune_params* p,
+                               double alpha, float* W_out_f32, uint8_t* mask_out,
+                               uint8_t* dense_rows_out, void* workspace, size_t workspace_bytes,
+                               th_stats* stats_out, int64_t* block_counts, th_stream_t stream) {
+  th_status chk = check_layer_args(W, wdt, c, b, X, xdt, n, H, p, workspace);
+  if (chk != TH_OK) return chk;
+  if (!(alpha >= 0.0 && alpha <= 1.0)) return fail(TH_ERR_INVALID_ARG, "alpha must be in [0, 1]");
+  if (c >= ((int64_t)1 << 31)) return fail(TH_ERR_INVALID_ARG, "c must be < 2^31");
+  const int64_t r = (int64_t)std::nearbyint(alpha * (double)c);  // rows kept dense
+  const int64_t cp = c - r;
+  AlphaLayout A = layout_alpha(workspace, c, cp, b, n, X != nullptr, p, xdt);
+  if (workspace_bytes < A.bytes) return fail(TH_ERR_WORKSPACE, "workspace too small");
+  const PruneLayout& L = A.L;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t nblk = cdiv(b, p->block);
+
+  TH_HIP(hipMemsetAsync(L.st, 0, sizeof(DevState), s), "memset state");
+  TH_HIP(hipMemsetAsync(A.sel, 0, sizeof(DevState), s), "memset selection state");
+  TH_HIP(hipMemsetAsync(L.counts, 0, nblk * sizeof(unsigned long long), s), "memset counts");
+  // G_qq: column norms of X, or (H_qq - lambda)/2 of a damped H
+  if (X) {
+    TH_HIP(launch_column_sq_norms(X, xdt, n, b, b, A.colsq, A.gdiag, s), "column norms");
+  } else {
+    TH_HIP(launch_lambda(H, b, p->lambda, p->lambda_is_relative, 1, A.sel, s), "lambda");
+    TH_HIP(launch_wanda_diag(H, b, A.sel, 1, A.gdiag, s), "G diagonal");
+  }
+  // the c - r rows of smallest (energy, row) are pruned, the rest stay dense; a
+  // non-finite energy (a non-finite weight) raises the layer's flag
+  TH_HIP(launch_row_energy(W, wdt, c, b, A.gdiag, A.scores, s), "row energy");
+  TH_HIP(launch_select_init(A.sel, (long long)cp, (long long)c, s), "select init");
+  for (int pass = 0; pass < 6; ++pass) {
+    TH_HIP(launch_select_scores_pass(A.scores, c, 1, 1, 0, A.sel, s), "select pass");
+    TH_HIP(launch_select_pick(A.sel, s), "select pick");
+  }
+  TH_HIP(launch_row_index(A.scores, c, A.sel, A.idx, A.rowmap, dense_rows_out, L.st, s),
+         "row index");
+
+  // the layer step on the compact rows
+  if (cp > 0) TH_HIP(launch_gather_rows(W, wdt, b, A.rowmap, cp, L.Wf, L.st, s), "gather");
+  th_status pre = inverse_factor(X, xdt, n, H, b, p, L, s);
+  if (pre != TH_OK) return pre;
+  if (cp > 0) {
+    th_status blocks = prune_blocks(L, cp, b, p, L.Wf, L.mask, s);
+    if (blocks != TH_OK) return blocks;
+  }
+  TH_HIP(launch_scatter_rows(W, wdt, c, b, A.idx, L.Wf, L.mask, W_out_f32, mask_out, s),
+         "scatter");
+  return finish_layer(L, nblk, stats_out, block_counts, s);
+}
+
 // ------------------------------------------------------ gated feed-forward
 
 th_status th_gated_ffn_input(const void* X, const void* W_gate, const void* W_up, th_dtype dt,

@@ -182,6 +182,18 @@ hipError_t launch_gated_ffn(const unsigned short* X, const unsigned short* Wg,
                             const unsigned short* Wu, unsigned short* Y, int64_t n, int64_t d,
                             int64_t f, hipStream_t s);
 
+// rows.hip
+hipError_t launch_row_energy(const void* W, th_dtype wdt, int64_t c, int64_t b, const float* g,
+                             float* s, hipStream_t st);
+hipError_t launch_row_index(const float* s, int64_t c, const DevState* sel, int32_t* idx,
+                            int32_t* rowmap, uint8_t* dense_out, DevState* layer,
+                            hipStream_t st);
+hipError_t launch_gather_rows(const void* W, th_dtype wdt, int64_t b, const int32_t* rowmap,
+                              int64_t cp, float* Wf, DevState* dst, hipStream_t st);
+hipError_t launch_scatter_rows(void* W, th_dtype wdt, int64_t c, int64_t b, const int32_t* idx,
+                               const float* Wf, const uint8_t* mc, float* Wout, uint8_t* mask,
+                               hipStream_t st);
+
 // update.hip
 // W[:, col0:col_end) -= Z[:, 0:K] R[r0:r0+K, col0:col_end) (Z pitch ldz); entries of
 // columns [mask_j0, mask_j0 + mask_w) with mask set are then zeroed.

@@ -24,7 +24,8 @@ def test_header_declares_the_path():
                  "th_column_sq_norms", "th_column_sq_norms_workspace_size", "th_prune_baseline",
                  "th_prune_sparsegpt", "th_prune_sparsegpt_workspace_size", "th_factor",
                  "th_factor_workspace_size", "th_prune_layer_factored",
-                 "th_prune_layer_factored_workspace_size", "th_gated_ffn_input"):
+                 "th_prune_layer_factored_workspace_size", "th_gated_ffn_input",
+                 "th_prune_layer_alpha", "th_prune_layer_alpha_workspace_size"):
         assert must in names
 
 
@@ -179,3 +180,21 @@ def test_factor_and_ffn_arguments_are_rejected_before_any_launch():
     assert L.th_gated_ffn_input(fake, fake, fake, _lib.TH_BF16, 4, 12, 4, fake, None) == 1
     assert L.th_gated_ffn_input(ctypes.c_void_p(0x1002), fake, fake, _lib.TH_BF16, 4, 8, 4, fake,
                                 None) == 1
+
+
+def test_alpha_arguments_are_rejected_before_any_launch():
+    L = _lib.lib()
+    out = ctypes.c_size_t(0)
+    p = _lib.make_params(pattern=(2, 4))
+    assert L.th_prune_layer_alpha_workspace_size(4096, 11008, 262144, 1, ctypes.byref(p), 0.1,
+                                                 ctypes.byref(out)) == 0
+    for bad in (-0.1, 1.5, float("nan")):
+        assert L.th_prune_layer_alpha_workspace_size(64, 128, 10, 1, ctypes.byref(p), bad,
+                                                     ctypes.byref(out)) == 1
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its checks first
+    args = [fake, _lib.TH_BF16, 8, 8, fake, _lib.TH_BF16, 8, None, ctypes.byref(p), 2.0, None, None,
+            None, fake, 1 << 30, None, None, None]
+    assert L.th_prune_layer_alpha(*args) == 1  # alpha > 1
+    args[9] = 0.1
+    args[7] = fake  # both X and H
+    assert L.th_prune_layer_alpha(*args) == 1
