@@ -6,11 +6,11 @@ Usage: python -m layer_wise_obs_amd.compare [--configs 1 2 3 4 5]
 
 For every layer and pattern of a workload: H from the layer's synthetic input
 stream (th_hessian_accumulate, th_hessian_finalize), then th_prune_layer (the
-method), th_prune_sparsegpt, th_prune_baseline with G_qq from th_column_sq_norms
-(Wanda) and without (magnitude), and th_reconstruction_error against
-G = (H - lambda I) / 2. Every step
-runs in the HIP library; this file only moves tensors and prints one JSON line per
-(workload, layer, pattern).
+method), th_prune_layer_alpha (alpha = 0.1, N:M patterns only), th_prune_sparsegpt,
+th_prune_baseline with G_qq from th_column_sq_norms (Wanda) and without
+(magnitude), and th_reconstruction_error against G = (H - lambda I) / 2. Every
+step runs in the HIP library; this file only moves tensors and prints one JSON
+line per (workload, layer, pattern).
 """
 from __future__ import annotations
 
@@ -69,6 +69,14 @@ def run_config(cid: int):
                 fn(W, H=H, params=params, W_out=Wout)
                 out["ms"][name] = round(_ms(t0), 3)
                 out["E_rel"][name] = L.reconstruction_error(W0.float(), Wout, G=G)[1]
+                del W, Wout
+            if pat[0] == "nm":  # the alpha = 0.1 variant the pages report for N:M
+                W = W0.clone()
+                Wout = torch.empty(W.shape, dtype=torch.float32, device=DEV)
+                t0 = time.perf_counter()
+                L.prune_layer_alpha(W, 0.1, H=H, params=params, W_out=Wout)
+                out["ms"]["thanos_alpha0.1"] = round(_ms(t0), 3)
+                out["E_rel"]["thanos_alpha0.1"] = L.reconstruction_error(W0.float(), Wout, G=G)[1]
                 del W, Wout
             for method in ("wanda", "magnitude"):
                 W = W0.clone()
