@@ -44,11 +44,15 @@ __device__ __forceinline__ int mat_idx(int r, int q) { return r * kMaxBlock + (q
 // VALU op each); for c >= kLdsFrom every lane stores its register j into a
 // per-wave LDS row and the entries are read back as wave-uniform 128-bit loads,
 // which moves part of the broadcast work from the VALU to the LDS pipe. The
-// pivot reciprocal is rcp plus one Newton step.
+// pivot reciprocal is rcp plus one Newton step. Each step's pivot goes straight
+// into its lane of a VGPR (v_writelane), and `lane` arrives through an opaque
+// move inside the caller's row loop: otherwise the compiler keeps all 64 pivots
+// and hoists all 64 lane masks as SGPRs for the whole loop and spills them.
+// The elimination runs at the fp32 VALU rate (a wave64 FMA takes four cycles of
+// a 16-lane SIMD): about 20 us of a 2:4 block's 37 us at c = 4096.
 constexpr int kLdsFrom = 32;
 
-__device__ __forceinline__ float gauss_jordan64(float (&reg)[64], float rhs, float* row) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ float gauss_jordan64(float (&reg)[64], float rhs, float* row, int lane) {
   float piv = 1.f;
   static_for<0, 64>([&](auto J) __attribute__((always_inline)) {
     constexpr int j = J;
@@ -58,7 +62,8 @@ __device__ __forceinline__ float gauss_jordan64(float (&reg)[64], float rhs, flo
     float pinv = __builtin_amdgcn_rcpf(p);
     pinv = pinv * fmaf(-p, pinv, 2.f);
     const float f = (lane == j) ? 0.f : reg[j] * pinv;
-    piv = (lane == j) ? p : piv;
+    // lane j's pivot, written straight into lane j (no select chain kept alive)
+    __asm__ volatile("v_writelane_b32 %0, %1, %2" : "+v"(piv) : "s"(p), "n"(j));
     rhs = fmaf(-f, rj, rhs);
     static_for<j + 1, 64>([&](auto C) __attribute__((always_inline)) {
       constexpr int c = C;
@@ -168,6 +173,11 @@ __global__ __launch_bounds__(kWaves * 64, 4) void solve_kernel(SolveArgs a) {
     }
     wave_sync();
     if (s > 0) {
+      // The lane index through an opaque move: the per-step lane masks are then
+      // formed inside the row loop (one compare each) instead of being hoisted out
+      // of it as 64-bit SGPR masks that spill.
+      int olane;
+      __asm__ volatile("v_mov_b32 %0, %1" : "=v"(olane) : "v"(lane));
       float reg[64];
       if (ROUTE == 0) {
         const bool act = lane < s;
@@ -177,11 +187,11 @@ __global__ __launch_bounds__(kWaves * 64, 4) void solve_kernel(SolveArgs a) {
           const bool in = (c < s) && act;
           const int qc = (c < s) ? sQ[wave][c] : 0;
           const float v = sM[mat_idx(qa, qc)];
-          reg[c] = in ? v : ((c == lane) ? 1.f : 0.f);
+          reg[c] = in ? v : ((c == olane) ? 1.f : 0.f);
         }
         const float u = act ? su[wave][lane] : 0.f;
         wave_sync();  // the gather's reads are done before the pivot row is written
-        const float z = gauss_jordan64(reg, u, (float*)sP[wave]);
+        const float z = gauss_jordan64(reg, u, (float*)sP[wave], olane);
         if (act) zrow[qa] = z;
       } else {
         const int p = Bb - s;
@@ -192,14 +202,14 @@ __global__ __launch_bounds__(kWaves * 64, 4) void solve_kernel(SolveArgs a) {
           const bool in = (c < p) && act;
           const int pc = (c < p) ? sP[wave][c] : 0;
           const float v = sM[mat_idx(pb, pc)];
-          reg[c] = in ? v : ((c == lane) ? 1.f : 0.f);
+          reg[c] = in ? v : ((c == olane) ? 1.f : 0.f);
         }
         float y = 0.f;
         if (act) {
           for (int t = 0; t < s; ++t) y = fmaf(su[wave][t], sM[mat_idx(sQ[wave][t], pb)], y);
         }
         wave_sync();  // the gather's reads of sP are done before it becomes the pivot row
-        const float x = gauss_jordan64(reg, y, (float*)sP[wave]);
+        const float x = gauss_jordan64(reg, y, (float*)sP[wave], olane);
         // v = [u on Q, -x on P], then z_q = (v N)_q for q in Q
         if (act) sbuf[wave][pb] = -x;
         if (s0) sbuf[wave][e0] = w0;
