@@ -130,17 +130,51 @@ __device__ __forceinline__ void pass_body(DevState* st, int64_t rows, int64_t f,
 }
 
 // Keys recomputed from the current weights: S = W^2 * g with g the per-column
-// score weight (1/[A_F]_qq for OBS, G_qq for Wanda).
+// score weight (1/[A_F]_qq for OBS, G_qq for Wanda). The pass streams W[:, j0:j1)
+// once, so it is bound by the loads: with 16-byte aligned rows each thread reads
+// four columns of W and g per 16-byte load, four loads in flight (the histogram
+// atomics are not the limit: without them a pass is only ~7% faster).
 __global__ __launch_bounds__(256) void select_pass_kernel(const float* __restrict__ W, int64_t c,
                                                           int64_t b, int64_t j0, int64_t j1,
                                                           const float* __restrict__ g,
                                                           DevState* st) {
   if (st->done) return;
-  pass_body(st, c, j1 - j0, [&](int64_t k, int64_t q) {
-    const int64_t col = j0 + q;
-    const float s = score_of(W[k * b + col], g[col]);
-    return make_key(s, (unsigned int)(k * b + col));
-  });
+  __shared__ unsigned int sh[kSelBins];
+  const int shift = st->shift;
+  int width;
+  digit_of(shift, width);
+  const int top = shift + width;
+  const unsigned long long prefix = st->prefix;
+  for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) sh[i] = 0u;
+  __syncthreads();
+  const unsigned long long dmask = (1ull << width) - 1ull;
+  auto count = [&](float w, float gq, int64_t flat) {
+    const unsigned long long key = make_key(score_of(w, gq), (unsigned int)flat);
+    const bool match = (top >= 64) || ((key >> top) == (prefix >> top));
+    if (match) atomicAdd(&sh[(key >> shift) & dmask], 1u);
+  };
+  const int64_t f = j1 - j0;
+  const bool vec = ((b & 3) == 0) && ((j0 & 3) == 0) && ((((uintptr_t)W | (uintptr_t)g) & 15) == 0);
+  const int64_t f4 = vec ? (f >> 2) : 0;
+  for (int64_t k = blockIdx.x; k < c; k += gridDim.x) {
+    const float* wr = W + k * b + j0;
+    const float* gr = g + j0;
+    const int64_t base = k * b + j0;
+#pragma unroll 4
+    for (int64_t v = threadIdx.x; v < f4; v += blockDim.x) {
+      const f32x4_t w4 = ((const f32x4_t*)wr)[v];
+      const f32x4_t g4 = ((const f32x4_t*)gr)[v];
+      const int64_t q = 4 * v;
+      count(w4[0], g4[0], base + q);
+      count(w4[1], g4[1], base + q + 1);
+      count(w4[2], g4[2], base + q + 2);
+      count(w4[3], g4[3], base + q + 3);
+    }
+    for (int64_t q = 4 * f4 + threadIdx.x; q < f; q += blockDim.x) count(wr[q], gr[q], base + q);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kSelBins; i += blockDim.x)
+    if (sh[i]) atomicAdd(&st->hist[i], sh[i]);
 }
 
 // Keys from given scores [c, f] (parity entry point).
