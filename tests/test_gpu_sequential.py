@@ -176,3 +176,19 @@ def test_sequential_mlp_block_matches_oracle():
     print("down", rep, flush=True)
     assert rep["ok"], rep
     assert np.all(m.reshape(d, -1, 4).sum(axis=2) == 2)
+
+
+def test_factored_from_fp32_activations():
+    """th_factor on fp32 X (the fp32 Hessian path) then the factored layer step:
+    bit-identical to th_prune_layer on the same fp32 X."""
+    _say("factored from fp32 X")
+    c, b, n = 96, 200, 1500
+    W = synth.weights(c, b, 0.02, 66, 100, torch.float32)
+    X = synth.activations(n, b, 66, 1, 3, 30.0, False, torch.float32)
+    Xd = X.to(DEV)
+    U, lam = L.factor(X=Xd, lam=0.01, relative=True)
+    params = L.make_params(sparsity=0.5, block=64)
+    Wa, fa, ma, ia = _prune(L.prune_layer_factored, W, U, params=params)
+    Wb, fb, mb, ib = _prune(L.prune_layer, W, X=Xd, params=params)
+    assert np.array_equal(fa, fb) and np.array_equal(ma, mb) and torch.equal(Wa, Wb)
+    assert abs(ib["lambda"] - lam) <= 1e-6 * lam
