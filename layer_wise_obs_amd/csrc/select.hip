@@ -50,11 +50,15 @@ __global__ void select_init_kernel(DevState* st, long long add_budget, long long
 }
 
 // Narrow the prefix by the digit whose bucket holds the rrem-th smallest key
-// (one workgroup of 256 threads), then clear the histogram for the next pass.
+// (one workgroup of 256 threads, 8 bins each), then clear the histogram for the
+// next pass. An inclusive scan of the per-thread sums finds the one thread whose
+// bins hold rank rrem (exclusive sum < rrem <= inclusive sum); that thread walks
+// its 8 bins. Integer counts throughout, so the result does not depend on order.
 __global__ __launch_bounds__(256) void select_pick_kernel(DevState* st) {
   if (st->done) return;
-  __shared__ unsigned int part[256];
+  __shared__ unsigned long long scan[256];
   __shared__ unsigned int hcopy[kSelBins];
+  __shared__ int found;
   const int tid = threadIdx.x;
   const int per = kSelBins / 256;  // 8 bins per thread
   unsigned int local = 0;
@@ -63,43 +67,46 @@ __global__ __launch_bounds__(256) void select_pick_kernel(DevState* st) {
     hcopy[tid * per + i] = h;
     local += h;
   }
-  part[tid] = local;
+  scan[tid] = local;
+  if (tid == 0) found = 0;
   __syncthreads();
-  if (tid == 0) {
-    const long long r = st->rrem;
-    long long cum = 0;
-    int d = -1;
-    for (int t = 0; t < 256 && d < 0; ++t) {
-      if (cum + (long long)part[t] >= r) {
-        for (int i = 0; i < per; ++i) {
-          const long long h = hcopy[t * per + i];
-          if (cum + h >= r) {
-            d = t * per + i;
-            break;
-          }
-          cum += h;
-        }
-      } else {
-        cum += part[t];
+  for (int off = 1; off < 256; off <<= 1) {
+    const unsigned long long v = tid >= off ? scan[tid - off] : 0ull;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  const long long r = st->rrem;
+  const long long incl = (long long)scan[tid], excl = incl - (long long)local;
+  if (excl < r && r <= incl) {
+    long long cum = excl;
+    int d = tid * per + per - 1;
+    for (int i = 0; i < per; ++i) {
+      const long long h = hcopy[tid * per + i];
+      if (cum + h >= r) {
+        d = tid * per + i;
+        break;
       }
+      cum += h;
     }
     const int shift = st->shift;
-    if (d < 0) {  // cannot happen when the histogram is consistent
-      st->tbound = st->prefix;
+    const long long inb = hcopy[d];
+    const long long rnew = r - cum;
+    st->prefix |= ((unsigned long long)d) << shift;
+    st->rrem = rnew;
+    if (inb == rnew || shift == 0) {
+      // every key of the bucket is within the r smallest (shift == 0: inb == 1)
+      st->tbound = st->prefix + (1ull << shift);
       st->done = 1;
     } else {
-      const long long inb = hcopy[d];
-      const long long rnew = r - cum;
-      st->prefix |= ((unsigned long long)d) << shift;
-      st->rrem = rnew;
-      if (inb == rnew || shift == 0) {
-        // every key of the bucket is within the r smallest (shift == 0: inb == 1)
-        st->tbound = st->prefix + (1ull << shift);
-        st->done = 1;
-      } else {
-        st->shift = (shift >= 20) ? shift - 11 : 0;
-      }
+      st->shift = (shift >= 20) ? shift - 11 : 0;
     }
+    found = 1;
+  }
+  __syncthreads();
+  if (tid == 0 && !found) {  // cannot happen when the histogram is consistent
+    st->tbound = st->prefix;
+    st->done = 1;
   }
   for (int i = tid; i < kSelBins; i += blockDim.x) st->hist[i] = 0u;
 }
