@@ -1,4 +1,4 @@
-// C ABI of libthanos: argument checks, workspace layout and the layer driver.
+// C ABI of libthanos: argument checks, workspace layout and the per-layer host sequence.
 //
 // th_prune_layer runs the whole per-layer path on one stream:
 //   Hessian (X given):  H = 2 X^T X (lower)  -> lambda on the device

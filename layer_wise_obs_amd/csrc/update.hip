@@ -6,7 +6,7 @@
 // the bf16 matrix cores with three-way split fp32 operands, gemm_x3.h; 64 x 64
 // tiles on the fp32 matrix cores for launches with few tiles), after which the
 // pruned entries of block J are set to exactly zero.
-// The kernel takes any column range and any K, so the driver can split one
+// The kernel takes any column range and any K, so the host code can split one
 // block's update into the columns it needs now and a deferred part that is
 // applied for several blocks at once (K = several blocks).
 //
