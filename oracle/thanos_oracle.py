@@ -46,7 +46,7 @@ __all__ = [
     "select_unstructured", "select_nm", "solve_rows", "schur_downdate",
     "prune_layer", "reconstruction_error", "column_sq_norms", "baseline_keys", "prune_baseline",
     "trailing_inverse_rows", "sparsegpt_column", "prune_sparsegpt", "silu", "gated_ffn_input",
-    "prune_mlp_sequential", "outlier_rows", "prune_layer_alpha",
+    "prune_mlp_sequential", "row_energies", "outlier_rows", "prune_layer_alpha",
 ]
 
 
@@ -184,19 +184,25 @@ def schur_downdate(A_F: np.ndarray, blk: int) -> np.ndarray:
     """
     AJJ = A_F[:blk, :blk]
     AJF = A_F[:blk, blk:]
-    return A_F[blk:, blk:] - A_F[blk:, :blk] @ np.linalg.solve(AJJ, AJF)
+    T = A_F[blk:, :blk] @ np.linalg.solve(AJJ, AJF)
+    return np.subtract(A_F[blk:, blk:], T, out=T)  # one b x b temporary, not two
 
 
 def prune_layer(W, G: np.ndarray, sparsity: float = 0.5, pattern=None, block: int = 128,
                 lam: float = 0.01, lam_relative: bool = True, score: str = "obs",
-                trace: list | None = None, max_blocks: int | None = None) -> dict:
+                trace: list | None = None, max_blocks: int | None = None,
+                on_block=None) -> dict:
     """Block-wise pruning with joint compensation (the layer step of the method).
 
     pattern: None for unstructured with the dynamic global budget, or (n, m).
     Returns W_hat (fp64), mask (True = pruned), per-block prune counts, lambda.
     trace (optional list) receives, per block, the scores the selection saw and
-    the remaining budget (for diagnosing near-ties in comparisons). max_blocks
-    stops after that many blocks (used only to time a bounded sample).
+    the remaining budget (for diagnosing near-ties in comparisons). on_block
+    (optional callable) is called as on_block(j0, S, r, sel, g) after each
+    block's selection, with the same scores (over F for unstructured, over J for
+    N:M) and the per-column score weights g over F, without copying them: a way
+    to record a summary of large layers. Neither changes the arithmetic.
+    max_blocks stops after that many blocks (used only to time a bounded sample).
 
     Procedure ("Pruning LLMs with Thanos", sections "The scaling problem, and what
     SparseGPT changes" (left-to-right blocks, finished columns frozen, updates only
@@ -251,6 +257,8 @@ def prune_layer(W, G: np.ndarray, sparsity: float = 0.5, pattern=None, block: in
         if trace is not None:
             trace.append({"j0": j0, "S": S.copy(),
                           "r": (ktot - pruned) if pattern is None else None})
+        if on_block is not None:
+            on_block(j0, S, (ktot - pruned) if pattern is None else None, sel, g)
         Z = solve_rows(Wc[:, j0:j0 + blk], A[:blk, :blk], sel)
         Wc[:, j0:] -= Z @ A[:blk, :]
         blockW = Wc[:, j0:j0 + blk]
@@ -278,11 +286,16 @@ def reconstruction_error(W, W_hat, G: np.ndarray):
     return E, (E / base if base > 0 else 0.0)
 
 
-def column_sq_norms(X_tok) -> np.ndarray:
+def column_sq_norms(X_tok, chunk: int = 8192) -> np.ndarray:
     """G_qq = sum_t X_tq^2 in fp64, rounded to fp32 (the squared input-feature norms
-    of the explainer's section "Wanda: Pruning by Weights and Activations")."""
-    X = _f64(X_tok)
-    return np.sum(X * X, axis=0).astype(np.float32)
+    of the explainer's section "Wanda: Pruning by Weights and Activations").
+    Summed over token chunks, so long streams need not exist in fp64 at once."""
+    n, b = X_tok.shape
+    acc = np.zeros(b, dtype=np.float64)
+    for t0 in range(0, n, chunk):
+        X = _f64(X_tok[t0:t0 + chunk])
+        acc += np.sum(X * X, axis=0)
+    return acc.astype(np.float32)
 
 
 def baseline_keys(W, gdiag=None) -> np.ndarray:
@@ -479,6 +492,14 @@ def prune_mlp_sequential(X_mlp, W_gate, W_up, W_down, sparsity: float = 0.5, pat
             "G_down": G_down}
 
 
+def row_energies(W, gdiag) -> np.ndarray:
+    """s_k = sum_q W_kq^2 G_qq, summed in fp64 from G_qq given in fp32 and rounded to
+    fp32 (the precision in which the alpha variant ranks rows; see outlier_rows)."""
+    W0 = _f64(W)
+    g = np.asarray(gdiag, dtype=np.float32).astype(np.float64)
+    return ((W0 * W0) @ g).astype(np.float32)
+
+
 def outlier_rows(W, gdiag, alpha: float) -> np.ndarray:
     """Rows kept dense by the alpha variant (True = dense).
 
@@ -491,10 +512,8 @@ def outlier_rows(W, gdiag, alpha: float) -> np.ndarray:
     value, ties to the higher row index (rows ordered by (s_k, k); the last ones
     stay dense).
     """
-    W0 = _f64(W)
-    c = W0.shape[0]
-    g = np.asarray(gdiag, dtype=np.float32).astype(np.float64)
-    s32 = ((W0 * W0) @ g).astype(np.float32)
+    c = _f64(W).shape[0]
+    s32 = row_energies(W, gdiag)
     r = int(np.round(np.float64(alpha) * c))
     order = np.lexsort((np.arange(c), s32))
     dense = np.zeros(c, dtype=bool)

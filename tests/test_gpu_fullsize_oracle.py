@@ -1,0 +1,175 @@
+"""Full-size parity with the fp64 oracle: every layer and pattern of the four large
+workloads (q_proj 4096x4096 2:4 on 262144 tokens; down_proj 4096x11008 2:4 and
+4:8 on 262144 tokens; the seven LLaMA-7B-shaped layers at 50% unstructured on
+131072 tokens; the LLaMA-2-70B-shaped k/v/q/o/down_proj at 60% unstructured and
+2:4 on 65536 tokens).
+
+The expected values were written by tests/golden/make_fullsize.py, which runs
+only the oracle on the seeded synthetic inputs (nothing from the GPU library).
+They hold, for a sample of output rows, the oracle's mask and W_hat, the error of
+each sampled row, and what is needed to tell an fp32 near-tie from a mistake; for
+unstructured layers also the per-block and per-row counts and the layer's error.
+
+Checks (bars of the method's parity):
+* masks row by row; a sampled row may differ only if, at its first differing
+  block, every differing decision is an fp32 near-tie in the oracle's own scores
+  (relative gap within TIE_MARGIN times the measured fp32 deviation of the
+  GPU factor's [H^-1]_qq from the oracle's), and at most MAX_FLIP_FRAC of the
+  sampled rows;
+* W_hat within 1e-3 relative (Frobenius) on the sampled rows whose masks agree;
+* the error of those rows within 1e-3 of the oracle's; unstructured: the whole
+  layer's error within 1e-3 of the oracle's, the exact global budget, and the
+  cumulative per-block counts within the oracle's near-tie population;
+* N:M: exact group counts on every row.
+
+Each case prints its GPU time; the stored oracle time is in the manifest.
+"""
+import json
+import os
+import time
+
+import numpy as np
+import pytest
+import torch
+
+from layer_wise_obs_amd import _lib as L
+from layer_wise_obs_amd import synth
+from tests import _parity as P
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "fullsize")
+MANIFEST = json.load(open(os.path.join(GOLD, "manifest.json"))) if os.path.exists(
+    os.path.join(GOLD, "manifest.json")) else {}
+CASES = sorted(MANIFEST)
+WINDOWS = (1e-6, 1e-5, 1e-4, 1e-3)  # relative windows of the stored near-tie counts
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+_HCACHE = {}
+
+
+def _hessian(cfg, stream):
+    """Damped H of a whole stream (kept while consecutive cases share it)."""
+    key = (cfg.cid, stream)
+    if key not in _HCACHE:
+        _HCACHE.clear()
+        torch.cuda.empty_cache()
+        s = cfg.streams[stream]
+        X = torch.empty((s.n, s.b), dtype=torch.bfloat16, device=DEV)
+        cfg.activations(stream, device=DEV, out=X)
+        H = torch.zeros((s.b, s.b), dtype=torch.float32, device=DEV)
+        L.hessian_accumulate(H, X)
+        lam = L.hessian_finalize(H, cfg.lambda_rel, True)
+        _HCACHE[key] = (H, lam, X if cfg.cid in (2, 3) else None)
+        del X
+    return _HCACHE[key]
+
+
+def _flip_explained(d, gap_or_dist, block, tol, m=None):
+    """d: differing columns of one row. At the first differing block every
+    differing decision must be a near-tie (gap <= tol) in the oracle's scores."""
+    j0 = (int(d[0]) // block) * block
+    first = d[(d >= j0) & (d < j0 + block)]
+    if m is None:  # unstructured: |S - T| / T per column
+        vals = gap_or_dist[first]
+    else:  # N:M: gap per group
+        vals = gap_or_dist[np.unique(first // m)]
+    return bool(np.all(vals <= tol)), float(np.max(vals))
+
+
+@pytest.mark.skipif(not CASES, reason="no stored full-size oracle results")
+@pytest.mark.parametrize("name", CASES)
+def test_fullsize_against_oracle(name):
+    g = np.load(os.path.join(GOLD, f"{name}.npz"))
+    meta = MANIFEST[name]
+    cfg = synth.config(meta["config"])
+    layer = [l for l in cfg.layers if l.name == meta["layer"]][0]
+    c, b = layer.c, layer.b
+    pat = meta["pattern"]
+    nm = pat[0] == "nm"
+    _say(f"{name}: {c}x{b} {'%d:%d' % (pat[1], pat[2]) if nm else 'unstructured %g' % pat[1]}, "
+         f"oracle step {meta['oracle_prune_s']} s (stored)")
+    H, lam, X = _hessian(cfg, layer.hessian)
+    W0 = cfg.weights(layer, device=DEV)
+    W = W0.clone()
+    Wout = torch.empty((c, b), dtype=torch.float32, device=DEV)
+    mask = torch.empty((c, b), dtype=torch.uint8, device=DEV)
+    params = (L.make_params(pattern=(pat[1], pat[2]), block=cfg.block, lam=cfg.lambda_rel) if nm
+              else L.make_params(sparsity=pat[1], block=cfg.block, lam=cfg.lambda_rel))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if X is not None:  # the benchmark's launch configuration: H built inside from X
+        info = L.prune_layer(W, X=X, params=params, W_out=Wout, mask_out=mask)
+    else:
+        info = L.prune_layer(W, H=H, params=params, W_out=Wout, mask_out=mask)
+    torch.cuda.synchronize()
+    _say(f"  GPU layer step {1e3 * (time.perf_counter() - t0):.1f} ms")
+    assert abs(info["lambda"] - float(g["lam"])) <= 1e-5 * float(g["lam"])
+    # the fp32 error of the GPU's score denominators sets what counts as a near-tie
+    U, _ = L.factor(X=X) if X is not None else L.factor(H=H, lam=lam, relative=False)
+    delta = P.denominator_error(U, g["diag_inv"])
+    del U
+    tol = P.tie_tolerance(delta)
+    _say(f"  [H^-1]_qq deviation {delta:.2e}, near-tie bound {tol:.2e}")
+    assert delta <= 1e-3
+
+    rows = g["rows"].astype(np.int64)
+    ridx = torch.tensor(rows, device=DEV)
+    m_ora = np.unpackbits(g["mask_rows"], axis=1, count=b).astype(bool)
+    m_gpu = mask[ridx].cpu().numpy().astype(bool)
+    w_gpu = Wout[ridx].cpu().numpy()
+    w_ora = g["what_rows"]
+    same = np.all(m_gpu == m_ora, axis=1)
+    worst = 0.0
+    for i in np.flatnonzero(~same):
+        d = np.flatnonzero(m_gpu[i] != m_ora[i])
+        ok, v = _flip_explained(d, g["gap_rows"][i] if nm else g["dist_rows"][i], cfg.block, tol,
+                                pat[2] if nm else None)
+        worst = max(worst, v)
+        assert ok, (name, int(rows[i]), int(d[0]), v)
+    nflip = int((~same).sum())
+    _say(f"  sampled rows {len(rows)}, flipped {nflip} (largest oracle gap at a flip {worst:.2e})")
+    assert nflip <= max(1, int(P.MAX_FLIP_FRAC * len(rows)))
+    err_w = P.rel_fro(w_gpu[same], w_ora[same].astype(np.float64))
+    _say(f"  W_hat on agreeing rows: {err_w:.2e} relative")
+    assert err_w <= P.W_RTOL
+    assert np.all(w_gpu[m_gpu] == 0.0)
+
+    # error of the agreeing sampled rows, from G = (H - lambda I) / 2
+    G = H.clone()
+    G.diagonal().sub_(lam)
+    G.mul_(0.5)
+    sidx = torch.tensor(rows[same], device=DEV)
+    e_gpu, _ = L.reconstruction_error(W0[sidx].float().contiguous(), Wout[sidx].contiguous(), G=G)
+    e_ora = float(np.sum(g["e_row"][same]))
+    _say(f"  error of agreeing rows: {e_gpu:.6g} vs oracle {e_ora:.6g}")
+    assert abs(e_gpu - e_ora) <= P.E_RTOL * e_ora
+
+    mk = mask.bool()
+    if nm:
+        n_, m_ = pat[1], pat[2]
+        assert bool((mk.view(c, -1, m_).sum(dim=2) == m_ - n_).all())
+        assert info["pruned"] == c * b * (m_ - n_) // m_
+    else:
+        k_total = int(g["k_total"])
+        assert info["pruned"] == k_total == int(mk.sum())
+        e_all, er_all = L.reconstruction_error(W0.float(), Wout, G=G)
+        _say(f"  layer error {e_all:.6g} vs oracle {float(g['e_all']):.6g}")
+        assert abs(e_all - float(g["e_all"])) <= P.E_RTOL * float(g["e_all"])
+        # cumulative per-block counts: a decision can differ only within the
+        # oracle's near-tie population of each block's threshold
+        w = min([i for i, x in enumerate(WINDOWS) if x >= tol] or [len(WINDOWS) - 1])
+        c_gpu = np.cumsum(np.asarray(info["counts"], np.int64))
+        c_ora = np.cumsum(g["counts"])
+        allow = np.cumsum(g["near_counts"][:, w])
+        diff = np.abs(c_gpu - c_ora)
+        _say(f"  cumulative block counts: max |diff| {int(diff.max())}, allowance at that block "
+             f"{int(allow[int(diff.argmax())])}")
+        assert np.all(diff <= allow)
+        rc = mk.sum(dim=1).cpu().numpy()
+        _say(f"  rows with the oracle's count: {np.mean(rc == g['row_counts']):.4f}")
+    del W, Wout, mask, G

@@ -346,3 +346,50 @@ def test_prune_layers_sharing_one_hessian():
         print(rep, flush=True)
         assert rep["ok"], rep
         assert info["pruned"] == ora["k_total"]
+
+
+@pytest.mark.parametrize("pattern", [None, (2, 4)])
+def test_prune_wide_layer_through_the_large_tile_update(pattern):
+    """4096 x 6144 with 8192 tokens: wide enough that the updates of W run on the
+    128 x 128 split-operand tiles (at least 1024 tiles per launch): the early
+    per-block updates of unstructured pruning and the deferred updates of N:M
+    beyond each group of eight blocks. Unstructured: the whole layer against the
+    oracle. 2:4: rows are independent given H, so the oracle prunes 256 sampled
+    rows (its own fp64 G) and the GPU's rows are compared with them."""
+    import time
+    c, b, n = 4096, 6144, 8192
+    _say(f"prune {c}x{b} n={n} {pattern or 'unstructured 0.5'} (128x128 update tiles)")
+    W, X = _inputs(c, b, n, 41, relu=True, outliers=60)
+    t0 = time.perf_counter()
+    G = O.gram(X)
+    rows = np.arange(c) if pattern is None else np.sort(
+        np.random.default_rng(41).choice(c, 256, replace=False))
+    trace, on_block = P.light_trace()
+    ora = O.prune_layer(W[torch.tensor(rows)], G, sparsity=0.5, pattern=pattern, block=128,
+                        on_block=on_block)
+    _say(f"  oracle {time.perf_counter() - t0:.1f} s")
+    t0 = time.perf_counter()
+    Wd, Wg, mg, info = _run_gpu(W, X, sparsity=0.5, pattern=pattern, block=128)
+    _say(f"  GPU call incl. copies {time.perf_counter() - t0:.1f} s")
+    # the fp32 error of the GPU's score denominators sets what counts as a near-tie
+    U, _ = L.factor(X=X.to(DEV))
+    delta = P.denominator_error(U, 1.0 / trace.g0[0])
+    del U
+    tol = P.tie_tolerance(delta)
+    _say(f"  [H^-1]_qq deviation {delta:.2e}, near-tie bound {tol:.2e}")
+    assert delta <= 1e-3
+    rep = P.compare_pruned(Wg[rows], mg[rows], ora, 128, pattern, trace,
+                           max_flip_frac=P.MAX_FLIP_FRAC, near_tie=tol)
+    print(rep, flush=True)
+    assert rep["ok"], rep
+    assert np.all(Wg[mg] == 0.0)
+    if pattern is None:
+        assert int(mg.sum()) == info["pruned"] == ora["k_total"]
+    else:
+        assert np.all(mg.reshape(c, -1, 4).sum(axis=2) == 2)
+    W32 = torch.tensor(O.thanos_oracle._f64(W[torch.tensor(rows)]), dtype=torch.float32,
+                       device=DEV)
+    e_gpu, _ = L.reconstruction_error(W32, torch.tensor(Wg[rows], device=DEV),
+                                      G=torch.tensor(G, dtype=torch.float32, device=DEV))
+    e_ora, _ = O.reconstruction_error(W[torch.tensor(rows)], ora["W_hat"], G)
+    assert abs(e_gpu - e_ora) <= P.E_RTOL * e_ora, (e_gpu, e_ora)

@@ -172,7 +172,11 @@ def test_sequential_mlp_block_matches_oracle():
     _, Wf, m, info = _prune(L.prune_layer_factored, Wdn, Ud, params=params)
     trace = []
     O.prune_layer(Wdn, ora["G_down"], pattern=(2, 4), block=block, trace=trace)
-    rep = P.compare_pruned(Wf, m, ora["down"], block, (2, 4), trace, max_flip_frac=0.05)
+    # down's input differs from the oracle's by bf16 roundings of the propagated
+    # activations (about 0.05% of the entries by one bf16 unit, 2^-8 relative), a
+    # perturbation of G far above fp32 rounding: near-ties up to 1e-3 are allowed
+    rep = P.compare_pruned(Wf, m, ora["down"], block, (2, 4), trace, max_flip_frac=0.05,
+                           near_tie=1e-3)
     print("down", rep, flush=True)
     assert rep["ok"], rep
     assert np.all(m.reshape(d, -1, 4).sum(axis=2) == 2)

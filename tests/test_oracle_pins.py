@@ -247,8 +247,9 @@ def test_p6_block_size_one_is_sparsegpt_column_update():
 # ---------------------------------------------------------------- P7
 
 def test_p7_one_block_is_least_squares_for_final_mask():
-    """B=b, lambda -> 0: W_hat is the least-squares reconstruction for its mask
-    ("It is exact for the chosen set of deletions")."""
+    """B=b, lambda -> 0: W_hat is the least-squares optimum for its fixed mask
+    ("Pruning LLMs with Thanos", section "Contribution one: solve a selected set
+    directly": the joint solve is exact for the set it deletes)."""
     W, X = _problem(3, 10, 200, RNG_SEED + 7)
     G = O.gram(X)
     out = O.prune_layer(W, G, sparsity=0.4, block=10, lam=1e-12)
@@ -347,6 +348,35 @@ def test_p11_wanda_ordering_and_diagonal_gram():
     ref = np.zeros(64, bool)
     ref[order[:32]] = True
     np.testing.assert_array_equal(o3["mask"].ravel(), ref)
+
+
+# ---------------------------------------------------------------- P27
+
+def test_p27_relative_damping_hand_values():
+    """Relative damping is one hundredth of the mean diagonal of the undamped
+    Hessian 2XX^T (the first workload's "0.01 times the mean of diag H", read on
+    H before damping; "Pruning LLMs with Thanos", section "One deletion with
+    compensation: the OBS view", damped form). Hand values: orthogonal features
+    of squared norms 1 and 4 give diag(2G) = (2, 8), so lambda = 0.05; features of
+    squared norms 5 and 10 with an off-diagonal Gram entry give diag(2G) =
+    (10, 20), so lambda = 0.15; absolute damping passes through unchanged."""
+    X = np.array([[1.0, 0.0], [0.0, 2.0]])  # token-major: two tokens, two features
+    G = O.gram(X)
+    assert G.tolist() == [[1.0, 0.0], [0.0, 4.0]]
+    assert O.damping(G, 0.01) == pytest.approx(0.05, rel=1e-14)
+    assert O.damping(G, 0.3, relative=False) == 0.3
+    np.testing.assert_allclose(O.hessian(G, O.damping(G, 0.01)), [[2.05, 0.0], [0.0, 8.05]],
+                               rtol=1e-14)
+    X2 = np.array([[1.0, 1.0], [0.0, 3.0], [2.0, 0.0]])
+    G2 = O.gram(X2)
+    assert G2[0, 1] == 1.0  # the off-diagonal entry does not enter lambda
+    assert O.damping(G2, 0.01) == pytest.approx(0.15, rel=1e-14)
+    # the layer step reports the lambda it applied
+    out = O.prune_layer(np.array([[0.3, -0.2]]), G, sparsity=0.5, block=2)
+    assert out["lam"] == pytest.approx(0.05, rel=1e-14)
+    out = O.prune_layer(np.array([[0.3, -0.2]]), G2, sparsity=0.5, block=2, lam=0.2,
+                        lam_relative=False)
+    assert out["lam"] == 0.2
 
 
 # ---------------------------------------------------------------- P12
@@ -781,6 +811,7 @@ def _pins_pass():
         test_p23_sparsegpt_per_block_quota_and_limits(0.3, [12, 12, 6])
         test_p24_silu_and_gated_ffn_input()
         test_p26_alpha_outlier_rows()
+        test_p27_relative_damping_hand_values()
     except AssertionError:
         return False
     return True
@@ -810,7 +841,8 @@ def _bad_keys_abs_times_g(W, gdiag=None):
 @pytest.mark.parametrize("mutation", ["downdate", "sign", "nm_ties", "score_diag_H",
                                       "baseline_power", "baseline_layer_budget",
                                       "sgpt_full_inverse", "sgpt_sign", "sgpt_row_quota",
-                                      "silu_mirrored", "alpha_smallest_rows"])
+                                      "silu_mirrored", "alpha_smallest_rows",
+                                      "damping_mean_G"])
 def test_planted_mistakes_are_caught(monkeypatch, mutation):
     assert _pins_pass()
     T = O.thanos_oracle
@@ -873,6 +905,12 @@ def test_planted_mistakes_are_caught(monkeypatch, mutation):
             return orig_rows(-W0, g, 0.0) if alpha == 0 else ~orig_rows(W0, g, 1.0 - alpha)
         monkeypatch.setattr(T, "outlier_rows", smallest)
         monkeypatch.setattr(O, "outlier_rows", smallest)
+    elif mutation == "damping_mean_G":
+        # the mean diagonal of G instead of the undamped Hessian 2G
+        def half(G, lam=0.01, relative=True):
+            return float(lam) * float(np.mean(np.diag(G))) if relative else float(lam)
+        monkeypatch.setattr(T, "damping", half)
+        monkeypatch.setattr(O, "damping", half)
     elif mutation == "silu_mirrored":
         # z * sigmoid(-z): the same odd part, the wrong function
         monkeypatch.setattr(T, "silu", lambda z: np.asarray(z, np.float64)
