@@ -24,7 +24,8 @@
  *     the b inputs). X is b x n with tokens as columns; it is passed token-major
  *     as X^T [n, b] (the same bytes as column-major X), row pitch ldx elements.
  *   - The caller owns every buffer, including the workspace. The library never
- *     allocates device memory.
+ *     allocates device memory; the one entry point without a workspace argument
+ *     (th_prune_layer_noalloc) uses a fixed array the library holds from load.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
  *     The factorisation of the Hessian also runs part of its work on a stream
  *     the library creates once per device and host thread (default priority);
@@ -143,6 +144,27 @@ th_status th_prune_layer(void* W, th_dtype wdt, int64_t c, int64_t b, const void
                          int64_t* block_counts, th_stream_t stream);
 th_status th_prune_layer_workspace_size(int64_t c, int64_t b, int64_t n, int32_t have_x,
                                         const th_prune_params* p, size_t* bytes /* host */);
+
+/* th_prune_layer without a workspace argument and without allocating, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation). Its device memory is one file-scope
+ * array of TH_NOALLOC_SCRATCH_BYTES bytes that every GPU the library runs on holds
+ * from the library's load until the process ends. th_prune_layer_workspace_size
+ * bounds what a call needs (less when the caller passes W_out_f32 and mask_out):
+ * square layers up to b = 1024 fit with X given, up to about b = 2000 with a
+ * given H. Arguments,
+ * results, synchronisation and errors as th_prune_layer; a layer that needs more
+ * scratch returns TH_ERR_WORKSPACE before anything is launched. The first call on
+ * a device (per host thread) looks up the array's address and creates the
+ * factorisation's side stream and events; no call allocates memory. All calls on
+ * one GPU share its array and every call clears what must start at zero: calls
+ * that overlap on one GPU (other host threads, other streams) race and must not
+ * be made. */
+#define TH_NOALLOC_SCRATCH_BYTES (64u << 20)
+th_status th_prune_layer_noalloc(void* W, th_dtype wdt, int64_t c, int64_t b, const void* X,
+                                 th_dtype xdt, int64_t n, const float* H, const th_prune_params* p,
+                                 float* W_out_f32, uint8_t* mask_out, th_stats* stats_out,
+                                 int64_t* block_counts, th_stream_t stream);
 
 /* Inverse factor of a damped Hessian, for layers that share one input (q/k/v,
  * gate/up): H^-1 = U^T U with U upper [EXPL, "SparseGPT: Second-Order

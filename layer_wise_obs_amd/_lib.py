@@ -53,6 +53,9 @@ _SIG = {
                        _P, _P, ctypes.c_size_t, ctypes.POINTER(Stats), ctypes.POINTER(_I64), _P],
     "th_prune_layer_workspace_size": [_I64, _I64, _I64, _I32, ctypes.POINTER(PruneParams),
                                       ctypes.POINTER(ctypes.c_size_t)],
+    "th_prune_layer_noalloc": [_P, _I32, _I64, _I64, _P, _I32, _I64, _P,
+                               ctypes.POINTER(PruneParams), _P, _P, ctypes.POINTER(Stats),
+                               ctypes.POINTER(_I64), _P],
     "th_factor": [_P, _I32, _I64, _P, _I64, ctypes.c_double, _I32, _P,
                   ctypes.POINTER(ctypes.c_double), _P, ctypes.c_size_t, _P],
     "th_factor_workspace_size": [_I64, _I64, _I32, ctypes.POINTER(ctypes.c_size_t)],
@@ -220,6 +223,28 @@ def prune_layer(W, X=None, H=None, params: PruneParams | None = None, W_out=None
     """Prune W (c x b, bf16/fp32) in place; returns stats and per-block counts."""
     return _layer_call(lib().th_prune_layer, lib().th_prune_layer_workspace_size, W, X, H,
                        params, W_out, mask_out, ws)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # TH_NOALLOC_SCRATCH_BYTES in include/thanos.h
+
+
+def prune_layer_noalloc(W, X=None, H=None, params: PruneParams | None = None, W_out=None,
+                        mask_out=None) -> dict:
+    """th_prune_layer_noalloc: the layer step in the library's fixed scratch array
+    (no workspace, nothing allocated); same results as prune_layer."""
+    _require_cuda(W, X, H, W_out, mask_out)
+    if params is None:
+        params = make_params()
+    c, b = W.shape
+    n = X.shape[0] if X is not None else 0
+    stats = Stats()
+    counts = (_I64 * (-(-b // params.block)))()
+    _check(lib().th_prune_layer_noalloc(
+        _ptr(W), _dtype_code(W), c, b, _ptr(X), _dtype_code(X) if X is not None else 0, n,
+        _ptr(H), ctypes.byref(params), _ptr(W_out), _ptr(mask_out), ctypes.byref(stats), counts,
+        _stream(W.device)))
+    return {"lambda": stats.lambda_used, "pruned": stats.total_pruned, "nblocks": stats.nblocks,
+            "counts": list(counts)}
 
 
 def factor(X=None, H=None, lam=0.01, relative=True, U=None, ws=None):

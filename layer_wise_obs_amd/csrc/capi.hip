@@ -18,6 +18,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -158,6 +159,11 @@ th_status check_params(int64_t c, int64_t b, const th_prune_params* p) {
 
 bool dtype_ok(th_dtype d) { return d == TH_F32 || d == TH_BF16; }
 
+// Stands for "no workspace argument" in the shared checks (the allocation-free
+// entry point brings its own); never dereferenced.
+const char kNoWorkspaceTag = 0;
+const void* const kNoWorkspace = &kNoWorkspaceTag;
+
 // Checks shared by the layer entry points (before anything is enqueued).
 th_status check_layer_args(const void* W, th_dtype wdt, int64_t c, int64_t b, const void* X,
                            th_dtype xdt, int64_t n, const float* H, const th_prune_params* p,
@@ -170,6 +176,7 @@ th_status check_layer_args(const void* W, th_dtype wdt, int64_t c, int64_t b, co
   if (X && n < 1) return fail(TH_ERR_INVALID_ARG, "n must be >= 1");
   if (X && xdt == TH_BF16 && (b % 8 || ((uintptr_t)X & 15)))
     return fail(TH_ERR_INVALID_ARG, "bf16 X needs b % 8 == 0 and 16-byte alignment");
+  if (workspace == kNoWorkspace) return TH_OK;
   if (!workspace) return fail(TH_ERR_INVALID_ARG, "workspace is NULL");
   if ((uintptr_t)workspace & 255) return fail(TH_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   return TH_OK;
@@ -194,7 +201,7 @@ th_status inverse_factor(const void* X, th_dtype xdt, int64_t n, const float* H,
   const bool obs = p->score == TH_SCORE_OBS;
   if (X) {
     float* Hb = L.R;  // R is free until the factor is reversed into it
-    TH_HIP(hipMemsetAsync(Hb, 0, (size_t)b * b * sizeof(float), s), "memset H");
+    TH_HIP(launch_zero(Hb, (size_t)b * b * sizeof(float), s), "clear H");
     th_status a = accumulate_into(Hb, X, xdt, n, b, b, L.syrk_part, s);
     if (a != TH_OK) return a;
     TH_HIP(launch_lambda(Hb, b, p->lambda, p->lambda_is_relative, 0, L.st, s), "lambda");
@@ -216,18 +223,18 @@ th_status finish_layer(const PruneLayout& L, int64_t nblk, th_stats* stats_out,
                        int64_t* block_counts, hipStream_t s) {
   DevState host;
   TH_HIP(hipMemcpyAsync(&host, L.st, offsetof(DevState, hist), hipMemcpyDeviceToHost, s), "state");
-  std::vector<unsigned long long> counts((size_t)nblk);
-  TH_HIP(hipMemcpyAsync(counts.data(), L.counts, nblk * sizeof(unsigned long long),
-                        hipMemcpyDeviceToHost, s),
-         "counts");
+  // counts are non-negative and below 2^63: the same bytes as int64_t
+  static_assert(sizeof(unsigned long long) == sizeof(int64_t), "count width");
+  if (block_counts)
+    TH_HIP(hipMemcpyAsync(block_counts, L.counts, nblk * sizeof(unsigned long long),
+                          hipMemcpyDeviceToHost, s),
+           "counts");
   TH_HIP(hipStreamSynchronize(s), "sync");
   if (stats_out) {
     stats_out->lambda_used = host.lambda;
     stats_out->total_pruned = host.pruned;
     stats_out->nblocks = nblk;
   }
-  if (block_counts)
-    for (int64_t i = 0; i < nblk; ++i) block_counts[i] = (int64_t)counts[i];
   if (host.nonfinite) return fail(TH_ERR_NONFINITE, "non-finite value in W or diag(H)");
   if (host.not_spd) return fail(TH_ERR_NOT_SPD, "damped Hessian is not positive definite");
   return TH_OK;
@@ -237,8 +244,8 @@ th_status finish_layer(const PruneLayout& L, int64_t nblk, th_stats* stats_out,
 th_status begin_layer(const PruneLayout& L, const void* W, th_dtype wdt, int64_t c, int64_t b,
                       const th_prune_params* p, float* Wf, hipStream_t s) {
   const int64_t nblk = cdiv(b, p->block);
-  TH_HIP(hipMemsetAsync(L.st, 0, sizeof(DevState), s), "memset state");
-  TH_HIP(hipMemsetAsync(L.counts, 0, nblk * sizeof(unsigned long long), s), "memset counts");
+  TH_HIP(launch_zero(L.st, sizeof(DevState), s), "clear state");
+  TH_HIP(launch_zero(L.counts, nblk * sizeof(unsigned long long), s), "clear counts");
   TH_HIP(launch_to_f32(W, wdt, c * b, Wf, L.st, s), "W to fp32");
   return TH_OK;
 }
@@ -387,6 +394,59 @@ th_status th_prune_layer(void* W, th_dtype wdt, int64_t c, int64_t b, const void
   return finish_layer(L, nblk, stats_out, block_counts, s);
 }
 
+// --------------------------------------------- allocation-free layer step
+
+namespace {
+// Device memory of the allocation-free entry point: a file-scope array that each
+// GPU holds from the library's load until the process ends. Host code never uses
+// its name as an address: the per-device address comes from hipGetSymbolAddress.
+constexpr size_t kScratchBytes = (size_t)TH_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// The scratch array's address on the current device, looked up once per device
+// (with that device current) and kept.
+th_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  TH_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(TH_ERR_INVALID_ARG, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    TH_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!p || ((uintptr_t)p & 255)) return fail(TH_ERR_HIP, "scratch address not 256-byte aligned");
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return TH_OK;
+}
+}  // namespace
+
+th_status th_prune_layer_noalloc(void* W, th_dtype wdt, int64_t c, int64_t b, const void* X,
+                                 th_dtype xdt, int64_t n, const float* H,
+                                 const th_prune_params* p, float* W_out_f32, uint8_t* mask_out,
+                                 th_stats* stats_out, int64_t* block_counts, th_stream_t stream) {
+  th_status chk = check_layer_args(W, wdt, c, b, X, xdt, n, H, p, kNoWorkspace);
+  if (chk != TH_OK) return chk;
+  const size_t need = layout_prune(nullptr, c, b, n, X != nullptr, p, W_out_f32 == nullptr,
+                                   mask_out == nullptr, xdt)
+                          .bytes;
+  if (need > kScratchBytes) {
+    g_last_error = "the layer needs " + std::to_string(need) +
+                   " bytes of scratch; th_prune_layer_noalloc holds " +
+                   std::to_string(kScratchBytes) + " (use th_prune_layer with a workspace)";
+    return TH_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  th_status st = scratch_on_current_device(&ws);
+  if (st != TH_OK) return st;
+  return th_prune_layer(W, wdt, c, b, X, xdt, n, H, p, W_out_f32, mask_out, ws, kScratchBytes,
+                        stats_out, block_counts, stream);
+}
+
 th_status th_prune_sparsegpt_workspace_size(int64_t c, int64_t b, int64_t n, int32_t have_x,
                                             const th_prune_params* p, size_t* bytes) {
   if (!bytes) return fail(TH_ERR_INVALID_ARG, "bytes is NULL");
@@ -513,7 +573,7 @@ th_status th_factor(const void* X, th_dtype xdt, int64_t n, const float* H, int6
   L.R = U;  // H from X accumulates in U, which then receives the factor
   L.P = F.P;
   L.syrk_part = F.syrk_part;
-  TH_HIP(hipMemsetAsync(F.st, 0, sizeof(DevState), s), "memset state");
+  TH_HIP(launch_zero(F.st, sizeof(DevState), s), "clear state");
   th_status pre = inverse_factor(X, xdt, n, H, b, &p, L, s);
   if (pre != TH_OK) return pre;
   DevState host;
@@ -619,9 +679,9 @@ th_status th_prune_layer_alpha(void* W, th_dtype wdt, int64_t c, int64_t b, cons
   hipStream_t s = (hipStream_t)stream;
   const int64_t nblk = cdiv(b, p->block);
 
-  TH_HIP(hipMemsetAsync(L.st, 0, sizeof(DevState), s), "memset state");
-  TH_HIP(hipMemsetAsync(A.sel, 0, sizeof(DevState), s), "memset selection state");
-  TH_HIP(hipMemsetAsync(L.counts, 0, nblk * sizeof(unsigned long long), s), "memset counts");
+  TH_HIP(launch_zero(L.st, sizeof(DevState), s), "clear state");
+  TH_HIP(launch_zero(A.sel, sizeof(DevState), s), "clear selection state");
+  TH_HIP(launch_zero(L.counts, nblk * sizeof(unsigned long long), s), "clear counts");
   // G_qq: column norms of X, or (H_qq - lambda)/2 of a damped H
   if (X) {
     TH_HIP(launch_column_sq_norms(X, xdt, n, b, b, A.colsq, A.gdiag, s), "column norms");
@@ -706,7 +766,7 @@ th_status th_reconstruction_error(const void* W, const void* What, th_dtype wdt,
   double* out = cv.take<double>(2);
   double scale = 1.0;
   if (X) {
-    TH_HIP(hipMemsetAsync(Gb, 0, (size_t)b * b * sizeof(float), s), "memset G");
+    TH_HIP(launch_zero(Gb, (size_t)b * b * sizeof(float), s), "clear G");
     th_status a = accumulate_into(Gb, X, xdt, n, b, b, nullptr, s);  // 2G, lower
     if (a != TH_OK) return a;
     TH_HIP(launch_damp_mirror(Gb, b, 0.f, s), "mirror");

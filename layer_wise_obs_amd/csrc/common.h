@@ -200,6 +200,7 @@ hipError_t launch_scatter_rows(void* W, th_dtype wdt, int64_t c, int64_t b, cons
 hipError_t launch_update(float* W, int64_t c, int64_t b, int64_t r0, int64_t K, int64_t ldz,
                          int64_t col0, int64_t col_end, const float* Z, const float* R,
                          const uint8_t* mask, int64_t mask_j0, int64_t mask_w, hipStream_t s);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_to_f32(const void* src, th_dtype dt, int64_t count, float* dst,
                          DevState* st, hipStream_t s);
 hipError_t launch_from_f32(const float* src, int64_t count, th_dtype dt, void* dst,

@@ -89,6 +89,17 @@ __global__ void to_f32_kernel(const void* __restrict__ src, int dt, int64_t n,
   if (bad && st) st->nonfinite = 1;
 }
 
+// Clears memory with vector stores (16 bytes per thread and step; a byte tail):
+// used instead of a runtime memset so that every step of a layer call is a kernel.
+__global__ void zero_kernel(uint4* __restrict__ p16, int64_t n16, unsigned char* __restrict__ tail,
+                            int ntail) {
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p16[i] = z;
+  if (blockIdx.x == 0 && (int)threadIdx.x < ntail) tail[threadIdx.x] = 0;
+}
+
 __global__ void from_f32_kernel(const float* __restrict__ src, int64_t n, int dt,
                                 void* __restrict__ dst) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
@@ -186,6 +197,16 @@ hipError_t launch_to_f32(const void* src, th_dtype dt, int64_t count, float* dst
                          hipStream_t s) {
   hipLaunchKernelGGL(to_f32_kernel, dim3(ew_grid(count)), dim3(256), 0, s, src, (int)dt, count,
                      dst, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return hipSuccess;
+  if ((uintptr_t)p & 15) return hipErrorInvalidValue;  // callers pass 256-byte aligned buffers
+  const int64_t n16 = (int64_t)(bytes / 16);
+  const int ntail = (int)(bytes % 16);
+  hipLaunchKernelGGL(zero_kernel, dim3(ew_grid(n16 > 0 ? n16 : 1)), dim3(256), 0, s, (uint4*)p, n16,
+                     (unsigned char*)p + n16 * 16, ntail);
   return hipGetLastError();
 }
 

@@ -25,7 +25,8 @@ def test_header_declares_the_path():
                  "th_prune_sparsegpt", "th_prune_sparsegpt_workspace_size", "th_factor",
                  "th_factor_workspace_size", "th_prune_layer_factored",
                  "th_prune_layer_factored_workspace_size", "th_gated_ffn_input",
-                 "th_prune_layer_alpha", "th_prune_layer_alpha_workspace_size"):
+                 "th_prune_layer_alpha", "th_prune_layer_alpha_workspace_size",
+                 "th_prune_layer_noalloc"):
         assert must in names
 
 
@@ -198,3 +199,19 @@ def test_alpha_arguments_are_rejected_before_any_launch():
     args[9] = 0.1
     args[7] = fake  # both X and H
     assert L.th_prune_layer_alpha(*args) == 1
+
+
+def test_noalloc_rejects_layers_beyond_its_scratch_before_any_launch():
+    """The allocation-free entry point checks the layer's scratch need against its
+    fixed array on the host and answers TH_ERR_WORKSPACE without touching a GPU."""
+    L = _lib.lib()
+    p = _lib.make_params(pattern=(2, 4))
+    dummy = ctypes.c_void_p(256)
+    st = L.th_prune_layer_noalloc(dummy, 1, 4096, 4096, None, 1, 0, dummy, ctypes.byref(p), None,
+                                  None, None, None, None)
+    assert st == 4
+    msg = L.th_last_error().decode()
+    assert "scratch" in msg and str(_lib.NOALLOC_SCRATCH_BYTES) in msg
+    # argument errors come first, as for th_prune_layer
+    assert L.th_prune_layer_noalloc(None, 1, 64, 64, None, 1, 0, dummy, ctypes.byref(p), None,
+                                    None, None, None, None) == 1
