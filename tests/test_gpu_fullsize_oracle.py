@@ -13,9 +13,10 @@ unstructured layers also the per-block and per-row counts and the layer's error.
 Checks (bars of the method's parity):
 * masks row by row; a sampled row may differ only if, at its first differing
   block, every differing decision is an fp32 near-tie in the oracle's own scores
-  (relative gap within TIE_MARGIN times the measured fp32 deviation of the
-  GPU factor's [H^-1]_qq from the oracle's), and at most MAX_FLIP_FRAC of the
-  sampled rows;
+  (relative gap <= NEAR_TIE_WIDE) and the row's error matches the oracle's row
+  (within ROW_E_RTOL: the other choice was as good), and at most MAX_FLIP_FRAC of
+  the sampled rows;
+* the GPU factor's [H^-1]_qq within 1e-3 of the oracle's diag(H^-1);
 * W_hat within 1e-3 relative (Frobenius) on the sampled rows whose masks agree;
 * the error of those rows within 1e-3 of the oracle's; unstructured: the whole
   layer's error within 1e-3 of the oracle's, the exact global budget, and the
@@ -109,13 +110,16 @@ def test_fullsize_against_oracle(name):
     torch.cuda.synchronize()
     _say(f"  GPU layer step {1e3 * (time.perf_counter() - t0):.1f} ms")
     assert abs(info["lambda"] - float(g["lam"])) <= 1e-5 * float(g["lam"])
-    # the fp32 error of the GPU's score denominators sets what counts as a near-tie
+    # the fp32 factor at full size: its [H^-1]_qq against the oracle's
     U, _ = L.factor(X=X) if X is not None else L.factor(H=H, lam=lam, relative=False)
     delta = P.denominator_error(U, g["diag_inv"])
     del U
-    tol = P.tie_tolerance(delta)
-    _say(f"  [H^-1]_qq deviation {delta:.2e}, near-tie bound {tol:.2e}")
+    _say(f"  [H^-1]_qq deviation {delta:.2e}")
     assert delta <= 1e-3
+    tol = P.NEAR_TIE_WIDE
+    G = H.clone()
+    G.diagonal().sub_(lam)
+    G.mul_(0.5)
 
     rows = g["rows"].astype(np.int64)
     ridx = torch.tensor(rows, device=DEV)
@@ -124,15 +128,25 @@ def test_fullsize_against_oracle(name):
     w_gpu = Wout[ridx].cpu().numpy()
     w_ora = g["what_rows"]
     same = np.all(m_gpu == m_ora, axis=1)
-    worst = 0.0
+    worst, worst_e = 0.0, 0.0
     for i in np.flatnonzero(~same):
         d = np.flatnonzero(m_gpu[i] != m_ora[i])
         ok, v = _flip_explained(d, g["gap_rows"][i] if nm else g["dist_rows"][i], cfg.block, tol,
                                 pat[2] if nm else None)
         worst = max(worst, v)
         assert ok, (name, int(rows[i]), int(d[0]), v)
+        if nm:  # the other path is as good: the row's own error against the oracle's row
+            ki = torch.tensor([int(rows[i])], device=DEV)
+            e_i, _ = L.reconstruction_error(W0[ki].float().contiguous(), Wout[ki].contiguous(),
+                                            G=G)
+            rel = abs(e_i - float(g["e_row"][i])) / float(g["e_row"][i])
+            worst_e = max(worst_e, rel)
+            assert rel <= P.ROW_E_RTOL, (name, int(rows[i]), rel)
+        # unstructured rows trade budget through the global selection: the layer's
+        # error is compared below
     nflip = int((~same).sum())
-    _say(f"  sampled rows {len(rows)}, flipped {nflip} (largest oracle gap at a flip {worst:.2e})")
+    _say(f"  sampled rows {len(rows)}, flipped {nflip} (largest oracle gap at a flip {worst:.2e}, "
+         f"largest row-error deviation of a flipped row {worst_e:.2e})")
     assert nflip <= max(1, int(P.MAX_FLIP_FRAC * len(rows)))
     err_w = P.rel_fro(w_gpu[same], w_ora[same].astype(np.float64))
     _say(f"  W_hat on agreeing rows: {err_w:.2e} relative")
@@ -140,9 +154,6 @@ def test_fullsize_against_oracle(name):
     assert np.all(w_gpu[m_gpu] == 0.0)
 
     # error of the agreeing sampled rows, from G = (H - lambda I) / 2
-    G = H.clone()
-    G.diagonal().sub_(lam)
-    G.mul_(0.5)
     sidx = torch.tensor(rows[same], device=DEV)
     e_gpu, _ = L.reconstruction_error(W0[sidx].float().contiguous(), Wout[sidx].contiguous(), G=G)
     e_ora = float(np.sum(g["e_row"][same]))
@@ -162,14 +173,15 @@ def test_fullsize_against_oracle(name):
         assert abs(e_all - float(g["e_all"])) <= P.E_RTOL * float(g["e_all"])
         # cumulative per-block counts: a decision can differ only within the
         # oracle's near-tie population of each block's threshold
-        w = min([i for i, x in enumerate(WINDOWS) if x >= tol] or [len(WINDOWS) - 1])
+        # (window 1e-5: the measured deviation of the score denominators is ~1e-5)
         c_gpu = np.cumsum(np.asarray(info["counts"], np.int64))
         c_ora = np.cumsum(g["counts"])
-        allow = np.cumsum(g["near_counts"][:, w])
         diff = np.abs(c_gpu - c_ora)
-        _say(f"  cumulative block counts: max |diff| {int(diff.max())}, allowance at that block "
-             f"{int(allow[int(diff.argmax())])}")
-        assert np.all(diff <= allow)
+        allows = np.cumsum(g["near_counts"], axis=0)
+        at = int(diff.argmax())
+        _say(f"  cumulative block counts: max |diff| {int(diff.max())} at block {at}; oracle "
+             f"near-tie population there (1e-6..1e-3): {allows[at].tolist()}")
+        assert np.all(diff <= allows[:, WINDOWS.index(1e-5)])
         rc = mk.sum(dim=1).cpu().numpy()
         _say(f"  rows with the oracle's count: {np.mean(rc == g['row_counts']):.4f}")
     del W, Wout, mask, G
