@@ -69,26 +69,49 @@ def syrk_traffic():
         return None
 
 
-def cpu_baseline(X, W, c, b, n, pattern, block, lam_rel, sparsity=0.5):
-    """fp64 oracle on a bounded sample, scaled to seconds per layer.
+def _host_facts():
+    """Cores this process may run on, the CPU model and the BLAS numpy uses."""
+    cores = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas, threads = "unknown", cores
+    try:
+        import numpy  # noqa: F401  (loads the BLAS that threadpoolctl then reports)
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            blas = (f"{info[0].get('internal_api')} {info[0].get('version')} "
+                    f"({info[0].get('architecture')} kernels)")
+            threads = max(i.get("num_threads", 1) for i in info)
+    except Exception:
+        pass
+    return cores, model, blas, threads
 
-    Sample: G from the first 1024 tokens (scaled by n/1024); the Cholesky check
-    and LU inverse of a damped 11008 x 11008 H at full size (unscaled); the first
-    3 column blocks of the block loop with all rows, scaled by the modelled flops
-    of all blocks (Schur downdate 2|F'|^2 B + 2|F'| B^2, update 2 c B |F|,
-    per-row solves c s^3/3)."""
+
+def cpu_baseline(X, W, c, b, n, pattern, block, lam_rel, sparsity=0.5):
+    """fp64 oracle on a bounded sample of the same workload, scaled to seconds per layer.
+
+    Measured: G from the first n/8 tokens (12.5% of the stream; scaled by 8), the
+    Cholesky check and LU inverse of the damped b x b H at full size, and the
+    first 3 column blocks of the block loop with all rows. Scaled: the G time by
+    the token ratio, the block time by the modelled flops of all blocks (Schur
+    downdate 2|F'|^2 B + 2|F'| B^2, update 2 c B |F|, per-row solves c s^3/3)."""
     import numpy as np
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
-    n_s = 1024
-    Xs = X[:n_s].float().cpu().numpy()
+    cores, model, blas, threads = _host_facts()
+    n_s = max(1024, n // 8)
     t0 = time.perf_counter()
-    G = O.gram(Xs)
-    t_g = (time.perf_counter() - t0) * (n / n_s)
+    G = np.zeros((b, b))
+    for a in range(0, n_s, 8192):  # copied to the host and summed chunk by chunk
+        G += O.gram(X[a:min(n_s, a + 8192)].cpu())
+    t_g_meas = time.perf_counter() - t0
+    t_g = t_g_meas * (n / n_s)
     Wn = W.float().cpu().numpy()
     k_s = 3
     t0 = time.perf_counter()
@@ -114,10 +137,14 @@ def cpu_baseline(X, W, c, b, n, pattern, block, lam_rel, sparsity=0.5):
     t_blocks = t_blocks_s * total / sampled
     value = t_g + t_inv + t_blocks
     return {"value": value, "unit": "s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"G on {n_s} of {n} tokens (x{n / n_s:.0f}); Cholesky check + LU inverse "
-                       f"at full b={b}; first {k_s} of {-(-b // block)} blocks with all {c} rows, "
-                       f"scaled by modelled flops (x{total / sampled:.1f}); phases s: "
-                       f"G {t_g:.1f}, inverse {t_inv:.1f}, blocks {t_blocks:.1f}")}
+            "sample": (f"G on {n_s} of {n} tokens ({100.0 * n_s / n:.1f}%, x{n / n_s:g}); Cholesky "
+                       f"check + LU inverse at full b={b}; first {k_s} of {-(-b // block)} blocks "
+                       f"with all {c} rows, scaled by modelled flops (x{total / sampled:.1f})"),
+            "measured_s": {"G_sample": round(t_g_meas, 2), "inverse": round(t_inv, 2),
+                           "blocks_sample": round(t_blocks_s, 2)},
+            "scaled_s": {"G": round(t_g, 1), "inverse": round(t_inv, 1), "blocks": round(t_blocks, 1)},
+            "host": {"cores_available": cores, "cpu": model, "blas": blas,
+                     "blas_threads": threads}}
 
 
 def main():
