@@ -315,7 +315,8 @@ th_status th_prune_baseline(void* W, th_dtype wdt, int64_t c, int64_t b, th_base
 /* U = upper-triangular factor with H^-1 = U^T U (U = chol_upper(H^-1), the factor
  * [EXPL, "SparseGPT"] computes once per layer), from a damped, full symmetric H
  * [b,b] fp32. U [b,b] fp32 (strict lower triangle zero). workspace: >= b*b*4 +
- * 2*ceil(b/128)*128*256*4 + 65536 bytes (TH_ERR_WORKSPACE if smaller). Returns
+ * 2*ceil(b/128)*128*256*4 + 2*2*3*256*ceil(b/256)*256 + 65536 bytes
+ * (TH_ERR_WORKSPACE if smaller). Returns
  * TH_ERR_NOT_SPD on a non-positive pivot.
  * Synchronises. */
 th_status th_debug_factor(const float* H, int64_t b, float* U, void* workspace,

@@ -25,12 +25,16 @@
 //   columns k+2, k+3) run on the caller's stream, the rest on a second stream as
 //   a persistent kernel of one workgroup per compute unit, so that the next
 //   pair's diagonal blocks, panels and row/column update (a chain of small,
-//   latency-bound kernels) run beside the bulk of the update.
+//   latency-bound kernels) run beside the bulk of the update. The rest set reads
+//   the pair's operands once more, pre-split into bf16 planes (rest_x3.h): its
+//   tiles are a symmetric rank-256 product like the Hessian's syrk and run on
+//   that kernel's pipeline, 256 x 256 per workgroup.
 // The panel and trailing GEMMs run on the bf16 matrix cores with three-way split
 // fp32 operands (gemm_x3.h: errors of the order of fp32 accumulation, at about a
 // third of the fp32 matrix-core time); the diagonal blocks stay in fp32.
 // At the end S holds L^-1 (lower); U is the element-wise reversal of S.
 #include "gemm_x3.h"
+#include "rest_x3.h"
 
 namespace th {
 
@@ -437,11 +441,6 @@ __host__ __device__ inline int64_t look_tiles(int k, int nblk) {
   if (kk + 2 < nblk) n += 2 * (int64_t)(nblk - kk - 2); // columns kk, kk+1 below
   return n;
 }
-__host__ __device__ inline int64_t rest_tiles(int k, int nblk) {
-  const int64_t lo = k + 4, hi = nblk - 1;  // rows i in [k+4, nblk-1], i-1 tiles each
-  if (lo > hi) return 0;
-  return (hi + lo - 2) * (hi - lo + 1) / 2;
-}
 
 __global__ __launch_bounds__(256, 2) void trailing_look_kernel(float* __restrict__ S, int64_t b,
                                                             int k, int nblk,
@@ -463,22 +462,6 @@ __global__ __launch_bounds__(256, 2) void trailing_look_kernel(float* __restrict
   pair_tile(S, b, k, i, j, P, smem);
 }
 
-// Persistent over the rest set: workgroup w takes tiles w, w + gridDim.x, ...
-// (row-major over rows i >= k+4, skipping columns k+2 and k+3).
-__global__ __launch_bounds__(256, 2) void trailing_rest_kernel(float* __restrict__ S, int64_t b,
-                                                            int k, int nblk, int64_t ntiles,
-                                                            const float* __restrict__ P) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kX3LdsBytes];
-  const int kk = k + 2;
-  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    int64_t rem = t;
-    int i = kk + 2;
-    while (rem >= i - 1) { rem -= i - 1; ++i; }
-    const int j = (int)rem < kk ? (int)rem : (int)rem + 2;
-    pair_tile(S, b, k, i, j, P, smem);
-    __syncthreads();  // the next tile's staging reuses the LDS planes
-  }
-}
 
 // U[a][c] = S[b-1-a][b-1-c] for c >= a, 0 below the diagonal (a flat reversal).
 __global__ void reverse_kernel(const float* __restrict__ S, float* __restrict__ U, int64_t b) {
@@ -528,7 +511,10 @@ hipError_t side_stream(SideStream*& out) {
 
 }  // namespace
 
-size_t chol_panel_floats(int64_t b) { return 2 * (size_t)cdiv(b, kNb) * kNb * kPP2; }
+// Two panel buffers, then two pre-split Y buffers (bf16, x3_y_elems each).
+size_t chol_panel_floats(int64_t b) {
+  return 2 * (size_t)cdiv(b, kNb) * kNb * kPP2 + (size_t)x3_y_elems(b);
+}
 
 hipError_t launch_chol_inv_inplace(float* S, int64_t b, float* P, DevState* st, hipStream_t s) {
   const int nblk = (int)cdiv(b, kNb);
@@ -536,8 +522,11 @@ hipError_t launch_chol_inv_inplace(float* S, int64_t b, float* P, DevState* st, 
   hipError_t e = side_stream(side);
   if (e != hipSuccess) return e;
   // Two panel buffers: pair p writes buffer p % 2 while the rest set of pair
-  // p - 1 may still read the other one.
+  // p - 1 may still read the other one; the same for the split Y buffers.
   const size_t pbuf = (size_t)cdiv(b, kNb) * kNb * kPP2;
+  unsigned short* Ybase = (unsigned short*)(P + 2 * pbuf);
+  const int64_t ldy = x3_ldy(b);
+  const int npr = (int)cdiv(nblk, 2);
   auto factor_and_panel = [&](int k, float* Pp) -> hipError_t {
     const int64_t k0 = (int64_t)k * kNb;
     const int nbk = (int)((b - k0) < kNb ? (b - k0) : kNb);
@@ -570,13 +559,26 @@ hipError_t launch_chol_inv_inplace(float* S, int64_t b, float* P, DevState* st, 
       if ((e = hipStreamWaitEvent(s, side->rest, 0)) != hipSuccess) return e;
       rest_pending = false;
     }
-    const int64_t nrest = rest_tiles(k, nblk);
+    // rest set: 256 x 256 tiles over block-row pairs from (k+4)/2 (pair-row pi has
+    // pi tiles: pair-columns 0..pi without (k+2)/2)
+    int64_t nrest = 0;
+    for (int pi = (k + 4) / 2; pi < npr; ++pi) nrest += pi;
     if (nrest > 0) {
+      // Y is built on the second stream too: rows k, k+1 of S and the pair's panel
+      // buffer are final once the chain reaches this point, and no later step of
+      // the chain writes them before the rest set has run
+      unsigned short* Yp = Ybase + (size_t)(pair & 1) * (size_t)x3_y_elems(b);
       if ((e = hipEventRecord(side->chain, s)) != hipSuccess) return e;
       if ((e = hipStreamWaitEvent(side->s2, side->chain, 0)) != hipSuccess) return e;
-      const int64_t grid = nrest < side->slots ? nrest : side->slots;
-      hipLaunchKernelGGL(trailing_rest_kernel, dim3((unsigned)grid), dim3(256), 0, side->s2, S, b,
-                         k, nblk, nrest, Pp);
+      hipLaunchKernelGGL(ybuild_kernel, dim3((unsigned)(ldy / 64), kX3Rows / 64), dim3(256), 0,
+                         side->s2, S, b, k, Pp, Yp, ldy);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      // one workgroup per compute unit on 7/8 of the units: the rest keep room for
+      // the next pair's chain (1/4, 1/16 and none were slower on the 11008 layer)
+      const int64_t slots = side->slots - side->slots / 8;
+      const int64_t grid = nrest < slots ? nrest : slots;
+      hipLaunchKernelGGL(rest_x3_kernel, dim3((unsigned)grid), dim3(256), 0, side->s2, S, b, k, Yp,
+                         ldy, nrest);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       if ((e = hipEventRecord(side->rest, side->s2)) != hipSuccess) return e;
       rest_pending = true;
