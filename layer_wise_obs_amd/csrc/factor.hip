@@ -477,14 +477,16 @@ __global__ void reverse_kernel(const float* __restrict__ S, float* __restrict__ 
 
 namespace {
 
-// A second stream and two events per device and host thread (created on first
-// use, kept until the process ends). Default priority, non-blocking. `slots` is
-// the rest set's persistent grid: one workgroup per compute unit, so that every
-// unit keeps room (LDS and registers) for one workgroup of the next pair's
-// diagonal factor, panels and row/column update, which run beside it.
+// Two more streams and three events per device and host thread (created on
+// first use, kept until the process ends). Default priority, non-blocking. s2
+// runs the rest sets one after the other; s3 builds each pair's split operands
+// while the previous rest set still runs. `slots` is the rest set's persistent
+// grid: one workgroup per compute unit, so that every unit keeps room (LDS and
+// registers) for one workgroup of the next pair's diagonal factor, panels and
+// row/column update, which run beside it.
 struct SideStream {
-  hipStream_t s2 = nullptr;
-  hipEvent_t chain = nullptr, rest = nullptr;
+  hipStream_t s2 = nullptr, s3 = nullptr;
+  hipEvent_t chain = nullptr, built = nullptr, rest = nullptr;
   int slots = 0;
 };
 
@@ -501,7 +503,9 @@ hipError_t side_stream(SideStream*& out) {
     if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
       return e;
     if ((e = hipEventCreateWithFlags(&t.chain, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&t.built, hipEventDisableTiming)) != hipSuccess) return e;
     if ((e = hipEventCreateWithFlags(&t.rest, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipStreamCreateWithFlags(&t.s3, hipStreamNonBlocking)) != hipSuccess) return e;
     if ((e = hipStreamCreateWithFlags(&t.s2, hipStreamNonBlocking)) != hipSuccess) return e;
     t.slots = ncu > 0 ? ncu : 1;
   }
@@ -542,9 +546,18 @@ hipError_t launch_chol_inv_inplace(float* S, int64_t b, float* P, DevState* st, 
   };
   // Steps in pairs (k, k+1): block row and column k+1 first, then one K = 256
   // update of everything else, split into the look-ahead set (stream s) and the
-  // rest set (side stream). The next pair's diagonal blocks and panels wait only
-  // for the look-ahead set; the next pair's update waits for the rest set.
-  // An odd last block is a single step.
+  // rest set (stream s2, on operands split on stream s3). The next pair's
+  // diagonal blocks and panels wait only for the look-ahead set; the next pair's
+  // look-ahead set waits for the rest set. The rest sets follow each other on s2
+  // without a cross-stream wait: each waits only for its operands, which are
+  // built beside the previous rest set. An odd last block is a single step.
+  //
+  // Buffer reuse: Y[p % 2] is written by the split of pair p after the chain of
+  // pair p, which follows the look-ahead set of pair p - 1, which waited for the
+  // rest set of pair p - 2 (the last reader of Y[p % 2]); P[p % 2] is rewritten
+  // by the chain of pair p + 2, after the look-ahead set of pair p + 1, which
+  // waited for the rest set of pair p, which waited for the split of pair p (the
+  // last reader of P[p % 2] besides the look-ahead set of pair p on stream s).
   bool rest_pending = false;
   for (int k = 0, pair = 0; k < nblk; k += 2, ++pair) {
     float* Pp = P + (size_t)(pair & 1) * pbuf;
@@ -554,25 +567,23 @@ hipError_t launch_chol_inv_inplace(float* S, int64_t b, float* P, DevState* st, 
                        Pp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = factor_and_panel(k + 1, Pp)) != hipSuccess) return e;
-    // the previous pair's rest set covers tiles of this pair's look-ahead set
-    if (rest_pending) {
-      if ((e = hipStreamWaitEvent(s, side->rest, 0)) != hipSuccess) return e;
-      rest_pending = false;
-    }
     // rest set: 256 x 256 tiles over block-row pairs from (k+4)/2 (pair-row pi has
     // pi tiles: pair-columns 0..pi without (k+2)/2)
     int64_t nrest = 0;
     for (int pi = (k + 4) / 2; pi < npr; ++pi) nrest += pi;
+    bool rest_now = false;
     if (nrest > 0) {
-      // Y is built on the second stream too: rows k, k+1 of S and the pair's panel
-      // buffer are final once the chain reaches this point, and no later step of
-      // the chain writes them before the rest set has run
+      // rows k, k+1 of S and the pair's panel buffer are final once the chain
+      // reaches this point: no later step of the chain writes them before the
+      // rest set has run, and the previous rest set does not touch them
       unsigned short* Yp = Ybase + (size_t)(pair & 1) * (size_t)x3_y_elems(b);
       if ((e = hipEventRecord(side->chain, s)) != hipSuccess) return e;
-      if ((e = hipStreamWaitEvent(side->s2, side->chain, 0)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(side->s3, side->chain, 0)) != hipSuccess) return e;
       hipLaunchKernelGGL(ybuild_kernel, dim3((unsigned)(ldy / 64), kX3Rows / 64), dim3(256), 0,
-                         side->s2, S, b, k, Pp, Yp, ldy);
+                         side->s3, S, b, k, Pp, Yp, ldy);
       if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = hipEventRecord(side->built, side->s3)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(side->s2, side->built, 0)) != hipSuccess) return e;
       // one workgroup per compute unit on 7/8 of the units: the rest keep room for
       // the next pair's chain (1/4, 1/16 and none were slower on the 11008 layer)
       const int64_t slots = side->slots - side->slots / 8;
@@ -580,6 +591,14 @@ hipError_t launch_chol_inv_inplace(float* S, int64_t b, float* P, DevState* st, 
       hipLaunchKernelGGL(rest_x3_kernel, dim3((unsigned)grid), dim3(256), 0, side->s2, S, b, k, Yp,
                          ldy, nrest);
       if ((e = hipGetLastError()) != hipSuccess) return e;
+      rest_now = true;
+    }
+    // the previous pair's rest set covers tiles of this pair's look-ahead set
+    if (rest_pending) {
+      if ((e = hipStreamWaitEvent(s, side->rest, 0)) != hipSuccess) return e;
+      rest_pending = false;
+    }
+    if (rest_now) {
       if ((e = hipEventRecord(side->rest, side->s2)) != hipSuccess) return e;
       rest_pending = true;
     }
