@@ -269,6 +269,7 @@ th_status prune_blocks(const PruneLayout& L, int64_t c, int64_t b, const th_prun
   const int64_t ldz = z_pitch(b, p);
   // the layer's budget k_total = round-half-even(p c b) joins at the first block
   const long long k_total = unstr ? (long long)std::nearbyint(p->sparsity * (double)c * (double)b) : 0;
+  bool next_digit_done = false;  // the previous update counted this block's first digit
   for (int64_t blk = 0; blk < nblk; ++blk) {
     const int64_t j0 = blk * B;
     const int64_t Bb = (b - j0) < B ? (b - j0) : B;
@@ -276,16 +277,39 @@ th_status prune_blocks(const PruneLayout& L, int64_t c, int64_t b, const th_prun
     if (unstr) {
       // the global selection scores every active column, so W[:, F] is updated in full
       const float* g = obs ? L.D + blk * b : L.gW;
-      TH_HIP(launch_select_init(L.st, blk == 0 ? k_total : 0, (long long)(c * (b - j0)), s),
-             "select init");
-      for (int pass = 0; pass < 6; ++pass) {
+      int first_pass = 0;
+      if (!next_digit_done) {
+        TH_HIP(launch_select_init(L.st, blk == 0 ? k_total : 0, (long long)(c * (b - j0)), s),
+               "select init");
+      } else {
+        // this block's selection was set up before the previous block's update, which
+        // also counted the first digit of its keys: the first pick needs no pass
+        TH_HIP(launch_select_pick(L.st, s), "select pick");
+        first_pass = 1;
+      }
+      for (int pass = first_pass; pass < 6; ++pass) {
         TH_HIP(launch_select_pass(Wf, c, b, j0, b, g, L.st, s), "select pass");
         TH_HIP(launch_select_pick(L.st, s), "select pick");
       }
       TH_HIP(launch_solve_unstructured(Wf, c, b, j0, B, L.R, Nb, g, L.Z, mask, L.st,
                                        L.counts + blk, s),
              "solve");
-      TH_HIP(launch_update(Wf, c, b, j0, Bb, B, j0, b, L.Z, L.R, mask, j0, Bb, s), "update");
+      const int64_t jn = j0 + Bb;  // the next block's active region starts here
+      // On 128 x 128 tiles the update also counts the first key digit of the next
+      // block (it writes all of that block's active region); on the small 64 x 64
+      // tiles of the late blocks a separate pass is cheaper.
+      next_digit_done = jn < b && update_large_tiles(c, j0, b);
+      if (next_digit_done) {
+        // after the solve (it reads this block's threshold and adds to the pruned
+        // count), before the update that fills the histogram
+        TH_HIP(launch_select_init(L.st, 0, (long long)(c * (b - jn)), s), "select init");
+        unsigned int* hist = (unsigned int*)((char*)L.st + offsetof(DevState, hist));
+        TH_HIP(launch_update(Wf, c, b, j0, Bb, B, j0, b, L.Z, L.R, mask, j0, Bb, s,
+                             obs ? L.D + (blk + 1) * b : L.gW, jn, hist),
+               "update");
+      } else {
+        TH_HIP(launch_update(Wf, c, b, j0, Bb, B, j0, b, L.Z, L.R, mask, j0, Bb, s), "update");
+      }
     } else {
       const int64_t per = ldz / B;  // blocks per super-block
       const int64_t sb0 = (blk / per) * ldz;

@@ -18,6 +18,7 @@ namespace th {
 constexpr int kMaxBlock = 128;  // largest column block B the kernels tile for
 constexpr int kSelBits = 11;    // radix-select digit width
 constexpr int kSelBins = 1 << kSelBits;
+constexpr int kSelCopies = 4;   // global histogram copies (workgroup i adds to copy i % 4)
 
 // Device-side state of one th_prune_layer call (lives in the workspace).
 struct DevState {
@@ -32,7 +33,9 @@ struct DevState {
   int nonfinite;               // NaN/Inf met in W or diag(H)
   double lambda;               // absolute damping used
   double diag_mean;            // mean(diag(2G))
-  unsigned int hist[kSelBins];
+  // Copies of the digit histogram, summed by the pick: a quarter of the
+  // workgroups adds to each, so fewer atomics meet on one address.
+  unsigned int hist[kSelCopies][kSelBins];
 };
 
 // Score S = w^2 * g in fp32, with g = 1/[A_F]_qq (OBS) or G_qq (Wanda).
@@ -196,10 +199,16 @@ hipError_t launch_scatter_rows(void* W, th_dtype wdt, int64_t c, int64_t b, cons
 
 // update.hip
 // W[:, col0:col_end) -= Z[:, 0:K] R[r0:r0+K, col0:col_end) (Z pitch ldz); entries of
-// columns [mask_j0, mask_j0 + mask_w) with mask set are then zeroed.
+// columns [mask_j0, mask_j0 + mask_w) with mask set are then zeroed. With hist set,
+// the new values of columns >= hist_j0 also add the first radix digit of their
+// selection keys (score_of(w, gn[col]), top 11 bits of the 64-bit key) to hist.
 hipError_t launch_update(float* W, int64_t c, int64_t b, int64_t r0, int64_t K, int64_t ldz,
                          int64_t col0, int64_t col_end, const float* Z, const float* R,
-                         const uint8_t* mask, int64_t mask_j0, int64_t mask_w, hipStream_t s);
+                         const uint8_t* mask, int64_t mask_j0, int64_t mask_w, hipStream_t s,
+                         const float* gn = nullptr, int64_t hist_j0 = 0,
+                         unsigned int* hist = nullptr);
+// Whether launch_update runs on 128 x 128 tiles (else 64 x 64) for this range.
+bool update_large_tiles(int64_t c, int64_t col0, int64_t col_end);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_to_f32(const void* src, th_dtype dt, int64_t count, float* dst,
                          DevState* st, hipStream_t s);

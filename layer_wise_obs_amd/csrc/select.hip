@@ -28,7 +28,7 @@ __device__ __forceinline__ void digit_of(int shift, int& width) {
 }
 
 __global__ void select_init_kernel(DevState* st, long long add_budget, long long ncand) {
-  for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) st->hist[i] = 0u;
+  for (int i = threadIdx.x; i < kSelCopies * kSelBins; i += blockDim.x) (&st->hist[0][0])[i] = 0u;
   if (threadIdx.x == 0) {
     const long long budget = st->budget + add_budget;
     st->budget = budget;
@@ -63,7 +63,9 @@ __global__ __launch_bounds__(256) void select_pick_kernel(DevState* st) {
   const int per = kSelBins / 256;  // 8 bins per thread
   unsigned int local = 0;
   for (int i = 0; i < per; ++i) {
-    const unsigned int h = st->hist[tid * per + i];
+    unsigned int h = 0u;
+#pragma unroll
+    for (int cp = 0; cp < kSelCopies; ++cp) h += st->hist[cp][tid * per + i];
     hcopy[tid * per + i] = h;
     local += h;
   }
@@ -108,7 +110,7 @@ __global__ __launch_bounds__(256) void select_pick_kernel(DevState* st) {
     st->tbound = st->prefix;
     st->done = 1;
   }
-  for (int i = tid; i < kSelBins; i += blockDim.x) st->hist[i] = 0u;
+  for (int i = tid; i < kSelCopies * kSelBins; i += blockDim.x) (&st->hist[0][0])[i] = 0u;
 }
 
 // Histogram of the current digit over the keys of rows k = blockIdx.x + m gridDim.x,
@@ -132,8 +134,9 @@ __device__ __forceinline__ void pass_body(DevState* st, int64_t rows, int64_t f,
     }
   }
   __syncthreads();
+  unsigned int* gh = st->hist[blockIdx.x % kSelCopies];
   for (int i = threadIdx.x; i < kSelBins; i += blockDim.x)
-    if (sh[i]) atomicAdd(&st->hist[i], sh[i]);
+    if (sh[i]) atomicAdd(&gh[i], sh[i]);
 }
 
 // Keys recomputed from the current weights: S = W^2 * g with g the per-column
@@ -180,8 +183,9 @@ __global__ __launch_bounds__(256) void select_pass_kernel(const float* __restric
     for (int64_t q = 4 * f4 + threadIdx.x; q < f; q += blockDim.x) count(wr[q], gr[q], base + q);
   }
   __syncthreads();
+  unsigned int* gh = st->hist[blockIdx.x % kSelCopies];
   for (int i = threadIdx.x; i < kSelBins; i += blockDim.x)
-    if (sh[i]) atomicAdd(&st->hist[i], sh[i]);
+    if (sh[i]) atomicAdd(&gh[i], sh[i]);
 }
 
 // Keys from given scores [c, f] (parity entry point).

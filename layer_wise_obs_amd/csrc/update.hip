@@ -19,16 +19,53 @@ namespace th {
 
 namespace {
 
+// First radix digit of the selection keys of the next block (unstructured): the
+// update writes every weight of the next active region, so it histograms the top
+// 11 bits of their 64-bit keys (the score bits >> 21: the flat index does not
+// reach that digit) exactly as the first selection pass would, into an LDS
+// histogram that is added to the global one at the end (integer counts, so the
+// result is that of the pass). hist_zero / hist_add / hist_flush are no-ops
+// without HIST.
+template <bool HIST>
+struct NextDigit {
+  unsigned int* sh;
+  __device__ __forceinline__ void zero() {
+    if constexpr (HIST)
+      for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) sh[i] = 0u;
+  }
+  __device__ __forceinline__ void add(float w, float g) {
+    if constexpr (HIST) atomicAdd(&sh[__float_as_uint(score_of(w, g)) >> 21], 1u);
+  }
+  // hist: kSelCopies histograms of kSelBins; this workgroup adds to copy i % kSelCopies
+  __device__ __forceinline__ void flush(unsigned int* __restrict__ hist) {
+    if constexpr (HIST) {
+      __syncthreads();
+      unsigned int* gh = hist + (blockIdx.x % kSelCopies) * kSelBins;
+      for (int i = threadIdx.x; i < kSelBins; i += blockDim.x)
+        if (sh[i]) atomicAdd(&gh[i], sh[i]);
+    }
+  }
+};
+
 // W[row0:, col0:] -= Z[rows, 0:K] R[r0:r0+K, cols]; zero the pruned entries of
-// columns [mask_j0, mask_jend).
+// columns [mask_j0, mask_jend); with HIST, the first key digit of columns >= hist_j0.
+template <bool HIST>
 __global__ __launch_bounds__(256, 2) void update_kernel(float* __restrict__ W, int64_t c, int64_t b,
                                                      int64_t r0, int K, int64_t ldz,
                                                      int64_t col_begin, int64_t col_end,
                                                      int ncol_tiles, const float* __restrict__ Z,
                                                      const float* __restrict__ R,
                                                      const uint8_t* __restrict__ mask,
-                                                     int64_t mask_j0, int64_t mask_jend) {
+                                                     int64_t mask_j0, int64_t mask_jend,
+                                                     const float* __restrict__ gn, int64_t hist_j0,
+                                                     unsigned int* __restrict__ hist) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kX3LdsBytes];
+  NextDigit<HIST> nd;
+  if constexpr (HIST) {
+    __shared__ unsigned int sh[kSelBins];
+    nd.sh = sh;
+  }
+  nd.zero();
   const int64_t row0 = (int64_t)(blockIdx.x / ncol_tiles) * 128;
   const int64_t col0 = col_begin + (int64_t)(blockIdx.x % ncol_tiles) * 128;
   const int rows = (int)((c - row0) < 128 ? (c - row0) : 128);
@@ -39,24 +76,45 @@ __global__ __launch_bounds__(256, 2) void update_kernel(float* __restrict__ W, i
   gemm_tile_x3<false>(Z + row0 * ldz, ldz, rows, R + r0 * b + col0, b, cols, K, acc, smem,
                              true);
   const bool masked = col0 < mask_jend && col0 + 128 > mask_j0;
+  // score weights of this lane's two columns (wave column 64 (wave & 1), then +32),
+  // loaded before the stores so that no load waits inside the loop below
+  float gv[2] = {0.f, 0.f};
+  if constexpr (HIST) {
+    const int cl = (int)((threadIdx.x >> 6) & 1) * 64 + (int)(threadIdx.x & 31);
+#pragma unroll
+    for (int tj = 0; tj < 2; ++tj)
+      if (cl + 32 * tj < cols && col0 + cl + 32 * tj >= hist_j0) gv[tj] = gn[col0 + cl + 32 * tj];
+  }
   gemm_foreach(acc, [&](int r, int cc, float v) {
     if (r < rows && cc < cols) {
       const int64_t row = row0 + r, col = col0 + cc;
       if (masked && col >= mask_j0 && col < mask_jend && mask[row * b + col]) v = 0.f;
       W[row * b + col] = v;
+      if (HIST && col >= hist_j0) nd.add(v, gv[(cc >> 5) & 1]);
     }
   });
+  nd.flush(hist);
 }
 
 // The same update on 64 x 64 tiles, for launches with few 128 x 128 tiles.
+template <bool HIST>
 __global__ __launch_bounds__(256, 2) void update64_kernel(float* __restrict__ W, int64_t c,
                                                        int64_t b, int64_t r0, int K, int64_t ldz,
                                                        int64_t col_begin, int64_t col_end,
                                                        int ncol_tiles, const float* __restrict__ Z,
                                                        const float* __restrict__ R,
                                                        const uint8_t* __restrict__ mask,
-                                                       int64_t mask_j0, int64_t mask_jend) {
+                                                       int64_t mask_j0, int64_t mask_jend,
+                                                       const float* __restrict__ gn,
+                                                       int64_t hist_j0,
+                                                       unsigned int* __restrict__ hist) {
   __shared__ __attribute__((aligned(16))) float smem[kG64LdsFloats];
+  NextDigit<HIST> nd;
+  if constexpr (HIST) {
+    __shared__ unsigned int sh[kSelBins];
+    nd.sh = sh;
+  }
+  nd.zero();
   const int64_t row0 = (int64_t)(blockIdx.x / ncol_tiles) * 64;
   const int64_t col0 = col_begin + (int64_t)(blockIdx.x % ncol_tiles) * 64;
   const int rows = (int)((c - row0) < 64 ? (c - row0) : 64);
@@ -67,13 +125,22 @@ __global__ __launch_bounds__(256, 2) void update64_kernel(float* __restrict__ W,
   g64_tile_f32<true, false>(Z + row0 * ldz, ldz, rows, R + r0 * b + col0, b, cols, K, acc, smem,
                             true);
   const bool masked = col0 < mask_jend && col0 + 64 > mask_j0;
+  // score weight of this lane's column (wave column 32 (wave & 1)), loaded before
+  // the stores so that no load waits inside the loop below
+  float gv = 0.f;
+  if constexpr (HIST) {
+    const int cl = (int)((threadIdx.x >> 6) & 1) * 32 + (int)(threadIdx.x & 31);
+    if (cl < cols && col0 + cl >= hist_j0) gv = gn[col0 + cl];
+  }
   g64_foreach(acc, [&](int r, int cc, float v) {
     if (r < rows && cc < cols) {
       const int64_t row = row0 + r, col = col0 + cc;
       if (masked && col >= mask_j0 && col < mask_jend && mask[row * b + col]) v = 0.f;
       W[row * b + col] = v;
+      if (HIST && col >= hist_j0) nd.add(v, gv);
     }
   });
+  nd.flush(hist);
 }
 
 __global__ void to_f32_kernel(const void* __restrict__ src, int dt, int64_t n,
@@ -174,22 +241,40 @@ unsigned ew_grid(int64_t n) {
 
 }  // namespace
 
+bool update_large_tiles(int64_t c, int64_t col0, int64_t col_end) {
+  // under ~4 tiles per CU the 64 x 64 tiles finish sooner
+  return cdiv(col_end - col0, 128) * cdiv(c, 128) >= 1024;
+}
+
 hipError_t launch_update(float* W, int64_t c, int64_t b, int64_t r0, int64_t K, int64_t ldz,
                          int64_t col0, int64_t col_end, const float* Z, const float* R,
-                         const uint8_t* mask, int64_t mask_j0, int64_t mask_w, hipStream_t s) {
+                         const uint8_t* mask, int64_t mask_j0, int64_t mask_w, hipStream_t s,
+                         const float* gn, int64_t hist_j0, unsigned int* hist) {
   if (col_end <= col0 || K <= 0) return hipSuccess;
+  if (hist && !gn) return hipErrorInvalidValue;
   const int nct = (int)cdiv(col_end - col0, 128);
   const int nrt = (int)cdiv(c, 128);
-  if ((int64_t)nct * nrt < 1024) {  // under ~4 tiles per CU: smaller tiles finish sooner
+  if (!update_large_tiles(c, col0, col_end)) {
     const int nct64 = (int)cdiv(col_end - col0, 64);
     const int nrt64 = (int)cdiv(c, 64);
-    hipLaunchKernelGGL(update64_kernel, dim3((unsigned)(nct64 * nrt64)), dim3(256), 0, s, W, c, b,
-                       r0, (int)K, ldz, col0, col_end, nct64, Z, R, mask, mask_j0,
-                       mask_j0 + mask_w);
+    if (hist)
+      hipLaunchKernelGGL(update64_kernel<true>, dim3((unsigned)(nct64 * nrt64)), dim3(256), 0, s, W,
+                         c, b, r0, (int)K, ldz, col0, col_end, nct64, Z, R, mask, mask_j0,
+                         mask_j0 + mask_w, gn, hist_j0, hist);
+    else
+      hipLaunchKernelGGL(update64_kernel<false>, dim3((unsigned)(nct64 * nrt64)), dim3(256), 0, s, W,
+                         c, b, r0, (int)K, ldz, col0, col_end, nct64, Z, R, mask, mask_j0,
+                         mask_j0 + mask_w, gn, hist_j0, hist);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(update_kernel, dim3((unsigned)(nct * nrt)), dim3(256), 0, s, W, c, b, r0,
-                     (int)K, ldz, col0, col_end, nct, Z, R, mask, mask_j0, mask_j0 + mask_w);
+  if (hist)
+    hipLaunchKernelGGL(update_kernel<true>, dim3((unsigned)(nct * nrt)), dim3(256), 0, s, W, c, b,
+                       r0, (int)K, ldz, col0, col_end, nct, Z, R, mask, mask_j0, mask_j0 + mask_w,
+                       gn, hist_j0, hist);
+  else
+    hipLaunchKernelGGL(update_kernel<false>, dim3((unsigned)(nct * nrt)), dim3(256), 0, s, W, c, b,
+                       r0, (int)K, ldz, col0, col_end, nct, Z, R, mask, mask_j0, mask_j0 + mask_w,
+                       gn, hist_j0, hist);
   return hipGetLastError();
 }
 
