@@ -19,6 +19,9 @@
 // Route B (s > 64, only when B > 64): with N = M^-1 and P = J \ Q (p = B - s < 64
 // entries), Rhat^-1 = N_QQ - N_QP N_PP^-1 N_PQ, so one p x p system suffices:
 //   N_PP x = N_PQ u^T,  v = [v_Q = u, v_P = -x],  z_Q = (v N)_Q.
+// Unstructured rows take either route, so that launch holds both M and N in LDS
+// (one workgroup per compute unit) and picks the route per row: one launch per
+// block instead of one per route, each of which paid the loads and the row scan.
 //
 // Masks: N:M ("The compression target: linear layers"; the explainer's "N:M
 // Semi-Structured Sparsity (2:4 Pattern)"): in every aligned group of m entries
@@ -90,9 +93,11 @@ struct SolveArgs {
   unsigned long long* blk_count;
 };
 
+// ROUTE: 0 route A, 1 route B, 2 the route of each row (M and N both in LDS).
 template <int MODE, int ROUTE>
-__global__ __launch_bounds__(kWaves * 64, 4) void solve_kernel(SolveArgs a) {
+__global__ __launch_bounds__(kWaves * 64, ROUTE == 2 ? 2 : 4) void solve_kernel(SolveArgs a) {
   __shared__ float sM[kMaxBlock * kMaxBlock];
+  __shared__ float sN2[ROUTE == 2 ? kMaxBlock * kMaxBlock : 1];
   __shared__ float sg[kMaxBlock];
   __shared__ float sbuf[kWaves][kMaxBlock];
   __shared__ float su[kWaves][kMaxBlock];
@@ -105,9 +110,10 @@ __global__ __launch_bounds__(kWaves * 64, 4) void solve_kernel(SolveArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Bb = a.Bb;
   const int64_t b = a.b, j0 = a.j0;
-  {  // M (or N): all 32 loads of a thread in flight at once, addresses clamped
-    const float* src = (ROUTE == 0) ? a.R + j0 * b + j0 : a.Nblk;
-    const int64_t ld = (ROUTE == 0) ? b : a.B;
+  // route B's matrix: N, in sM (route B alone) or in sN2 (both routes)
+  float* const sN = (ROUTE == 2) ? sN2 : sM;
+  // M (or N): all 32 loads of a thread in flight at once, addresses clamped
+  auto load_mat = [&](const float* src, int64_t ld, float* dst) {
     constexpr int kPer = kMaxBlock * kMaxBlock / (kWaves * 64);
     float v[kPer];
 #pragma unroll
@@ -119,9 +125,11 @@ __global__ __launch_bounds__(kWaves * 64, 4) void solve_kernel(SolveArgs a) {
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
       const int idx = e * kWaves * 64 + tid, r = idx >> 7, q = idx & (kMaxBlock - 1);
-      if (r < Bb && q < Bb) sM[mat_idx(r, q)] = v[e];
+      if (r < Bb && q < Bb) dst[mat_idx(r, q)] = v[e];
     }
-  }
+  };
+  if (ROUTE != 1) load_mat(a.R + j0 * b + j0, b, sM);
+  if (ROUTE != 0) load_mat(a.Nblk, a.B, sN);
   for (int q = tid; q < Bb; q += blockDim.x) {
     float gq;
     if (a.g_mode == 0) gq = __fdiv_rn(1.0f, a.R[(j0 + q) * b + j0 + q]);
@@ -156,6 +164,7 @@ __global__ __launch_bounds__(kWaves * 64, 4) void solve_kernel(SolveArgs a) {
       if (ROUTE == 0 && s > 64) continue;
       if (ROUTE == 1 && s <= 64) continue;
     }
+    const bool rb = (ROUTE == 1) || (ROUTE == 2 && s > 64);  // this row takes route B (uniform)
     uint8_t* mrow = a.mask + k * b + j0;
     if (v0) mrow[e0] = s0 ? 1 : 0;
     if (v1) mrow[e1] = s1 ? 1 : 0;
@@ -165,7 +174,7 @@ __global__ __launch_bounds__(kWaves * 64, 4) void solve_kernel(SolveArgs a) {
     const int pos0 = __popcll(m0 & lt), pos1 = __popcll(m0) + __popcll(m1 & lt);
     if (s0) { sQ[wave][pos0] = e0; su[wave][pos0] = w0; }
     if (s1) { sQ[wave][pos1] = e1; su[wave][pos1] = w1; }
-    if (ROUTE == 1) {
+    if (rb) {
       const unsigned long long n0 = __ballot(v0 && !s0), n1 = __ballot(v1 && !s1);
       const int pp0 = __popcll(n0 & lt), pp1 = __popcll(n0) + __popcll(n1 & lt);
       if (v0 && !s0) sP[wave][pp0] = e0;
@@ -179,7 +188,7 @@ __global__ __launch_bounds__(kWaves * 64, 4) void solve_kernel(SolveArgs a) {
       int olane;
       __asm__ volatile("v_mov_b32 %0, %1" : "=v"(olane) : "v"(lane));
       float reg[64];
-      if (ROUTE == 0) {
+      if (!rb) {
         const bool act = lane < s;
         const int qa = act ? sQ[wave][lane] : 0;
 #pragma unroll
@@ -201,12 +210,12 @@ __global__ __launch_bounds__(kWaves * 64, 4) void solve_kernel(SolveArgs a) {
         for (int c = 0; c < 64; ++c) {
           const bool in = (c < p) && act;
           const int pc = (c < p) ? sP[wave][c] : 0;
-          const float v = sM[mat_idx(pb, pc)];
+          const float v = sN[mat_idx(pb, pc)];
           reg[c] = in ? v : ((c == olane) ? 1.f : 0.f);
         }
         float y = 0.f;
         if (act) {
-          for (int t = 0; t < s; ++t) y = fmaf(su[wave][t], sM[mat_idx(sQ[wave][t], pb)], y);
+          for (int t = 0; t < s; ++t) y = fmaf(su[wave][t], sN[mat_idx(sQ[wave][t], pb)], y);
         }
         wave_sync();  // the gather's reads of sP are done before it becomes the pivot row
         const float x = gauss_jordan64(reg, y, (float*)sP[wave], olane);
@@ -218,8 +227,8 @@ __global__ __launch_bounds__(kWaves * 64, 4) void solve_kernel(SolveArgs a) {
         float z0 = 0.f, z1 = 0.f;
         for (int t = 0; t < Bb; ++t) {
           const float vt = sbuf[wave][t];
-          if (v0) z0 = fmaf(vt, sM[mat_idx(t, e0)], z0);
-          if (v1) z1 = fmaf(vt, sM[mat_idx(t, e1)], z1);
+          if (v0) z0 = fmaf(vt, sN[mat_idx(t, e0)], z0);
+          if (v1) z1 = fmaf(vt, sN[mat_idx(t, e1)], z1);
         }
         if (s0) zrow[e0] = z0;
         if (s1) zrow[e1] = z1;
@@ -306,10 +315,13 @@ hipError_t launch_solve_unstructured(const float* W, int64_t c, int64_t b, int64
   a.B = (int)B; a.n = 0; a.m = 1; a.R = R; a.Nblk = Nblk;
   a.g = g; a.g_mode = 2;  // per-column score weight given (1/[A_F]_qq or G_qq)
   a.Z = Z; a.ldz = B; a.mask = mask; a.st = st; a.blk_count = blk_count;
-  hipLaunchKernelGGL((solve_kernel<1, 0>), dim3(solve_grid(c)), dim3(kWaves * 64), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.Bb <= 64) return e;
-  hipLaunchKernelGGL((solve_kernel<1, 1>), dim3(solve_grid(c)), dim3(kWaves * 64), 0, s, a);
+  if (a.Bb <= 64)
+    hipLaunchKernelGGL((solve_kernel<1, 0>), dim3(solve_grid(c)), dim3(kWaves * 64), 0, s, a);
+  else
+    // one workgroup per compute unit fits (M and N take 128 KB of LDS): a grid of
+    // 256 runs in one round, each wave taking its rows in turn
+    hipLaunchKernelGGL((solve_kernel<1, 2>), dim3(solve_grid(c) < 256 ? solve_grid(c) : 256),
+                       dim3(kWaves * 64), 0, s, a);
   return hipGetLastError();
 }
 
