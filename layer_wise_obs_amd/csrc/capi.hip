@@ -74,6 +74,9 @@ struct PruneLayout {
   float* Wf;
   uint8_t* mask;
   float* syrk_part;
+  unsigned long long* cand;  // unstructured: candidate keys of the selection
+  unsigned int* cand_n;      // and their count per segment
+  int64_t cand_quota;        // keys per segment
   size_t bytes;
 };
 
@@ -122,6 +125,14 @@ PruneLayout layout_prune(void* ws, int64_t c, int64_t b, int64_t n, bool have_x,
   L.Z = cv.take<float>((size_t)c * (sgpt ? super_pitch(b, B) : z_pitch(b, p)));
   L.Wf = need_wf ? cv.take<float>((size_t)c * b) : nullptr;
   L.mask = need_mask ? cv.take<uint8_t>((size_t)c * b) : nullptr;
+  L.cand = nullptr;
+  L.cand_n = nullptr;
+  L.cand_quota = 0;
+  if (!sgpt && unstr) {
+    L.cand_quota = select_quota(c, b);
+    L.cand = cv.take<unsigned long long>((size_t)(select_segments(c) * L.cand_quota));
+    L.cand_n = cv.take<unsigned int>((size_t)select_segments(c));
+  }
   L.syrk_part = nullptr;
   if (have_x && xdt == TH_BF16) {
     const int splits = syrk_bf16_splits(n, b);
@@ -288,7 +299,8 @@ th_status prune_blocks(const PruneLayout& L, int64_t c, int64_t b, const th_prun
         first_pass = 1;
       }
       for (int pass = first_pass; pass < 6; ++pass) {
-        TH_HIP(launch_select_pass(Wf, c, b, j0, b, g, L.st, s), "select pass");
+        TH_HIP(launch_select_pass(Wf, c, b, j0, b, g, L.st, s, L.cand, L.cand_n, L.cand_quota),
+               "select pass");
         TH_HIP(launch_select_pick(L.st, s), "select pick");
       }
       TH_HIP(launch_solve_unstructured(Wf, c, b, j0, B, L.R, Nb, g, L.Z, mask, L.st,

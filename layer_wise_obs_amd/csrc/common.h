@@ -33,6 +33,8 @@ struct DevState {
   int nonfinite;               // NaN/Inf met in W or diag(H)
   double lambda;               // absolute damping used
   double diag_mean;            // mean(diag(2G))
+  int cand_state;              // candidate list: 0 not built, 1 valid, 2 not usable
+  int cand_over;               // a workgroup's candidates did not fit its segment
   // Copies of the digit histogram, summed by the pick: a quarter of the
   // workgroups adds to each, so fewer atomics meet on one address.
   unsigned int hist[kSelCopies][kSelBins];
@@ -151,8 +153,16 @@ hipError_t launch_block_inverses(const float* Ublk, int64_t b, int64_t B, float*
 hipError_t launch_select_init(DevState* st, long long add_budget, long long ncand,
                               hipStream_t s);
 // One radix pass over the keys of W[:, j0:j1) with score weights g, then the pick.
+// Candidate list of the global selection: one segment of `quota` keys per
+// workgroup of the pass grid, and a count per segment.
+int64_t select_segments(int64_t c);
+int64_t select_quota(int64_t c, int64_t b);
+// cand / cand_n: select_segments(c) * quota keys and select_segments(c) counts, or
+// nullptr (every pass then reads W).
 hipError_t launch_select_pass(const float* W, int64_t c, int64_t b, int64_t j0, int64_t j1,
-                              const float* g, DevState* st, hipStream_t s);
+                              const float* g, DevState* st, hipStream_t s,
+                              unsigned long long* cand = nullptr, unsigned int* cand_n = nullptr,
+                              int64_t quota = 0);
 hipError_t launch_select_pick(DevState* st, hipStream_t s);
 hipError_t launch_select_scores_pass(const float* scores, int64_t c, int64_t f,
                                      int64_t b_full, int64_t j0, DevState* st, hipStream_t s);

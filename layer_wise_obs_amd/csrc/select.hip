@@ -16,6 +16,14 @@
 // scope fence in every workgroup would). Budget, prefix and threshold stay on
 // the device: the host launches a fixed number of passes and finished passes
 // exit at once.
+//
+// Candidate list: the first pass whose prefix is not empty (the second digit)
+// still reads every key, and also stores the keys that match its prefix -- the
+// bucket of the first digit, a few percent of the region -- in a segment of its
+// workgroup (an LDS counter gives each key its slot; no global atomics). The later
+// passes of the block read only those segments: every key they count matches a
+// longer prefix, so it is in the list. A segment that would overflow makes the
+// list unusable and the later passes read W again, as without a list.
 #include "common.h"
 
 namespace th {
@@ -36,6 +44,8 @@ __global__ void select_init_kernel(DevState* st, long long add_budget, long long
     st->rrem = r;
     st->prefix = 0ull;
     st->shift = 53;
+    st->cand_state = 0;
+    st->cand_over = 0;
     if (r <= 0) {
       st->done = 1;
       st->tbound = 0ull;
@@ -56,6 +66,8 @@ __global__ void select_init_kernel(DevState* st, long long add_budget, long long
 // its 8 bins. Integer counts throughout, so the result does not depend on order.
 __global__ __launch_bounds__(256) void select_pick_kernel(DevState* st) {
   if (st->done) return;
+  // the pass just counted was the one that builds the candidate list
+  const bool built = st->cand_state == 0 && st->shift < 53;
   __shared__ unsigned long long scan[256];
   __shared__ unsigned int hcopy[kSelBins];
   __shared__ int found;
@@ -105,6 +117,7 @@ __global__ __launch_bounds__(256) void select_pick_kernel(DevState* st) {
     }
     found = 1;
   }
+  if (tid == 0 && built) st->cand_state = st->cand_over ? 2 : 1;
   __syncthreads();
   if (tid == 0 && !found) {  // cannot happen when the histogram is consistent
     st->tbound = st->prefix;
@@ -147,21 +160,53 @@ __device__ __forceinline__ void pass_body(DevState* st, int64_t rows, int64_t f,
 __global__ __launch_bounds__(256) void select_pass_kernel(const float* __restrict__ W, int64_t c,
                                                           int64_t b, int64_t j0, int64_t j1,
                                                           const float* __restrict__ g,
-                                                          DevState* st) {
+                                                          DevState* st,
+                                                          unsigned long long* __restrict__ cand,
+                                                          unsigned int* __restrict__ cand_n,
+                                                          int64_t quota) {
   if (st->done) return;
   __shared__ unsigned int sh[kSelBins];
+  __shared__ unsigned int slot;
   const int shift = st->shift;
   int width;
   digit_of(shift, width);
   const int top = shift + width;
   const unsigned long long prefix = st->prefix;
+  const int cstate = st->cand_state;
   for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) sh[i] = 0u;
+  if (threadIdx.x == 0) slot = 0u;
   __syncthreads();
   const unsigned long long dmask = (1ull << width) - 1ull;
+  auto flush = [&]() {
+    __syncthreads();
+    unsigned int* gh = st->hist[blockIdx.x % kSelCopies];
+    for (int i = threadIdx.x; i < kSelBins; i += blockDim.x)
+      if (sh[i]) atomicAdd(&gh[i], sh[i]);
+  };
+  if (cstate == 1) {  // the keys of the list (gridDim.x segments: this pass's grid)
+    const unsigned long long* seg = cand + (int64_t)blockIdx.x * quota;
+    const unsigned int n = cand_n[blockIdx.x];
+    for (unsigned int i = threadIdx.x; i < n; i += blockDim.x) {
+      const unsigned long long key = seg[i];
+      if ((key >> top) == (prefix >> top)) atomicAdd(&sh[(key >> shift) & dmask], 1u);
+    }
+    flush();
+    return;
+  }
+  const bool build = cstate == 0 && shift < 53 && cand != nullptr;
+  if (cstate == 0 && shift < 53 && cand == nullptr && blockIdx.x == 0 && threadIdx.x == 0)
+    st->cand_over = 1;  // no list buffer: the later passes read W
+  unsigned long long* seg = build ? cand + (int64_t)blockIdx.x * quota : nullptr;
   auto count = [&](float w, float gq, int64_t flat) {
     const unsigned long long key = make_key(score_of(w, gq), (unsigned int)flat);
     const bool match = (top >= 64) || ((key >> top) == (prefix >> top));
-    if (match) atomicAdd(&sh[(key >> shift) & dmask], 1u);
+    if (match) {
+      atomicAdd(&sh[(key >> shift) & dmask], 1u);
+      if (build) {
+        const unsigned int at = atomicAdd(&slot, 1u);
+        if (at < (unsigned long long)quota) seg[at] = key;
+      }
+    }
   };
   const int64_t f = j1 - j0;
   const bool vec = ((b & 3) == 0) && ((j0 & 3) == 0) && ((((uintptr_t)W | (uintptr_t)g) & 15) == 0);
@@ -182,10 +227,12 @@ __global__ __launch_bounds__(256) void select_pass_kernel(const float* __restric
     }
     for (int64_t q = 4 * f4 + threadIdx.x; q < f; q += blockDim.x) count(wr[q], gr[q], base + q);
   }
-  __syncthreads();
-  unsigned int* gh = st->hist[blockIdx.x % kSelCopies];
-  for (int i = threadIdx.x; i < kSelBins; i += blockDim.x)
-    if (sh[i]) atomicAdd(&gh[i], sh[i]);
+  flush();
+  if (build && threadIdx.x == 0) {
+    const unsigned int n = slot;
+    cand_n[blockIdx.x] = n < (unsigned long long)quota ? n : (unsigned int)quota;
+    if (n > (unsigned long long)quota) st->cand_over = 1;
+  }
 }
 
 // Keys from given scores [c, f] (parity entry point).
@@ -212,10 +259,22 @@ static unsigned pass_grid(int64_t rows) {
   return (unsigned)(g < 1 ? 1 : g);
 }
 
+int64_t select_segments(int64_t c) { return pass_grid(c); }
+
+// One eighth of a segment's keys (a workgroup's rows times the layer's columns):
+// the first digit's bucket at the threshold holds a few percent of them.
+int64_t select_quota(int64_t c, int64_t b) {
+  const int64_t rows = cdiv(c, (int64_t)pass_grid(c));
+  const int64_t q = cdiv(rows * b, (int64_t)8);
+  return q < 64 ? 64 : q;
+}
+
 hipError_t launch_select_pass(const float* W, int64_t c, int64_t b, int64_t j0, int64_t j1,
-                              const float* g, DevState* st, hipStream_t s) {
+                              const float* g, DevState* st, hipStream_t s,
+                              unsigned long long* cand, unsigned int* cand_n, int64_t quota) {
+  if (cand && (!cand_n || quota <= 0)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(select_pass_kernel, dim3(pass_grid(c)), dim3(256), 0, s, W, c, b, j0, j1, g,
-                     st);
+                     st, cand, cand_n, quota);
   return hipGetLastError();
 }
 
