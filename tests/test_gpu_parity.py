@@ -265,6 +265,26 @@ def test_prune_unstructured_high_sparsity_small_block():
     _check_layer(W, X, sparsity=0.7, pattern=None, block=48)
 
 
+@pytest.mark.parametrize("c,b", [(256, 512), (130, 392)])
+def test_prune_unstructured_all_scores_tied(c, b):
+    """Every score equal: |w| constant and X a multiple of the identity, so G, H and
+    every 1/[A_F]_qq are multiples of the identity and the selection keys differ
+    only by their flat index. The global selection then needs every radix digit
+    (down to the last index bits), the first digit's bucket is the whole region
+    (the candidate list overflows and the later passes read W again), and the
+    result is fixed exactly: the lowest flat indices go first, and with a diagonal
+    H the compensation leaves the other weights unchanged."""
+    _say(f"prune unstructured, all scores tied, c={c} b={b}")
+    rng = np.random.default_rng(77)
+    W = torch.tensor(np.where(rng.random((c, b)) < 0.5, -0.02, 0.02), dtype=torch.bfloat16)
+    X = torch.tensor(np.eye(b) * 2.0, dtype=torch.bfloat16)
+    ora, Wg, mg, info = _check_layer(W, X, sparsity=0.5, pattern=None, block=128,
+                                     max_flip_frac=0.0)
+    assert np.array_equal(mg, ora["mask"])
+    W32 = W.float().numpy()
+    assert np.array_equal(Wg, np.where(mg, 0.0, W32))
+
+
 @pytest.mark.parametrize("pattern", [None, (2, 4)])
 def test_prune_wanda_score(pattern):
     _say(f"prune wanda score {pattern}")
