@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include <type_traits>
@@ -37,8 +38,9 @@ struct DevState {
   int cand_over;               // a workgroup's candidates did not fit its segment
   // Copies of the digit histogram, summed by the pick: a quarter of the
   // workgroups adds to each, so fewer atomics meet on one address.
-  unsigned int hist[kSelCopies][kSelBins];
+  alignas(16) unsigned int hist[kSelCopies][kSelBins];
 };
+static_assert(offsetof(DevState, hist) % 16 == 0, "16-byte loads of the histogram");
 
 // Score S = w^2 * g in fp32, with g = 1/[A_F]_qq (OBS) or G_qq (Wanda).
 // One definition for every kernel that ranks weights, so that keys computed

@@ -61,50 +61,71 @@ __global__ void select_init_kernel(DevState* st, long long add_budget, long long
 
 // Narrow the prefix by the digit whose bucket holds the rrem-th smallest key
 // (one workgroup of 256 threads, 8 bins each), then clear the histogram for the
-// next pass. An inclusive scan of the per-thread sums finds the one thread whose
-// bins hold rank rrem (exclusive sum < rrem <= inclusive sum); that thread walks
-// its 8 bins. Integer counts throughout, so the result does not depend on order.
+// next pass. An inclusive scan of the per-thread sums (within each wave by lane
+// shuffles, then over the four wave totals) finds the one thread whose bins hold
+// rank rrem (exclusive sum < rrem <= inclusive sum); that thread walks its 8
+// bins. Integer counts throughout, so the result does not depend on order.
 __global__ __launch_bounds__(256) void select_pick_kernel(DevState* st) {
   if (st->done) return;
   // the pass just counted was the one that builds the candidate list
   const bool built = st->cand_state == 0 && st->shift < 53;
-  __shared__ unsigned long long scan[256];
-  __shared__ unsigned int hcopy[kSelBins];
+  __shared__ unsigned long long wsum[4];
   __shared__ int found;
-  const int tid = threadIdx.x;
-  const int per = kSelBins / 256;  // 8 bins per thread
-  unsigned int local = 0;
-  for (int i = 0; i < per; ++i) {
-    unsigned int h = 0u;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int per = kSelBins / 256;  // 8 bins per thread
+  static_assert(per == 8, "two 16-byte loads per copy");
+  // this thread's 8 bins summed over the copies: two 16-byte loads per copy, all
+  // in flight at once
+  u32x4_t a[kSelCopies], c[kSelCopies];
 #pragma unroll
-    for (int cp = 0; cp < kSelCopies; ++cp) h += st->hist[cp][tid * per + i];
-    hcopy[tid * per + i] = h;
-    local += h;
+  for (int cp = 0; cp < kSelCopies; ++cp) {
+    const u32x4_t* src = (const u32x4_t*)&st->hist[cp][tid * per];
+    a[cp] = src[0];
+    c[cp] = src[1];
   }
-  scan[tid] = local;
+  unsigned int h[per];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = 0u;
+    h[4 + e] = 0u;
+#pragma unroll
+    for (int cp = 0; cp < kSelCopies; ++cp) {
+      h[e] += a[cp][e];
+      h[4 + e] += c[cp][e];
+    }
+  }
+  unsigned long long local = 0;
+#pragma unroll
+  for (int e = 0; e < per; ++e) local += h[e];
+  // inclusive scan inside the wave
+  unsigned long long incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned long long v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) wsum[wave] = incl;
   if (tid == 0) found = 0;
   __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const unsigned long long v = tid >= off ? scan[tid - off] : 0ull;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
-  }
+  for (int w = 0; w < wave; ++w) incl += wsum[w];
   const long long r = st->rrem;
-  const long long incl = (long long)scan[tid], excl = incl - (long long)local;
-  if (excl < r && r <= incl) {
+  const long long excl = (long long)incl - (long long)local;
+  if (excl < r && r <= (long long)incl) {
     long long cum = excl;
     int d = tid * per + per - 1;
-    for (int i = 0; i < per; ++i) {
-      const long long h = hcopy[tid * per + i];
-      if (cum + h >= r) {
-        d = tid * per + i;
-        break;
+    long long inb = h[per - 1];
+#pragma unroll
+    for (int e = per - 1; e >= 0; --e) {  // the first bin (from the left) that reaches r
+      long long before = excl;
+#pragma unroll
+      for (int t = 0; t < e; ++t) before += h[t];
+      if (before < r && before + (long long)h[e] >= r) {
+        d = tid * per + e;
+        cum = before;
+        inb = h[e];
       }
-      cum += h;
     }
     const int shift = st->shift;
-    const long long inb = hcopy[d];
     const long long rnew = r - cum;
     st->prefix |= ((unsigned long long)d) << shift;
     st->rrem = rnew;
@@ -123,7 +144,13 @@ __global__ __launch_bounds__(256) void select_pick_kernel(DevState* st) {
     st->tbound = st->prefix;
     st->done = 1;
   }
-  for (int i = tid; i < kSelCopies * kSelBins; i += blockDim.x) (&st->hist[0][0])[i] = 0u;
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int cp = 0; cp < kSelCopies; ++cp) {
+    u32x4_t* dst = (u32x4_t*)&st->hist[cp][tid * per];
+    dst[0] = z;
+    dst[1] = z;
+  }
 }
 
 // Histogram of the current digit over the keys of rows k = blockIdx.x + m gridDim.x,
