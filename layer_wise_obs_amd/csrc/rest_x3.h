@@ -151,11 +151,17 @@ __global__ __launch_bounds__(256, 1) void rest_x3_kernel(float* __restrict__ S, 
       // panel (plane p, operand o) at sb + (2 p + o) * kX3PanelBytes
       auto fa = [&](int p, int a) { return x3d::frag(sb + (2 * p) * kX3PanelBytes, wrow * 128 + a * 32, lane); };
       auto fbf = [&](int p, int c) { return x3d::frag(sb + (2 * p + 1) * kX3PanelBytes, wcol * 128 + c * 32, lane); };
-      bf16x8_t ah[4], bh[4], ax[4], bx[4];
+      bf16x8_t ah[4], bh[4], ax[4], bx[4], am[4], bm[4];
 #pragma unroll
       for (int a = 0; a < 4; ++a) { ah[a] = fa(0, a); ax[a] = fa(2, a); }
 #pragma unroll
       for (int c = 0; c < 4; ++c) { bh[c] = fbf(0, c); bx[c] = fbf(2, c); }
+      // the middle plane's reads go out with the others, in their own registers, so
+      // they are in flight while the first products run
+#pragma unroll
+      for (int a = 0; a < 4; ++a) am[a] = fa(1, a);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bm[c] = fbf(1, c);
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -164,16 +170,12 @@ __global__ __launch_bounds__(256, 1) void rest_x3_kernel(float* __restrict__ S, 
           acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[a], bx[c], acc[a][c], 0, 0, 0);
         }
 #pragma unroll
-      for (int a = 0; a < 4; ++a) ax[a] = fa(1, a);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) bx[c] = fbf(1, c);
-#pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ax[a], bx[c], acc[a][c], 0, 0, 0);
-          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ax[a], bh[c], acc[a][c], 0, 0, 0);
-          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[a], bx[c], acc[a][c], 0, 0, 0);
+          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am[a], bm[c], acc[a][c], 0, 0, 0);
+          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am[a], bh[c], acc[a][c], 0, 0, 0);
+          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[a], bm[c], acc[a][c], 0, 0, 0);
         }
 #pragma unroll
       for (int a = 0; a < 4; ++a)
