@@ -87,6 +87,38 @@ __device__ __forceinline__ void dma12(const void* const (&g)[12], const void* ld
         "v"(g[7]), "v"(g[8]), "v"(g[9]), "v"(g[10]), "v"(g[11]));
 }
 
+// The same twelve loads with a wave-uniform global base (SGPR pair) and one
+// 32-bit byte offset per load and lane (saddr form): the offsets stay fixed for
+// a tile, and a stage only moves the base.
+__device__ __forceinline__ void dma12s(const unsigned (&vo)[12], const void* gbase, const void* lds) {
+  const unsigned base = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)lds);
+  const uint64_t gb = (uint64_t)(uintptr_t)gbase;
+  // readfirstlane returns int: go through unsigned so the low half is not sign-extended
+  const uint64_t g =
+      ((uint64_t)(unsigned)__builtin_amdgcn_readfirstlane((unsigned)(gb >> 32)) << 32) |
+      (uint64_t)(unsigned)__builtin_amdgcn_readfirstlane((unsigned)gb);
+  unsigned saved;
+  __asm__ volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %14\n\t"
+      "s_add_u32 m0, %1, 4096\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, %14\n\t"
+      "s_add_u32 m0, %1, 8192\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %4, %14\n\t"
+      "s_add_u32 m0, %1, 12288\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %5, %14\n\t"
+      "s_add_u32 m0, %1, 16384\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %6, %14\n\t"
+      "s_add_u32 m0, %1, 20480\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %7, %14\n\t"
+      "s_add_u32 m0, %1, 24576\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %8, %14\n\t"
+      "s_add_u32 m0, %1, 28672\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %9, %14\n\t"
+      "s_add_u32 m0, %1, 32768\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %10, %14\n\t"
+      "s_add_u32 m0, %1, 36864\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %11, %14\n\t"
+      "s_add_u32 m0, %1, 40960\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %12, %14\n\t"
+      "s_add_u32 m0, %1, 45056\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %13, %14\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(base), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "v"(vo[3]), "v"(vo[4]), "v"(vo[5]),
+        "v"(vo[6]), "v"(vo[7]), "v"(vo[8]), "v"(vo[9]), "v"(vo[10]), "v"(vo[11]), "s"(g));
+}
+
 }  // namespace x3d
 
 // Rest set of pair (k, k+1): tiles of 256 x 256 over block-row pairs pi >= (k+4)/2
@@ -122,18 +154,20 @@ __global__ __launch_bounds__(256, 1) void rest_x3_kernel(float* __restrict__ S, 
     const int64_t row0 = (int64_t)pi * kX3Tile, col0 = (int64_t)pj * kX3Tile;
 
     // chunk m of this wave: c = wave + 4 m; plane c / 16, operand (c / 8) % 2
-    // (0: rows of the tile, 1: columns), k-row pair c % 8 of the stage
-    auto issue = [&](int st, unsigned char* sbase) {
-      const void* g[12];
+    // (0: rows of the tile, 1: columns), k-row pair c % 8 of the stage. Byte
+    // offsets from the stage's first k row (fixed for the tile; at most 3 planes
+    // of 256 rows of b elements, far below 4 GB).
+    unsigned vo[12];
 #pragma unroll
-      for (int m = 0; m < 12; ++m) {
-        const int c = wave + 4 * m;
-        const int p = c >> 4, o = (c >> 3) & 1, r = c & 7;
-        const int tr = 2 * r + lk;  // k row inside the stage
-        const int fg = lr ^ ((tr & 3) << 2);
-        g[m] = Y + p * pstride + (int64_t)(st * kX3StageK + tr) * ldy + (o ? col0 : row0) + fg * 8;
-      }
-      x3d::dma12(g, sbase + wave * 1024);
+    for (int m = 0; m < 12; ++m) {
+      const int c = wave + 4 * m;
+      const int p = c >> 4, o = (c >> 3) & 1, r = c & 7;
+      const int tr = 2 * r + lk;  // k row inside the stage
+      const int fg = lr ^ ((tr & 3) << 2);
+      vo[m] = (unsigned)((p * pstride + (int64_t)tr * ldy + (o ? col0 : row0) + fg * 8) * 2);
+    }
+    auto issue = [&](int st, unsigned char* sbase) {
+      x3d::dma12s(vo, Y + (int64_t)st * kX3StageK * ldy, sbase + wave * 1024);
     };
 
     f32x16_t acc[4][4];
@@ -145,60 +179,79 @@ __global__ __launch_bounds__(256, 1) void rest_x3_kernel(float* __restrict__ S, 
         for (int r = 0; r < 16; ++r) acc[a][c][r] = 0.f;
 
     // Per block the six products accumulate smallest first (l h, h l, m m, m h,
-    // h m, h h); done plane by plane so that at most two planes of fragments are
-    // live: h and l, then h and m, then h.
-    auto compute = [&](const unsigned char* sb) {
+    // h m, h h). A stage's 24 operand fragments (three planes of the row and the
+    // column panels) are read into one of two register sets while the previous
+    // stage's products run: the barrier that releases stage it+1 sits before the
+    // last 16 products of stage it, and stage it+1's reads go out behind it.
+    struct Frags {
+      bf16x8_t ah[4], bh[4], al[4], bl[4], am[4], bm[4];
+    };
+    auto read_frags = [&](const unsigned char* sb, Frags& F) {
       // panel (plane p, operand o) at sb + (2 p + o) * kX3PanelBytes
       auto fa = [&](int p, int a) { return x3d::frag(sb + (2 * p) * kX3PanelBytes, wrow * 128 + a * 32, lane); };
       auto fbf = [&](int p, int c) { return x3d::frag(sb + (2 * p + 1) * kX3PanelBytes, wcol * 128 + c * 32, lane); };
-      bf16x8_t ah[4], bh[4], ax[4], bx[4], am[4], bm[4];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) { ah[a] = fa(0, a); ax[a] = fa(2, a); }
+      for (int a = 0; a < 4; ++a) { F.ah[a] = fa(0, a); F.al[a] = fa(2, a); F.am[a] = fa(1, a); }
 #pragma unroll
-      for (int c = 0; c < 4; ++c) { bh[c] = fbf(0, c); bx[c] = fbf(2, c); }
-      // the middle plane's reads go out with the others, in their own registers, so
-      // they are in flight while the first products run
-#pragma unroll
-      for (int a = 0; a < 4; ++a) am[a] = fa(1, a);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) bm[c] = fbf(1, c);
+      for (int c = 0; c < 4; ++c) { F.bh[c] = fbf(0, c); F.bl[c] = fbf(2, c); F.bm[c] = fbf(1, c); }
+    };
+    auto products_12 = [&](const Frags& F) {  // l h, h l, m m, m h, h m
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ax[a], bh[c], acc[a][c], 0, 0, 0);
-          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[a], bx[c], acc[a][c], 0, 0, 0);
+          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.al[a], F.bh[c], acc[a][c], 0, 0, 0);
+          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.ah[a], F.bl[c], acc[a][c], 0, 0, 0);
         }
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am[a], bm[c], acc[a][c], 0, 0, 0);
-          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am[a], bh[c], acc[a][c], 0, 0, 0);
-          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[a], bm[c], acc[a][c], 0, 0, 0);
+          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.am[a], F.bm[c], acc[a][c], 0, 0, 0);
+          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.am[a], F.bh[c], acc[a][c], 0, 0, 0);
+          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.ah[a], F.bm[c], acc[a][c], 0, 0, 0);
         }
+    };
+    auto products_3 = [&](const Frags& F) {  // h h
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[a], bh[c], acc[a][c], 0, 0, 0);
+          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.ah[a], F.bh[c], acc[a][c], 0, 0, 0);
     };
 
     __syncthreads();  // the previous tile's last reads are done before its buffers refill
     issue(0, sm0);
     issue(1, sm1);
-    for (int it0 = 0; it0 < nst; it0 += kX3Stages) {
-      static_for<0, kX3Stages>([&](auto U) __attribute__((always_inline)) {
+    issue(2, sm2);
+    __asm__ volatile("s_waitcnt vmcnt(24)" ::: "memory");  // stage 0 (this wave's part)
+    __syncthreads();
+    Frags F0, F1;
+    read_frags(sm0, F0);
+    // Unrolled by 6 (two register sets, three buffers) so that every index is a
+    // constant. Stage s lives in buffer s % 3.
+    for (int it0 = 0; it0 < nst; it0 += 6) {
+      static_for<0, 6>([&](auto U) __attribute__((always_inline)) {
         constexpr int u = U;
         const int it = it0 + u;
         if (it < nst) {
-          // stage it complete for this wave (stage it+1's twelve loads may be in flight)
-          if (it + 1 < nst) __asm__ volatile("s_waitcnt vmcnt(12)" ::: "memory");
-          else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          __syncthreads();
-          // buffer (u+2)%3 was last read in iteration it-1, before this barrier
-          if (it + 2 < nst) issue(it + 2, buf(std::integral_constant<int, (u + 2) % kX3Stages>{}));
-          compute(buf(std::integral_constant<int, u>{}));
+          Frags& cur = (u % 2 == 0) ? F0 : F1;
+          Frags& nxt = (u % 2 == 0) ? F1 : F0;
+          products_12(cur);
+          // keep those products (and the last use of the l and m fragments) above
+          // the barrier, so that the next stage's fragments can take their registers
+          __builtin_amdgcn_sched_barrier(0);
+          if (it + 1 < nst) {
+            // stage it+1 complete for this wave (stage it+2's twelve loads may be in
+            // flight); after the barrier it is complete for all, and every wave's
+            // reads of stage it (done before its products above) are over
+            if (it + 2 < nst) __asm__ volatile("s_waitcnt vmcnt(12)" ::: "memory");
+            else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (it + 3 < nst) issue(it + 3, buf(std::integral_constant<int, u % kX3Stages>{}));
+            read_frags(buf(std::integral_constant<int, (u + 1) % kX3Stages>{}), nxt);
+          }
+          products_3(cur);
         }
       });
     }
