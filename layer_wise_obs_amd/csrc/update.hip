@@ -49,11 +49,15 @@ struct NextDigit {
 
 // W[row0:, col0:] -= Z[rows, 0:K] R[r0:r0+K, cols]; zero the pruned entries of
 // columns [mask_j0, mask_jend); with HIST, the first key digit of columns >= hist_j0.
+// Tiles t = blockIdx.x + i gridDim.x: with HIST the grid is a few workgroups per
+// compute unit, so that each one adds its histogram to the global one once, after
+// all its tiles (the global atomics of one flush per tile met on the same bins).
 template <bool HIST>
 __global__ __launch_bounds__(256, 2) void update_kernel(float* __restrict__ W, int64_t c, int64_t b,
                                                      int64_t r0, int K, int64_t ldz,
                                                      int64_t col_begin, int64_t col_end,
-                                                     int ncol_tiles, const float* __restrict__ Z,
+                                                     int ncol_tiles, int64_t ntiles,
+                                                     const float* __restrict__ Z,
                                                      const float* __restrict__ R,
                                                      const uint8_t* __restrict__ mask,
                                                      int64_t mask_j0, int64_t mask_jend,
@@ -66,8 +70,11 @@ __global__ __launch_bounds__(256, 2) void update_kernel(float* __restrict__ W, i
     nd.sh = sh;
   }
   nd.zero();
-  const int64_t row0 = (int64_t)(blockIdx.x / ncol_tiles) * 128;
-  const int64_t col0 = col_begin + (int64_t)(blockIdx.x % ncol_tiles) * 128;
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+  // every wave is done with the previous tile's operands before they are restaged
+  if (t != (int64_t)blockIdx.x) __syncthreads();
+  const int64_t row0 = (t / ncol_tiles) * 128;
+  const int64_t col0 = col_begin + (t % ncol_tiles) * 128;
   const int rows = (int)((c - row0) < 128 ? (c - row0) : 128);
   const int cols = (int)((col_end - col0) < 128 ? (col_end - col0) : 128);
   f32x16_t acc[2][2];
@@ -93,6 +100,7 @@ __global__ __launch_bounds__(256, 2) void update_kernel(float* __restrict__ W, i
       if (HIST && col >= hist_j0) nd.add(v, gv[(cc >> 5) & 1]);
     }
   });
+  }
   nd.flush(hist);
 }
 
@@ -267,14 +275,18 @@ hipError_t launch_update(float* W, int64_t c, int64_t b, int64_t r0, int64_t K, 
                          mask_j0 + mask_w, gn, hist_j0, hist);
     return hipGetLastError();
   }
-  if (hist)
-    hipLaunchKernelGGL(update_kernel<true>, dim3((unsigned)(nct * nrt)), dim3(256), 0, s, W, c, b,
-                       r0, (int)K, ldz, col0, col_end, nct, Z, R, mask, mask_j0, mask_j0 + mask_w,
-                       gn, hist_j0, hist);
-  else
-    hipLaunchKernelGGL(update_kernel<false>, dim3((unsigned)(nct * nrt)), dim3(256), 0, s, W, c, b,
-                       r0, (int)K, ldz, col0, col_end, nct, Z, R, mask, mask_j0, mask_j0 + mask_w,
-                       gn, hist_j0, hist);
+  const int64_t ntiles = (int64_t)nct * nrt;
+  if (hist) {
+    // two workgroups per compute unit fit (LDS), 256 compute units
+    const int64_t grid = ntiles < 512 ? ntiles : 512;
+    hipLaunchKernelGGL(update_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, W, c, b, r0,
+                       (int)K, ldz, col0, col_end, nct, ntiles, Z, R, mask, mask_j0,
+                       mask_j0 + mask_w, gn, hist_j0, hist);
+  } else {
+    hipLaunchKernelGGL(update_kernel<false>, dim3((unsigned)ntiles), dim3(256), 0, s, W, c, b, r0,
+                       (int)K, ldz, col0, col_end, nct, ntiles, Z, R, mask, mask_j0,
+                       mask_j0 + mask_w, gn, hist_j0, hist);
+  }
   return hipGetLastError();
 }
 
