@@ -77,14 +77,8 @@ __global__ __launch_bounds__(256, 2) void update_kernel(float* __restrict__ W, i
   const int64_t col0 = col_begin + (t % ncol_tiles) * 128;
   const int rows = (int)((c - row0) < 128 ? (c - row0) : 128);
   const int cols = (int)((col_end - col0) < 128 ? (col_end - col0) : 128);
-  f32x16_t acc[2][2];
-  float* C = W + row0 * b + col0;
-  gemm_load_c(acc, C, b, rows, cols);  // W tile, then W - Z R
-  gemm_tile_x3<false>(Z + row0 * ldz, ldz, rows, R + r0 * b + col0, b, cols, K, acc, smem,
-                             true);
-  const bool masked = col0 < mask_jend && col0 + 128 > mask_j0;
   // score weights of this lane's two columns (wave column 64 (wave & 1), then +32),
-  // loaded before the stores so that no load waits inside the loop below
+  // loaded before the GEMM so that their latency hides behind it
   float gv[2] = {0.f, 0.f};
   if constexpr (HIST) {
     const int cl = (int)((threadIdx.x >> 6) & 1) * 64 + (int)(threadIdx.x & 31);
@@ -92,6 +86,12 @@ __global__ __launch_bounds__(256, 2) void update_kernel(float* __restrict__ W, i
     for (int tj = 0; tj < 2; ++tj)
       if (cl + 32 * tj < cols && col0 + cl + 32 * tj >= hist_j0) gv[tj] = gn[col0 + cl + 32 * tj];
   }
+  f32x16_t acc[2][2];
+  float* C = W + row0 * b + col0;
+  gemm_load_c(acc, C, b, rows, cols);  // W tile, then W - Z R
+  gemm_tile_x3<false>(Z + row0 * ldz, ldz, rows, R + r0 * b + col0, b, cols, K, acc, smem,
+                             true);
+  const bool masked = col0 < mask_jend && col0 + 128 > mask_j0;
   gemm_foreach(acc, [&](int r, int cc, float v) {
     if (r < rows && cc < cols) {
       const int64_t row = row0 + r, col = col0 + cc;
