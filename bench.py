@@ -63,7 +63,7 @@ def syrk_traffic():
     if the kernel source changed since the counters were taken."""
     import hashlib
     import re
-    prof = os.path.join(ROOT, "profiles", "syrk_bf16_down_proj_11008x262144_traffic.md")
+    prof = os.path.join(ROOT, "profiles", "syrk_rect_down_proj_11008x262144_traffic.md")
     try:
         txt = open(prof).read()
         d = json.loads(re.search(r"```json\n(.*?)\n```", txt, re.S).group(1))
@@ -217,9 +217,12 @@ def main():
     ms_step = elapsed * 1000.0 / max(args.steps, 1)
     _log(f"{ms_step:.2f} ms per layer")
 
-    # dominant kernel: the bf16 syrk, same launch as inside the step
+    # dominant kernel: the bf16 syrk, same launch as inside the step (with a
+    # workspace, as th_prune_layer gives it: 384 x 256 rectangles, the last round's
+    # tiles cut into pieces summed by a fix-up kernel; the events cover both)
     H = torch.zeros((b, b), dtype=torch.float32, device=dev)
-    syrk_ms = _ev_time(lambda: L.hessian_accumulate(H, X), max(args.steps, 3), stream)
+    hws = L.workspace(L.hessian_workspace_size(n, b), dev)
+    syrk_ms = _ev_time(lambda: L.hessian_accumulate(H, X, hws), max(args.steps, 3), stream)
     syrk_avg = sum(syrk_ms) / len(syrk_ms)
     syrk_flops = float(n) * b * (b + 1)  # one triangle of X^T X: n*b(b+1)
     achieved = syrk_flops / (syrk_avg * 1e-3) / 1e12
@@ -227,7 +230,7 @@ def main():
 
     # the layer from a given Hessian (factor + block loop only)
     H.zero_()
-    L.hessian_accumulate(H, X)
+    L.hessian_accumulate(H, X, hws)
     lam_h = L.hessian_finalize(H, lam_rel, True)
 
     def step_h():
@@ -279,7 +282,8 @@ def main():
         "config": {"workload": f"down_proj {c}x{b}, {pat_name}, block {block}, X {n} tokens bf16 "
                                f"({'ReLU-like, ' if st.relu else ''}{st.outlier_count} channels x{st.outlier_scale:g}), "
                                f"lambda {lam_rel} relative"},
-        "roofline": {"bound": "mfma", "kernel": "syrk_bf16_kernel", "achieved": achieved,
+        "roofline": {"bound": "mfma", "kernel": "syrk_rect_kernel (+ syrk_rect_fix_kernel)",
+                     "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": syrk_traffic() if args.layer == "down_proj-4096x11008" else None,
                      "launch_ms": syrk_avg,

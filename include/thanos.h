@@ -322,6 +322,20 @@ th_status th_prune_baseline(void* W, th_dtype wdt, int64_t c, int64_t b, th_base
 th_status th_debug_factor(const float* H, int64_t b, float* U, void* workspace,
                           size_t workspace_bytes, th_stream_t stream);
 
+/* H += 2 X^T X on the lower triangle through the 384 x 256 rectangles that
+ * th_hessian_accumulate takes for large layers (bf16 X, [EXPL, "SparseGPT:
+ * Second-Order Reconstruction at Scale"]), with the work split fixed here
+ * instead of by the device: whole tiles in rounds of P workgroups, each remaining
+ * tile cut into m pieces of consecutive 32-token stages whose sums are added in a
+ * fixed order (m = 0: chosen as for the device's compute units; m = 1: those
+ * tiles whole as well). Arguments as th_hessian_accumulate with t >= 32 and
+ * ldx < 2^25; 1 <= P <= 4096, 0 <= m <= t / 32; workspace: >= (number of cut
+ * tiles) * m * 98304 * 4 bytes (TH_ERR_WORKSPACE if smaller; ceil(b/384) *
+ * ceil(b/256) * m * 98304 * 4 always suffices). Asynchronous. */
+th_status th_debug_syrk_rect(float* H, const void* X_chunk, int64_t t, int64_t b, int64_t ldx,
+                             int32_t P, int32_t m, void* workspace, size_t workspace_bytes,
+                             th_stream_t stream);
+
 /* Message for the last non-OK status on this thread (never NULL). */
 const char* th_last_error(void);
 

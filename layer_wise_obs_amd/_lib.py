@@ -82,6 +82,7 @@ _SIG = {
     "th_debug_select_global": [_P, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P,
                                ctypes.c_size_t, _P],
     "th_debug_factor": [_P, _I64, _P, _P, ctypes.c_size_t, _P],
+    "th_debug_syrk_rect": [_P, _P, _I64, _I64, _I64, _I32, _I32, _P, ctypes.c_size_t, _P],
     "th_column_sq_norms_workspace_size": [_I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
     "th_column_sq_norms": [_P, _I32, _I64, _I64, _I64, _P, _P, ctypes.c_size_t, _P],
     "th_prune_baseline": [_P, _I32, _I64, _I64, _I32, _P, ctypes.POINTER(PruneParams), _P, _P],
@@ -378,6 +379,17 @@ def debug_select_global(scores, b_full: int, j0: int, blk: int, r: int):
     _check(lib().th_debug_select_global(_ptr(scores), c, f, b_full, j0, blk, r, _ptr(mask),
                                         _ptr(s_k), _ptr(ws), ws.numel(), _stream(scores.device)))
     return mask, s_k
+
+
+def debug_syrk_rect(H, X, P, m=0):
+    """H (b x b fp32, lower) += 2 X^T X through the rectangles: whole tiles in rounds
+    of P workgroups, the rest cut into m pieces each (m = 0: chosen)."""
+    _require_cuda(H, X)
+    t, b = X.shape
+    tiles = -(-b // 384) * -(-b // 256)  # bounds the cut tiles
+    ws = workspace(tiles * max(m, 16) * 98304 * 4, H.device)
+    _check(lib().th_debug_syrk_rect(_ptr(H), _ptr(X), t, b, X.stride(0), P, m, _ptr(ws),
+                                    ws.numel(), _stream(X.device)))
 
 
 def debug_factor(H):

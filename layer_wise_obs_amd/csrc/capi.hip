@@ -135,11 +135,8 @@ PruneLayout layout_prune(void* ws, int64_t c, int64_t b, int64_t n, bool have_x,
   }
   L.syrk_part = nullptr;
   if (have_x && xdt == TH_BF16) {
-    const int splits = syrk_bf16_splits(n, b);
-    if (splits > 1) {
-      const int64_t nt = cdiv(b, 256);
-      L.syrk_part = cv.take<float>((size_t)splits * (nt * (nt + 1) / 2) * 256 * 256);
-    }
+    const size_t nf = syrk_bf16_workspace_floats(n, b);
+    if (nf > 0) L.syrk_part = cv.take<float>(nf);
   }
   L.bytes = cv.off;
   return L;
@@ -347,9 +344,7 @@ const char* th_last_error(void) { return g_last_error.c_str(); }
 
 th_status th_hessian_workspace_size(int64_t t, int64_t b, size_t* bytes) {
   if (!bytes || t < 0 || b < 1) return fail(TH_ERR_INVALID_ARG, "bad arguments");
-  const int splits = syrk_bf16_splits(t, b);
-  const int64_t nt = cdiv(b, 256);
-  *bytes = splits > 1 ? (size_t)splits * (nt * (nt + 1) / 2) * 256 * 256 * sizeof(float) : 0;
+  *bytes = syrk_bf16_workspace_floats(t, b) * sizeof(float);
   return TH_OK;
 }
 
@@ -567,11 +562,8 @@ FactorLayout layout_factor(void* ws, int64_t b, int64_t n, bool have_x, th_dtype
   F.P = cv.take<float>(chol_panel_floats(b));
   F.syrk_part = nullptr;
   if (have_x && xdt == TH_BF16) {
-    const int splits = syrk_bf16_splits(n, b);
-    if (splits > 1) {
-      const int64_t nt = cdiv(b, 256);
-      F.syrk_part = cv.take<float>((size_t)splits * (nt * (nt + 1) / 2) * 256 * 256);
-    }
+    const size_t nf = syrk_bf16_workspace_floats(n, b);
+    if (nf > 0) F.syrk_part = cv.take<float>(nf);
   }
   F.bytes = cv.off;
   return F;
@@ -921,6 +913,25 @@ th_status th_debug_factor(const float* H, int64_t b, float* U, void* workspace,
   TH_HIP(hipMemcpyAsync(&flag, &st->not_spd, sizeof(int), hipMemcpyDeviceToHost, s), "flag");
   TH_HIP(hipStreamSynchronize(s), "sync");
   if (flag) return fail(TH_ERR_NOT_SPD, "damped Hessian is not positive definite");
+  return TH_OK;
+}
+
+th_status th_debug_syrk_rect(float* H, const void* X, int64_t t, int64_t b, int64_t ldx, int32_t P,
+                             int32_t m, void* workspace, size_t workspace_bytes,
+                             th_stream_t stream) {
+  if (!H || !X) return fail(TH_ERR_INVALID_ARG, "NULL argument");
+  if (t < 32 || b < 1 || ldx < b || ldx >= ((int64_t)1 << 25) || P < 1 || P > 4096 || m < 0 ||
+      m > t / 32)
+    return fail(TH_ERR_INVALID_ARG,
+                "need t >= 32, 1 <= b <= ldx < 2^25, 1 <= P <= 4096, 0 <= m <= t / 32");
+  if (ldx % 8 || b % 8 || ((uintptr_t)X & 15))
+    return fail(TH_ERR_INVALID_ARG, "bf16 X needs b % 8 == 0, ldx % 8 == 0 and 16-byte alignment");
+  const size_t need = syrk_rect_workspace_floats(t, b, P, m) * sizeof(float);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(TH_ERR_WORKSPACE, "workspace too small");
+  TH_HIP(launch_syrk_rect(H, (const unsigned short*)X, t, b, ldx, (float*)workspace, P, m,
+                          (hipStream_t)stream),
+         "syrk rectangles");
   return TH_OK;
 }
 

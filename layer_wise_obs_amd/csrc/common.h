@@ -109,8 +109,15 @@ __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 
 // ---------------------------------------------------------------- launchers
 // hessian.hip
 int syrk_bf16_splits(int64_t t, int64_t b);
+// workspace (floats) of the bf16 syrk for t tokens of b features: 0 when none helps
+size_t syrk_bf16_workspace_floats(int64_t t, int64_t b);
 hipError_t launch_syrk_bf16(float* H, const unsigned short* X, int64_t t, int64_t b, int64_t ldx,
                             float* partials, int splits, hipStream_t s);
+// the 384 x 256 rectangles, whole tiles in rounds of P workgroups and the rest cut
+// into m pieces each (m = 0: chosen); part holds syrk_rect_workspace_floats
+size_t syrk_rect_workspace_floats(int64_t t, int64_t b, int P, int m);
+hipError_t launch_syrk_rect(float* H, const unsigned short* X, int64_t t, int64_t b, int64_t ldx,
+                            float* part, int P, int m, hipStream_t s);
 hipError_t launch_syrk_f32(float* H, const float* X, int64_t t, int64_t b, int64_t ldx,
                            hipStream_t s);
 hipError_t launch_lambda(const float* H, int64_t b, double lam, int rel, int h_is_damped,

@@ -248,6 +248,280 @@ __global__ __launch_bounds__(kDThreads) void syrk_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------------------- 384 x 256 tiles
+// The same pipeline on 384 x 256 rectangles (384 rows of H, 256 columns): each
+// wave owns 192 x 128 (6 x 4 accumulator blocks, 384 registers, AGPRs and VGPRs
+// together), so a 32-token stage brings 40 KB into LDS for 1.5x the MFMA work of
+// a 256 x 256 tile (32 KB): 17% fewer staged bytes per flop. A stage is five
+// sub-panels of 128 features (three of the rows, two of the columns), each 32
+// token rows of 256 bytes with the 16-byte pieces XOR-swizzled by (token & 3)
+// like the square tiles' panels. Loads use the saddr form: a wave-uniform stage
+// base plus per-lane offsets fixed for the whole tile.
+constexpr int kRR = 384, kRC = 256;            // rows x columns of a rectangle
+constexpr int kRSub = 128;                     // features per sub-panel
+constexpr int kRSubRow = kRSub * 2;            // 256 bytes: one token row of a sub-panel
+constexpr int kRSubBytes = kDBK * kRSubRow;    // 8 KB
+constexpr int kRStageBytes = 5 * kRSubBytes;   // 40 KB
+constexpr int kRStages = 4;
+constexpr int kRLoads = kRStageBytes / 1024 / 4;  // 1 KB loads per wave per stage
+static_assert(kRLoads == 10, "lds_dma10s");
+
+// column tiles of strip r that hold an entry on or below the diagonal
+__host__ __device__ __forceinline__ int rect_cols(int r, int64_t b) {
+  const int64_t last = ((int64_t)kRR * (r + 1) < b ? (int64_t)kRR * (r + 1) : b) - 1;
+  return (int)(last / kRC) + 1;
+}
+
+// Tile order: super-tiles of 4 strips x 8 column tiles, as for the squares.
+__device__ __forceinline__ void rect_tile_of(int lin, int nstrips, int64_t b, int& ti, int& tj) {
+  for (int sr = 0; sr * kSupR < nstrips; ++sr) {
+    const int r0 = sr * kSupR, r1 = min(nstrips, r0 + kSupR);
+    const int cmax = rect_cols(r1 - 1, b);
+    for (int sc = 0; sc * kSupC < cmax; ++sc) {
+      const int c0 = sc * kSupC, c1 = c0 + kSupC;
+      int cnt = 0;
+      for (int r = r0; r < r1; ++r) cnt += max(0, min(c1, rect_cols(r, b)) - c0);
+      if (lin < cnt) {
+        for (int r = r0; r < r1; ++r) {
+          const int w = max(0, min(c1, rect_cols(r, b)) - c0);
+          if (lin < w) {
+            ti = r;
+            tj = c0 + lin;
+            return;
+          }
+          lin -= w;
+        }
+      }
+      lin -= cnt;
+    }
+  }
+  ti = tj = 0;  // not reached for lin < the tile count
+}
+
+// Offset of (token t, piece fg) inside a 128-feature sub-panel.
+__device__ __forceinline__ int rpiece_off(int t, int fg) {
+  return t * kRSubRow + ((fg ^ ((t & 3) << 2)) << 4);
+}
+
+// MFMA operand (32 features from f0 of a sub-panel x 16 tokens from ks16), lane
+// layout as in tr_frag.
+__device__ __forceinline__ bf16x8_t rtr_frag(const unsigned char* sub, int f0, int ks16, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int fb = f0 + ((g & 1) << 4) + ((s & 3) << 2);
+  const int tb = ks16 + ((g >> 1) << 3) + (s >> 2);
+  const int fg = fb >> 3, within = (fb & 7) << 1;
+  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16_t*)(sub + rpiece_off(tb, fg) + within));
+  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16_t*)(sub + rpiece_off(tb + 4, fg) + within));
+  typedef short v8i16_t __attribute__((ext_vector_type(8)));
+  const v8i16_t r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
+// Work split: the first F = ntiles / P * P tiles run whole, in F rounds of P
+// workgroups (P = the compute units); each of the T < P remaining tiles is cut
+// into m pieces of consecutive 32-token stages, piece i of tile j being
+// workgroup F P + i T + j, with m chosen so that the T m pieces fill whole rounds
+// of P well. A whole tile is added to H at once; piece i T + j goes to slot
+// i T + j of the workspace, in the accumulators' register order, and
+// syrk_rect_fix_kernel adds the m pieces of each tile in order of i. Workgroups
+// are numbered XCD-major (each XCD's concurrent workgroups take consecutive
+// tiles, or consecutive tiles' pieces of the same stages).
+struct RectSplit {
+  int F, T, m;  // whole tiles, tiles cut in pieces, pieces per cut tile
+  int nk;       // 32-token stages per tile
+  int per_xcd;  // workgroups per XCD in the whole-tile and the piece parts
+  int pper_xcd;
+};
+constexpr int kRTileElems = kRR * kRC;  // one slot: 98304 floats
+
+__global__ __launch_bounds__(kDThreads, 1) void syrk_rect_kernel(
+    float* __restrict__ H, const unsigned short* __restrict__ X, int64_t t, int64_t b, int64_t ldx,
+    int nstrips, RectSplit sp, float* __restrict__ part) {
+  const int wg = blockIdx.x;
+  const int nk = sp.nk;
+  int lin, s0 = 0, s1 = nk, slot = -1;
+  if (wg < 8 * sp.per_xcd) {
+    lin = (wg % 8) * sp.per_xcd + wg / 8;
+    if (lin >= sp.F) return;
+  } else {
+    const int w = wg - 8 * sp.per_xcd;
+    const int p = (w % 8) * sp.pper_xcd + w / 8;  // piece i T + j
+    if (p >= sp.T * sp.m) return;
+    const int i = p / sp.T, j = p % sp.T;
+    lin = sp.F + j;
+    s0 = (int)((int64_t)i * nk / sp.m);
+    s1 = (int)((int64_t)(i + 1) * nk / sp.m);
+    slot = p;
+  }
+  int ti, tj;
+  rect_tile_of(lin, nstrips, b, ti, tj);
+  const int64_t I0 = (int64_t)ti * kRR, J0 = (int64_t)tj * kRC;
+
+  __shared__ __attribute__((aligned(1024))) unsigned char sm0[kRStageBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char sm1[kRStageBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char sm2[kRStageBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char sm3[kRStageBytes];
+  auto buf = [&](auto S) -> unsigned char* {
+    constexpr int s = decltype(S)::value;
+    if constexpr (s == 0) return sm0;
+    else if constexpr (s == 1) return sm1;
+    else if constexpr (s == 2) return sm2;
+    else return sm3;
+  };
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wrow = wave >> 1, wcol = wave & 1;
+  const int lr = lane & 31, lk = lane >> 5;
+
+  // Loader: chunk q (0..39) of a stage is sub-panel q/8, token rows 4(q%8) ..
+  // 4(q%8)+3, at LDS offset 1024 q; wave w loads q = w + 4m, m = 2k + o
+  // (k = 0..4, o = 0, 1): sub-panel k, token rows 4w + 16o + 0..3. Lane l writes
+  // bytes [16 l, 16 l + 16) of its chunk: token row 4w + 16o + l/16, LDS piece
+  // l%16, which holds the feature piece (l%16) ^ 4(row & 3) (row & 3 = (l/16) & 3
+  // for both o). The per-lane offset vo[k] is that of o = 0; o = 1 is 16 token
+  // rows further, a uniform step taken in the second base address.
+  unsigned vo[5];
+  {
+    const int tr = 4 * wave + (lane >> 4);
+    const int fg = (lane & 15) ^ ((tr & 3) << 2);
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+      int64_t f = (k < 3 ? I0 + k * kRSub : J0 + (k - 3) * kRSub) + fg * 8;
+      f = f < b ? f : 0;  // features past b only feed outputs that are never stored
+      vo[k] = (unsigned)(((int64_t)tr * ldx + f) * 2);
+    }
+  }
+  // t is a multiple of 32 (the caller adds the remaining tokens separately).
+  // Stages past the piece are loaded too (at most three, never read) so that every
+  // stage has the same number of loads for the vmcnt waits; past the end of the
+  // tokens they re-read the last stage.
+  auto issue_stage = [&](int st, unsigned char* sbase) {
+    const int64_t tok0 = (int64_t)st * kDBK;
+    const int64_t br = tok0 < t - kDBK ? tok0 : t - kDBK;
+    lds_dma10s(vo, X + br * ldx, X + (br + 16) * ldx, sbase + wave * 1024);
+  };
+
+  f32x16_t acc[6][4];
+#pragma unroll
+  for (int a = 0; a < 6; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][c][r] = 0.f;
+
+  bf16x8_t af0[6], bf0[4], af1[6], bf1[4];
+  auto read_frags = [&](const unsigned char* sb, int ks, bf16x8_t (&af)[6], bf16x8_t (&bf)[4]) {
+#pragma unroll
+    for (int a = 0; a < 6; ++a) {
+      const int fa = wrow * 192 + a * 32;
+      af[a] = rtr_frag(sb + (fa >> 7) * kRSubBytes, fa & 127, ks * 16, lane);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      bf[c] = rtr_frag(sb + (3 + wcol) * kRSubBytes, c * 32, ks * 16, lane);
+  };
+  // 256 accumulator registers are AGPRs: the compiler places the results of the
+  // MFMA builtin there. The other 128 (rows a = 4, 5) are kept in VGPRs through
+  // the VGPR form of the instruction written out (operands and accumulators as
+  // "v"); their results are read only after the loop, behind explicit wait states.
+  auto mfmas = [&](const bf16x8_t (&af)[6], const bf16x8_t (&bf)[4]) {
+#pragma unroll
+    for (int a = 0; a < 6; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (a < 4) {
+          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bf[c], acc[a][c], 0, 0, 0);
+        } else {
+          __asm__ volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                           : "+v"(acc[a][c])
+                           : "v"(af[a]), "v"(bf[c]));
+        }
+      }
+  };
+
+  const int n = s1 - s0;
+  issue_stage(s0, sm0);
+  issue_stage(s0 + 1, sm1);
+  issue_stage(s0 + 2, sm2);
+  __asm__ volatile("s_waitcnt vmcnt(20)" ::: "memory");
+  __syncthreads();
+  read_frags(sm0, 0, af0, bf0);
+  for (int l0 = 0; l0 < n; l0 += kRStages) {
+    static_for<0, kRStages>([&](auto U) __attribute__((always_inline)) {
+      constexpr int u = U;
+      const int l = l0 + u;
+      if (l < n) {
+        issue_stage(s0 + l + 3, buf(std::integral_constant<int, (u + 3) % kRStages>{}));
+        read_frags(buf(std::integral_constant<int, u>{}), 1, af1, bf1);
+        mfmas(af0, bf0);
+        __asm__ volatile("s_waitcnt vmcnt(20)" ::: "memory");
+        unsigned char* nb = buf(std::integral_constant<int, (u + 1) % kRStages>{});
+        __syncthreads();
+        read_frags(nb, 0, af0, bf0);
+        mfmas(af1, bf1);
+      }
+    });
+  }
+  // wait states between the last written-out MFMA and the first read of its result
+  __asm__ volatile("s_waitcnt vmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+
+  if (slot < 0) {
+#pragma unroll
+    for (int a = 0; a < 6; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = I0 + wrow * 192 + a * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
+          const int64_t col = J0 + wcol * 128 + c * 32 + lr;
+          if (row < b && col < b && col <= row) H[row * b + col] += 2.0f * acc[a][c][r];
+        }
+  } else {
+    float* dst = part + (int64_t)slot * kRTileElems;
+#pragma unroll
+    for (int a = 0; a < 6; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          dst[((wave * 6 + a) * 4 + c) * 1024 + r * 64 + lane] = acc[a][c][r];
+  }
+}
+
+// H += 2 (sum of the m pieces in order) for each cut tile. Block (g, j): tile F + j,
+// accumulator group g = (wave * 6 + a) * 4 + c (1024 floats, r * 64 + lane); each
+// thread takes four consecutive lanes: four consecutive columns of one row.
+__global__ __launch_bounds__(256) void syrk_rect_fix_kernel(float* __restrict__ H,
+                                                            const float* __restrict__ part,
+                                                            int64_t b, int nstrips, RectSplit sp) {
+  const int j = blockIdx.y, g = blockIdx.x;
+  int ti, tj;
+  rect_tile_of(sp.F + j, nstrips, b, ti, tj);
+  const int64_t I0 = (int64_t)ti * kRR, J0 = (int64_t)tj * kRC;
+  const int wave = g / 24, a = (g / 4) % 6, c = g % 4;
+  const int wrow = wave >> 1, wcol = wave & 1;
+  const int e = threadIdx.x * 4;
+  const int r = e >> 6, lane = e & 63;
+  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < sp.m; ++i)
+    s += *(const f32x4_t*)(part + ((int64_t)i * sp.T + j) * kRTileElems + g * 1024 + e);
+  const int64_t row = I0 + wrow * 192 + a * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+  const int64_t col = J0 + wcol * 128 + c * 32 + (lane & 31);  // a multiple of 4; b % 8 == 0
+  if (row >= b || col >= b || col > row) return;
+  float* h = H + row * b + col;
+  if (col + 3 <= row && ((uintptr_t)h & 15) == 0) {
+    f32x4_t v = *(f32x4_t*)h;
+    v += 2.0f * s;
+    *(f32x4_t*)h = v;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (col + q <= row) h[q] += 2.0f * s[q];
+  }
+}
+
 // Fixed-order sum of the token splits: H += 2 * sum_s partial_s.
 __global__ void syrk_reduce_kernel(float* __restrict__ H, const float* __restrict__ partials,
                                    int64_t b, int ntiles, int splits) {
@@ -406,9 +680,119 @@ int syrk_bf16_splits(int64_t t, int64_t b) {
   return (int)splits;
 }
 
+namespace {
+
+// compute units of the current device (the persistent grid of the rectangles)
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  return n;
+}
+
+int64_t rect_tiles(int64_t b) {
+  const int nstrips = (int)cdiv(b, kRR);
+  int64_t n = 0;
+  for (int r = 0; r < nstrips; ++r) n += rect_cols(r, b);
+  return n;
+}
+
+// The rectangles pay when every workgroup gets at least 64 stages (2048 tokens).
+bool rect_applies(int64_t t, int64_t b, int P) {
+  return t >= kDBK && rect_tiles(b) * (t / kDBK) >= (int64_t)64 * P;
+}
+
+// Whole tiles in complete rounds of P, the rest cut into m pieces each (m = 0 when
+// nothing is cut): m minimises the rounds the pieces take, in tiles' time, among
+// 1..min(nk / 32, 4P / T) (pieces of at least 32 stages, at most 4P slots); m = 1
+// runs those tiles whole as well. m_force > 0 fixes m (1 <= m_force <= nk).
+RectSplit rect_split(int64_t ntiles, int nk, int P, int m_force) {
+  RectSplit sp;
+  sp.nk = nk;
+  sp.F = (int)(ntiles / P * P);
+  sp.T = (int)(ntiles - sp.F);
+  sp.m = 0;
+  if (sp.T > 0) {
+    if (m_force > 0) {
+      sp.m = m_force;
+    } else {
+      int mmax = nk / 32;
+      if (mmax > 4 * P / sp.T) mmax = 4 * P / sp.T;
+      double best = 1.0;  // m = 1: one more round of whole tiles
+      sp.m = 1;
+      for (int m = 2; m <= mmax; ++m) {
+        const double cost = (double)cdiv((int64_t)sp.T * m, P) / m;
+        if (cost < best - 1e-9) {
+          best = cost;
+          sp.m = m;
+        }
+      }
+    }
+    if (sp.m == 1) {
+      sp.F = (int)ntiles;
+      sp.T = 0;
+      sp.m = 0;
+    }
+  }
+  sp.per_xcd = (int)cdiv(sp.F, 8);
+  sp.pper_xcd = (int)cdiv((int64_t)sp.T * sp.m, 8);
+  return sp;
+}
+
+size_t rect_workspace_floats(const RectSplit& sp) { return (size_t)sp.T * sp.m * kRTileElems; }
+
+}  // namespace
+
+size_t syrk_bf16_workspace_floats(int64_t t, int64_t b) {
+  const int splits = syrk_bf16_splits(t, b);
+  const int64_t nt = cdiv(b, kTile);
+  // the square tiles' token splits (also taken when ldx rules out the rectangles)
+  const size_t sq = splits > 1 ? (size_t)splits * (size_t)(nt * (nt + 1) / 2) * kTile * kTile : 0;
+  const int P = device_cus();
+  if (!rect_applies(t, b, P)) return sq;
+  const size_t r = rect_workspace_floats(rect_split(rect_tiles(b), (int)(t / kDBK), P, 0));
+  return r > sq ? r : sq;
+}
+
+size_t syrk_rect_workspace_floats(int64_t t, int64_t b, int P, int m) {
+  if (t < kDBK) return 0;
+  return rect_workspace_floats(rect_split(rect_tiles(b), (int)(t / kDBK), P, m));
+}
+
+hipError_t launch_syrk_rect(float* H, const unsigned short* X, int64_t t, int64_t b, int64_t ldx,
+                            float* part, int P, int m, hipStream_t s) {
+  const int64_t tf = t / kDBK * kDBK;  // whole stages; the rest goes to the square tiles
+  if (tf > 0) {
+    const int nstrips = (int)cdiv(b, kRR);
+    const RectSplit sp = rect_split(rect_tiles(b), (int)(tf / kDBK), P, m);
+    const int grid = 8 * (sp.per_xcd + sp.pper_xcd);
+    hipLaunchKernelGGL(syrk_rect_kernel, dim3(grid), dim3(kDThreads), 0, s, H, X, tf, b, ldx,
+                       nstrips, sp, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (sp.T > 0) {
+      hipLaunchKernelGGL(syrk_rect_fix_kernel, dim3(96, sp.T), dim3(256), 0, s, H, part, b, nstrips,
+                         sp);  // 96 groups of 1024 floats per tile, four per thread
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  if (tf == t) return hipSuccess;
+  return launch_syrk_bf16(H, X + tf * ldx, t - tf, b, ldx, nullptr, 1, s);
+}
+
 hipError_t launch_syrk_bf16(float* H, const unsigned short* X, int64_t t, int64_t b, int64_t ldx,
                             float* partials, int splits, hipStream_t s) {
   if (t <= 0 || b <= 0) return hipSuccess;
+  if (partials != nullptr && (int64_t)64 * ldx < ((int64_t)1 << 31)) {
+    // 384 x 256 rectangles on a persistent grid (per-lane load offsets of 32
+    // token rows stay below 2^31 bytes); the workspace holds the split tiles
+    const int P = device_cus();
+    if (rect_applies(t, b, P)) return launch_syrk_rect(H, X, t, b, ldx, partials, P, 0, s);
+  }
   const int nt = (int)cdiv(b, kTile);
   const int ntiles = nt * (nt + 1) / 2;
   const int per_xcd = (int)cdiv(ntiles, 8);

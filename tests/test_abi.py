@@ -26,7 +26,7 @@ def test_header_declares_the_path():
                  "th_factor_workspace_size", "th_prune_layer_factored",
                  "th_prune_layer_factored_workspace_size", "th_gated_ffn_input",
                  "th_prune_layer_alpha", "th_prune_layer_alpha_workspace_size",
-                 "th_prune_layer_noalloc"):
+                 "th_prune_layer_noalloc", "th_debug_syrk_rect"):
         assert must in names
 
 
@@ -85,10 +85,15 @@ def test_invalid_arguments_are_rejected_before_any_launch():
 def test_workspace_size_queries():
     L = _lib.lib()
     out = ctypes.c_size_t(0)
+    # 659 rectangles of 384 x 256 (without a device the split assumes 256 compute
+    # units): 512 whole in two rounds, the other 147 cut into 5 pieces of 8192 / 5
+    # stages, one slot of 384 x 256 floats per piece
     assert L.th_hessian_workspace_size(262144, 11008, ctypes.byref(out)) == 0
-    assert out.value == 0  # 946 tiles: no token split
+    assert out.value == 147 * 5 * 384 * 256 * 4
     assert L.th_hessian_workspace_size(262144, 4096, ctypes.byref(out)) == 0
-    assert out.value > 0  # 136 tiles: token split with a fixed-order reduction
+    assert out.value > 0  # 101 rectangles, all cut into pieces
+    assert L.th_hessian_workspace_size(1000, 520, ctypes.byref(out)) == 0
+    assert out.value > 0  # 10 square tiles: token split with a fixed-order reduction
     assert L.th_reconstruction_error_workspace_size(4096, 11008, 0, ctypes.byref(out)) == 0
     assert out.value >= 2 * 4096 * 11008 * 4
 

@@ -57,6 +57,33 @@ def test_hessian_bf16_matches_oracle(t, b, ws):
     assert np.all(np.triu(H, 1) == 0.0)  # the strict upper triangle is untouched
 
 
+# The rectangles with the work split fixed: wgs workgroups per round of whole
+# tiles, the remaining tiles cut into m pieces of 32-token stages (m = 0: chosen,
+# which for these short inputs keeps every tile whole; m = t // 32: one stage per
+# piece); ragged t leaves t % 32 tokens to the square tiles.
+@pytest.mark.parametrize("t,b,wgs,m", [(1000, 520, 1, 0), (1000, 520, 3, 4), (1000, 520, 8, 0),
+                                       (1000, 520, 8, 31), (1000, 520, 16, 5),
+                                       (2080, 1032, 4, 3), (64, 8, 4, 2), (4127, 1160, 24, 0),
+                                       (4127, 1160, 7, 7)])
+def test_hessian_rectangles_match_oracle(t, b, wgs, m):
+    _say(f"hessian rectangles t={t} b={b} wgs={wgs} m={m}")
+    _, X = _inputs(4, b, t, 14, relu=True)
+    Xd = X.to(DEV)
+    H = torch.zeros((b, b), dtype=torch.float32, device=DEV)
+    L.debug_syrk_rect(H, Xd, wgs, m)
+    Hc = H.cpu().numpy()
+    G = O.gram(X)
+    assert P.rel_fro(_tril(Hc), _tril(2 * G)) <= P.H_RTOL
+    assert np.all(np.triu(Hc, 1) == 0.0)
+    # exact bf16 products summed in fp32 in another order: close to the square tiles
+    Hs = _gpu_hessian(X).cpu().numpy()
+    assert P.rel_fro(_tril(Hc), _tril(Hs)) <= 1e-6
+    # a fixed summation order: bit-identical on a second call
+    H2 = torch.zeros_like(H)
+    L.debug_syrk_rect(H2, Xd, wgs, m)
+    assert torch.equal(H, H2)
+
+
 def test_hessian_f32_and_finalize():
     _say("hessian f32 + finalize (config 1 shapes)")
     cfg = synth.config(1)
