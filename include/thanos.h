@@ -102,9 +102,11 @@ typedef struct {
  * fp32 and accumulate in fp32 on the matrix cores; TH_F32: fp32 FMA). ldx >= b
  * and, for TH_BF16, b % 8 == 0, ldx % 8 == 0 and a 16-byte aligned X. H: b x b fp32, zeroed by
  * the caller before the first chunk; the strict upper triangle is not touched.
- * workspace (optional, may be NULL with workspace_bytes 0) lets small b split the
- * token range over more workgroups; size from th_hessian_workspace_size. The
- * summation order is fixed, so repeated calls give bit-identical H. Asynchronous. */
+ * workspace (optional, may be NULL with workspace_bytes 0; 16-byte aligned) lets
+ * small b split the token range over more workgroups and large b run 384 x 256
+ * tiles with the last round's tiles cut into token pieces; size from
+ * th_hessian_workspace_size. The summation order is fixed, so repeated calls give
+ * bit-identical H. Asynchronous. */
 th_status th_hessian_accumulate(float* H, const void* X_chunk, th_dtype xdt, int64_t t,
                                 int64_t b, int64_t ldx, void* workspace,
                                 size_t workspace_bytes, th_stream_t stream);
@@ -330,8 +332,9 @@ th_status th_debug_factor(const float* H, int64_t b, float* U, void* workspace,
  * fixed order (m = 0: chosen as for the device's compute units; m = 1: those
  * tiles whole as well). Arguments as th_hessian_accumulate with t >= 32 and
  * ldx < 2^25; 1 <= P <= 4096, 0 <= m <= t / 32; workspace: >= (number of cut
- * tiles) * m * 98304 * 4 bytes (TH_ERR_WORKSPACE if smaller; ceil(b/384) *
- * ceil(b/256) * m * 98304 * 4 always suffices). Asynchronous. */
+ * tiles) * (m * 98304 + 1) * 4 bytes (TH_ERR_WORKSPACE if smaller;
+ * ceil(b/384) * ceil(b/256) * (m * 98304 + 1) * 4 always suffices), 16-byte
+ * aligned. Asynchronous. */
 th_status th_debug_syrk_rect(float* H, const void* X_chunk, int64_t t, int64_t b, int64_t ldx,
                              int32_t P, int32_t m, void* workspace, size_t workspace_bytes,
                              th_stream_t stream);

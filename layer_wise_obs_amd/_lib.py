@@ -387,7 +387,7 @@ def debug_syrk_rect(H, X, P, m=0):
     _require_cuda(H, X)
     t, b = X.shape
     tiles = -(-b // 384) * -(-b // 256)  # bounds the cut tiles
-    ws = workspace(tiles * max(m, 16) * 98304 * 4, H.device)
+    ws = workspace(tiles * max(m, 16) * 98304 * 4 + 4 * tiles, H.device)
     _check(lib().th_debug_syrk_rect(_ptr(H), _ptr(X), t, b, X.stride(0), P, m, _ptr(ws),
                                     ws.numel(), _stream(X.device)))
 

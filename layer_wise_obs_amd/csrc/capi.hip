@@ -209,9 +209,15 @@ th_status inverse_factor(const void* X, th_dtype xdt, int64_t n, const float* H,
   const bool obs = p->score == TH_SCORE_OBS;
   if (X) {
     float* Hb = L.R;  // R is free until the factor is reversed into it
-    TH_HIP(launch_zero(Hb, (size_t)b * b * sizeof(float), s), "clear H");
-    th_status a = accumulate_into(Hb, X, xdt, n, b, b, L.syrk_part, s);
-    if (a != TH_OK) return a;
+    if (xdt == TH_BF16) {
+      const int splits = L.syrk_part ? syrk_bf16_splits(n, b) : 1;
+      TH_HIP(launch_syrk_bf16_set(Hb, (const unsigned short*)X, n, b, b, L.syrk_part, splits, s),
+             "syrk_bf16");
+    } else {
+      TH_HIP(launch_zero(Hb, (size_t)b * b * sizeof(float), s), "clear H");
+      th_status a = accumulate_into(Hb, X, xdt, n, b, b, L.syrk_part, s);
+      if (a != TH_OK) return a;
+    }
     TH_HIP(launch_lambda(Hb, b, p->lambda, p->lambda_is_relative, 0, L.st, s), "lambda");
     if (!obs) TH_HIP(launch_wanda_diag(Hb, b, L.st, 0, L.gW, s), "wanda diag");
     TH_HIP(launch_flip_lower(Hb, L.S, b, L.st, 1, s), "flip");
@@ -361,6 +367,7 @@ th_status th_hessian_accumulate(float* H, const void* X, th_dtype xdt, int64_t t
   float* part = nullptr;
   if (workspace && need > 0) {
     if (workspace_bytes < need) return fail(TH_ERR_WORKSPACE, "workspace too small");
+    if ((uintptr_t)workspace & 15) return fail(TH_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
     part = (float*)workspace;
   }
   return accumulate_into(H, X, xdt, t, b, ldx, part, (hipStream_t)stream);
@@ -929,8 +936,9 @@ th_status th_debug_syrk_rect(float* H, const void* X, int64_t t, int64_t b, int6
   const size_t need = syrk_rect_workspace_floats(t, b, P, m) * sizeof(float);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(TH_ERR_WORKSPACE, "workspace too small");
+  if ((uintptr_t)workspace & 15) return fail(TH_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   TH_HIP(launch_syrk_rect(H, (const unsigned short*)X, t, b, ldx, (float*)workspace, P, m,
-                          (hipStream_t)stream),
+                          (hipStream_t)stream, false),
          "syrk rectangles");
   return TH_OK;
 }

@@ -117,7 +117,11 @@ hipError_t launch_syrk_bf16(float* H, const unsigned short* X, int64_t t, int64_
 // into m pieces each (m = 0: chosen); part holds syrk_rect_workspace_floats
 size_t syrk_rect_workspace_floats(int64_t t, int64_t b, int P, int m);
 hipError_t launch_syrk_rect(float* H, const unsigned short* X, int64_t t, int64_t b, int64_t ldx,
-                            float* part, int P, int m, hipStream_t s);
+                            float* part, int P, int m, hipStream_t s, bool overwrite);
+// H = 2 X^T X on the lower triangle (the rectangles write every lower entry;
+// otherwise H is cleared first and accumulated into)
+hipError_t launch_syrk_bf16_set(float* H, const unsigned short* X, int64_t t, int64_t b,
+                                int64_t ldx, float* partials, int splits, hipStream_t s);
 hipError_t launch_syrk_f32(float* H, const float* X, int64_t t, int64_t b, int64_t ldx,
                            hipStream_t s);
 hipError_t launch_lambda(const float* H, int64_t b, double lam, int rel, int h_is_damped,

@@ -329,10 +329,11 @@ __device__ __forceinline__ bf16x8_t rtr_frag(const unsigned char* sub, int f0, i
 // are numbered XCD-major (each XCD's concurrent workgroups take consecutive
 // tiles, or consecutive tiles' pieces of the same stages).
 struct RectSplit {
-  int F, T, m;  // whole tiles, tiles cut in pieces, pieces per cut tile
-  int nk;       // 32-token stages per tile
-  int per_xcd;  // workgroups per XCD in the whole-tile and the piece parts
+  int F, T, m;    // whole tiles, tiles cut in pieces, pieces per cut tile
+  int nk;         // 32-token stages per tile
+  int per_xcd;    // workgroups per XCD in the whole-tile and the piece parts
   int pper_xcd;
+  int overwrite;  // H = 2 X^T X (every lower entry is written) instead of H +=
 };
 constexpr int kRTileElems = kRR * kRC;  // one slot: 98304 floats
 
@@ -358,6 +359,9 @@ __global__ __launch_bounds__(kDThreads, 1) void syrk_rect_kernel(
   int ti, tj;
   rect_tile_of(lin, nstrips, b, ti, tj);
   const int64_t I0 = (int64_t)ti * kRR, J0 = (int64_t)tj * kRC;
+  // the first piece of a cut tile records the tile for the fix-up kernel
+  if (slot >= 0 && slot < sp.T && threadIdx.x == 0)
+    reinterpret_cast<int*>(part + (int64_t)sp.T * sp.m * kRTileElems)[slot] = (ti << 16) | tj;
 
   __shared__ __attribute__((aligned(1024))) unsigned char sm0[kRStageBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char sm1[kRStageBytes];
@@ -476,7 +480,8 @@ __global__ __launch_bounds__(kDThreads, 1) void syrk_rect_kernel(
         for (int r = 0; r < 16; ++r) {
           const int64_t row = I0 + wrow * 192 + a * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
           const int64_t col = J0 + wcol * 128 + c * 32 + lr;
-          if (row < b && col < b && col <= row) H[row * b + col] += 2.0f * acc[a][c][r];
+          if (row < b && col < b && col <= row)
+            H[row * b + col] = 2.0f * acc[a][c][r] + (sp.overwrite ? 0.f : H[row * b + col]);
         }
   } else {
     float* dst = part + (int64_t)slot * kRTileElems;
@@ -495,11 +500,11 @@ __global__ __launch_bounds__(kDThreads, 1) void syrk_rect_kernel(
 // thread takes four consecutive lanes: four consecutive columns of one row.
 __global__ __launch_bounds__(256) void syrk_rect_fix_kernel(float* __restrict__ H,
                                                             const float* __restrict__ part,
-                                                            int64_t b, int nstrips, RectSplit sp) {
+                                                            int64_t b, RectSplit sp) {
   const int j = blockIdx.y, g = blockIdx.x;
-  int ti, tj;
-  rect_tile_of(sp.F + j, nstrips, b, ti, tj);
-  const int64_t I0 = (int64_t)ti * kRR, J0 = (int64_t)tj * kRC;
+  // tile F + j, as its first piece recorded it (slot j's entry after the slots)
+  const int tij = reinterpret_cast<const int*>(part + (int64_t)sp.T * sp.m * kRTileElems)[j];
+  const int64_t I0 = (int64_t)(tij >> 16) * kRR, J0 = (int64_t)(tij & 0xffff) * kRC;
   const int wave = g / 24, a = (g / 4) % 6, c = g % 4;
   const int wrow = wave >> 1, wcol = wave & 1;
   const int e = threadIdx.x * 4;
@@ -512,13 +517,13 @@ __global__ __launch_bounds__(256) void syrk_rect_fix_kernel(float* __restrict__ 
   if (row >= b || col >= b || col > row) return;
   float* h = H + row * b + col;
   if (col + 3 <= row && ((uintptr_t)h & 15) == 0) {
-    f32x4_t v = *(f32x4_t*)h;
-    v += 2.0f * s;
+    f32x4_t v = 2.0f * s;
+    if (!sp.overwrite) v += *(const f32x4_t*)h;
     *(f32x4_t*)h = v;
   } else {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      if (col + q <= row) h[q] += 2.0f * s[q];
+      if (col + q <= row) h[q] = 2.0f * s[q] + (sp.overwrite ? 0.f : h[q]);
   }
 }
 
@@ -739,10 +744,14 @@ RectSplit rect_split(int64_t ntiles, int nk, int P, int m_force) {
   }
   sp.per_xcd = (int)cdiv(sp.F, 8);
   sp.pper_xcd = (int)cdiv((int64_t)sp.T * sp.m, 8);
+  sp.overwrite = 0;
   return sp;
 }
 
-size_t rect_workspace_floats(const RectSplit& sp) { return (size_t)sp.T * sp.m * kRTileElems; }
+// the pieces' slots, then one int per cut tile (its coordinates, for the fix-up)
+size_t rect_workspace_floats(const RectSplit& sp) {
+  return sp.T > 0 ? (size_t)sp.T * sp.m * kRTileElems + sp.T : 0;
+}
 
 }  // namespace
 
@@ -763,19 +772,20 @@ size_t syrk_rect_workspace_floats(int64_t t, int64_t b, int P, int m) {
 }
 
 hipError_t launch_syrk_rect(float* H, const unsigned short* X, int64_t t, int64_t b, int64_t ldx,
-                            float* part, int P, int m, hipStream_t s) {
+                            float* part, int P, int m, hipStream_t s, bool overwrite) {
   const int64_t tf = t / kDBK * kDBK;  // whole stages; the rest goes to the square tiles
   if (tf > 0) {
     const int nstrips = (int)cdiv(b, kRR);
-    const RectSplit sp = rect_split(rect_tiles(b), (int)(tf / kDBK), P, m);
+    RectSplit sp = rect_split(rect_tiles(b), (int)(tf / kDBK), P, m);
+    sp.overwrite = overwrite ? 1 : 0;
     const int grid = 8 * (sp.per_xcd + sp.pper_xcd);
     hipLaunchKernelGGL(syrk_rect_kernel, dim3(grid), dim3(kDThreads), 0, s, H, X, tf, b, ldx,
                        nstrips, sp, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (sp.T > 0) {
-      hipLaunchKernelGGL(syrk_rect_fix_kernel, dim3(96, sp.T), dim3(256), 0, s, H, part, b, nstrips,
-                         sp);  // 96 groups of 1024 floats per tile, four per thread
+      // 96 groups of 1024 floats per tile, four per thread
+      hipLaunchKernelGGL(syrk_rect_fix_kernel, dim3(96, sp.T), dim3(256), 0, s, H, part, b, sp);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -784,14 +794,30 @@ hipError_t launch_syrk_rect(float* H, const unsigned short* X, int64_t t, int64_
   return launch_syrk_bf16(H, X + tf * ldx, t - tf, b, ldx, nullptr, 1, s);
 }
 
+namespace {
+// the rectangles are taken with a workspace, when the work is large enough and
+// the per-lane load offsets of 32 token rows stay below 2^31 bytes
+bool rect_taken(int64_t t, int64_t b, int64_t ldx, const float* partials, int P) {
+  return partials != nullptr && (int64_t)64 * ldx < ((int64_t)1 << 31) && rect_applies(t, b, P);
+}
+}  // namespace
+
+hipError_t launch_syrk_bf16_set(float* H, const unsigned short* X, int64_t t, int64_t b,
+                                int64_t ldx, float* partials, int splits, hipStream_t s) {
+  const int P = device_cus();
+  if (t > 0 && b > 0 && rect_taken(t, b, ldx, partials, P))
+    return launch_syrk_rect(H, X, t, b, ldx, partials, P, 0, s, true);
+  const hipError_t e = launch_zero(H, (size_t)b * b * sizeof(float), s);
+  if (e != hipSuccess) return e;
+  return launch_syrk_bf16(H, X, t, b, ldx, partials, splits, s);
+}
+
 hipError_t launch_syrk_bf16(float* H, const unsigned short* X, int64_t t, int64_t b, int64_t ldx,
                             float* partials, int splits, hipStream_t s) {
   if (t <= 0 || b <= 0) return hipSuccess;
-  if (partials != nullptr && (int64_t)64 * ldx < ((int64_t)1 << 31)) {
-    // 384 x 256 rectangles on a persistent grid (per-lane load offsets of 32
-    // token rows stay below 2^31 bytes); the workspace holds the split tiles
+  {
     const int P = device_cus();
-    if (rect_applies(t, b, P)) return launch_syrk_rect(H, X, t, b, ldx, partials, P, 0, s);
+    if (rect_taken(t, b, ldx, partials, P)) return launch_syrk_rect(H, X, t, b, ldx, partials, P, 0, s, false);
   }
   const int nt = (int)cdiv(b, kTile);
   const int ntiles = nt * (nt + 1) / 2;

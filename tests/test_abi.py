@@ -87,9 +87,9 @@ def test_workspace_size_queries():
     out = ctypes.c_size_t(0)
     # 659 rectangles of 384 x 256 (without a device the split assumes 256 compute
     # units): 512 whole in two rounds, the other 147 cut into 5 pieces of 8192 / 5
-    # stages, one slot of 384 x 256 floats per piece
+    # stages, one slot of 384 x 256 floats per piece and one int per cut tile
     assert L.th_hessian_workspace_size(262144, 11008, ctypes.byref(out)) == 0
-    assert out.value == 147 * 5 * 384 * 256 * 4
+    assert out.value == (147 * 5 * 384 * 256 + 147) * 4
     assert L.th_hessian_workspace_size(262144, 4096, ctypes.byref(out)) == 0
     assert out.value > 0  # 101 rectangles, all cut into pieces
     assert L.th_hessian_workspace_size(1000, 520, ctypes.byref(out)) == 0
