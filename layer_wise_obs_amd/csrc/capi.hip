@@ -67,6 +67,7 @@ struct PruneLayout {
   float* R;
   float* P;
   float* Ublk;
+  float* UblkT;
   float* Nblk;
   float* D;
   float* gW;
@@ -118,6 +119,7 @@ PruneLayout layout_prune(void* ws, int64_t c, int64_t b, int64_t n, bool have_x,
   L.R = cv.take<float>((size_t)b * b);
   L.P = factor ? cv.take<float>(chol_panel_floats(b)) : nullptr;
   L.Ublk = sgpt ? nullptr : cv.take<float>((size_t)nblk * B * B);
+  L.UblkT = sgpt ? nullptr : cv.take<float>((size_t)nblk * B * B);
   L.Nblk = (!sgpt && needs_complement(p)) ? cv.take<float>((size_t)nblk * B * B) : nullptr;
   const bool unstr = p->pattern.kind == TH_UNSTRUCTURED;
   L.D = (!sgpt && unstr && p->score == TH_SCORE_OBS) ? cv.take<float>((size_t)nblk * b) : nullptr;
@@ -204,8 +206,12 @@ th_status accumulate_into(float* H, const void* X, th_dtype xdt, int64_t t, int6
 // Damped H (from X through the syrk, or given), its flipped lower triangle in S,
 // then U with H^-1 = U^T U in R (in-place Cholesky and inverse of S, reversed).
 // Wanda's G_qq goes to L.gW when the score asks for it.
+// zero_block: 0 leaves U exactly upper triangular in R; B (the block loop's block
+// size) zeroes below the diagonal only inside the diagonal blocks, all that the
+// per-block slices read.
 th_status inverse_factor(const void* X, th_dtype xdt, int64_t n, const float* H, int64_t b,
-                         const th_prune_params* p, const PruneLayout& L, hipStream_t s) {
+                         const th_prune_params* p, const PruneLayout& L, hipStream_t s,
+                         int64_t zero_block) {
   const bool obs = p->score == TH_SCORE_OBS;
   if (X) {
     float* Hb = L.R;  // R is free until the factor is reversed into it
@@ -227,7 +233,7 @@ th_status inverse_factor(const void* X, th_dtype xdt, int64_t n, const float* H,
     TH_HIP(launch_flip_lower(H, L.S, b, L.st, 0, s), "flip");
   }
   TH_HIP(launch_chol_inv_inplace(L.S, b, L.P, L.st, s), "cholesky/inverse");
-  TH_HIP(launch_reverse(L.S, L.R, b, s), "reverse");
+  TH_HIP(launch_reverse(L.S, L.R, b, zero_block, s), "reverse");
   return TH_OK;
 }
 
@@ -272,13 +278,13 @@ th_status prune_blocks(const PruneLayout& L, int64_t c, int64_t b, const th_prun
   const int64_t nblk = cdiv(b, B);
   const bool unstr = p->pattern.kind == TH_UNSTRUCTURED;
   const bool obs = p->score == TH_SCORE_OBS;
-  TH_HIP(launch_save_diag_blocks(L.R, b, B, L.Ublk, s), "diag blocks");
+  TH_HIP(launch_save_diag_blocks(L.R, b, B, L.Ublk, L.UblkT, s), "diag blocks");
   // S is free once reversed into R: it holds the fp64 partial sums
   if (L.D)
     TH_HIP(launch_colnorm_downdate(L.R, b, B, L.D, (double*)L.S, (size_t)b * b / 2, s),
            "column norms");
   if (L.Nblk) TH_HIP(launch_block_inverses(L.Ublk, b, B, L.Nblk, s), "block inverses");
-  TH_HIP(launch_transform_rows(L.R, b, B, L.Ublk, s), "transform rows");
+  TH_HIP(launch_transform_rows(L.R, b, B, L.UblkT, s), "transform rows");
 
   const int64_t ldz = z_pitch(b, p);
   // the layer's budget k_total = round-half-even(p c b) joins at the first block
@@ -423,7 +429,7 @@ th_status th_prune_layer(void* W, th_dtype wdt, int64_t c, int64_t b, const void
 
   th_status st0 = begin_layer(L, W, wdt, c, b, p, Wf, s);
   if (st0 != TH_OK) return st0;
-  th_status pre = inverse_factor(X, xdt, n, H, b, p, L, s);
+  th_status pre = inverse_factor(X, xdt, n, H, b, p, L, s, p->block);
   if (pre != TH_OK) return pre;
 
   th_status blocks = prune_blocks(L, c, b, p, Wf, mask, s);
@@ -516,7 +522,7 @@ th_status th_prune_sparsegpt(void* W, th_dtype wdt, int64_t c, int64_t b, const 
 
   th_status st0 = begin_layer(L, W, wdt, c, b, p, Wf, s);  // the budget grows block by block
   if (st0 != TH_OK) return st0;
-  th_status pre = inverse_factor(X, xdt, n, H, b, p, L, s);
+  th_status pre = inverse_factor(X, xdt, n, H, b, p, L, s, 0);
   if (pre != TH_OK) return pre;
   TH_HIP(launch_sgpt_gdiag(L.R, b, L.gW, s), "score weights");
 
@@ -609,7 +615,7 @@ th_status th_factor(const void* X, th_dtype xdt, int64_t n, const float* H, int6
   L.P = F.P;
   L.syrk_part = F.syrk_part;
   TH_HIP(launch_zero(F.st, sizeof(DevState), s), "clear state");
-  th_status pre = inverse_factor(X, xdt, n, H, b, &p, L, s);
+  th_status pre = inverse_factor(X, xdt, n, H, b, &p, L, s, 0);  // U is the output
   if (pre != TH_OK) return pre;
   DevState host;
   TH_HIP(hipMemcpyAsync(&host, F.st, offsetof(DevState, hist), hipMemcpyDeviceToHost, s), "state");
@@ -737,7 +743,7 @@ th_status th_prune_layer_alpha(void* W, th_dtype wdt, int64_t c, int64_t b, cons
 
   // the layer step on the compact rows
   if (cp > 0) TH_HIP(launch_gather_rows(W, wdt, b, A.rowmap, cp, L.Wf, L.st, s), "gather");
-  th_status pre = inverse_factor(X, xdt, n, H, b, p, L, s);
+  th_status pre = inverse_factor(X, xdt, n, H, b, p, L, s, p->block);
   if (pre != TH_OK) return pre;
   if (cp > 0) {
     th_status blocks = prune_blocks(L, cp, b, p, L.Wf, L.mask, s);
@@ -915,7 +921,7 @@ th_status th_debug_factor(const float* H, int64_t b, float* U, void* workspace,
   TH_HIP(hipMemsetAsync(st, 0, sizeof(DevState), s), "memset");
   TH_HIP(launch_flip_lower(H, S, b, st, 0, s), "flip");
   TH_HIP(launch_chol_inv_inplace(S, b, P, st, s), "cholesky/inverse");
-  TH_HIP(launch_reverse(S, U, b, s), "reverse");
+  TH_HIP(launch_reverse(S, U, b, 0, s), "reverse");
   int flag = 0;
   TH_HIP(hipMemcpyAsync(&flag, &st->not_spd, sizeof(int), hipMemcpyDeviceToHost, s), "flag");
   TH_HIP(hipStreamSynchronize(s), "sync");

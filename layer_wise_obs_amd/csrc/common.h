@@ -147,12 +147,15 @@ hipError_t launch_baseline_nm(void* W, th_dtype wdt, int64_t c, int64_t b, const
 size_t chol_panel_floats(int64_t b);
 hipError_t launch_chol_inv_inplace(float* S, int64_t b, float* panel, DevState* st,
                                    hipStream_t s);
-hipError_t launch_reverse(const float* S, float* U, int64_t b, hipStream_t s);
+// U = the reversal of S's lower triangle, zero below the diagonal: everywhere when
+// zero_block is 0, else only inside the diagonal blocks of that size (what the
+// per-block slices read; the rest of the strict lower triangle is left as is)
+hipError_t launch_reverse(const float* S, float* U, int64_t b, int64_t zero_block, hipStream_t s);
 
 // prep.hip
-hipError_t launch_save_diag_blocks(const float* U, int64_t b, int64_t B, float* Ublk,
+hipError_t launch_save_diag_blocks(const float* U, int64_t b, int64_t B, float* Ublk, float* UblkT,
                                    hipStream_t s);
-hipError_t launch_transform_rows(float* R, int64_t b, int64_t B, const float* Ublk,
+hipError_t launch_transform_rows(float* R, int64_t b, int64_t B, const float* UblkT,
                                  hipStream_t s);
 // D[r][q] = sum_{i = rB .. q} U_iq^2 (fp64 sums); scratch (optional, e.g. the free
 // S buffer) of at least ceil(b/B)*b doubles selects the two-pass coalesced version.

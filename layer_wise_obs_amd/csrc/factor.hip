@@ -463,13 +463,37 @@ __global__ __launch_bounds__(256, 2) void trailing_look_kernel(float* __restrict
 }
 
 
-// U[a][c] = S[b-1-a][b-1-c] for c >= a, 0 below the diagonal (a flat reversal).
-__global__ void reverse_kernel(const float* __restrict__ S, float* __restrict__ U, int64_t b) {
-  const int64_t n = b * b;
-  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < n;
-       x += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t a = x / b, c = x - a * b;
-    U[x] = (c >= a) ? S[n - 1 - x] : 0.f;
+// U[a][c] = S[b-1-a][b-1-c] for c >= a (a flat reversal); 0 below the diagonal,
+// everywhere (zb = 0) or only inside the diagonal blocks of size zb. Block (a, y):
+// row a, columns 1024 y .. 1024 y + 1023, four per thread (16-byte accesses when
+// b % 4 == 0).
+__global__ __launch_bounds__(256) void reverse_kernel(const float* __restrict__ S,
+                                                      float* __restrict__ U, int64_t b,
+                                                      int64_t zb) {
+  const int64_t a = blockIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.y * 1024 + threadIdx.x * 4;
+  if (c0 >= b) return;
+  const int64_t zfrom = zb == 0 ? 0 : a / zb * zb;  // zeros in columns [zfrom, a)
+  if (c0 + 3 < zfrom) return;
+  float* dst = U + a * b + c0;
+  const float* src = S + (b - 1 - a) * b + (b - 1 - c0);  // src[-q] is column c0 + q
+  if ((b & 3) == 0 && c0 + 3 < b) {
+    if (c0 >= a) {
+      const f32x4_t x = *(const f32x4_t*)(src - 3);
+      *(f32x4_t*)dst = f32x4_t{x[3], x[2], x[1], x[0]};
+      return;
+    }
+    if (c0 + 3 < a && c0 >= zfrom) {
+      *(f32x4_t*)dst = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      return;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t c = c0 + q;
+    if (c >= b) break;
+    if (c >= a) dst[q] = src[-q];
+    else if (c >= zfrom) dst[q] = 0.f;
   }
 }
 
@@ -613,11 +637,9 @@ hipError_t launch_chol_inv_inplace(float* S, int64_t b, float* P, DevState* st, 
   return e;
 }
 
-hipError_t launch_reverse(const float* S, float* U, int64_t b, hipStream_t s) {
-  const int64_t n = b * b;
-  int64_t blocks = cdiv(n, 256);
-  if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(reverse_kernel, dim3((unsigned)blocks), dim3(256), 0, s, S, U, b);
+hipError_t launch_reverse(const float* S, float* U, int64_t b, int64_t zero_block, hipStream_t s) {
+  hipLaunchKernelGGL(reverse_kernel, dim3((unsigned)b, (unsigned)cdiv(b, 1024)), dim3(256), 0, s, S,
+                     U, b, zero_block);
   return hipGetLastError();
 }
 

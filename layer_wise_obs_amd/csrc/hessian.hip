@@ -638,25 +638,51 @@ __global__ void damp_mirror_kernel(float* __restrict__ H, int64_t b, float lam) 
 
 // S = P H P restricted to its lower triangle, P the reversal permutation:
 // S[i][j] = H[b-1-j][b-1-i] for j <= i (a lower entry of H), + lambda on the diagonal.
-__global__ void flip_lower_kernel(const float* __restrict__ H, float* __restrict__ S, int64_t b,
-                                  const DevState* st, int add_lambda) {
-  __shared__ float tile[32][33];
-  const int64_t I0 = (int64_t)blockIdx.y * 32, J0 = (int64_t)blockIdx.x * 32;
+// 64 x 64 tiles through LDS, 16-byte global accesses when b % 4 == 0.
+__global__ __launch_bounds__(256) void flip_lower_kernel(const float* __restrict__ H,
+                                                         float* __restrict__ S, int64_t b,
+                                                         const DevState* st, int add_lambda) {
+  __shared__ float tile[64][65];  // tile[r][c] = H[b-1-(J0+r)][b-1-(I0+c)]
+  const int64_t I0 = (int64_t)blockIdx.y * 64, J0 = (int64_t)blockIdx.x * 64;
   if (J0 > I0) return;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  // Read H rows b-1-(J0+r), columns b-1-(I0+tx): a column-reversed, row-reversed block.
-  for (int r = ty; r < 32; r += 8) {
-    const int64_t hr = b - 1 - (J0 + r), hc = b - 1 - (I0 + tx);
-    tile[r][tx] = (hr >= 0 && hc >= 0) ? H[hr * b + hc] : 0.f;
+  const int tid = threadIdx.x;
+  const bool vec = (b & 3) == 0 && I0 + 64 <= b && J0 + 64 <= b;
+  if (vec) {
+    // row r: H columns b-I0-64 .. b-I0-1 as 16 float4; thread: row tid/16 + 16p, piece tid%16
+    const int v = tid & 15;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = (tid >> 4) + 16 * p;
+      const f32x4_t x = *(const f32x4_t*)(H + (b - 1 - (J0 + r)) * b + (b - I0 - 64) + 4 * v);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tile[r][63 - 4 * v - q] = x[q];
+    }
+  } else {
+    for (int e = tid; e < 64 * 64; e += 256) {
+      const int r = e >> 6, c = e & 63;
+      const int64_t hr = b - 1 - (J0 + r), hc = b - 1 - (I0 + c);
+      tile[r][c] = (hr >= 0 && hc >= 0) ? H[hr * b + hc] : 0.f;
+    }
   }
   __syncthreads();
   const float lam = add_lambda ? (float)st->lambda : 0.f;
-  for (int r = ty; r < 32; r += 8) {
-    const int64_t i = I0 + r, j = J0 + tx;
-    if (i < b && j < b && j <= i) {
-      float v = tile[tx][r];  // = H[b-1-j][b-1-i]
-      if (i == j) v += lam;
-      S[i * b + j] = v;
+  // output row i = I0 + c, columns j = J0 + 4w .. +3 (tile[4w + q][c])
+  const int w = tid & 15;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int c = (tid >> 4) + 16 * p;
+    const int64_t i = I0 + c, j = J0 + 4 * w;
+    if (i >= b) continue;
+    f32x4_t y;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) y[q] = tile[4 * w + q][c] + ((j + q == i) ? lam : 0.f);
+    float* dst = S + i * b + j;
+    if (vec && j + 3 <= i) {
+      *(f32x4_t*)dst = y;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (j + q < b && j + q <= i) dst[q] = y[q];
     }
   }
 }
@@ -857,7 +883,7 @@ hipError_t launch_damp_mirror(float* H, int64_t b, float lam, hipStream_t s) {
 
 hipError_t launch_flip_lower(const float* H, float* S, int64_t b, const DevState* st,
                              int add_lambda, hipStream_t s) {
-  const int nt = (int)cdiv(b, 32);
+  const int nt = (int)cdiv(b, 64);
   hipLaunchKernelGGL(flip_lower_kernel, dim3(nt, nt), dim3(256), 0, s, H, S, b, st, add_lambda);
   return hipGetLastError();
 }

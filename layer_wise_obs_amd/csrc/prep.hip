@@ -7,34 +7,40 @@
 // "Contribution one: solve a selected set directly": R = rows Q of the inverse
 // Hessian, R-hat = its principal submatrix on Q -- both are slices of A_F[J, F].
 //
-//   save_diag_blocks : Ublk[J] = U_JJ                        (B x B, zero padded)
-//   transform_rows   : R[J, F] = U_JJ^T U[J, F] in place      (fp32 MFMA)
+//   save_diag_blocks : Ublk[J] = U_JJ, UblkT[J] = U_JJ^T       (B x B, zero padded)
+//   transform_rows   : R[J, F] = U_JJ^T U[J, F] in place      (split-bf16 MFMA)
 //   colnorm_downdate : D[J][q] = 1/[A_F]_qq for q in F        (OBS score weight over F)
 //   block_inverses   : N[J] = (A_F[J,J])^-1 = V_JJ V_JJ^T, V_JJ = U_JJ^-1
 //                      (used when a row selects more than half of a block)
 #include "gemm_f32.h"
+#include "gemm_x3.h"
 
 namespace th {
 
 namespace {
 
+// Ublk[J] = U_JJ and UblkT[J] = U_JJ^T (upper / lower triangular, zero padded).
 __global__ void save_diag_blocks_kernel(const float* __restrict__ U, int64_t b, int64_t B,
-                                        float* __restrict__ Ublk) {
+                                        float* __restrict__ Ublk, float* __restrict__ UblkT) {
   const int64_t blk = blockIdx.x;
   const int64_t j0 = blk * B;
   const int64_t Bb = (b - j0) < B ? (b - j0) : B;
   float* dst = Ublk + blk * B * B;
+  float* dstT = UblkT + blk * B * B;
   for (int64_t e = threadIdx.x; e < B * B; e += blockDim.x) {
     const int64_t a = e / B, c = e % B;
-    dst[e] = (a < Bb && c < Bb) ? U[(j0 + a) * b + j0 + c] : 0.f;
+    const float v = (a < Bb && c < Bb && c >= a) ? U[(j0 + a) * b + j0 + c] : 0.f;
+    dst[e] = v;
+    dstT[c * B + a] = v;
   }
 }
 
-// One workgroup per (block J, 128-wide column tile of F).
+// One workgroup per (block J, 128-wide column tile of F): the product on the bf16
+// matrix cores with split fp32 operands (errors of the order of fp32 accumulation).
 __global__ __launch_bounds__(256, 2) void transform_rows_kernel(float* __restrict__ R, int64_t b,
                                                              int64_t B, int nblk,
-                                                             const float* __restrict__ Ublk) {
-  __shared__ __attribute__((aligned(16))) float smem[kGemmLdsFloats];
+                                                             const float* __restrict__ UblkT) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kX3LdsBytes];
   int rem = blockIdx.x, blk = 0;
   int64_t ntile = 0;
   for (;;) {
@@ -51,9 +57,9 @@ __global__ __launch_bounds__(256, 2) void transform_rows_kernel(float* __restric
   const int cols = (int)((b - col0) < 128 ? (b - col0) : 128);
   f32x16_t acc[2][2];
   gemm_zero(acc);
-  // A[i][kk] = U_JJ[kk][i] (i contiguous), B[kk][jj] = U[j0+kk][col0+jj]
-  gemm_tile_f32<false, false>(Ublk + (int64_t)blk * B * B, B, Bb, R + j0 * b + col0, b, cols, Bb,
-                              acc, smem);
+  // A[i][kk] = U_JJ[kk][i] = UblkT[i][kk] (k contiguous), B[kk][jj] = U[j0+kk][col0+jj]
+  gemm_tile_x3<false>(UblkT + (int64_t)blk * B * B, B, Bb, R + j0 * b + col0, b, cols, Bb, acc,
+                      smem);
   gemm_foreach(acc, [&](int r, int c, float v) {
     if (r < Bb && c < cols) R[(j0 + r) * b + col0 + c] = v;
   });
@@ -157,20 +163,20 @@ __global__ __launch_bounds__(1024) void block_inverse_kernel(const float* __rest
 
 }  // namespace
 
-hipError_t launch_save_diag_blocks(const float* U, int64_t b, int64_t B, float* Ublk,
+hipError_t launch_save_diag_blocks(const float* U, int64_t b, int64_t B, float* Ublk, float* UblkT,
                                    hipStream_t s) {
   const int nblk = (int)cdiv(b, B);
-  hipLaunchKernelGGL(save_diag_blocks_kernel, dim3(nblk), dim3(256), 0, s, U, b, B, Ublk);
+  hipLaunchKernelGGL(save_diag_blocks_kernel, dim3(nblk), dim3(256), 0, s, U, b, B, Ublk, UblkT);
   return hipGetLastError();
 }
 
-hipError_t launch_transform_rows(float* R, int64_t b, int64_t B, const float* Ublk,
+hipError_t launch_transform_rows(float* R, int64_t b, int64_t B, const float* UblkT,
                                  hipStream_t s) {
   const int nblk = (int)cdiv(b, B);
   int64_t total = 0;
   for (int k = 0; k < nblk; ++k) total += cdiv(b - (int64_t)k * B, 128);
   hipLaunchKernelGGL(transform_rows_kernel, dim3((unsigned)total), dim3(256), 0, s, R, b, B, nblk,
-                     Ublk);
+                     UblkT);
   return hipGetLastError();
 }
 
