@@ -70,6 +70,7 @@ struct PruneLayout {
   float* UblkT;
   float* Nblk;
   float* D;
+  double* Dpart;  // per-block parts of D's column sums (fp64)
   float* gW;
   float* Z;
   float* Wf;
@@ -122,7 +123,9 @@ PruneLayout layout_prune(void* ws, int64_t c, int64_t b, int64_t n, bool have_x,
   L.UblkT = sgpt ? nullptr : cv.take<float>((size_t)nblk * B * B);
   L.Nblk = (!sgpt && needs_complement(p)) ? cv.take<float>((size_t)nblk * B * B) : nullptr;
   const bool unstr = p->pattern.kind == TH_UNSTRUCTURED;
-  L.D = (!sgpt && unstr && p->score == TH_SCORE_OBS) ? cv.take<float>((size_t)nblk * b) : nullptr;
+  const bool colnorm = !sgpt && unstr && p->score == TH_SCORE_OBS;
+  L.D = colnorm ? cv.take<float>((size_t)nblk * b) : nullptr;
+  L.Dpart = colnorm ? cv.take<double>((size_t)nblk * b) : nullptr;
   L.gW = (sgpt || p->score == TH_SCORE_WANDA) ? cv.take<float>((size_t)b) : nullptr;
   L.Z = cv.take<float>((size_t)c * (sgpt ? super_pitch(b, B) : z_pitch(b, p)));
   L.Wf = need_wf ? cv.take<float>((size_t)c * b) : nullptr;
@@ -206,9 +209,22 @@ th_status accumulate_into(float* H, const void* X, th_dtype xdt, int64_t t, int6
 // Damped H (from X through the syrk, or given), its flipped lower triangle in S,
 // then U with H^-1 = U^T U in R (in-place Cholesky and inverse of S, reversed).
 // Wanda's G_qq goes to L.gW when the score asks for it.
+// The per-block slices of U (in R) for blocks jlo .. jhi-1: the diagonal blocks
+// (and their transposes), the column norms' parts and the block inverses when the
+// layer needs them, then the transformed rows R[J, F] = U_JJ^T U[J, F] in place.
+// Each block reads and writes only its own rows of R.
+hipError_t slices_for(const PruneLayout& L, int64_t b, int64_t B, int jlo, int jhi,
+                      hipStream_t s) {
+  hipError_t e = launch_save_diag_blocks(L.R, b, B, L.Ublk, L.UblkT, jlo, jhi, s);
+  if (e == hipSuccess && L.D) e = launch_colnorm_partial(L.R, b, B, L.Dpart, jlo, jhi, s);
+  if (e == hipSuccess && L.Nblk) e = launch_block_inverses(L.Ublk, b, B, L.Nblk, jlo, jhi, s);
+  if (e == hipSuccess) e = launch_transform_rows(L.R, b, B, L.UblkT, jlo, jhi, s);
+  return e;
+}
+
 // zero_block: 0 leaves U exactly upper triangular in R; B (the block loop's block
 // size) zeroes below the diagonal only inside the diagonal blocks, all that the
-// per-block slices read.
+// per-block slices read, and prepares those slices too.
 th_status inverse_factor(const void* X, th_dtype xdt, int64_t n, const float* H, int64_t b,
                          const th_prune_params* p, const PruneLayout& L, hipStream_t s,
                          int64_t zero_block) {
@@ -232,8 +248,14 @@ th_status inverse_factor(const void* X, th_dtype xdt, int64_t n, const float* H,
     if (!obs) TH_HIP(launch_wanda_diag(H, b, L.st, 1, L.gW, s), "wanda diag");
     TH_HIP(launch_flip_lower(H, L.S, b, L.st, 0, s), "flip");
   }
+  if (zero_block == 0) {
+    TH_HIP(launch_chol_inv_inplace(L.S, b, L.P, L.st, s), "cholesky/inverse");
+    TH_HIP(launch_reverse(L.S, L.R, b, 0, s), "reverse");
+    return TH_OK;
+  }
   TH_HIP(launch_chol_inv_inplace(L.S, b, L.P, L.st, s), "cholesky/inverse");
   TH_HIP(launch_reverse(L.S, L.R, b, zero_block, s), "reverse");
+  TH_HIP(slices_for(L, b, zero_block, 0, (int)cdiv(b, zero_block), s), "slices");
   return TH_OK;
 }
 
@@ -272,19 +294,15 @@ th_status begin_layer(const PruneLayout& L, const void* W, th_dtype wdt, int64_t
 
 // The per-block slices of U (in L.R) and the block loop: What in Wf, the mask,
 // per-block counts and the pruned total in the device state.
+// prepared: inverse_factor (with zero_block = B) has already made the slices.
 th_status prune_blocks(const PruneLayout& L, int64_t c, int64_t b, const th_prune_params* p,
-                       float* Wf, uint8_t* mask, hipStream_t s) {
+                       float* Wf, uint8_t* mask, hipStream_t s, bool prepared) {
   const int64_t B = p->block;
   const int64_t nblk = cdiv(b, B);
   const bool unstr = p->pattern.kind == TH_UNSTRUCTURED;
   const bool obs = p->score == TH_SCORE_OBS;
-  TH_HIP(launch_save_diag_blocks(L.R, b, B, L.Ublk, L.UblkT, s), "diag blocks");
-  // S is free once reversed into R: it holds the fp64 partial sums
-  if (L.D)
-    TH_HIP(launch_colnorm_downdate(L.R, b, B, L.D, (double*)L.S, (size_t)b * b / 2, s),
-           "column norms");
-  if (L.Nblk) TH_HIP(launch_block_inverses(L.Ublk, b, B, L.Nblk, s), "block inverses");
-  TH_HIP(launch_transform_rows(L.R, b, B, L.UblkT, s), "transform rows");
+  if (!prepared) TH_HIP(slices_for(L, b, B, 0, (int)nblk, s), "slices");
+  if (L.D) TH_HIP(launch_colnorm_scan(L.Dpart, b, B, L.D, s), "column norms");
 
   const int64_t ldz = z_pitch(b, p);
   // the layer's budget k_total = round-half-even(p c b) joins at the first block
@@ -432,7 +450,7 @@ th_status th_prune_layer(void* W, th_dtype wdt, int64_t c, int64_t b, const void
   th_status pre = inverse_factor(X, xdt, n, H, b, p, L, s, p->block);
   if (pre != TH_OK) return pre;
 
-  th_status blocks = prune_blocks(L, c, b, p, Wf, mask, s);
+  th_status blocks = prune_blocks(L, c, b, p, Wf, mask, s, true);
   if (blocks != TH_OK) return blocks;
   TH_HIP(launch_from_f32(Wf, c * b, wdt, W, s), "cast back");
   return finish_layer(L, nblk, stats_out, block_counts, s);
@@ -654,7 +672,7 @@ th_status th_prune_layer_factored(void* W, th_dtype wdt, int64_t c, int64_t b, c
   if (st0 != TH_OK) return st0;
   // the slices are formed in place, so the caller's factor is copied first
   TH_HIP(hipMemcpyAsync(L.R, U, (size_t)b * b * sizeof(float), hipMemcpyDeviceToDevice, s), "U");
-  th_status blocks = prune_blocks(L, c, b, p, Wf, mask, s);
+  th_status blocks = prune_blocks(L, c, b, p, Wf, mask, s, false);
   if (blocks != TH_OK) return blocks;
   TH_HIP(launch_from_f32(Wf, c * b, wdt, W, s), "cast back");
   return finish_layer(L, cdiv(b, p->block), stats_out, block_counts, s);
@@ -746,7 +764,7 @@ th_status th_prune_layer_alpha(void* W, th_dtype wdt, int64_t c, int64_t b, cons
   th_status pre = inverse_factor(X, xdt, n, H, b, p, L, s, p->block);
   if (pre != TH_OK) return pre;
   if (cp > 0) {
-    th_status blocks = prune_blocks(L, cp, b, p, L.Wf, L.mask, s);
+    th_status blocks = prune_blocks(L, cp, b, p, L.Wf, L.mask, s, true);
     if (blocks != TH_OK) return blocks;
   }
   TH_HIP(launch_scatter_rows(W, wdt, c, b, A.idx, L.Wf, L.mask, W_out_f32, mask_out, s),

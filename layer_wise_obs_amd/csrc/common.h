@@ -152,17 +152,22 @@ hipError_t launch_chol_inv_inplace(float* S, int64_t b, float* panel, DevState* 
 // per-block slices read; the rest of the strict lower triangle is left as is)
 hipError_t launch_reverse(const float* S, float* U, int64_t b, int64_t zero_block, hipStream_t s);
 
+
 // prep.hip
+// The per-block preparation, for blocks jlo .. jhi-1 of size B:
 hipError_t launch_save_diag_blocks(const float* U, int64_t b, int64_t B, float* Ublk, float* UblkT,
-                                   hipStream_t s);
-hipError_t launch_transform_rows(float* R, int64_t b, int64_t B, const float* UblkT,
-                                 hipStream_t s);
+                                   int jlo, int jhi, hipStream_t s);
+hipError_t launch_transform_rows(float* R, int64_t b, int64_t B, const float* UblkT, int jlo,
+                                 int jhi, hipStream_t s);
+// Dpart[r][q] = sum over rows i <= q of block r of U_iq^2 (fp64), then
+// D[r][q] = 1 / sum_{r' >= r} Dpart[r'][q] once every block's part is in
+hipError_t launch_colnorm_partial(const float* U, int64_t b, int64_t B, double* Dpart, int jlo,
+                                  int jhi, hipStream_t s);
+hipError_t launch_colnorm_scan(const double* Dpart, int64_t b, int64_t B, float* D, hipStream_t s);
 // D[r][q] = sum_{i = rB .. q} U_iq^2 (fp64 sums); scratch (optional, e.g. the free
 // S buffer) of at least ceil(b/B)*b doubles selects the two-pass coalesced version.
-hipError_t launch_colnorm_downdate(const float* U, int64_t b, int64_t B, float* D,
-                                   double* scratch, size_t scratch_doubles, hipStream_t s);
-hipError_t launch_block_inverses(const float* Ublk, int64_t b, int64_t B, float* Nblk,
-                                 hipStream_t s);
+hipError_t launch_block_inverses(const float* Ublk, int64_t b, int64_t B, float* Nblk, int jlo,
+                                 int jhi, hipStream_t s);
 
 // select.hip
 // budget += add_budget, then r = budget - pruned keys are to be found among ncand.

@@ -9,7 +9,8 @@
 //
 //   save_diag_blocks : Ublk[J] = U_JJ, UblkT[J] = U_JJ^T       (B x B, zero padded)
 //   transform_rows   : R[J, F] = U_JJ^T U[J, F] in place      (split-bf16 MFMA)
-//   colnorm_downdate : D[J][q] = 1/[A_F]_qq for q in F        (OBS score weight over F)
+//   colnorm partial  : per block row J, sum over its rows i <= q of U_iq^2 (fp64)
+//   colnorm scan     : D[J][q] = 1/[A_F]_qq for q in F        (OBS score weight over F)
 //   block_inverses   : N[J] = (A_F[J,J])^-1 = V_JJ V_JJ^T, V_JJ = U_JJ^-1
 //                      (used when a row selects more than half of a block)
 #include "gemm_f32.h"
@@ -20,18 +21,31 @@ namespace th {
 namespace {
 
 // Ublk[J] = U_JJ and UblkT[J] = U_JJ^T (upper / lower triangular, zero padded).
-__global__ void save_diag_blocks_kernel(const float* __restrict__ U, int64_t b, int64_t B,
-                                        float* __restrict__ Ublk, float* __restrict__ UblkT) {
-  const int64_t blk = blockIdx.x;
+// Block (x, y): block jlo + x, 32 x 32 sub-tile y of it, transposed through LDS so
+// that both copies are written a row at a time.
+__global__ __launch_bounds__(256) void save_diag_blocks_kernel(const float* __restrict__ U,
+                                                               int64_t b, int64_t B,
+                                                               float* __restrict__ Ublk,
+                                                               float* __restrict__ UblkT, int jlo) {
+  __shared__ float tile[32][33];
+  const int64_t blk = jlo + (int64_t)blockIdx.x;
   const int64_t j0 = blk * B;
   const int64_t Bb = (b - j0) < B ? (b - j0) : B;
+  const int nsub = (int)cdiv(B, 32);
+  const int64_t a0 = (int64_t)(blockIdx.y / nsub) * 32, c0 = (int64_t)(blockIdx.y % nsub) * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   float* dst = Ublk + blk * B * B;
   float* dstT = UblkT + blk * B * B;
-  for (int64_t e = threadIdx.x; e < B * B; e += blockDim.x) {
-    const int64_t a = e / B, c = e % B;
+  for (int r = ty; r < 32; r += 8) {
+    const int64_t a = a0 + r, c = c0 + tx;
     const float v = (a < Bb && c < Bb && c >= a) ? U[(j0 + a) * b + j0 + c] : 0.f;
-    dst[e] = v;
-    dstT[c * B + a] = v;
+    if (a < B && c < B) dst[a * B + c] = v;
+    tile[r][tx] = v;
+  }
+  __syncthreads();
+  for (int r = ty; r < 32; r += 8) {
+    const int64_t c = c0 + r, a = a0 + tx;  // dstT[c][a] = U_JJ[a][c]
+    if (a < B && c < B) dstT[c * B + a] = tile[tx][r];
   }
 }
 
@@ -39,9 +53,10 @@ __global__ void save_diag_blocks_kernel(const float* __restrict__ U, int64_t b, 
 // matrix cores with split fp32 operands (errors of the order of fp32 accumulation).
 __global__ __launch_bounds__(256, 2) void transform_rows_kernel(float* __restrict__ R, int64_t b,
                                                              int64_t B, int nblk,
-                                                             const float* __restrict__ UblkT) {
+                                                             const float* __restrict__ UblkT,
+                                                             int jlo) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kX3LdsBytes];
-  int rem = blockIdx.x, blk = 0;
+  int rem = blockIdx.x, blk = jlo;
   int64_t ntile = 0;
   for (;;) {
     const int64_t j0 = (int64_t)blk * B;
@@ -65,32 +80,14 @@ __global__ __launch_bounds__(256, 2) void transform_rows_kernel(float* __restric
   });
 }
 
-// One thread per column q: walk up the column of U accumulating squares and
-// record 1/(partial sum) at every block start j0 <= q (fallback for tiny B).
-__global__ void colnorm_kernel(const float* __restrict__ U, int64_t b, int64_t B,
-                               float* __restrict__ D) {
-  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (q >= b) return;
-  double s = 0.0;
-  int64_t blk = q / B;
-  for (int64_t i = q; i >= 0; --i) {
-    const double u = U[i * b + q];
-    s += u * u;
-    if (i == blk * B) {
-      D[blk * b + q] = __fdiv_rn(1.0f, (float)s);
-      --blk;
-    }
-  }
-}
-
-// The same sums in two coalesced passes: P[r][q] = sum over rows i of block r
+// The column sums in two coalesced passes: P[r][q] = sum over rows i of block r
 // with i <= q of U_iq^2 (one workgroup per block row and 256 columns), then per
 // column a suffix sum over the blocks, stored as its reciprocal:
 // D[r][q] = 1 / sum_{r' >= r} P[r'][q], q >= r B.
 __global__ void colnorm_partial_kernel(const float* __restrict__ U, int64_t b, int64_t B,
-                                       double* __restrict__ P) {
+                                       double* __restrict__ P, int jlo) {
   const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t r = blockIdx.y;
+  const int64_t r = jlo + (int64_t)blockIdx.y;
   if (q >= b) return;
   const int64_t j0 = r * B;
   const int64_t j1 = (j0 + B) < b ? (j0 + B) : b;
@@ -116,10 +113,10 @@ __global__ void colnorm_scan_kernel(const double* __restrict__ P, int64_t b, int
 // N = (U_JJ^T U_JJ)^-1 = V V^T with V = U_JJ^-1 (upper), in fp64.
 __global__ __launch_bounds__(1024) void block_inverse_kernel(const float* __restrict__ Ublk,
                                                              int64_t b, int64_t B,
-                                                             float* __restrict__ Nblk) {
+                                                             float* __restrict__ Nblk, int jlo) {
   extern __shared__ double V[];  // B x (B+1)
   const int64_t P = B + 1;
-  const int64_t blk = blockIdx.x;
+  const int64_t blk = jlo + (int64_t)blockIdx.x;
   const int64_t j0 = blk * B;
   const int Bb = (int)((b - j0) < B ? (b - j0) : B);
   const float* Ub = Ublk + blk * B * B;
@@ -164,46 +161,47 @@ __global__ __launch_bounds__(1024) void block_inverse_kernel(const float* __rest
 }  // namespace
 
 hipError_t launch_save_diag_blocks(const float* U, int64_t b, int64_t B, float* Ublk, float* UblkT,
-                                   hipStream_t s) {
-  const int nblk = (int)cdiv(b, B);
-  hipLaunchKernelGGL(save_diag_blocks_kernel, dim3(nblk), dim3(256), 0, s, U, b, B, Ublk, UblkT);
+                                   int jlo, int jhi, hipStream_t s) {
+  if (jhi <= jlo) return hipSuccess;
+  const unsigned nsub = (unsigned)cdiv(B, 32);
+  hipLaunchKernelGGL(save_diag_blocks_kernel, dim3(jhi - jlo, nsub * nsub), dim3(256), 0, s, U, b,
+                     B, Ublk, UblkT, jlo);
   return hipGetLastError();
 }
 
-hipError_t launch_transform_rows(float* R, int64_t b, int64_t B, const float* UblkT,
-                                 hipStream_t s) {
-  const int nblk = (int)cdiv(b, B);
+hipError_t launch_transform_rows(float* R, int64_t b, int64_t B, const float* UblkT, int jlo,
+                                 int jhi, hipStream_t s) {
+  if (jhi <= jlo) return hipSuccess;
   int64_t total = 0;
-  for (int k = 0; k < nblk; ++k) total += cdiv(b - (int64_t)k * B, 128);
-  hipLaunchKernelGGL(transform_rows_kernel, dim3((unsigned)total), dim3(256), 0, s, R, b, B, nblk,
-                     UblkT);
+  for (int k = jlo; k < jhi; ++k) total += cdiv(b - (int64_t)k * B, 128);
+  hipLaunchKernelGGL(transform_rows_kernel, dim3((unsigned)total), dim3(256), 0, s, R, b, B, jhi,
+                     UblkT, jlo);
   return hipGetLastError();
 }
 
-hipError_t launch_colnorm_downdate(const float* U, int64_t b, int64_t B, float* D,
-                                   double* scratch, size_t scratch_doubles, hipStream_t s) {
-  const int64_t nblk = cdiv(b, B);
-  if (scratch && (size_t)(nblk * b) <= scratch_doubles) {
-    hipLaunchKernelGGL(colnorm_partial_kernel, dim3((unsigned)cdiv(b, 256), (unsigned)nblk),
-                       dim3(256), 0, s, U, b, B, scratch);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(colnorm_scan_kernel, dim3((unsigned)cdiv(b, 256)), dim3(256), 0, s, scratch,
-                       b, B, (int)nblk, D);
-    return hipGetLastError();
-  }
-  hipLaunchKernelGGL(colnorm_kernel, dim3((unsigned)cdiv(b, 256)), dim3(256), 0, s, U, b, B, D);
+hipError_t launch_colnorm_partial(const float* U, int64_t b, int64_t B, double* Dpart, int jlo,
+                                  int jhi, hipStream_t s) {
+  if (jhi <= jlo) return hipSuccess;
+  hipLaunchKernelGGL(colnorm_partial_kernel, dim3((unsigned)cdiv(b, 256), (unsigned)(jhi - jlo)),
+                     dim3(256), 0, s, U, b, B, Dpart, jlo);
   return hipGetLastError();
 }
 
-hipError_t launch_block_inverses(const float* Ublk, int64_t b, int64_t B, float* Nblk,
-                                 hipStream_t s) {
-  const int nblk = (int)cdiv(b, B);
+hipError_t launch_colnorm_scan(const double* Dpart, int64_t b, int64_t B, float* D, hipStream_t s) {
+  hipLaunchKernelGGL(colnorm_scan_kernel, dim3((unsigned)cdiv(b, 256)), dim3(256), 0, s, Dpart, b,
+                     B, (int)cdiv(b, B), D);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_inverses(const float* Ublk, int64_t b, int64_t B, float* Nblk, int jlo,
+                                 int jhi, hipStream_t s) {
+  if (jhi <= jlo) return hipSuccess;
   const size_t lds = (size_t)B * (B + 1) * sizeof(double);
   hipError_t a = hipFuncSetAttribute((const void*)block_inverse_kernel,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (a != hipSuccess) return a;
-  hipLaunchKernelGGL(block_inverse_kernel, dim3(nblk), dim3(1024), lds, s, Ublk, b, B, Nblk);
+  hipLaunchKernelGGL(block_inverse_kernel, dim3(jhi - jlo), dim3(1024), lds, s, Ublk, b, B, Nblk,
+                     jlo);
   return hipGetLastError();
 }
 

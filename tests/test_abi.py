@@ -220,3 +220,50 @@ def test_noalloc_rejects_layers_beyond_its_scratch_before_any_launch():
     # argument errors come first, as for th_prune_layer
     assert L.th_prune_layer_noalloc(None, 1, 64, 64, None, 1, 0, dummy, ctypes.byref(p), None,
                                     None, None, None, None) == 1
+
+
+def _gpu_present():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_gpu_present(), reason="calls the layer entry points on fake device pointers")
+@pytest.mark.parametrize("pattern,have_x,b", [(None, True, 304), ((2, 4), True, 304),
+                                               (None, False, 1000), ((2, 4), False, 11008),
+                                               (None, True, 11008)])
+def test_workspace_queries_match_the_calls(pattern, have_x, b):
+    """Each size query gives exactly what its call carves: with that many bytes the
+    call gets past its workspace check (and stops at the first device call, as no
+    device is present); one byte fewer is TH_ERR_WORKSPACE before anything runs."""
+    L = _lib.lib()
+    p = _lib.make_params(sparsity=0.6 if pattern is None else 0.5, pattern=pattern, block=128)
+    c, n, alpha = 150, 262144 if b == 11008 else 1000, 0.05
+    fake, ws = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x10000000)
+    x = fake if have_x else None
+    h = None if have_x else fake
+    st = _lib.Stats()
+    counts = (_lib._I64 * (-(-b // 128)))()
+    out = ctypes.c_size_t(0)
+    calls = [
+        (L.th_prune_layer_workspace_size, (c, b, n if have_x else 0, int(have_x), ctypes.byref(p)),
+         lambda nb: L.th_prune_layer(fake, _lib.TH_BF16, c, b, x, _lib.TH_BF16, n if have_x else 0,
+                                     h, ctypes.byref(p), None, None, ws, nb, ctypes.byref(st),
+                                     counts, None)),
+        (L.th_prune_layer_alpha_workspace_size,
+         (c, b, n if have_x else 0, int(have_x), ctypes.byref(p), ctypes.c_double(alpha)),
+         lambda nb: L.th_prune_layer_alpha(fake, _lib.TH_BF16, c, b, x, _lib.TH_BF16,
+                                           n if have_x else 0, h, ctypes.byref(p),
+                                           ctypes.c_double(alpha), None, None, None, ws, nb,
+                                           ctypes.byref(st), counts, None)),
+        (L.th_prune_sparsegpt_workspace_size, (c, b, n if have_x else 0, int(have_x), ctypes.byref(p)),
+         lambda nb: L.th_prune_sparsegpt(fake, _lib.TH_BF16, c, b, x, _lib.TH_BF16,
+                                         n if have_x else 0, h, ctypes.byref(p), None, None, ws, nb,
+                                         ctypes.byref(st), counts, None)),
+    ]
+    for size_fn, args, call in calls:
+        assert size_fn(*args, ctypes.byref(out)) == 0
+        assert call(out.value - 1) == _lib.TH_ERR_WORKSPACE
+        assert call(out.value) not in (0, _lib.TH_ERR_WORKSPACE, _lib.TH_ERR_INVALID_ARG)
