@@ -43,7 +43,8 @@ namespace th {
 // 32-bit byte offsets vo[k] (< 2^31) from two wave-uniform 64-bit bases (SGPRs),
 // g0 for the even loads and g1 for the odd ones. Load m = 2k + o takes vo[k]
 // from g_o and writes the 1 KB chunk at lds + 4096 m. No result registers;
-// completion is tracked by the callers' vmcnt waits.
+// completion is tracked by the callers' vmcnt waits. The s_add_u32 that step M0
+// write SCC, which the clobber list declares.
 __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
   // readfirstlane returns int: go through unsigned so the low half is not sign-extended
   return ((uint64_t)(unsigned)__builtin_amdgcn_readfirstlane((unsigned)(x >> 32)) << 32) |
@@ -70,7 +71,8 @@ __device__ __forceinline__ void lds_dma10s(const unsigned (&vo)[5], const void* 
       "s_add_u32 m0, %1, 36864\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %6, %8\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(base), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "v"(vo[3]), "v"(vo[4]), "s"(g0), "s"(g1));
+      : "s"(base), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "v"(vo[3]), "v"(vo[4]), "s"(g0), "s"(g1)
+      : "scc");
 }
 
 }  // namespace th
