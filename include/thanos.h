@@ -339,6 +339,19 @@ th_status th_debug_syrk_rect(float* H, const void* X_chunk, int64_t t, int64_t b
                              int32_t P, int32_t m, void* workspace, size_t workspace_bytes,
                              th_stream_t stream);
 
+/* W[:, col0:col_end] -= Z[:, 0:K] R[r0:r0+K, col0:col_end] on operands split once into
+ * three bf16 planes and 256 x 256 tiles, the update the N:M block loop applies to
+ * the columns past each group of eight blocks ["Pruning LLMs with Thanos", section
+ * "Contribution one: solve a selected set directly": every block's compensation
+ * reaches all still-active columns]. W [c, b] fp32 (pitch b), Z [c, ldz] fp32,
+ * R [>= r0+K, b] fp32, all device. K % 16 == 0, 0 <= col0 < col_end <= b, ldz >= K.
+ * workspace: >= 3 * ceil(K/64)*64 * (ceil(c/256) + ceil((col_end-col0)/256)) * 256 * 2
+ * bytes (TH_ERR_WORKSPACE if smaller), 16-byte aligned. Asynchronous. */
+th_status th_debug_far_update(float* W, int64_t c, int64_t b, const float* Z, int64_t ldz,
+                              const float* R, int64_t r0, int64_t K, int64_t col0,
+                              int64_t col_end, void* workspace, size_t workspace_bytes,
+                              th_stream_t stream);
+
 /* Message for the last non-OK status on this thread (never NULL). */
 const char* th_last_error(void);
 

@@ -83,6 +83,8 @@ _SIG = {
                                ctypes.c_size_t, _P],
     "th_debug_factor": [_P, _I64, _P, _P, ctypes.c_size_t, _P],
     "th_debug_syrk_rect": [_P, _P, _I64, _I64, _I64, _I32, _I32, _P, ctypes.c_size_t, _P],
+    "th_debug_far_update": [_P, _I64, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _P,
+                            ctypes.c_size_t, _P],
     "th_column_sq_norms_workspace_size": [_I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
     "th_column_sq_norms": [_P, _I32, _I64, _I64, _I64, _P, _P, ctypes.c_size_t, _P],
     "th_prune_baseline": [_P, _I32, _I64, _I64, _I32, _P, ctypes.POINTER(PruneParams), _P, _P],
@@ -390,6 +392,18 @@ def debug_syrk_rect(H, X, P, m=0):
     ws = workspace(tiles * max(m, 16) * 98304 * 4 + 4 * tiles, H.device)
     _check(lib().th_debug_syrk_rect(_ptr(H), _ptr(X), t, b, X.stride(0), P, m, _ptr(ws),
                                     ws.numel(), _stream(X.device)))
+
+
+def debug_far_update(W, Z, R, r0, K, col0, col_end):
+    """W[:, col0:col_end] -= Z[:, :K] R[r0:r0+K, col0:col_end] (split-bf16 planes, 256 tiles)."""
+    _require_cuda(W, Z, R)
+    c, b = W.shape
+    kp = -(-K // 64) * 64
+    nbytes = 3 * kp * (-(-c // 256) + -(-(col_end - col0) // 256)) * 256 * 2
+    ws = workspace(nbytes, W.device)
+    _check(lib().th_debug_far_update(_ptr(W), c, b, _ptr(Z), Z.stride(0), _ptr(R), r0, K, col0,
+                                     col_end, _ptr(ws), ws.numel(), _stream(W.device)))
+    return ws
 
 
 def debug_factor(H):

@@ -76,6 +76,7 @@ struct PruneLayout {
   float* Wf;
   uint8_t* mask;
   float* syrk_part;
+  unsigned short* Yfar;      // N:M: the far-column update's split operands
   unsigned long long* cand;  // unstructured: candidate keys of the selection
   unsigned int* cand_n;      // and their count per segment
   int64_t cand_quota;        // keys per segment
@@ -128,6 +129,11 @@ PruneLayout layout_prune(void* ws, int64_t c, int64_t b, int64_t n, bool have_x,
   L.Dpart = colnorm ? cv.take<double>((size_t)nblk * b) : nullptr;
   L.gW = (sgpt || p->score == TH_SCORE_WANDA) ? cv.take<float>((size_t)b) : nullptr;
   L.Z = cv.take<float>((size_t)c * (sgpt ? super_pitch(b, B) : z_pitch(b, p)));
+  // the first group's far columns are the widest
+  const int64_t ldz = sgpt ? 0 : z_pitch(b, p);
+  L.Yfar = (!sgpt && !unstr && b > ldz && far_x3_applies(c, b - ldz, ldz))
+               ? cv.take<unsigned short>(far_x3_elems(c, b - ldz, ldz))
+               : nullptr;
   L.Wf = need_wf ? cv.take<float>((size_t)c * b) : nullptr;
   L.mask = need_mask ? cv.take<uint8_t>((size_t)c * b) : nullptr;
   L.cand = nullptr;
@@ -358,9 +364,14 @@ th_status prune_blocks(const PruneLayout& L, int64_t c, int64_t b, const th_prun
                              Nb, Zb, ldz, mask, L.st, L.counts + blk, s),
              "solve");
       TH_HIP(launch_update(Wf, c, b, j0, Bb, ldz, j0, s1, Zb, L.R, mask, j0, Bb, s), "update");
-      if (j0 + Bb == s1 && s1 < b)  // last block of the super-block: the deferred columns
-        TH_HIP(launch_update(Wf, c, b, sb0, s1 - sb0, ldz, s1, b, L.Z, L.R, mask, 0, 0, s),
-               "deferred update");
+      if (j0 + Bb == s1 && s1 < b) {  // last block of the super-block: the deferred columns
+        if (L.Yfar && far_x3_applies(c, b - s1, s1 - sb0))
+          TH_HIP(launch_far_update(Wf, c, b, sb0, s1 - sb0, ldz, s1, b, L.Z, L.R, L.Yfar, s),
+                 "deferred update");
+        else
+          TH_HIP(launch_update(Wf, c, b, sb0, s1 - sb0, ldz, s1, b, L.Z, L.R, mask, 0, 0, s),
+                 "deferred update");
+      }
     }
   }
   return TH_OK;
@@ -964,6 +975,23 @@ th_status th_debug_syrk_rect(float* H, const void* X, int64_t t, int64_t b, int6
   TH_HIP(launch_syrk_rect(H, (const unsigned short*)X, t, b, ldx, (float*)workspace, P, m,
                           (hipStream_t)stream, false),
          "syrk rectangles");
+  return TH_OK;
+}
+
+th_status th_debug_far_update(float* W, int64_t c, int64_t b, const float* Z, int64_t ldz,
+                              const float* R, int64_t r0, int64_t K, int64_t col0,
+                              int64_t col_end, void* workspace, size_t workspace_bytes,
+                              th_stream_t stream) {
+  if (!W || !Z || !R || !workspace) return fail(TH_ERR_INVALID_ARG, "NULL argument");
+  if (c < 1 || b < 1 || K < 16 || K % 16 || ldz < K || r0 < 0 || col0 < 0 || col_end <= col0 ||
+      col_end > b)
+    return fail(TH_ERR_INVALID_ARG, "bad shape");
+  if ((uintptr_t)workspace & 15) return fail(TH_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (workspace_bytes < far_x3_elems(c, col_end - col0, K) * sizeof(unsigned short))
+    return fail(TH_ERR_WORKSPACE, "workspace too small");
+  TH_HIP(launch_far_update(W, c, b, r0, K, ldz, col0, col_end, Z, R, (unsigned short*)workspace,
+                           (hipStream_t)stream),
+         "far update");
   return TH_OK;
 }
 

@@ -26,7 +26,7 @@ def test_header_declares_the_path():
                  "th_factor_workspace_size", "th_prune_layer_factored",
                  "th_prune_layer_factored_workspace_size", "th_gated_ffn_input",
                  "th_prune_layer_alpha", "th_prune_layer_alpha_workspace_size",
-                 "th_prune_layer_noalloc", "th_debug_syrk_rect"):
+                 "th_prune_layer_noalloc", "th_debug_syrk_rect", "th_debug_far_update"):
         assert must in names
 
 

@@ -84,6 +84,28 @@ def test_hessian_rectangles_match_oracle(t, b, wgs, m):
     assert torch.equal(H, H2)
 
 
+# The far-column update of the N:M block loop (operands split once into bf16 planes,
+# 256 x 256 tiles) against the product in fp64: ragged rows and columns (tiles
+# past c and past the column range), K of one and of eight blocks, a column range
+# starting inside W.
+@pytest.mark.parametrize("c,b,K,r0,col0", [(300, 900, 128, 0, 128), (520, 1300, 1024, 128, 260),
+                                           (1000, 2050, 256, 512, 1026), (64, 300, 16, 16, 40)])
+def test_far_update_matches_fp64(c, b, K, r0, col0):
+    _say(f"far update c={c} b={b} K={K} r0={r0} col0={col0}")
+    g = np.random.default_rng(c + b + K)
+    W = g.standard_normal((c, b)).astype(np.float32)
+    Z = g.standard_normal((c, K + 8)).astype(np.float32) * 0.1
+    R = g.standard_normal((r0 + K + 3, b)).astype(np.float32) * 0.1
+    Wd = torch.from_numpy(W).to(DEV)
+    L.debug_far_update(Wd, torch.from_numpy(Z).to(DEV), torch.from_numpy(R).to(DEV), r0, K, col0, b)
+    got = Wd.cpu().numpy().astype(np.float64)
+    ref = W.astype(np.float64)
+    ref[:, col0:] -= Z[:, :K].astype(np.float64) @ R[r0:r0 + K, col0:].astype(np.float64)
+    assert np.array_equal(got[:, :col0], ref[:, :col0])  # columns before the range untouched
+    err = np.abs(got - ref).max() / np.abs(ref[:, col0:]).max()
+    assert err <= 1e-5, err
+
+
 def test_hessian_f32_and_finalize():
     _say("hessian f32 + finalize (config 1 shapes)")
     cfg = synth.config(1)
@@ -398,14 +420,15 @@ def test_prune_layers_sharing_one_hessian():
 @pytest.mark.parametrize("pattern", [None, (2, 4)])
 def test_prune_wide_layer_through_the_large_tile_update(pattern):
     """4096 x 6144 with 8192 tokens: wide enough that the updates of W run on the
-    128 x 128 split-operand tiles (at least 1024 tiles per launch): the early
-    per-block updates of unstructured pruning and the deferred updates of N:M
-    beyond each group of eight blocks. Unstructured: the whole layer against the
+    large tiles: the early per-block updates of unstructured pruning on the
+    128 x 128 split-operand tiles (at least 1024 tiles per launch), the deferred
+    updates of N:M beyond each group of eight blocks on 256 x 256 tiles of
+    operands split once into bf16 planes. Unstructured: the whole layer against the
     oracle. 2:4: rows are independent given H, so the oracle prunes 256 sampled
     rows (its own fp64 G) and the GPU's rows are compared with them."""
     import time
     c, b, n = 4096, 6144, 8192
-    _say(f"prune {c}x{b} n={n} {pattern or 'unstructured 0.5'} (128x128 update tiles)")
+    _say(f"prune {c}x{b} n={n} {pattern or 'unstructured 0.5'} (large update tiles)")
     W, X = _inputs(c, b, n, 41, relu=True, outliers=60)
     t0 = time.perf_counter()
     G = O.gram(X)
