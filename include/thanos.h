@@ -345,8 +345,12 @@ th_status th_debug_syrk_rect(float* H, const void* X_chunk, int64_t t, int64_t b
  * "Contribution one: solve a selected set directly": every block's compensation
  * reaches all still-active columns]. W [c, b] fp32 (pitch b), Z [c, ldz] fp32,
  * R [>= r0+K, b] fp32, all device. K % 16 == 0, 0 <= col0 < col_end <= b, ldz >= K.
- * workspace: >= 3 * ceil(K/64)*64 * (ceil(c/256) + ceil((col_end-col0)/256)) * 256 * 2
- * bytes (TH_ERR_WORKSPACE if smaller), 16-byte aligned. Asynchronous. */
+ * The tiles of a last, partial round of one workgroup per compute unit run in
+ * pieces of consecutive k stages whose sums are subtracted in a fixed order.
+ * workspace: the split planes, Y = 3 * ceil(K/64)*64 * (ceil(c/256) +
+ * ceil((col_end-col0)/256)) * 256 * 2 bytes rounded up to a multiple of 256, then
+ * 256 piece slots of 256 KB: >= Y + 67108864 bytes (TH_ERR_WORKSPACE if smaller),
+ * 16-byte aligned. Asynchronous. */
 th_status th_debug_far_update(float* W, int64_t c, int64_t b, const float* Z, int64_t ldz,
                               const float* R, int64_t r0, int64_t K, int64_t col0,
                               int64_t col_end, void* workspace, size_t workspace_bytes,

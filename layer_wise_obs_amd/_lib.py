@@ -399,7 +399,8 @@ def debug_far_update(W, Z, R, r0, K, col0, col_end):
     _require_cuda(W, Z, R)
     c, b = W.shape
     kp = -(-K // 64) * 64
-    nbytes = 3 * kp * (-(-c // 256) + -(-(col_end - col0) // 256)) * 256 * 2
+    ybytes = 3 * kp * (-(-c // 256) + -(-(col_end - col0) // 256)) * 256 * 2
+    nbytes = -(-ybytes // 256) * 256 + 256 * 256 * 256 * 4  # planes, then 256 piece slots
     ws = workspace(nbytes, W.device)
     _check(lib().th_debug_far_update(_ptr(W), c, b, _ptr(Z), Z.stride(0), _ptr(R), r0, K, col0,
                                      col_end, _ptr(ws), ws.numel(), _stream(W.device)))

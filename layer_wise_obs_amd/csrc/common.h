@@ -242,7 +242,8 @@ hipError_t launch_update(float* W, int64_t c, int64_t b, int64_t r0, int64_t K, 
 bool update_large_tiles(int64_t c, int64_t col0, int64_t col_end);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 // far_x3.hip: W[:, col0:col_end] -= Z[:, 0:K] R[r0:r0+K, col0:col_end] on operands
-// split once into bf16 planes (Y: far_x3_elems(c, col_end - col0, K) bf16)
+// split once into bf16 planes (Y: far_x3_elems(c, col_end - col0, K) bf16, the
+// planes followed by the slots of tiles run in pieces)
 bool far_x3_applies(int64_t c, int64_t ncols, int64_t K);
 size_t far_x3_elems(int64_t c, int64_t ncols_max, int64_t K);
 hipError_t launch_far_update(float* W, int64_t c, int64_t b, int64_t r0, int64_t K, int64_t ldz,

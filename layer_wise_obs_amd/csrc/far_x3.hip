@@ -10,6 +10,11 @@
 // buffer Y -- columns 0 .. ldA-1 hold Z^T (one per row of W), columns ldA .. hold R
 // -- and far_x3_kernel runs 256 x 256 tiles of W on the direct global->LDS
 // pipeline of x3_pipe.h with the six products per block, then writes W - acc.
+// A tile takes about as long whatever the number of tiles beside it, so a launch
+// costs whole rounds of one workgroup per compute unit. The tiles of a last,
+// partial round are therefore cut into m pieces of consecutive k stages that
+// fill one round: each piece writes its sums to a slot, and far_fix_kernel
+// subtracts a tile's m slots from W in a fixed order (deterministic).
 #include "x3_pipe.h"
 
 namespace th {
@@ -74,13 +79,27 @@ __global__ __launch_bounds__(256) void far_build_kernel(const float* __restrict_
   }
 }
 
-// W[0:nrows, col0:col0+ncols] -= Y[:, 0:nrows]^T Y[:, ldA:ldA+ncols] over nst stages of
-// 16 k rows; tile lin -> (lin % nti, lin / nti). One workgroup per tile.
+// Work split of one far-column product: tiles 0 .. nwhole-1 run whole (workgroup
+// w of that launch: tile (w % 8) per_xcd + w / 8, so an XCD's workgroups take
+// consecutive tiles), tiles nwhole .. ntiles-1 in m pieces each (workgroup p of the
+// pieces' launch: piece p % m of tile nwhole + p / m, stages [i nst / m, (i+1) nst / m)).
+struct FarSplit {
+  int nst, nti, ntiles, nwhole, per_xcd, m;
+};
+
+// Slot layout of a piece: float4 number (((a * 4 + cc) * 4 + r / 4) * 256 + thread)
+// holds accumulator values r .. r+3 of block (a, cc) of that thread.
+constexpr int kFarSlotFloats = kX3Tile * kX3Tile;
+
+// W[0:nrows, col0:col0+ncols] -= Y[:, 0:nrows]^T Y[:, ldA:ldA+ncols] over 16-row k
+// stages; tile lin -> (lin % nti, lin / nti). One workgroup per whole tile, or (PIECES)
+// per piece, which writes its slot instead of W.
+template <bool PIECES>
 __global__ __launch_bounds__(256, 1) void far_x3_kernel(float* __restrict__ W, int64_t nrows, int64_t b,
                                                          int64_t col0, int64_t ncols,
                                                          const unsigned short* __restrict__ Y,
                                                          int64_t ldy, int64_t ldA, int64_t kp,
-                                                         int nst, int nti, int ntiles, int per_xcd) {
+                                                         FarSplit sp, float* __restrict__ slots) {
   __shared__ __attribute__((aligned(1024))) unsigned char sm0[kX3StageBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char sm1[kX3StageBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char sm2[kX3StageBytes];
@@ -97,11 +116,22 @@ __global__ __launch_bounds__(256, 1) void far_x3_kernel(float* __restrict__ W, i
   const int lr = lane & 31, lk = lane >> 5;
   const int64_t pstride = kp * ldy;
   const int wg = blockIdx.x;
-  const int lin = (wg % 8) * per_xcd + wg / 8;  // an XCD's workgroups take consecutive tiles
-  if (lin >= ntiles) return;
+  int lin, st0, nst;
+  if (!PIECES) {
+    lin = (wg % 8) * sp.per_xcd + wg / 8;
+    if (lin >= sp.nwhole) return;
+    st0 = 0;
+    nst = sp.nst;
+  } else {
+    const int piece = wg;
+    lin = sp.nwhole + piece / sp.m;
+    const int i = piece % sp.m;
+    st0 = i * sp.nst / sp.m;
+    nst = (i + 1) * sp.nst / sp.m - st0;  // at least 3 (the host's choice of m)
+  }
   {
     // tiles column-major: the concurrent tiles of an XCD share column panels
-    const int ti = lin % nti, tj = lin / nti;
+    const int ti = lin % sp.nti, tj = lin / sp.nti;
     const int64_t row0 = (int64_t)ti * kX3Tile, ycol0 = ldA + (int64_t)tj * kX3Tile;
 
     // chunk m of this wave: c = wave + 4 m; plane c / 16, operand (c / 8) % 2
@@ -118,7 +148,7 @@ __global__ __launch_bounds__(256, 1) void far_x3_kernel(float* __restrict__ W, i
       vo[m] = (unsigned)((p * pstride + (int64_t)tr * ldy + (o ? ycol0 : row0) + fg * 8) * 2);
     }
     auto issue = [&](int st, unsigned char* sbase) {
-      x3d::dma12s(vo, Y + (int64_t)st * kX3StageK * ldy, sbase + wave * 1024);
+      x3d::dma12s(vo, Y + (int64_t)(st0 + st) * kX3StageK * ldy, sbase + wave * 1024);
     };
 
     f32x16_t acc[4][4];
@@ -206,6 +236,19 @@ __global__ __launch_bounds__(256, 1) void far_x3_kernel(float* __restrict__ W, i
       });
     }
 
+    if constexpr (PIECES) {
+      float4* slot = (float4*)(slots + (int64_t)wg * kFarSlotFloats);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq)
+            slot[((a * 4 + cc) * 4 + rq) * 256 + tid] =
+                make_float4(acc[a][cc][4 * rq], acc[a][cc][4 * rq + 1], acc[a][cc][4 * rq + 2],
+                            acc[a][cc][4 * rq + 3]);
+    } else {
+
     // W = W - acc: read-modify-write in four groups of 64 values per lane (one row
     // of 32 x 32 blocks each), the loads of group a+1 in flight while group a is
     // stored. One buffer resource per group starting at its first row: rows past c
@@ -261,9 +304,58 @@ __global__ __launch_bounds__(256, 1) void far_x3_kernel(float* __restrict__ W, i
         for (int e = 0; e < 64; ++e) cur[e] = nxt[e];
       }
     });
+    }
   }
 }
 
+// W -= the sum of a cut tile's m slots (added in slot order). Sixteen workgroups per
+// cut tile, one per accumulator block (a, cc) of far_x3_kernel's threads: thread t
+// takes the values thread t held there (its 16 KB of each slot are contiguous),
+// reads all of W's 16 values first, then writes them back.
+__global__ __launch_bounds__(256) void far_fix_kernel(float* __restrict__ W, int64_t nrows, int64_t b,
+                                                      int64_t col0, int64_t ncols,
+                                                      const float* __restrict__ slots, FarSplit sp) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wrow = wave >> 1, wcol = wave & 1;
+  const int lr = lane & 31, lk = lane >> 5;
+  const int tl = blockIdx.x >> 4, a = (blockIdx.x >> 2) & 3, cc = blockIdx.x & 3;
+  const int lin = sp.nwhole + tl;
+  const int ti = lin % sp.nti, tj = lin / sp.nti;
+  const int64_t rel = (int64_t)tj * kX3Tile + wcol * 128 + cc * 32 + lr;
+  if (rel >= ncols) return;
+  const int64_t rb = (int64_t)ti * kX3Tile + wrow * 128 + a * 32 + 4 * lk;
+  float* wcolp = W + col0 + rel;
+  float w[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t row = rb + 8 * (r >> 2) + (r & 3);
+    w[r] = row < nrows ? wcolp[row * b] : 0.f;
+  }
+  const float4* base = (const float4*)(slots + (int64_t)tl * sp.m * kFarSlotFloats) +
+                       (a * 4 + cc) * 4 * 256 + tid;
+  float4 sum[4];
+#pragma unroll
+  for (int rq = 0; rq < 4; ++rq) sum[rq] = base[rq * 256];
+  for (int i = 1; i < sp.m; ++i) {
+    const float4* sl = base + (int64_t)i * (kFarSlotFloats / 4);
+    float4 v[4];
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) v[rq] = sl[rq * 256];
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      sum[rq].x += v[rq].x; sum[rq].y += v[rq].y; sum[rq].z += v[rq].z; sum[rq].w += v[rq].w;
+    }
+  }
+#pragma unroll
+  for (int rq = 0; rq < 4; ++rq) {
+    const float vals[4] = {sum[rq].x, sum[rq].y, sum[rq].z, sum[rq].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t row = rb + 8 * rq + e;  // value r = 4 rq + e: row 8 (r/4) + (r%4)
+      if (row < nrows) wcolp[row * b] = w[4 * rq + e] - vals[e];
+    }
+  }
+}
 
 constexpr int64_t kFarMinTiles = 96;  // fewer 256 x 256 tiles: the 128 x 128 update is as fast
 
@@ -279,6 +371,44 @@ FarDims far_dims(int64_t c, int64_t ncols, int64_t K) {
   return d;
 }
 
+// Y's three planes, rounded up to 256 bytes; the piece slots follow.
+int64_t far_y_elems(const FarDims& d) { return cdiv(3 * d.kp * d.ldy, 128) * 128; }
+
+constexpr int kFarMaxPieces = 256;  // slots in the workspace (256 KB each)
+
+int far_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  return n;
+}
+
+// Whole rounds of P tiles run whole; the T tiles of a last, partial round are cut
+// into m = floor(P' / T) pieces (P' = min(P, slots)) when that gives at least two,
+// each piece at least three stages (the pipeline keeps three stages in flight).
+FarSplit far_split(int nti, int ntiles, int nst, int P) {
+  FarSplit sp;
+  sp.nst = nst;
+  sp.nti = nti;
+  sp.ntiles = ntiles;
+  const int cap = P < kFarMaxPieces ? P : kFarMaxPieces;
+  const int T = ntiles % P;
+  int m = T > 0 ? cap / T : 1;
+  if (m > nst / 3) m = nst / 3;
+  if (m < 2) {
+    sp.nwhole = ntiles;
+    sp.m = 1;
+  } else {
+    sp.nwhole = ntiles - T;
+    sp.m = m;
+  }
+  sp.per_xcd = (int)cdiv(sp.nwhole, 8);
+  return sp;
+}
+
 }  // namespace
 
 bool far_x3_applies(int64_t c, int64_t ncols, int64_t K) {
@@ -290,7 +420,7 @@ bool far_x3_applies(int64_t c, int64_t ncols, int64_t K) {
 
 size_t far_x3_elems(int64_t c, int64_t ncols_max, int64_t K) {
   const FarDims d = far_dims(c, ncols_max, K);
-  return (size_t)(3 * d.kp * d.ldy);
+  return (size_t)(far_y_elems(d) + (int64_t)kFarMaxPieces * kFarSlotFloats * 2);
 }
 
 hipError_t launch_far_update(float* W, int64_t c, int64_t b, int64_t r0, int64_t K, int64_t ldz,
@@ -304,10 +434,20 @@ hipError_t launch_far_update(float* W, int64_t c, int64_t b, int64_t r0, int64_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nti = (int)(d.ldA / kX3Tile), ntj = (int)(d.ldB / kX3Tile);
-  const int ntiles = nti * ntj;
-  const int per_xcd = (int)cdiv(ntiles, 8);
-  hipLaunchKernelGGL(far_x3_kernel, dim3((unsigned)(per_xcd * 8)), dim3(256), 0, s, W, c, b, col0,
-                     ncols, Y, d.ldy, d.ldA, d.kp, (int)(K / kX3StageK), nti, ntiles, per_xcd);
+  const FarSplit sp = far_split(nti, nti * ntj, (int)(K / kX3StageK), far_cus());
+  float* slots = (float*)(Y + far_y_elems(d));
+  const int ncut = sp.ntiles - sp.nwhole;
+  if (sp.nwhole > 0) {
+    hipLaunchKernelGGL(far_x3_kernel<false>, dim3((unsigned)(8 * sp.per_xcd)), dim3(256), 0, s, W,
+                       c, b, col0, ncols, Y, d.ldy, d.ldA, d.kp, sp, slots);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (ncut == 0) return hipSuccess;
+  hipLaunchKernelGGL(far_x3_kernel<true>, dim3((unsigned)(ncut * sp.m)), dim3(256), 0, s, W, c, b,
+                     col0, ncols, Y, d.ldy, d.ldA, d.kp, sp, slots);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(far_fix_kernel, dim3((unsigned)(ncut * 16)), dim3(256), 0, s, W, c, b, col0, ncols,
+                     (const float*)slots, sp);
   return hipGetLastError();
 }
 

@@ -87,9 +87,13 @@ def test_hessian_rectangles_match_oracle(t, b, wgs, m):
 # The far-column update of the N:M block loop (operands split once into bf16 planes,
 # 256 x 256 tiles) against the product in fp64: ragged rows and columns (tiles
 # past c and past the column range), K of one and of eight blocks, a column range
-# starting inside W.
+# starting inside W. Tiles beyond whole rounds of one workgroup per compute unit
+# run in pieces of k stages: the first three cases on 256 compute units have 8, 15
+# and 16 tiles (2, 17 and 5 pieces each), the fourth one stage (whole tiles only),
+# the last 272 tiles (256 whole, 16 in 4 pieces), run twice for bit-identity.
 @pytest.mark.parametrize("c,b,K,r0,col0", [(300, 900, 128, 0, 128), (520, 1300, 1024, 128, 260),
-                                           (1000, 2050, 256, 512, 1026), (64, 300, 16, 16, 40)])
+                                           (1000, 2050, 256, 512, 1026), (64, 300, 16, 16, 40),
+                                           (4096, 4400, 192, 64, 48)])
 def test_far_update_matches_fp64(c, b, K, r0, col0):
     _say(f"far update c={c} b={b} K={K} r0={r0} col0={col0}")
     g = np.random.default_rng(c + b + K)
@@ -104,6 +108,10 @@ def test_far_update_matches_fp64(c, b, K, r0, col0):
     assert np.array_equal(got[:, :col0], ref[:, :col0])  # columns before the range untouched
     err = np.abs(got - ref).max() / np.abs(ref[:, col0:]).max()
     assert err <= 1e-5, err
+    if c >= 4096:
+        W2 = torch.from_numpy(W).to(DEV)
+        L.debug_far_update(W2, torch.from_numpy(Z).to(DEV), torch.from_numpy(R).to(DEV), r0, K, col0, b)
+        assert torch.equal(W2, Wd)
 
 
 def test_hessian_f32_and_finalize():
