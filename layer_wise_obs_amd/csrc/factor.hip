@@ -608,10 +608,17 @@ hipError_t launch_chol_inv_inplace(float* S, int64_t b, float* P, DevState* st, 
       if ((e = hipGetLastError()) != hipSuccess) return e;
       if ((e = hipEventRecord(side->built, side->s3)) != hipSuccess) return e;
       if ((e = hipStreamWaitEvent(side->s2, side->built, 0)) != hipSuccess) return e;
-      // one workgroup per compute unit on 7/8 of the units: the rest keep room for
-      // the next pair's chain (1/4, 1/16 and none were slower on the 11008 layer)
+      // One workgroup per compute unit on 7/8 of the units: the rest keep room for
+      // the next pair's chain (1/4, 1/16 and none were slower on the 11008 layer).
+      // A tile takes about as long however many run beside it, so the set costs
+      // whole rounds: where a grid that leaves 3/32 of the units free saves a
+      // round, take it (leaving 1/16 or 1/32 free there was slower: the chain
+      // beside it slows down); the grid is then spread evenly over the rounds.
       const int64_t slots = side->slots - side->slots / 8;
-      const int64_t grid = nrest < slots ? nrest : slots;
+      const int64_t wide = side->slots - 3 * side->slots / 32;
+      int64_t rounds = cdiv(nrest, slots);
+      if (rounds > 1 && cdiv(nrest, rounds - 1) <= wide) --rounds;
+      const int64_t grid = cdiv(nrest, rounds);
       hipLaunchKernelGGL(rest_x3_kernel, dim3((unsigned)grid), dim3(256), 0, side->s2, S, b, k, Yp,
                          ldy, nrest);
       if ((e = hipGetLastError()) != hipSuccess) return e;
