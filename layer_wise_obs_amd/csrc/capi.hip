@@ -314,6 +314,9 @@ th_status prune_blocks(const PruneLayout& L, int64_t c, int64_t b, const th_prun
   // the layer's budget k_total = round-half-even(p c b) joins at the first block
   const long long k_total = unstr ? (long long)std::nearbyint(p->sparsity * (double)c * (double)b) : 0;
   bool next_digit_done = false;  // the previous update counted this block's first digit
+  // N:M with at most 64 pruned per block row (every block takes route A): the
+  // block-local compensation runs inside the solve (one launch per block)
+  const bool local = !unstr && solve_nm_local_applies(B, p->pattern.n, p->pattern.m);
   for (int64_t blk = 0; blk < nblk; ++blk) {
     const int64_t j0 = blk * B;
     const int64_t Bb = (b - j0) < B ? (b - j0) : B;
@@ -360,10 +363,19 @@ th_status prune_blocks(const PruneLayout& L, int64_t c, int64_t b, const th_prun
       const int64_t sb0 = (blk / per) * ldz;
       const int64_t s1 = (sb0 + ldz) < b ? (sb0 + ldz) : b;
       float* Zb = L.Z + (blk % per) * B;
-      TH_HIP(launch_solve_nm(Wf, c, b, j0, B, p->pattern.n, p->pattern.m, L.R, obs ? nullptr : L.gW,
-                             Nb, Zb, ldz, mask, L.st, L.counts + blk, s),
-             "solve");
-      TH_HIP(launch_update(Wf, c, b, j0, Bb, ldz, j0, s1, Zb, L.R, mask, j0, Bb, s), "update");
+      if (local) {
+        // left-looking inside the group: the solve subtracts the earlier blocks'
+        // compensation from its rows first and writes the block's final weights
+        TH_HIP(launch_solve_nm_local(Wf, c, b, j0, B, p->pattern.n, p->pattern.m, L.R,
+                                     obs ? nullptr : L.gW, Zb, ldz, sb0, mask, L.st,
+                                     L.counts + blk, s),
+               "solve");
+      } else {
+        TH_HIP(launch_solve_nm(Wf, c, b, j0, B, p->pattern.n, p->pattern.m, L.R,
+                               obs ? nullptr : L.gW, Nb, Zb, ldz, mask, L.st, L.counts + blk, s),
+               "solve");
+        TH_HIP(launch_update(Wf, c, b, j0, Bb, ldz, j0, s1, Zb, L.R, mask, j0, Bb, s), "update");
+      }
       if (j0 + Bb == s1 && s1 < b) {  // last block of the super-block: the deferred columns
         if (L.Yfar && far_x3_applies(c, b - s1, s1 - sb0))
           TH_HIP(launch_far_update(Wf, c, b, sb0, s1 - sb0, ldz, s1, b, L.Z, L.R, L.Yfar, s),

@@ -250,6 +250,181 @@ __global__ __launch_bounds__(kWaves * 64, ROUTE == 2 ? 2 : 4) void solve_kernel(
   }
 }
 
+// N:M, route A (s <= 64), with the block-local compensation of the block's group
+// folded into the solve. Under N:M no budget couples the rows, so each row's
+// blocks can be taken left-looking: before scoring block J, a workgroup
+// subtracts from its kWaves rows' W[k, J] the compensation of the earlier blocks
+// of the same group -- their coefficients (Z, columns 0 .. Kp of the group's
+// rows) times their slices R[J_i, J] -- and after the solve it writes the block's
+// final weights: W[k, q] - (z M)[q] on the kept columns, exact zeros on the
+// pruned ones ("Pruning LLMs with Thanos", section "Contribution one: solve a
+// selected set directly"). The columns past the group are updated once per group,
+// by the far-column update, from the same Z. This replaces one update launch per
+// block; the arithmetic is the same products summed in another order.
+//
+// The group's product: thread (g = tid / 128, q = tid % 128) sums over its
+// quarter of the K = Kp inner index for all kWaves rows of the batch (R read once
+// per workgroup, the rows' Z entries wave-uniform); the four partial sums meet
+// in LDS (the space of M, which is loaded after them) and are added in a fixed
+// order, so the result does not depend on timing.
+__global__ __launch_bounds__(kWaves * 64, 4) void solve_nm_local_kernel(SolveArgs a, float* Ww,
+                                                                         int64_t r0, int Kp) {
+  __shared__ float sM[kMaxBlock * kMaxBlock];
+  __shared__ float sg[kMaxBlock];
+  __shared__ float sbuf[kWaves][kMaxBlock];
+  __shared__ float su[kWaves][kMaxBlock];
+  __shared__ int sQ[kWaves][kMaxBlock];
+  __shared__ __attribute__((aligned(16))) int sP[kWaves][64];
+  __shared__ unsigned long long scount[kWaves];
+  static_assert(4 * kWaves * kMaxBlock <= kMaxBlock * kMaxBlock, "partials fit in sM");
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int Bb = a.Bb;
+  const int64_t b = a.b, j0 = a.j0, c = a.c, ldz = a.ldz;
+  const float* Zg = a.Z - Kp;  // the group's first coefficient column
+  for (int q = tid; q < Bb; q += blockDim.x) {
+    float gq;
+    if (a.g_mode == 0) gq = __fdiv_rn(1.0f, a.R[(j0 + q) * b + j0 + q]);
+    else gq = a.g[j0 + q];
+    sg[q] = gq;
+  }
+  const unsigned long long lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+  unsigned long long count = 0;
+
+  {  // one batch of kWaves rows per workgroup: no loop for values to be hoisted across
+    const int64_t kb = (int64_t)blockIdx.x * kWaves;
+    const int64_t k = kb + wave;
+    const bool rowv = k < c;
+    const int e0 = lane, e1 = lane + 64;
+    const bool v0 = e0 < Bb, v1 = e1 < Bb;
+    float* wrow = Ww + (rowv ? k : 0) * b + j0;
+    float w0 = (rowv && v0) ? wrow[e0] : 0.f;
+    float w1 = (rowv && v1) ? wrow[e1] : 0.f;
+    if (Kp > 0) {
+      const int q = tid & (kMaxBlock - 1);
+      const int g = __builtin_amdgcn_readfirstlane(tid >> 7);
+      const int kbeg = g * Kp / 4, kend = (g + 1) * Kp / 4;
+      const float* Rq = a.R + (r0 + kbeg) * b + j0 + (q < Bb ? q : Bb - 1);
+      int64_t zoff[kWaves];
+#pragma unroll
+      for (int r = 0; r < kWaves; ++r) zoff[r] = ((kb + r) < c ? (kb + r) : (c - 1)) * ldz;
+      float acc[kWaves];
+#pragma unroll
+      for (int r = 0; r < kWaves; ++r) acc[r] = 0.f;
+      // R in chunks of kU rows, the next chunk's loads issued before this chunk's
+      // products (one chunk in flight behind the arithmetic)
+      constexpr int kU = 8;
+      const int nfull = (kend - kbeg) / kU;
+      float rv[kU], rn[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) rn[u] = nfull > 0 ? Rq[(int64_t)u * b] : 0.f;
+      for (int ch = 0; ch < nfull; ++ch) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) rv[u] = rn[u];
+        if (ch + 1 < nfull) {
+#pragma unroll
+          for (int u = 0; u < kU; ++u) rn[u] = Rq[(int64_t)((ch + 1) * kU + u) * b];
+        }
+        const int kk0 = kbeg + ch * kU;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+#pragma unroll
+          for (int r = 0; r < kWaves; ++r) acc[r] = fmaf(Zg[zoff[r] + kk0 + u], rv[u], acc[r]);
+        }
+      }
+      for (int kk = kbeg + nfull * kU; kk < kend; ++kk) {
+        const float r1 = Rq[(int64_t)(kk - kbeg) * b];
+#pragma unroll
+        for (int r = 0; r < kWaves; ++r) acc[r] = fmaf(Zg[zoff[r] + kk], r1, acc[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < kWaves; ++r) sM[(g * kWaves + r) * kMaxBlock + q] = acc[r];
+      __syncthreads();
+      const float* p0 = sM + wave * kMaxBlock;
+      constexpr int kPart = kWaves * kMaxBlock;
+      if (v0) w0 -= ((p0[e0] + p0[kPart + e0]) + p0[2 * kPart + e0]) + p0[3 * kPart + e0];
+      if (v1) w1 -= ((p0[e1] + p0[kPart + e1]) + p0[2 * kPart + e1]) + p0[3 * kPart + e1];
+      __syncthreads();  // the partial sums are read before M overwrites them
+    }
+    {  // M = [A_F]_{J,J}: all 32 loads of a thread in flight at once, addresses clamped
+      constexpr int kPer = kMaxBlock * kMaxBlock / (kWaves * 64);
+      const float* src = a.R + j0 * b + j0;
+      float v[kPer];
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        const int idx = e * kWaves * 64 + tid, r = idx >> 7, q = idx & (kMaxBlock - 1);
+        const int rr = r < Bb ? r : Bb - 1, qq = q < Bb ? q : Bb - 1;
+        v[e] = src[rr * b + qq];
+      }
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        const int idx = e * kWaves * 64 + tid, r = idx >> 7, q = idx & (kMaxBlock - 1);
+        if (r < Bb && q < Bb) sM[mat_idx(r, q)] = v[e];
+      }
+    }
+    __syncthreads();
+    if (rowv) {
+      if (v0) sbuf[wave][e0] = score_of(w0, sg[e0]);
+      if (v1) sbuf[wave][e1] = score_of(w1, sg[e1]);
+      wave_sync();
+      const bool s0 = v0 && nm_pruned(sbuf[wave], e0, a.n, a.m);
+      const bool s1 = v1 && nm_pruned(sbuf[wave], e1, a.n, a.m);
+      const unsigned long long m0 = __ballot(s0), m1 = __ballot(s1);
+      const int s = __popcll(m0) + __popcll(m1);
+      uint8_t* mrow = a.mask + k * b + j0;
+      if (v0) mrow[e0] = s0 ? 1 : 0;
+      if (v1) mrow[e1] = s1 ? 1 : 0;
+      float* zrow = a.Z + k * ldz;
+      if (v0 && !s0) zrow[e0] = 0.f;
+      if (v1 && !s1) zrow[e1] = 0.f;
+      const int pos0 = __popcll(m0 & lt), pos1 = __popcll(m0) + __popcll(m1 & lt);
+      if (s0) { sQ[wave][pos0] = e0; su[wave][pos0] = w0; }
+      if (s1) { sQ[wave][pos1] = e1; su[wave][pos1] = w1; }
+      wave_sync();
+      float d0 = 0.f, d1 = 0.f;
+      if (s > 0) {
+        int olane;
+        __asm__ volatile("v_mov_b32 %0, %1" : "=v"(olane) : "v"(lane));
+        float reg[64];
+        const bool act = lane < s;
+        const int qa = act ? sQ[wave][lane] : 0;
+  #pragma unroll
+        for (int cc = 0; cc < 64; ++cc) {
+          const bool in = (cc < s) && act;
+          const int qc = (cc < s) ? sQ[wave][cc] : 0;
+          const float v = sM[mat_idx(qa, qc)];
+          reg[cc] = in ? v : ((cc == olane) ? 1.f : 0.f);
+        }
+        const float u = act ? su[wave][lane] : 0.f;
+        wave_sync();
+        const float z = gauss_jordan64(reg, u, (float*)sP[wave], olane);
+        if (act) zrow[qa] = z;
+        // the block's own compensation: d_e = sum over the selected t of z_t M[Q_t, e]
+        const float za = act ? z : 0.f;
+        for (int t = 0; t < s; ++t) {
+          const float zt = bcast(za, t);
+          const int qt = __builtin_amdgcn_readlane(qa, t);
+          d0 = fmaf(zt, sM[mat_idx(qt, e0)], d0);
+          d1 = fmaf(zt, sM[mat_idx(qt, e1)], d1);
+        }
+      }
+      if (v0) wrow[e0] = s0 ? 0.f : w0 - d0;
+      if (v1) wrow[e1] = s1 ? 0.f : w1 - d1;
+      count = (unsigned long long)s;
+    }
+  }
+  if (lane == 0) scount[wave] = count;
+  __syncthreads();
+  if (tid == 0) {
+    unsigned long long tot = 0;
+    for (int w = 0; w < kWaves; ++w) tot += scount[w];
+    if (tot) {
+      atomicAdd((unsigned long long*)&a.st->pruned, tot);
+      atomicAdd(a.blk_count, tot);
+    }
+  }
+}
+
 // Parity entry: N:M selection on given scores, one wave per row.
 __global__ __launch_bounds__(256) void debug_select_nm_kernel(const float* __restrict__ S,
                                                               int64_t c, int64_t blk, int n,
@@ -302,6 +477,28 @@ hipError_t launch_solve_nm(const float* W, int64_t c, int64_t b, int64_t j0, int
     hipLaunchKernelGGL((solve_kernel<0, 0>), dim3(solve_grid(c)), dim3(kWaves * 64), 0, s, a);
   else
     hipLaunchKernelGGL((solve_kernel<0, 1>), dim3(solve_grid(c)), dim3(kWaves * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+bool solve_nm_local_applies(int64_t Bb, int n, int m) { return Bb / m * (m - n) <= 64; }
+
+hipError_t launch_solve_nm_local(float* W, int64_t c, int64_t b, int64_t j0, int64_t B, int n,
+                                 int m, const float* R, const float* gW, float* Z, int64_t ldz,
+                                 int64_t r0, uint8_t* mask, DevState* st,
+                                 unsigned long long* blk_count, hipStream_t s) {
+  SolveArgs a;
+  a.W = W; a.c = c; a.b = b; a.j0 = j0;
+  a.Bb = (int)((b - j0) < B ? (b - j0) : B);
+  a.B = (int)B; a.n = n; a.m = m; a.R = R; a.Nblk = nullptr;
+  a.g = gW; a.g_mode = gW ? 2 : 0;
+  a.Z = Z; a.ldz = ldz; a.mask = mask; a.st = st; a.blk_count = blk_count;
+  if (!solve_nm_local_applies(a.Bb, n, m) || j0 < r0) return hipErrorInvalidValue;
+  if (c == 0) return hipSuccess;
+  // one batch of kWaves rows per workgroup
+  const int64_t g = cdiv(c, kWaves);
+  if (g > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(solve_nm_local_kernel, dim3((unsigned)g), dim3(kWaves * 64), 0, s, a, W, r0,
+                     (int)(j0 - r0));
   return hipGetLastError();
 }
 
