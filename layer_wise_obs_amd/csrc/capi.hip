@@ -302,7 +302,8 @@ th_status begin_layer(const PruneLayout& L, const void* W, th_dtype wdt, int64_t
 // per-block counts and the pruned total in the device state.
 // prepared: inverse_factor (with zero_block = B) has already made the slices.
 th_status prune_blocks(const PruneLayout& L, int64_t c, int64_t b, const th_prune_params* p,
-                       float* Wf, uint8_t* mask, hipStream_t s, bool prepared) {
+                       float* Wf, uint8_t* mask, hipStream_t s, bool prepared,
+                       void* Wout = nullptr, th_dtype wdt = TH_F32, bool* cast_done = nullptr) {
   const int64_t B = p->block;
   const int64_t nblk = cdiv(b, B);
   const bool unstr = p->pattern.kind == TH_UNSTRUCTURED;
@@ -317,6 +318,8 @@ th_status prune_blocks(const PruneLayout& L, int64_t c, int64_t b, const th_prun
   // N:M with at most 64 pruned per block row (every block takes route A): the
   // block-local compensation runs inside the solve (one launch per block)
   const bool local = !unstr && solve_nm_local_applies(B, p->pattern.n, p->pattern.m);
+  // there every block's solve writes its final columns, in the output dtype too
+  if (cast_done) *cast_done = local && Wout;
   for (int64_t blk = 0; blk < nblk; ++blk) {
     const int64_t j0 = blk * B;
     const int64_t Bb = (b - j0) < B ? (b - j0) : B;
@@ -368,7 +371,7 @@ th_status prune_blocks(const PruneLayout& L, int64_t c, int64_t b, const th_prun
         // compensation from its rows first and writes the block's final weights
         TH_HIP(launch_solve_nm_local(Wf, c, b, j0, B, p->pattern.n, p->pattern.m, L.R,
                                      obs ? nullptr : L.gW, Zb, ldz, sb0, mask, L.st,
-                                     L.counts + blk, s),
+                                     L.counts + blk, Wout, wdt, s),
                "solve");
       } else {
         TH_HIP(launch_solve_nm(Wf, c, b, j0, B, p->pattern.n, p->pattern.m, L.R,
@@ -473,9 +476,10 @@ th_status th_prune_layer(void* W, th_dtype wdt, int64_t c, int64_t b, const void
   th_status pre = inverse_factor(X, xdt, n, H, b, p, L, s, p->block);
   if (pre != TH_OK) return pre;
 
-  th_status blocks = prune_blocks(L, c, b, p, Wf, mask, s, true);
+  bool cast_done = false;
+  th_status blocks = prune_blocks(L, c, b, p, Wf, mask, s, true, W, wdt, &cast_done);
   if (blocks != TH_OK) return blocks;
-  TH_HIP(launch_from_f32(Wf, c * b, wdt, W, s), "cast back");
+  if (!cast_done) TH_HIP(launch_from_f32(Wf, c * b, wdt, W, s), "cast back");
   return finish_layer(L, nblk, stats_out, block_counts, s);
 }
 
@@ -695,9 +699,10 @@ th_status th_prune_layer_factored(void* W, th_dtype wdt, int64_t c, int64_t b, c
   if (st0 != TH_OK) return st0;
   // the slices are formed in place, so the caller's factor is copied first
   TH_HIP(hipMemcpyAsync(L.R, U, (size_t)b * b * sizeof(float), hipMemcpyDeviceToDevice, s), "U");
-  th_status blocks = prune_blocks(L, c, b, p, Wf, mask, s, false);
+  bool cast_done = false;
+  th_status blocks = prune_blocks(L, c, b, p, Wf, mask, s, false, W, wdt, &cast_done);
   if (blocks != TH_OK) return blocks;
-  TH_HIP(launch_from_f32(Wf, c * b, wdt, W, s), "cast back");
+  if (!cast_done) TH_HIP(launch_from_f32(Wf, c * b, wdt, W, s), "cast back");
   return finish_layer(L, cdiv(b, p->block), stats_out, block_counts, s);
 }
 

@@ -54,6 +54,8 @@ __device__ __forceinline__ int mat_idx(int r, int q) { return r * kMaxBlock + (q
 // The elimination runs at the fp32 VALU rate (a wave64 FMA takes four cycles of
 // a 16-lane SIMD): about 20 us of a 2:4 block's 37 us at c = 4096.
 constexpr int kLdsFrom = 32;
+// Largest inner dimension of the folded group product (seven earlier blocks of 128).
+constexpr int kLocalMaxK = 7 * kMaxBlock;
 
 __device__ __forceinline__ float gauss_jordan64(float (&reg)[64], float rhs, float* row, int lane) {
   float piv = 1.f;
@@ -268,15 +270,18 @@ __global__ __launch_bounds__(kWaves * 64, ROUTE == 2 ? 2 : 4) void solve_kernel(
 // in LDS (the space of M, which is loaded after them) and are added in a fixed
 // order, so the result does not depend on timing.
 __global__ __launch_bounds__(kWaves * 64, 4) void solve_nm_local_kernel(SolveArgs a, float* Ww,
-                                                                         int64_t r0, int Kp) {
-  __shared__ float sM[kMaxBlock * kMaxBlock];
+                                                                         int64_t r0, int Kp,
+                                                                         void* Wout, int out_bf16) {
+  __shared__ __attribute__((aligned(16))) float sM[kMaxBlock * kMaxBlock];
   __shared__ float sg[kMaxBlock];
   __shared__ float sbuf[kWaves][kMaxBlock];
   __shared__ float su[kWaves][kMaxBlock];
   __shared__ int sQ[kWaves][kMaxBlock];
   __shared__ __attribute__((aligned(16))) int sP[kWaves][64];
   __shared__ unsigned long long scount[kWaves];
-  static_assert(4 * kWaves * kMaxBlock <= kMaxBlock * kMaxBlock, "partials fit in sM");
+  static_assert(kWaves == 8, "the staged coefficients are read as two float4 per inner index");
+  static_assert(4 * kWaves * kMaxBlock + kWaves * kLocalMaxK <= kMaxBlock * kMaxBlock,
+                "partial sums and staged coefficients fit in the space of M");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Bb = a.Bb;
@@ -301,19 +306,42 @@ __global__ __launch_bounds__(kWaves * 64, 4) void solve_nm_local_kernel(SolveArg
     float w0 = (rowv && v0) ? wrow[e0] : 0.f;
     float w1 = (rowv && v1) ? wrow[e1] : 0.f;
     if (Kp > 0) {
+      // the batch's coefficients of the earlier blocks, kk-major (8 rows per kk),
+      // staged in the space of M behind the partial sums
+      constexpr int kPart = kWaves * kMaxBlock;
+      float* const sZ = sM + 4 * kPart;
+      {  // all loads of a thread in flight at once (Kp <= kLocalMaxK < 2 * 512)
+        constexpr int kH = (kLocalMaxK + kWaves * 64 - 1) / (kWaves * 64);
+        float zv[kWaves][kH];
+#pragma unroll
+        for (int r = 0; r < kWaves; ++r) {
+          const int64_t row = (kb + r) < c ? (kb + r) : (c - 1);
+#pragma unroll
+          for (int h = 0; h < kH; ++h) {
+            const int kk = tid + h * kWaves * 64;
+            zv[r][h] = kk < Kp ? Zg[row * ldz + kk] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < kWaves; ++r) {
+#pragma unroll
+          for (int h = 0; h < kH; ++h) {
+            const int kk = tid + h * kWaves * 64;
+            if (kk < Kp) sZ[kk * kWaves + r] = zv[r][h];
+          }
+        }
+      }
+      __syncthreads();
       const int q = tid & (kMaxBlock - 1);
       const int g = __builtin_amdgcn_readfirstlane(tid >> 7);
       const int kbeg = g * Kp / 4, kend = (g + 1) * Kp / 4;
       const float* Rq = a.R + (r0 + kbeg) * b + j0 + (q < Bb ? q : Bb - 1);
-      int64_t zoff[kWaves];
-#pragma unroll
-      for (int r = 0; r < kWaves; ++r) zoff[r] = ((kb + r) < c ? (kb + r) : (c - 1)) * ldz;
       float acc[kWaves];
 #pragma unroll
       for (int r = 0; r < kWaves; ++r) acc[r] = 0.f;
       // R in chunks of kU rows, the next chunk's loads issued before this chunk's
       // products (one chunk in flight behind the arithmetic)
-      constexpr int kU = 8;
+      constexpr int kU = 16;
       const int nfull = (kend - kbeg) / kU;
       float rv[kU], rn[kU];
 #pragma unroll
@@ -325,23 +353,29 @@ __global__ __launch_bounds__(kWaves * 64, 4) void solve_nm_local_kernel(SolveArg
 #pragma unroll
           for (int u = 0; u < kU; ++u) rn[u] = Rq[(int64_t)((ch + 1) * kU + u) * b];
         }
-        const int kk0 = kbeg + ch * kU;
+        const float4* zc = (const float4*)(sZ + (kbeg + ch * kU) * kWaves);
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-#pragma unroll
-          for (int r = 0; r < kWaves; ++r) acc[r] = fmaf(Zg[zoff[r] + kk0 + u], rv[u], acc[r]);
+          const float4 za = zc[2 * u], zb = zc[2 * u + 1];
+          acc[0] = fmaf(za.x, rv[u], acc[0]);
+          acc[1] = fmaf(za.y, rv[u], acc[1]);
+          acc[2] = fmaf(za.z, rv[u], acc[2]);
+          acc[3] = fmaf(za.w, rv[u], acc[3]);
+          acc[4] = fmaf(zb.x, rv[u], acc[4]);
+          acc[5] = fmaf(zb.y, rv[u], acc[5]);
+          acc[6] = fmaf(zb.z, rv[u], acc[6]);
+          acc[7] = fmaf(zb.w, rv[u], acc[7]);
         }
       }
       for (int kk = kbeg + nfull * kU; kk < kend; ++kk) {
         const float r1 = Rq[(int64_t)(kk - kbeg) * b];
 #pragma unroll
-        for (int r = 0; r < kWaves; ++r) acc[r] = fmaf(Zg[zoff[r] + kk], r1, acc[r]);
+        for (int r = 0; r < kWaves; ++r) acc[r] = fmaf(sZ[kk * kWaves + r], r1, acc[r]);
       }
 #pragma unroll
       for (int r = 0; r < kWaves; ++r) sM[(g * kWaves + r) * kMaxBlock + q] = acc[r];
       __syncthreads();
       const float* p0 = sM + wave * kMaxBlock;
-      constexpr int kPart = kWaves * kMaxBlock;
       if (v0) w0 -= ((p0[e0] + p0[kPart + e0]) + p0[2 * kPart + e0]) + p0[3 * kPart + e0];
       if (v1) w1 -= ((p0[e1] + p0[kPart + e1]) + p0[2 * kPart + e1]) + p0[3 * kPart + e1];
       __syncthreads();  // the partial sums are read before M overwrites them
@@ -408,8 +442,20 @@ __global__ __launch_bounds__(kWaves * 64, 4) void solve_nm_local_kernel(SolveArg
           d1 = fmaf(zt, sM[mat_idx(qt, e1)], d1);
         }
       }
-      if (v0) wrow[e0] = s0 ? 0.f : w0 - d0;
-      if (v1) wrow[e1] = s1 ? 0.f : w1 - d1;
+      const float f0 = s0 ? 0.f : w0 - d0, f1 = s1 ? 0.f : w1 - d1;
+      if (v0) wrow[e0] = f0;
+      if (v1) wrow[e1] = f1;
+      if (Wout) {  // the block's columns are final: the output dtype's copy too
+        if (out_bf16) {
+          unsigned short* o = (unsigned short*)Wout + k * b + j0;
+          if (v0) o[e0] = f32_to_bf16_rne(f0);
+          if (v1) o[e1] = f32_to_bf16_rne(f1);
+        } else {
+          float* o = (float*)Wout + k * b + j0;
+          if (v0) o[e0] = f0;
+          if (v1) o[e1] = f1;
+        }
+      }
       count = (unsigned long long)s;
     }
   }
@@ -485,20 +531,22 @@ bool solve_nm_local_applies(int64_t Bb, int n, int m) { return Bb / m * (m - n) 
 hipError_t launch_solve_nm_local(float* W, int64_t c, int64_t b, int64_t j0, int64_t B, int n,
                                  int m, const float* R, const float* gW, float* Z, int64_t ldz,
                                  int64_t r0, uint8_t* mask, DevState* st,
-                                 unsigned long long* blk_count, hipStream_t s) {
+                                 unsigned long long* blk_count, void* Wout, th_dtype wdt,
+                                 hipStream_t s) {
   SolveArgs a;
   a.W = W; a.c = c; a.b = b; a.j0 = j0;
   a.Bb = (int)((b - j0) < B ? (b - j0) : B);
   a.B = (int)B; a.n = n; a.m = m; a.R = R; a.Nblk = nullptr;
   a.g = gW; a.g_mode = gW ? 2 : 0;
   a.Z = Z; a.ldz = ldz; a.mask = mask; a.st = st; a.blk_count = blk_count;
-  if (!solve_nm_local_applies(a.Bb, n, m) || j0 < r0) return hipErrorInvalidValue;
+  if (!solve_nm_local_applies(a.Bb, n, m) || j0 < r0 || j0 - r0 > kLocalMaxK)
+    return hipErrorInvalidValue;
   if (c == 0) return hipSuccess;
   // one batch of kWaves rows per workgroup
   const int64_t g = cdiv(c, kWaves);
   if (g > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(solve_nm_local_kernel, dim3((unsigned)g), dim3(kWaves * 64), 0, s, a, W, r0,
-                     (int)(j0 - r0));
+                     (int)(j0 - r0), Wout, wdt == TH_BF16 ? 1 : 0);
   return hipGetLastError();
 }
 
