@@ -433,14 +433,19 @@ __global__ __launch_bounds__(kWaves * 64, 4) void solve_nm_local_kernel(SolveArg
         wave_sync();
         const float z = gauss_jordan64(reg, u, (float*)sP[wave], olane);
         if (act) zrow[qa] = z;
-        // the block's own compensation: d_e = sum over the selected t of z_t M[Q_t, e]
+        // the block's own compensation: d_e = sum over the selected t of z_t M[Q_t, e],
+        // unrolled over all 64 lanes (lanes past s hold z = 0 and Q = 0, so they add
+        // exact zeros) so that the reads of M are independent of each other
         const float za = act ? z : 0.f;
-        for (int t = 0; t < s; ++t) {
+        static_for<0, 64>([&](auto T) __attribute__((always_inline)) {
+          constexpr int t = T;
           const float zt = bcast(za, t);
           const int qt = __builtin_amdgcn_readlane(qa, t);
-          d0 = fmaf(zt, sM[mat_idx(qt, e0)], d0);
-          d1 = fmaf(zt, sM[mat_idx(qt, e1)], d1);
-        }
+          // mat_idx(qt, e1) = mat_idx(qt, e0) + 64 (the swizzle changes the low 5 bits only)
+          const int i0 = mat_idx(qt, e0);
+          d0 = fmaf(zt, sM[i0], d0);
+          d1 = fmaf(zt, sM[i0 + 64], d1);
+        });
       }
       const float f0 = s0 ? 0.f : w0 - d0, f1 = s1 ? 0.f : w1 - d1;
       if (v0) wrow[e0] = f0;
