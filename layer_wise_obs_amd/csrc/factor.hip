@@ -221,34 +221,55 @@ __device__ __forceinline__ f32x16_t lds_mfma_tile32(f32x16_t acc, FA&& a, FB&& b
 // update, so wave 0 updates that tile and factors it while the other waves
 // finish the step.
 // A block narrower than 128 (the last one) is padded with the identity.
-__global__ __launch_bounds__(256) void diag_factor_kernel(float* __restrict__ S, int64_t b,
-                                                          int64_t k0, int nbk, DevState* st) {
-  // This kernel and the panel and row/column updates form the serial chain that
-  // runs beside the rest set of the previous pair: their waves issue first.
-  __builtin_amdgcn_s_setprio(3);
-  __shared__ float sS[kNb * kSP];
-  __shared__ float sP[3 * kBase * kPP];
-  __shared__ float sT[kBase16 * kPP16];
-  __shared__ int bad;
-  const int tid = threadIdx.x, wave = tid >> 6;
-  if (tid == 0) bad = 0;
-  {  // all 64 loads of a thread in flight at once (addresses clamped into the block)
-    constexpr int kPer = kNb * kNb / 256;
-    float v[kPer];
+// LDS of a diagonal factorisation (the split-operand GEMM of the fused launches
+// below stages its operands in the same space before the block is formed there).
+struct DiagLds {
+  float sS[kNb * kSP];
+  float sP[3 * kBase * kPP];
+  float sT[kBase16 * kPP16];
+  int bad;
+};
+static_assert(sizeof(DiagLds) >= (size_t)kX3LdsBytes, "GEMM staging fits in the diagonal LDS");
+
+// The block of S at (k0, k0) into sS: lower triangle, identity padding past nbk.
+__device__ __forceinline__ void diag_load(const float* __restrict__ S, int64_t b, int64_t k0,
+                                          int nbk, float* sS) {
+  const int tid = threadIdx.x;
+  // all 64 loads of a thread in flight at once (addresses clamped into the block)
+  constexpr int kPer = kNb * kNb / 256;
+  float v[kPer];
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int idx = e * 256 + tid, i = idx >> 7, j = idx & (kNb - 1);
-      const int ii = i < nbk ? i : nbk - 1, jj = j < nbk ? j : nbk - 1;
-      v[e] = S[(k0 + ii) * b + k0 + jj];
-    }
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int idx = e * 256 + tid, i = idx >> 7, j = idx & (kNb - 1);
-      const float pad = (i == j) ? 1.f : 0.f;
-      sS[i * kSP + j] = (i < nbk && j < nbk && j <= i) ? v[e] : pad;
-    }
+  for (int e = 0; e < kPer; ++e) {
+    const int idx = e * 256 + tid, i = idx >> 7, j = idx & (kNb - 1);
+    const int ii = i < nbk ? i : nbk - 1, jj = j < nbk ? j : nbk - 1;
+    v[e] = S[(k0 + ii) * b + k0 + jj];
   }
-  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int idx = e * 256 + tid, i = idx >> 7, j = idx & (kNb - 1);
+    const float pad = (i == j) ? 1.f : 0.f;
+    sS[i * kSP + j] = (i < nbk && j < nbk && j <= i) ? v[e] : pad;
+  }
+}
+
+// The accumulators of a 128 x 128 GEMM tile (the updated diagonal block) into sS,
+// as diag_load would have read them from S.
+__device__ __forceinline__ void diag_from_acc(const f32x16_t (&acc)[2][2], int nbk, float* sS) {
+  gemm_foreach(acc, [&](int r, int c, float v) {
+    const float pad = (r == c) ? 1.f : 0.f;
+    sS[r * kSP + c] = (r < nbk && c < nbk && c <= r) ? v : pad;
+  });
+}
+
+// Factor the block in sS (all 256 threads; sS complete and visible): X = L^-1
+// written back over the block of S at (k0, k0), zeros above the diagonal.
+__device__ __forceinline__ void diag_factor_body(float* __restrict__ S, int64_t b, int64_t k0,
+                                                 int nbk, DevState* st, DiagLds& L) {
+  float* const sS = L.sS;
+  float* const sP = L.sP;
+  float* const sT = L.sT;
+  int& bad = L.bad;
+  const int tid = threadIdx.x, wave = tid >> 6;
   auto blk = [&](int i, int j) { return sS + (kBase * i) * kSP + kBase * j; };
   // trailing tile q of step t: (i, j), t < i < 4, 0 <= j <= i, row-major order
   auto trailing_tile = [&](int t, int q) {
@@ -319,6 +340,18 @@ __global__ __launch_bounds__(256) void diag_factor_kernel(float* __restrict__ S,
     if (i < nbk && j < nbk) S[(k0 + i) * b + k0 + j] = v;
   }
   if (tid == 0 && bad) st->not_spd = 1;
+}
+
+__global__ __launch_bounds__(256) void diag_factor_kernel(float* __restrict__ S, int64_t b,
+                                                          int64_t k0, int nbk, DevState* st) {
+  // This kernel and the panel and row/column updates form the serial chain that
+  // runs beside the rest set of the previous pair: their waves issue first.
+  __builtin_amdgcn_s_setprio(3);
+  __shared__ DiagLds L;
+  if (threadIdx.x == 0) L.bad = 0;
+  diag_load(S, b, k0, nbk, L.sS);
+  __syncthreads();
+  diag_factor_body(S, b, k0, nbk, st, L);
 }
 
 // Panel rows Lp_i live in a buffer of pitch kPP2 = 256: the panel of an even step
@@ -397,6 +430,39 @@ __global__ __launch_bounds__(256, 2) void trailing_next_kernel(float* __restrict
   trailing_tile(S, b, k, kNb, i, j, P, smem);
 }
 
+// (3a') Step k's update of block row and column k+1 and the factorisation of
+// block k+1 in one launch: workgroup 0 updates the diagonal tile (k+1, k+1) straight
+// into LDS and factors it while the others update the rest of block row and
+// column k+1 (read next by the panel of step k+1). Workgroup t >= 1 takes
+// trailing_next's tile t - 1 below the diagonal one and tile t past it.
+__global__ __launch_bounds__(256, 2) void next_diag_kernel(float* __restrict__ S, int64_t b, int k,
+                                                         int nblk, const float* __restrict__ P,
+                                                         DevState* st) {
+  __shared__ __attribute__((aligned(16))) DiagLds L;
+  unsigned char* const smem = (unsigned char*)&L;
+  if (blockIdx.x == 0) {
+    __builtin_amdgcn_s_setprio(3);
+    const int64_t i0 = (int64_t)(k + 1) * kNb;
+    const int nbk = (int)((b - i0) < kNb ? (b - i0) : kNb);
+    const float* Pk = P + (k & 1) * kNb;
+    f32x16_t acc[2][2];
+    gemm_load_c(acc, S + i0 * b + i0, b, nbk, nbk);
+    gemm_tile_x3<true>(Pk + i0 * kPP2, kPP2, nbk, Pk + i0 * kPP2, kPP2, nbk, kNb, acc, smem, true);
+    __syncthreads();  // the staging space is free again
+    if (threadIdx.x == 0) L.bad = 0;
+    diag_from_acc(acc, nbk, L.sS);
+    __syncthreads();
+    diag_factor_body(S, b, i0, nbk, st, L);
+    return;
+  }
+  __builtin_amdgcn_s_setprio(2);
+  const int t = (int)blockIdx.x - 1;
+  const int q = t < k + 1 ? t : t + 1;
+  if (q >= nblk) return;
+  const int i = q <= k + 1 ? k + 1 : q, j = q <= k + 1 ? q : k + 1;
+  trailing_tile(S, b, k, kNb, i, j, P, smem);
+}
+
 // (3b) The rest of steps k and k+1 together (k even, both blocks full): tile
 // (i, j), i > k+1, j <= i, with K = 256 from the two panels [Lp_i(k) | Lp_i(k+1)]:
 //   j <  k  : S[i,j] -= [Lp_i(k) Lp_i(k+1)] [S[k,j] ; S[k+1,j]]   (the final X rows)
@@ -462,6 +528,47 @@ __global__ __launch_bounds__(256, 2) void trailing_look_kernel(float* __restrict
   pair_tile(S, b, k, i, j, P, smem);
 }
 
+
+// The look-ahead set of pair (k, k+1) and the factorisation of block k+2 in one
+// launch: workgroup 0 applies both steps to the diagonal tile (k+2, k+2) straight
+// into LDS (K = 256) and factors it while the others run the rest of the
+// look-ahead set; workgroup t >= 1 takes the set's tile t - 1 below the diagonal
+// one and tile t past it.
+__global__ __launch_bounds__(256, 2) void look_diag_kernel(float* __restrict__ S, int64_t b, int k,
+                                                         int nblk, const float* __restrict__ P,
+                                                         DevState* st) {
+  __shared__ __attribute__((aligned(16))) DiagLds L;
+  unsigned char* const smem = (unsigned char*)&L;
+  const int kk = k + 2;
+  if (blockIdx.x == 0) {
+    __builtin_amdgcn_s_setprio(3);
+    const int64_t i0 = (int64_t)kk * kNb;
+    const int nbk = (int)((b - i0) < kNb ? (b - i0) : kNb);
+    f32x16_t acc[2][2];
+    gemm_load_c(acc, S + i0 * b + i0, b, nbk, nbk);
+    gemm_tile_x3<true>(P + i0 * kPP2, kPP2, nbk, P + i0 * kPP2, kPP2, nbk, 2 * kNb, acc, smem,
+                       true);
+    __syncthreads();  // the staging space is free again
+    if (threadIdx.x == 0) L.bad = 0;
+    diag_from_acc(acc, nbk, L.sS);
+    __syncthreads();
+    diag_factor_body(S, b, i0, nbk, st, L);
+    return;
+  }
+  __builtin_amdgcn_s_setprio(2);
+  int q = (int)blockIdx.x - 1, i, j;
+  if (q >= kk) ++q;  // (kk, kk) is workgroup 0's
+  if (q <= kk) {
+    i = kk; j = q;
+  } else if (kk + 1 < nblk && q <= 2 * kk + 2) {
+    i = kk + 1; j = q - (kk + 1);
+  } else {
+    q -= (kk + 1) + (kk + 1 < nblk ? kk + 2 : 0);
+    i = kk + 2 + (q >> 1); j = kk + (q & 1);
+    if (i >= nblk) return;
+  }
+  pair_tile(S, b, k, i, j, P, smem);
+}
 
 // U[a][c] = S[b-1-a][b-1-c] for c >= a (a flat reversal); 0 below the diagonal,
 // everywhere (zb = 0) or only inside the diagonal blocks of size zb. Block (a, y):
@@ -555,18 +662,21 @@ hipError_t launch_chol_inv_inplace(float* S, int64_t b, float* P, DevState* st, 
   unsigned short* Ybase = (unsigned short*)(P + 2 * pbuf);
   const int64_t ldy = x3_ldy(b);
   const int npr = (int)cdiv(nblk, 2);
-  auto factor_and_panel = [&](int k, float* Pp) -> hipError_t {
+  auto factor = [&](int k) -> hipError_t {
     const int64_t k0 = (int64_t)k * kNb;
     const int nbk = (int)((b - k0) < kNb ? (b - k0) : kNb);
     hipLaunchKernelGGL(diag_factor_kernel, dim3(1), dim3(256), 0, s, S, b, k0, nbk, st);
-    hipError_t e2 = hipGetLastError();
-    if (e2 != hipSuccess) return e2;
+    return hipGetLastError();
+  };
+  auto panel = [&](int k, float* Pp) -> hipError_t {
+    const int64_t k0 = (int64_t)k * kNb;
+    const int nbk = (int)((b - k0) < kNb ? (b - k0) : kNb);
     const int nrow = nblk - k - 1;
     if (nrow + k > 0) {
       hipLaunchKernelGGL(panel_kernel, dim3(nrow + k), dim3(256), 0, s, S, b, k, nbk, nrow, Pp);
-      e2 = hipGetLastError();
+      return hipGetLastError();
     }
-    return e2;
+    return hipSuccess;
   };
   // Steps in pairs (k, k+1): block row and column k+1 first, then one K = 256
   // update of everything else, split into the look-ahead set (stream s) and the
@@ -583,14 +693,17 @@ hipError_t launch_chol_inv_inplace(float* S, int64_t b, float* P, DevState* st, 
   // waited for the rest set of pair p, which waited for the split of pair p (the
   // last reader of P[p % 2] besides the look-ahead set of pair p on stream s).
   bool rest_pending = false;
+  bool factored = false;  // block k's factor came with the previous look-ahead set
   for (int k = 0, pair = 0; k < nblk; k += 2, ++pair) {
     float* Pp = P + (size_t)(pair & 1) * pbuf;
-    if ((e = factor_and_panel(k, Pp)) != hipSuccess) return e;
+    if (!factored && (e = factor(k)) != hipSuccess) return e;
+    if ((e = panel(k, Pp)) != hipSuccess) return e;
     if (k + 1 >= nblk) break;
-    hipLaunchKernelGGL(trailing_next_kernel, dim3((unsigned)nblk), dim3(256), 0, s, S, b, k, nblk,
-                       Pp);
+    // block row and column k+1, with block k+1 factored beside them
+    hipLaunchKernelGGL(next_diag_kernel, dim3((unsigned)nblk), dim3(256), 0, s, S, b, k, nblk, Pp,
+                       st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = factor_and_panel(k + 1, Pp)) != hipSuccess) return e;
+    if ((e = panel(k + 1, Pp)) != hipSuccess) return e;
     // rest set: 256 x 256 tiles over block-row pairs from (k+4)/2 (pair-row pi has
     // pi tiles: pair-columns 0..pi without (k+2)/2)
     int64_t nrest = 0;
@@ -633,10 +746,12 @@ hipError_t launch_chol_inv_inplace(float* S, int64_t b, float* P, DevState* st, 
       if ((e = hipEventRecord(side->rest, side->s2)) != hipSuccess) return e;
       rest_pending = true;
     }
+    // the look-ahead set, with block k+2 factored beside it
     const int64_t nlook = look_tiles(k, nblk);
+    factored = nlook > 0;
     if (nlook > 0) {
-      hipLaunchKernelGGL(trailing_look_kernel, dim3((unsigned)nlook), dim3(256), 0, s, S, b, k,
-                         nblk, Pp);
+      hipLaunchKernelGGL(look_diag_kernel, dim3((unsigned)nlook), dim3(256), 0, s, S, b, k, nblk,
+                         Pp, st);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
