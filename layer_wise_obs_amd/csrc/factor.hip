@@ -25,7 +25,11 @@
 //   columns k+2, k+3) run on the caller's stream, the rest on a second stream as
 //   a persistent kernel of one workgroup per compute unit, so that the next
 //   pair's diagonal blocks, panels and row/column update (a chain of small,
-//   latency-bound kernels) run beside the bulk of the update. The rest set reads
+//   latency-bound kernels) run beside the bulk of the update. Each diagonal
+//   factorisation after the first shares a launch with the update that precedes
+//   it on the chain (block row and column k+1, or the look-ahead set): its
+//   workgroup updates the diagonal tile straight into LDS and factors it while
+//   the launch's other workgroups update the remaining tiles. The rest set reads
 //   the pair's operands once more, pre-split into bf16 planes (rest_x3.h): its
 //   tiles are a symmetric rank-256 product like the Hessian's syrk and run on
 //   that kernel's pipeline, 256 x 256 per workgroup.
@@ -415,26 +419,12 @@ __device__ __forceinline__ void trailing_tile(float* __restrict__ S, int64_t b, 
   });
 }
 
-// (3a) First part of an even step k of a pair: only block row k+1 (tiles
-// (k+1, j), j <= k+1) and block column k+1 (tiles (i, k+1), i > k+1), which the
-// factorisation of block k+1 needs. Tile q < k+2 is (k+1, q), else (q, k+1).
-__global__ __launch_bounds__(256, 2) void trailing_next_kernel(float* __restrict__ S, int64_t b,
-                                                            int k, int nblk,
-                                                            const float* __restrict__ P) {
-  // on the serial chain (see diag_factor_kernel)
-  __builtin_amdgcn_s_setprio(2);
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kX3LdsBytes];
-  const int q = blockIdx.x;
-  if (q >= nblk) return;
-  const int i = q <= k + 1 ? k + 1 : q, j = q <= k + 1 ? q : k + 1;
-  trailing_tile(S, b, k, kNb, i, j, P, smem);
-}
-
 // (3a') Step k's update of block row and column k+1 and the factorisation of
 // block k+1 in one launch: workgroup 0 updates the diagonal tile (k+1, k+1) straight
 // into LDS and factors it while the others update the rest of block row and
 // column k+1 (read next by the panel of step k+1). Workgroup t >= 1 takes
-// trailing_next's tile t - 1 below the diagonal one and tile t past it.
+// tile q = t - 1 (below the diagonal one) or q = t (past it), where tile q < k+2
+// is (k+1, q) and otherwise (q, k+1).
 __global__ __launch_bounds__(256, 2) void next_diag_kernel(float* __restrict__ S, int64_t b, int k,
                                                          int nblk, const float* __restrict__ P,
                                                          DevState* st) {
@@ -507,27 +497,6 @@ __host__ __device__ inline int64_t look_tiles(int k, int nblk) {
   if (kk + 2 < nblk) n += 2 * (int64_t)(nblk - kk - 2); // columns kk, kk+1 below
   return n;
 }
-
-__global__ __launch_bounds__(256, 2) void trailing_look_kernel(float* __restrict__ S, int64_t b,
-                                                            int k, int nblk,
-                                                            const float* __restrict__ P) {
-  // on the serial chain (see diag_factor_kernel)
-  __builtin_amdgcn_s_setprio(2);
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kX3LdsBytes];
-  const int kk = k + 2;
-  int q = blockIdx.x, i, j;
-  if (q <= kk) {
-    i = kk; j = q;
-  } else if (kk + 1 < nblk && q <= 2 * kk + 2) {
-    i = kk + 1; j = q - (kk + 1);
-  } else {
-    q -= (kk + 1) + (kk + 1 < nblk ? kk + 2 : 0);
-    i = kk + 2 + (q >> 1); j = kk + (q & 1);
-    if (i >= nblk) return;
-  }
-  pair_tile(S, b, k, i, j, P, smem);
-}
-
 
 // The look-ahead set of pair (k, k+1) and the factorisation of block k+2 in one
 // launch: workgroup 0 applies both steps to the diagonal tile (k+2, k+2) straight
