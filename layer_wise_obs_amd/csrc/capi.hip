@@ -317,7 +317,7 @@ th_status prune_blocks(const PruneLayout& L, int64_t c, int64_t b, const th_prun
   bool next_digit_done = false;  // the previous update counted this block's first digit
   // N:M with at most 64 pruned per block row (every block takes route A): the
   // block-local compensation runs inside the solve (one launch per block)
-  const bool local = !unstr && solve_nm_local_applies(B, p->pattern.n, p->pattern.m);
+  const bool local = !unstr && solve_nm_local_applies(b, B, p->pattern.n, p->pattern.m);
   // there every block's solve writes its final columns, in the output dtype too
   if (cast_done) *cast_done = local && Wout;
   for (int64_t blk = 0; blk < nblk; ++blk) {

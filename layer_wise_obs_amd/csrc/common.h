@@ -193,12 +193,12 @@ hipError_t launch_solve_nm(const float* W, int64_t c, int64_t b, int64_t j0, int
                            int m, const float* R, const float* gW, const float* Nblk, float* Z,
                            int64_t ldz, uint8_t* mask, DevState* st, unsigned long long* blk_count,
                            hipStream_t s);
-// N:M with the group's block-local compensation folded in (route A only:
-// solve_nm_local_applies). Reads W[:, J] less Z[:, 0:j0-r0] R[r0:j0, J] (Z: the
+// N:M with the group's block-local compensation folded in (route A and even
+// widths only: solve_nm_local_applies). Reads W[:, J] less Z[:, 0:j0-r0] R[r0:j0, J] (Z: the
 // group's coefficients, whose first column belongs to block row r0), writes the
 // block's final W[:, J], its mask and its coefficients Z[:, j0-r0 : j0-r0+B];
 // with Wout, also the final W[:, J] in dtype wdt (c x b, row-major).
-bool solve_nm_local_applies(int64_t Bb, int n, int m);
+bool solve_nm_local_applies(int64_t b, int64_t B, int n, int m);
 hipError_t launch_solve_nm_local(float* W, int64_t c, int64_t b, int64_t j0, int64_t B, int n,
                                  int m, const float* R, const float* gW, float* Z, int64_t ldz,
                                  int64_t r0, uint8_t* mask, DevState* st,

@@ -255,7 +255,7 @@ __global__ __launch_bounds__(kWaves * 64, ROUTE == 2 ? 2 : 4) void solve_kernel(
 // N:M, route A (s <= 64), with the block-local compensation of the block's group
 // folded into the solve. Under N:M no budget couples the rows, so each row's
 // blocks can be taken left-looking: before scoring block J, a workgroup
-// subtracts from its kWaves rows' W[k, J] the compensation of the earlier blocks
+// subtracts from its rows' W[k, J] the compensation of the earlier blocks
 // of the same group -- their coefficients (Z, columns 0 .. Kp of the group's
 // rows) times their slices R[J_i, J] -- and after the solve it writes the block's
 // final weights: W[k, q] - (z M)[q] on the kept columns, exact zeros on the
@@ -264,24 +264,26 @@ __global__ __launch_bounds__(kWaves * 64, ROUTE == 2 ? 2 : 4) void solve_kernel(
 // by the far-column update, from the same Z. This replaces one update launch per
 // block; the arithmetic is the same products summed in another order.
 //
-// The group's product: thread (g = tid / 128, q = tid % 128) sums over its
-// quarter of the K = Kp inner index for all kWaves rows of the batch (R read once
-// per workgroup, the rows' Z entries wave-uniform); the four partial sums meet
-// in LDS (the space of M, which is loaded after them) and are added in a fixed
-// order, so the result does not depend on timing.
-__global__ __launch_bounds__(kWaves * 64, 4) void solve_nm_local_kernel(SolveArgs a, float* Ww,
-                                                                         int64_t r0, int Kp,
-                                                                         void* Wout, int out_bf16) {
+// A workgroup takes kLocalRows rows (one wave each). The group's product runs on
+// the fp32 matrix cores (v_mfma_f32_16x16x4f32: the 16 rows of the batch times
+// 16-column pieces of R[r0:j0, J]): the batch's coefficients are staged in LDS
+// first (the space of M, which is loaded after the product), R is read from global
+// memory in full 128-byte row pieces, three chunks ahead, and the four quarters of
+// the inner index meet in LDS, added in a fixed order.
+constexpr int kLocalRows = 16;
+
+__global__ __launch_bounds__(kLocalRows * 64, 4) void solve_nm_local_kernel(
+    SolveArgs a, float* Ww, int64_t r0, int Kp, void* Wout, int out_bf16) {
+  constexpr int kW = kLocalRows;
   __shared__ __attribute__((aligned(16))) float sM[kMaxBlock * kMaxBlock];
   __shared__ float sg[kMaxBlock];
-  __shared__ float sbuf[kWaves][kMaxBlock];
-  __shared__ float su[kWaves][kMaxBlock];
-  __shared__ int sQ[kWaves][kMaxBlock];
-  __shared__ __attribute__((aligned(16))) int sP[kWaves][64];
-  __shared__ unsigned long long scount[kWaves];
-  static_assert(kWaves == 8, "the staged coefficients are read as two float4 per inner index");
-  static_assert(4 * kWaves * kMaxBlock + kWaves * kLocalMaxK <= kMaxBlock * kMaxBlock,
-                "partial sums and staged coefficients fit in the space of M");
+  __shared__ float sbuf[kW][kMaxBlock];
+  __shared__ float su[kW][kMaxBlock];
+  __shared__ int sQ[kW][kMaxBlock];
+  __shared__ __attribute__((aligned(16))) int sP[kW][64];
+  __shared__ unsigned long long scount[kW];
+  static_assert(kW * kLocalMaxK <= kMaxBlock * kMaxBlock, "staged coefficients fit in M's space");
+  static_assert(4 * kW * kMaxBlock <= kMaxBlock * kMaxBlock, "partial sums fit in M's space");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Bb = a.Bb;
@@ -296,179 +298,191 @@ __global__ __launch_bounds__(kWaves * 64, 4) void solve_nm_local_kernel(SolveArg
   const unsigned long long lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
   unsigned long long count = 0;
 
-  {  // one batch of kWaves rows per workgroup: no loop for values to be hoisted across
-    const int64_t kb = (int64_t)blockIdx.x * kWaves;
-    const int64_t k = kb + wave;
-    const bool rowv = k < c;
-    const int e0 = lane, e1 = lane + 64;
-    const bool v0 = e0 < Bb, v1 = e1 < Bb;
-    float* wrow = Ww + (rowv ? k : 0) * b + j0;
-    float w0 = (rowv && v0) ? wrow[e0] : 0.f;
-    float w1 = (rowv && v1) ? wrow[e1] : 0.f;
-    if (Kp > 0) {
-      // the batch's coefficients of the earlier blocks, kk-major (8 rows per kk),
-      // staged in the space of M behind the partial sums
-      constexpr int kPart = kWaves * kMaxBlock;
-      float* const sZ = sM + 4 * kPart;
-      {  // all loads of a thread in flight at once (Kp <= kLocalMaxK < 2 * 512)
-        constexpr int kH = (kLocalMaxK + kWaves * 64 - 1) / (kWaves * 64);
-        float zv[kWaves][kH];
+  const int64_t kb = (int64_t)blockIdx.x * kW;
+  const int64_t k = kb + wave;
+  const bool rowv = k < c;
+  const int e0 = lane, e1 = lane + 64;
+  const bool v0 = e0 < Bb, v1 = e1 < Bb;
+  float* wrow = Ww + (rowv ? k : 0) * b + j0;
+  float w0 = (rowv && v0) ? wrow[e0] : 0.f;
+  float w1 = (rowv && v1) ? wrow[e1] : 0.f;
+  if (Kp > 0) {
+    float* const sZ = sM;  // sZ[kk * kW + r]
+    {  // all loads of a thread in flight at once (Kp <= kLocalMaxK)
+      constexpr int kH = (kLocalMaxK + kW * 64 - 1) / (kW * 64);
+      float zv[kW][kH];
 #pragma unroll
-        for (int r = 0; r < kWaves; ++r) {
-          const int64_t row = (kb + r) < c ? (kb + r) : (c - 1);
+      for (int r = 0; r < kW; ++r) {
+        const int64_t row = (kb + r) < c ? (kb + r) : (c - 1);
 #pragma unroll
-          for (int h = 0; h < kH; ++h) {
-            const int kk = tid + h * kWaves * 64;
-            zv[r][h] = kk < Kp ? Zg[row * ldz + kk] : 0.f;
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < kWaves; ++r) {
-#pragma unroll
-          for (int h = 0; h < kH; ++h) {
-            const int kk = tid + h * kWaves * 64;
-            if (kk < Kp) sZ[kk * kWaves + r] = zv[r][h];
-          }
+        for (int h = 0; h < kH; ++h) {
+          const int kk = tid + h * kW * 64;
+          zv[r][h] = kk < Kp ? Zg[row * ldz + kk] : 0.f;
         }
       }
-      __syncthreads();
-      const int q = tid & (kMaxBlock - 1);
-      const int g = __builtin_amdgcn_readfirstlane(tid >> 7);
-      const int kbeg = g * Kp / 4, kend = (g + 1) * Kp / 4;
-      const float* Rq = a.R + (r0 + kbeg) * b + j0 + (q < Bb ? q : Bb - 1);
-      float acc[kWaves];
 #pragma unroll
-      for (int r = 0; r < kWaves; ++r) acc[r] = 0.f;
-      // R in chunks of kU rows, the next chunk's loads issued before this chunk's
-      // products (one chunk in flight behind the arithmetic)
-      constexpr int kU = 16;
-      const int nfull = (kend - kbeg) / kU;
-      float rv[kU], rn[kU];
+      for (int r = 0; r < kW; ++r) {
 #pragma unroll
-      for (int u = 0; u < kU; ++u) rn[u] = nfull > 0 ? Rq[(int64_t)u * b] : 0.f;
-      for (int ch = 0; ch < nfull; ++ch) {
-#pragma unroll
-        for (int u = 0; u < kU; ++u) rv[u] = rn[u];
-        if (ch + 1 < nfull) {
-#pragma unroll
-          for (int u = 0; u < kU; ++u) rn[u] = Rq[(int64_t)((ch + 1) * kU + u) * b];
+        for (int h = 0; h < kH; ++h) {
+          const int kk = tid + h * kW * 64;
+          if (kk < Kp) sZ[kk * kW + r] = zv[r][h];
         }
-        const float4* zc = (const float4*)(sZ + (kbeg + ch * kU) * kWaves);
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const float4 za = zc[2 * u], zb = zc[2 * u + 1];
-          acc[0] = fmaf(za.x, rv[u], acc[0]);
-          acc[1] = fmaf(za.y, rv[u], acc[1]);
-          acc[2] = fmaf(za.z, rv[u], acc[2]);
-          acc[3] = fmaf(za.w, rv[u], acc[3]);
-          acc[4] = fmaf(zb.x, rv[u], acc[4]);
-          acc[5] = fmaf(zb.y, rv[u], acc[5]);
-          acc[6] = fmaf(zb.z, rv[u], acc[6]);
-          acc[7] = fmaf(zb.w, rv[u], acc[7]);
-        }
-      }
-      for (int kk = kbeg + nfull * kU; kk < kend; ++kk) {
-        const float r1 = Rq[(int64_t)(kk - kbeg) * b];
-#pragma unroll
-        for (int r = 0; r < kWaves; ++r) acc[r] = fmaf(sZ[kk * kWaves + r], r1, acc[r]);
-      }
-#pragma unroll
-      for (int r = 0; r < kWaves; ++r) sM[(g * kWaves + r) * kMaxBlock + q] = acc[r];
-      __syncthreads();
-      const float* p0 = sM + wave * kMaxBlock;
-      if (v0) w0 -= ((p0[e0] + p0[kPart + e0]) + p0[2 * kPart + e0]) + p0[3 * kPart + e0];
-      if (v1) w1 -= ((p0[e1] + p0[kPart + e1]) + p0[2 * kPart + e1]) + p0[3 * kPart + e1];
-      __syncthreads();  // the partial sums are read before M overwrites them
-    }
-    {  // M = [A_F]_{J,J}: all 32 loads of a thread in flight at once, addresses clamped
-      constexpr int kPer = kMaxBlock * kMaxBlock / (kWaves * 64);
-      const float* src = a.R + j0 * b + j0;
-      float v[kPer];
-#pragma unroll
-      for (int e = 0; e < kPer; ++e) {
-        const int idx = e * kWaves * 64 + tid, r = idx >> 7, q = idx & (kMaxBlock - 1);
-        const int rr = r < Bb ? r : Bb - 1, qq = q < Bb ? q : Bb - 1;
-        v[e] = src[rr * b + qq];
-      }
-#pragma unroll
-      for (int e = 0; e < kPer; ++e) {
-        const int idx = e * kWaves * 64 + tid, r = idx >> 7, q = idx & (kMaxBlock - 1);
-        if (r < Bb && q < Bb) sM[mat_idx(r, q)] = v[e];
       }
     }
     __syncthreads();
-    if (rowv) {
-      if (v0) sbuf[wave][e0] = score_of(w0, sg[e0]);
-      if (v1) sbuf[wave][e1] = score_of(w1, sg[e1]);
-      wave_sync();
-      const bool s0 = v0 && nm_pruned(sbuf[wave], e0, a.n, a.m);
-      const bool s1 = v1 && nm_pruned(sbuf[wave], e1, a.n, a.m);
-      const unsigned long long m0 = __ballot(s0), m1 = __ballot(s1);
-      const int s = __popcll(m0) + __popcll(m1);
-      uint8_t* mrow = a.mask + k * b + j0;
-      if (v0) mrow[e0] = s0 ? 1 : 0;
-      if (v1) mrow[e1] = s1 ? 1 : 0;
-      float* zrow = a.Z + k * ldz;
-      if (v0 && !s0) zrow[e0] = 0.f;
-      if (v1 && !s1) zrow[e1] = 0.f;
-      const int pos0 = __popcll(m0 & lt), pos1 = __popcll(m0) + __popcll(m1 & lt);
-      if (s0) { sQ[wave][pos0] = e0; su[wave][pos0] = w0; }
-      if (s1) { sQ[wave][pos1] = e1; su[wave][pos1] = w1; }
-      wave_sync();
-      float d0 = 0.f, d1 = 0.f;
-      if (s > 0) {
-        int olane;
-        __asm__ volatile("v_mov_b32 %0, %1" : "=v"(olane) : "v"(lane));
-        float reg[64];
-        const bool act = lane < s;
-        const int qa = act ? sQ[wave][lane] : 0;
-  #pragma unroll
-        for (int cc = 0; cc < 64; ++cc) {
-          const bool in = (cc < s) && act;
-          const int qc = (cc < s) ? sQ[wave][cc] : 0;
-          const float v = sM[mat_idx(qa, qc)];
-          reg[cc] = in ? v : ((cc == olane) ? 1.f : 0.f);
-        }
-        const float u = act ? su[wave][lane] : 0.f;
-        wave_sync();
-        const float z = gauss_jordan64(reg, u, (float*)sP[wave], olane);
-        if (act) zrow[qa] = z;
-        // the block's own compensation: d_e = sum over the selected t of z_t M[Q_t, e],
-        // unrolled over all 64 lanes (lanes past s hold z = 0 and Q = 0, so they add
-        // exact zeros) so that the reads of M are independent of each other
-        const float za = act ? z : 0.f;
-        static_for<0, 64>([&](auto T) __attribute__((always_inline)) {
-          constexpr int t = T;
-          const float zt = bcast(za, t);
-          const int qt = __builtin_amdgcn_readlane(qa, t);
-          // mat_idx(qt, e1) = mat_idx(qt, e0) + 64 (the swizzle changes the low 5 bits only)
-          const int i0 = mat_idx(qt, e0);
-          d0 = fmaf(zt, sM[i0], d0);
-          d1 = fmaf(zt, sM[i0 + 64], d1);
-        });
+    // Wave w takes columns 32 (w % 4) .. +31 and quarter w / 4 of the inner index.
+    // Per step of 4 inner indices a lane reads two adjacent columns of one row of R
+    // (8 bytes; a row of 16 lanes covers 128 contiguous bytes) and feeds two MFMAs:
+    //   A[i][kk] = Z[row i][kk]            (lane: i = lane % 16, kk = step + lane / 16)
+    //   B_e[kk][j] = R[r0 + kk][j0 + c0 + 2 j + e], e = 0, 1 (lane: kk as A, j = lane % 16)
+    const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform, in scalar registers
+    const int cq = wv & 3, ks = wv >> 2;
+    const int kbeg = ks * Kp / 4, kend = (ks + 1) * Kp / 4;
+    const int li = lane & 15, lk = lane >> 4;
+    const int c0 = cq * 32 + 2 * li;  // even; Bb is even on this path
+    const float* Rc = a.R + r0 * b + j0 + (c0 < Bb ? c0 : Bb - 2);
+    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    // R in chunks of kU steps, three chunks in flight. Loads and LDS reads past the
+    // range are clamped into it (no branch around a load) and their coefficient is
+    // multiplied by zero: R and Z are finite, so those products add exact zeros.
+    constexpr int kU = 8, kC = 4 * kU;
+    float2 ra[kU], rb[kU], rc[kU];
+    auto load_chunk = [&](int kk0, float2 (&dst)[kU]) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int kk = kk0 + 4 * u + lk;
+        dst[u] = *(const float2*)(Rc + (int64_t)(kk < kend ? kk : kend - 1) * b);
       }
-      const float f0 = s0 ? 0.f : w0 - d0, f1 = s1 ? 0.f : w1 - d1;
-      if (v0) wrow[e0] = f0;
-      if (v1) wrow[e1] = f1;
-      if (Wout) {  // the block's columns are final: the output dtype's copy too
-        if (out_bf16) {
-          unsigned short* o = (unsigned short*)Wout + k * b + j0;
-          if (v0) o[e0] = f32_to_bf16_rne(f0);
-          if (v1) o[e1] = f32_to_bf16_rne(f1);
-        } else {
-          float* o = (float*)Wout + k * b + j0;
-          if (v0) o[e0] = f0;
-          if (v1) o[e1] = f1;
-        }
+    };
+    auto mfma_chunk = [&](int kk0, const float2 (&src)[kU]) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int kk = kk0 + 4 * u + lk;
+        const float zi = sZ[(kk < kend ? kk : kend - 1) * kW + li] * (kk < kend ? 1.f : 0.f);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(zi, src[u].x, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(zi, src[u].y, acc1, 0, 0, 0);
       }
-      count = (unsigned long long)s;
+    };
+    if (kend > kbeg) {  // wave-uniform
+      load_chunk(kbeg, ra);
+      load_chunk(kbeg + kC, rb);
+      load_chunk(kbeg + 2 * kC, rc);
     }
+    for (int kk0 = kbeg; kk0 < kend; kk0 += 3 * kC) {
+      mfma_chunk(kk0, ra);
+      if (kk0 + 3 * kC < kend) load_chunk(kk0 + 3 * kC, ra);
+      if (kk0 + kC < kend) {
+        mfma_chunk(kk0 + kC, rb);
+        if (kk0 + 4 * kC < kend) load_chunk(kk0 + 4 * kC, rb);
+      }
+      if (kk0 + 2 * kC < kend) {
+        mfma_chunk(kk0 + 2 * kC, rc);
+        if (kk0 + 5 * kC < kend) load_chunk(kk0 + 5 * kC, rc);
+      }
+    }
+    __syncthreads();  // every wave is done with the staged coefficients
+    // D_e[i][j] in register r of lane l: i = 4 (l / 16) + r, j = l % 16 -> column c0 + e
+    float* const part = sM;  // part[quarter][row][column]
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float* pr = part + (ks * kW + 4 * lk + r) * kMaxBlock + c0;
+      *(float2*)pr = float2{acc0[r], acc1[r]};
+    }
+    __syncthreads();
+    const float* p0 = part + wave * kMaxBlock;
+    constexpr int kPart = kW * kMaxBlock;
+    if (v0) w0 -= ((p0[e0] + p0[kPart + e0]) + p0[2 * kPart + e0]) + p0[3 * kPart + e0];
+    if (v1) w1 -= ((p0[e1] + p0[kPart + e1]) + p0[2 * kPart + e1]) + p0[3 * kPart + e1];
+    __syncthreads();  // the partial sums are read before M overwrites them
+  }
+  {  // M = [A_F]_{J,J}: all 16 loads of a thread in flight at once, addresses clamped
+    constexpr int kPer = kMaxBlock * kMaxBlock / (kW * 64);
+    const float* src = a.R + j0 * b + j0;
+    float v[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int idx = e * kW * 64 + tid, r = idx >> 7, q = idx & (kMaxBlock - 1);
+      const int rr = r < Bb ? r : Bb - 1, qq = q < Bb ? q : Bb - 1;
+      v[e] = src[rr * b + qq];
+    }
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int idx = e * kW * 64 + tid, r = idx >> 7, q = idx & (kMaxBlock - 1);
+      if (r < Bb && q < Bb) sM[mat_idx(r, q)] = v[e];
+    }
+  }
+  __syncthreads();
+  if (rowv) {
+    if (v0) sbuf[wave][e0] = score_of(w0, sg[e0]);
+    if (v1) sbuf[wave][e1] = score_of(w1, sg[e1]);
+    wave_sync();
+    const bool s0 = v0 && nm_pruned(sbuf[wave], e0, a.n, a.m);
+    const bool s1 = v1 && nm_pruned(sbuf[wave], e1, a.n, a.m);
+    const unsigned long long m0 = __ballot(s0), m1 = __ballot(s1);
+    const int s = __popcll(m0) + __popcll(m1);
+    uint8_t* mrow = a.mask + k * b + j0;
+    if (v0) mrow[e0] = s0 ? 1 : 0;
+    if (v1) mrow[e1] = s1 ? 1 : 0;
+    float* zrow = a.Z + k * ldz;
+    if (v0 && !s0) zrow[e0] = 0.f;
+    if (v1 && !s1) zrow[e1] = 0.f;
+    const int pos0 = __popcll(m0 & lt), pos1 = __popcll(m0) + __popcll(m1 & lt);
+    if (s0) { sQ[wave][pos0] = e0; su[wave][pos0] = w0; }
+    if (s1) { sQ[wave][pos1] = e1; su[wave][pos1] = w1; }
+    wave_sync();
+    float d0 = 0.f, d1 = 0.f;
+    if (s > 0) {
+      int olane;
+      __asm__ volatile("v_mov_b32 %0, %1" : "=v"(olane) : "v"(lane));
+      float reg[64];
+      const bool act = lane < s;
+      const int qa = act ? sQ[wave][lane] : 0;
+#pragma unroll
+      for (int cc = 0; cc < 64; ++cc) {
+        const bool in = (cc < s) && act;
+        const int qc = (cc < s) ? sQ[wave][cc] : 0;
+        const float v = sM[mat_idx(qa, qc)];
+        reg[cc] = in ? v : ((cc == olane) ? 1.f : 0.f);
+      }
+      const float u = act ? su[wave][lane] : 0.f;
+      wave_sync();
+      const float z = gauss_jordan64(reg, u, (float*)sP[wave], olane);
+      if (act) zrow[qa] = z;
+      // the block's own compensation: d_e = sum over the selected t of z_t M[Q_t, e],
+      // unrolled over all 64 lanes (lanes past s hold z = 0 and Q = 0, so they add
+      // exact zeros) so that the reads of M are independent of each other
+      const float za = act ? z : 0.f;
+      static_for<0, 64>([&](auto T) __attribute__((always_inline)) {
+        constexpr int t = T;
+        const float zt = bcast(za, t);
+        const int qt = __builtin_amdgcn_readlane(qa, t);
+        // mat_idx(qt, e1) = mat_idx(qt, e0) + 64 (the swizzle changes the low 5 bits only)
+        const int i0 = mat_idx(qt, e0);
+        d0 = fmaf(zt, sM[i0], d0);
+        d1 = fmaf(zt, sM[i0 + 64], d1);
+      });
+    }
+    const float f0 = s0 ? 0.f : w0 - d0, f1 = s1 ? 0.f : w1 - d1;
+    if (v0) wrow[e0] = f0;
+    if (v1) wrow[e1] = f1;
+    if (Wout) {  // the block's columns are final: the output dtype's copy too
+      if (out_bf16) {
+        unsigned short* o = (unsigned short*)Wout + k * b + j0;
+        if (v0) o[e0] = f32_to_bf16_rne(f0);
+        if (v1) o[e1] = f32_to_bf16_rne(f1);
+      } else {
+        float* o = (float*)Wout + k * b + j0;
+        if (v0) o[e0] = f0;
+        if (v1) o[e1] = f1;
+      }
+    }
+    count = (unsigned long long)s;
   }
   if (lane == 0) scount[wave] = count;
   __syncthreads();
   if (tid == 0) {
     unsigned long long tot = 0;
-    for (int w = 0; w < kWaves; ++w) tot += scount[w];
+    for (int w = 0; w < kW; ++w) tot += scount[w];
     if (tot) {
       atomicAdd((unsigned long long*)&a.st->pruned, tot);
       atomicAdd(a.blk_count, tot);
@@ -531,7 +545,10 @@ hipError_t launch_solve_nm(const float* W, int64_t c, int64_t b, int64_t j0, int
   return hipGetLastError();
 }
 
-bool solve_nm_local_applies(int64_t Bb, int n, int m) { return Bb / m * (m - n) <= 64; }
+bool solve_nm_local_applies(int64_t b, int64_t B, int n, int m) {
+  // route A in every block; even widths for the 8-byte reads of R
+  return B / m * (m - n) <= 64 && b % 2 == 0 && B % 2 == 0;
+}
 
 hipError_t launch_solve_nm_local(float* W, int64_t c, int64_t b, int64_t j0, int64_t B, int n,
                                  int m, const float* R, const float* gW, float* Z, int64_t ldz,
@@ -544,14 +561,14 @@ hipError_t launch_solve_nm_local(float* W, int64_t c, int64_t b, int64_t j0, int
   a.B = (int)B; a.n = n; a.m = m; a.R = R; a.Nblk = nullptr;
   a.g = gW; a.g_mode = gW ? 2 : 0;
   a.Z = Z; a.ldz = ldz; a.mask = mask; a.st = st; a.blk_count = blk_count;
-  if (!solve_nm_local_applies(a.Bb, n, m) || j0 < r0 || j0 - r0 > kLocalMaxK)
+  if (!solve_nm_local_applies(b, B, n, m) || j0 < r0 || j0 - r0 > kLocalMaxK)
     return hipErrorInvalidValue;
   if (c == 0) return hipSuccess;
-  // one batch of kWaves rows per workgroup
-  const int64_t g = cdiv(c, kWaves);
+  // one batch of kLocalRows rows per workgroup
+  const int64_t g = cdiv(c, kLocalRows);
   if (g > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(solve_nm_local_kernel, dim3((unsigned)g), dim3(kWaves * 64), 0, s, a, W, r0,
-                     (int)(j0 - r0), Wout, wdt == TH_BF16 ? 1 : 0);
+  hipLaunchKernelGGL(solve_nm_local_kernel, dim3((unsigned)g), dim3(kLocalRows * 64), 0, s, a, W,
+                     r0, (int)(j0 - r0), Wout, wdt == TH_BF16 ? 1 : 0);
   return hipGetLastError();
 }
 
