@@ -193,7 +193,7 @@ hipError_t launch_solve_nm(const float* W, int64_t c, int64_t b, int64_t j0, int
                            int m, const float* R, const float* gW, const float* Nblk, float* Z,
                            int64_t ldz, uint8_t* mask, DevState* st, unsigned long long* blk_count,
                            hipStream_t s);
-// N:M with the group's block-local compensation folded in (route A and even
+// N:M with the group's block-local compensation folded in (route A and 4-aligned
 // widths only: solve_nm_local_applies). Reads W[:, J] less Z[:, 0:j0-r0] R[r0:j0, J] (Z: the
 // group's coefficients, whose first column belongs to block row r0), writes the
 // block's final W[:, J], its mask and its coefficients Z[:, j0-r0 : j0-r0+B];

@@ -268,8 +268,8 @@ __global__ __launch_bounds__(kWaves * 64, ROUTE == 2 ? 2 : 4) void solve_kernel(
 // the fp32 matrix cores (v_mfma_f32_16x16x4f32: the 16 rows of the batch times
 // 16-column pieces of R[r0:j0, J]): the batch's coefficients are staged in LDS
 // first (the space of M, which is loaded after the product), R is read from global
-// memory in full 128-byte row pieces, three chunks ahead, and the four quarters of
-// the inner index meet in LDS, added in a fixed order.
+// memory in 256-byte row pieces, three chunks ahead, and the eight parts of the
+// inner index meet in LDS, added in a fixed order.
 constexpr int kLocalRows = 16;
 
 __global__ __launch_bounds__(kLocalRows * 64, 4) void solve_nm_local_kernel(
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kLocalRows * 64, 4) void solve_nm_local_kernel(
   __shared__ __attribute__((aligned(16))) int sP[kW][64];
   __shared__ unsigned long long scount[kW];
   static_assert(kW * kLocalMaxK <= kMaxBlock * kMaxBlock, "staged coefficients fit in M's space");
-  static_assert(4 * kW * kMaxBlock <= kMaxBlock * kMaxBlock, "partial sums fit in M's space");
+  static_assert(kW / 2 * kW * kMaxBlock <= kMaxBlock * kMaxBlock, "partial sums fit in M's space");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Bb = a.Bb;
@@ -330,37 +330,42 @@ __global__ __launch_bounds__(kLocalRows * 64, 4) void solve_nm_local_kernel(
       }
     }
     __syncthreads();
-    // Wave w takes columns 32 (w % 4) .. +31 and quarter w / 4 of the inner index.
-    // Per step of 4 inner indices a lane reads two adjacent columns of one row of R
-    // (8 bytes; a row of 16 lanes covers 128 contiguous bytes) and feeds two MFMAs:
+    // Wave w takes columns 64 (w % 2) .. +63 and eighth w / 2 of the inner index.
+    // Per step of 4 inner indices a lane reads four adjacent columns of one row of R
+    // (16 bytes; a row of 16 lanes covers 256 contiguous bytes) and feeds four MFMAs:
     //   A[i][kk] = Z[row i][kk]            (lane: i = lane % 16, kk = step + lane / 16)
-    //   B_e[kk][j] = R[r0 + kk][j0 + c0 + 2 j + e], e = 0, 1 (lane: kk as A, j = lane % 16)
+    //   B_e[kk][j] = R[r0 + kk][j0 + c0 + 4 j + e], e = 0..3 (lane: kk as A, j = lane % 16)
     const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform, in scalar registers
-    const int cq = wv & 3, ks = wv >> 2;
-    const int kbeg = ks * Kp / 4, kend = (ks + 1) * Kp / 4;
+    const int ch = wv & 1, ks = wv >> 1;
+    constexpr int kSplit = kW / 2;
+    const int kbeg = ks * Kp / kSplit, kend = (ks + 1) * Kp / kSplit;
     const int li = lane & 15, lk = lane >> 4;
-    const int c0 = cq * 32 + 2 * li;  // even; Bb is even on this path
-    const float* Rc = a.R + r0 * b + j0 + (c0 < Bb ? c0 : Bb - 2);
-    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    const int c0 = ch * 64 + 4 * li;  // a multiple of 4; Bb is too on this path
+    const float* Rc = a.R + r0 * b + j0 + (c0 < Bb ? c0 : Bb - 4);
+    f32x4_t acc[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // R in chunks of kU steps, three chunks in flight. Loads and LDS reads past the
     // range are clamped into it (no branch around a load) and their coefficient is
     // multiplied by zero: R and Z are finite, so those products add exact zeros.
-    constexpr int kU = 8, kC = 4 * kU;
-    float2 ra[kU], rb[kU], rc[kU];
-    auto load_chunk = [&](int kk0, float2 (&dst)[kU]) {
+    constexpr int kU = 4, kC = 4 * kU;
+    float4 ra[kU], rb[kU], rc[kU];
+    auto load_chunk = [&](int kk0, float4 (&dst)[kU]) {
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int kk = kk0 + 4 * u + lk;
-        dst[u] = *(const float2*)(Rc + (int64_t)(kk < kend ? kk : kend - 1) * b);
+        dst[u] = *(const float4*)(Rc + (int64_t)(kk < kend ? kk : kend - 1) * b);
       }
     };
-    auto mfma_chunk = [&](int kk0, const float2 (&src)[kU]) {
+    auto mfma_chunk = [&](int kk0, const float4 (&src)[kU]) {
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int kk = kk0 + 4 * u + lk;
         const float zi = sZ[(kk < kend ? kk : kend - 1) * kW + li] * (kk < kend ? 1.f : 0.f);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(zi, src[u].x, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(zi, src[u].y, acc1, 0, 0, 0);
+        acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(zi, src[u].x, acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(zi, src[u].y, acc[1], 0, 0, 0);
+        acc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(zi, src[u].z, acc[2], 0, 0, 0);
+        acc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(zi, src[u].w, acc[3], 0, 0, 0);
       }
     };
     if (kend > kbeg) {  // wave-uniform
@@ -382,17 +387,23 @@ __global__ __launch_bounds__(kLocalRows * 64, 4) void solve_nm_local_kernel(
     }
     __syncthreads();  // every wave is done with the staged coefficients
     // D_e[i][j] in register r of lane l: i = 4 (l / 16) + r, j = l % 16 -> column c0 + e
-    float* const part = sM;  // part[quarter][row][column]
+    float* const part = sM;  // part[eighth][row][column]
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float* pr = part + (ks * kW + 4 * lk + r) * kMaxBlock + c0;
-      *(float2*)pr = float2{acc0[r], acc1[r]};
+      *(float4*)pr = float4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
     }
     __syncthreads();
     const float* p0 = part + wave * kMaxBlock;
     constexpr int kPart = kW * kMaxBlock;
-    if (v0) w0 -= ((p0[e0] + p0[kPart + e0]) + p0[2 * kPart + e0]) + p0[3 * kPart + e0];
-    if (v1) w1 -= ((p0[e1] + p0[kPart + e1]) + p0[2 * kPart + e1]) + p0[3 * kPart + e1];
+    float s0 = 0.f, s1 = 0.f;  // the eighths in a fixed order
+#pragma unroll
+    for (int e = 0; e < kSplit; ++e) {
+      s0 += p0[e * kPart + e0];
+      s1 += p0[e * kPart + e1];
+    }
+    if (v0) w0 -= s0;
+    if (v1) w1 -= s1;
     __syncthreads();  // the partial sums are read before M overwrites them
   }
   {  // M = [A_F]_{J,J}: all 16 loads of a thread in flight at once, addresses clamped
@@ -546,8 +557,8 @@ hipError_t launch_solve_nm(const float* W, int64_t c, int64_t b, int64_t j0, int
 }
 
 bool solve_nm_local_applies(int64_t b, int64_t B, int n, int m) {
-  // route A in every block; even widths for the 8-byte reads of R
-  return B / m * (m - n) <= 64 && b % 2 == 0 && B % 2 == 0;
+  // route A in every block; widths that are multiples of 4 for the 16-byte reads of R
+  return B / m * (m - n) <= 64 && b % 4 == 0 && B % 4 == 0;
 }
 
 hipError_t launch_solve_nm_local(float* W, int64_t c, int64_t b, int64_t j0, int64_t B, int n,
