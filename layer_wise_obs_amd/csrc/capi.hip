@@ -371,7 +371,7 @@ th_status prune_blocks(const PruneLayout& L, int64_t c, int64_t b, const th_prun
         // compensation from its rows first and writes the block's final weights
         TH_HIP(launch_solve_nm_local(Wf, c, b, j0, B, p->pattern.n, p->pattern.m, L.R,
                                      obs ? nullptr : L.gW, Zb, ldz, sb0, mask, L.st,
-                                     L.counts + blk, Wout, wdt, s),
+                                     L.counts + blk, Wout, wdt, s1, s),
                "solve");
       } else {
         TH_HIP(launch_solve_nm(Wf, c, b, j0, B, p->pattern.n, p->pattern.m, L.R,

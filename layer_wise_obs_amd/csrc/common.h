@@ -197,13 +197,15 @@ hipError_t launch_solve_nm(const float* W, int64_t c, int64_t b, int64_t j0, int
 // widths only: solve_nm_local_applies). Reads W[:, J] less Z[:, 0:j0-r0] R[r0:j0, J] (Z: the
 // group's coefficients, whose first column belongs to block row r0), writes the
 // block's final W[:, J], its mask and its coefficients Z[:, j0-r0 : j0-r0+B];
-// with Wout, also the final W[:, J] in dtype wdt (c x b, row-major).
+// with Wout, also the final W[:, J] in dtype wdt (c x b, row-major). group_end:
+// the end column of the block's group (the next block's reads of R are prefetched
+// when it lies inside).
 bool solve_nm_local_applies(int64_t b, int64_t B, int n, int m);
 hipError_t launch_solve_nm_local(float* W, int64_t c, int64_t b, int64_t j0, int64_t B, int n,
                                  int m, const float* R, const float* gW, float* Z, int64_t ldz,
                                  int64_t r0, uint8_t* mask, DevState* st,
                                  unsigned long long* blk_count, void* Wout, th_dtype wdt,
-                                 hipStream_t s);
+                                 int64_t group_end, hipStream_t s);
 hipError_t launch_solve_unstructured(const float* W, int64_t c, int64_t b, int64_t j0, int64_t B,
                                      const float* R, const float* Nblk, const float* g,
                                      float* Z, uint8_t* mask, DevState* st,

@@ -273,7 +273,8 @@ __global__ __launch_bounds__(kWaves * 64, ROUTE == 2 ? 2 : 4) void solve_kernel(
 constexpr int kLocalRows = 16;
 
 __global__ __launch_bounds__(kLocalRows * 64, 4) void solve_nm_local_kernel(
-    SolveArgs a, float* Ww, int64_t r0, int Kp, void* Wout, int out_bf16) {
+    SolveArgs a, float* Ww, int64_t r0, int Kp, void* Wout, int out_bf16, int64_t pf_r0,
+    int pf_rows, int64_t pf_col0, int pf_cols) {
   constexpr int kW = kLocalRows;
   __shared__ __attribute__((aligned(16))) float sM[kMaxBlock * kMaxBlock];
   __shared__ float sg[kMaxBlock];
@@ -297,6 +298,19 @@ __global__ __launch_bounds__(kLocalRows * 64, 4) void solve_nm_local_kernel(
   }
   const unsigned long long lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
   unsigned long long count = 0;
+
+  // What the next block of the group reads of R (rows pf_r0 .. +pf_rows, columns
+  // pf_col0 .. +pf_cols: its M and the slab of its group product) is pulled into
+  // L2 now: workgroup w runs on XCD w % 8, and the 32 workgroups of an XCD read
+  // 32 rows apart, 16 bytes per thread. The values are consumed (an empty asm)
+  // only at the end, so nothing waits for them before then.
+  f32x4_t pf = {0.f, 0.f, 0.f, 0.f};
+  {
+    const int nx = (int)((gridDim.x + 7) / 8), widx = (int)(blockIdx.x / 8);
+    const int seg = tid & 31, row = widx + nx * (tid >> 5);
+    if (row < pf_rows && 4 * seg < pf_cols)
+      pf = *(const f32x4_t*)(a.R + (pf_r0 + row) * a.b + pf_col0 + 4 * seg);
+  }
 
   const int64_t kb = (int64_t)blockIdx.x * kW;
   const int64_t k = kb + wave;
@@ -490,6 +504,7 @@ __global__ __launch_bounds__(kLocalRows * 64, 4) void solve_nm_local_kernel(
     count = (unsigned long long)s;
   }
   if (lane == 0) scount[wave] = count;
+  __asm__ volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(pf[2]), "v"(pf[3]));
   __syncthreads();
   if (tid == 0) {
     unsigned long long tot = 0;
@@ -565,7 +580,7 @@ hipError_t launch_solve_nm_local(float* W, int64_t c, int64_t b, int64_t j0, int
                                  int m, const float* R, const float* gW, float* Z, int64_t ldz,
                                  int64_t r0, uint8_t* mask, DevState* st,
                                  unsigned long long* blk_count, void* Wout, th_dtype wdt,
-                                 hipStream_t s) {
+                                 int64_t group_end, hipStream_t s) {
   SolveArgs a;
   a.W = W; a.c = c; a.b = b; a.j0 = j0;
   a.Bb = (int)((b - j0) < B ? (b - j0) : B);
@@ -578,8 +593,12 @@ hipError_t launch_solve_nm_local(float* W, int64_t c, int64_t b, int64_t j0, int
   // one batch of kLocalRows rows per workgroup
   const int64_t g = cdiv(c, kLocalRows);
   if (g > 0x7fffffff) return hipErrorInvalidValue;
+  // the next block, if it belongs to the same group (rows r0 .. its end, its columns)
+  const int64_t jn = j0 + a.Bb;
+  const int64_t bn = jn < group_end ? ((b - jn) < B ? (b - jn) : B) : 0;
+  const int pf_rows = bn > 0 ? (int)(jn + bn - r0) : 0;
   hipLaunchKernelGGL(solve_nm_local_kernel, dim3((unsigned)g), dim3(kLocalRows * 64), 0, s, a, W,
-                     r0, (int)(j0 - r0), Wout, wdt == TH_BF16 ? 1 : 0);
+                     r0, (int)(j0 - r0), Wout, wdt == TH_BF16 ? 1 : 0, r0, pf_rows, jn, (int)bn);
   return hipGetLastError();
 }
 
