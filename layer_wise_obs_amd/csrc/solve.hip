@@ -301,9 +301,11 @@ __global__ __launch_bounds__(kLocalRows * 64, 4) void solve_nm_local_kernel(
 
   // What the next block of the group reads of R (rows pf_r0 .. +pf_rows, columns
   // pf_col0 .. +pf_cols: its M and the slab of its group product) is pulled into
-  // L2 now: workgroup w runs on XCD w % 8, and the 32 workgroups of an XCD read
-  // 32 rows apart, 16 bytes per thread. The values are consumed (an empty asm)
-  // only at the end, so nothing waits for them before then.
+  // L2 now: workgroup w runs on XCD w % 8, and each of the nx workgroups of an
+  // XCD reads every nx-th row (32 rows per workgroup, 16 bytes per thread). The
+  // values are consumed by an empty asm at the end; since the load counter
+  // completes in order, the first wait for this block's own loads also covers
+  // these, whose latency thus overlaps that of the block's first loads.
   f32x4_t pf = {0.f, 0.f, 0.f, 0.f};
   {
     const int nx = (int)((gridDim.x + 7) / 8), widx = (int)(blockIdx.x / 8);
