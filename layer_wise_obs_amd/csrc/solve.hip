@@ -96,18 +96,18 @@ struct SolveArgs {
 };
 
 // ROUTE: 0 route A, 1 route B, 2 the route of each row (M and N both in LDS).
-template <int MODE, int ROUTE>
-__global__ __launch_bounds__(kWaves * 64, ROUTE == 2 ? 2 : 4) void solve_kernel(SolveArgs a) {
+template <int MODE, int ROUTE, int NW = kWaves>
+__global__ __launch_bounds__(NW * 64, NW == 16 ? 4 : (ROUTE == 2 ? 2 : 4)) void solve_kernel(SolveArgs a) {
   __shared__ float sM[kMaxBlock * kMaxBlock];
   __shared__ float sN2[ROUTE == 2 ? kMaxBlock * kMaxBlock : 1];
   __shared__ float sg[kMaxBlock];
-  __shared__ float sbuf[kWaves][kMaxBlock];
-  __shared__ float su[kWaves][kMaxBlock];
-  __shared__ int sQ[kWaves][kMaxBlock];
+  __shared__ float sbuf[NW][kMaxBlock];
+  __shared__ float su[NW][kMaxBlock];
+  __shared__ int sQ[NW][kMaxBlock];
   // sP (route B's complement list) is read only by the gather before the
   // elimination, which then reuses the same words as its LDS pivot row.
-  __shared__ __attribute__((aligned(16))) int sP[kWaves][64];
-  __shared__ unsigned long long scount[kWaves];
+  __shared__ __attribute__((aligned(16))) int sP[NW][64];
+  __shared__ unsigned long long scount[NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Bb = a.Bb;
@@ -116,17 +116,17 @@ __global__ __launch_bounds__(kWaves * 64, ROUTE == 2 ? 2 : 4) void solve_kernel(
   float* const sN = (ROUTE == 2) ? sN2 : sM;
   // M (or N): all 32 loads of a thread in flight at once, addresses clamped
   auto load_mat = [&](const float* src, int64_t ld, float* dst) {
-    constexpr int kPer = kMaxBlock * kMaxBlock / (kWaves * 64);
+    constexpr int kPer = kMaxBlock * kMaxBlock / (NW * 64);
     float v[kPer];
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
-      const int idx = e * kWaves * 64 + tid, r = idx >> 7, q = idx & (kMaxBlock - 1);
+      const int idx = e * NW * 64 + tid, r = idx >> 7, q = idx & (kMaxBlock - 1);
       const int rr = r < Bb ? r : Bb - 1, qq = q < Bb ? q : Bb - 1;
       v[e] = src[rr * ld + qq];
     }
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
-      const int idx = e * kWaves * 64 + tid, r = idx >> 7, q = idx & (kMaxBlock - 1);
+      const int idx = e * NW * 64 + tid, r = idx >> 7, q = idx & (kMaxBlock - 1);
       if (r < Bb && q < Bb) dst[mat_idx(r, q)] = v[e];
     }
   };
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kWaves * 64, ROUTE == 2 ? 2 : 4) void solve_kernel(
   const unsigned long long lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
   unsigned long long count = 0;
 
-  for (int64_t k = (int64_t)blockIdx.x * kWaves + wave; k < a.c; k += (int64_t)gridDim.x * kWaves) {
+  for (int64_t k = (int64_t)blockIdx.x * NW + wave; k < a.c; k += (int64_t)gridDim.x * NW) {
     const int e0 = lane, e1 = lane + 64;
     const bool v0 = e0 < Bb, v1 = e1 < Bb;
     const float* wrow = a.W + k * b + j0;
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kWaves * 64, ROUTE == 2 ? 2 : 4) void solve_kernel(
   __syncthreads();
   if (tid == 0) {
     unsigned long long tot = 0;
-    for (int w = 0; w < kWaves; ++w) tot += scount[w];
+    for (int w = 0; w < NW; ++w) tot += scount[w];
     if (tot) {
       atomicAdd((unsigned long long*)&a.st->pruned, tot);
       atomicAdd(a.blk_count, tot);
@@ -617,10 +617,11 @@ hipError_t launch_solve_unstructured(const float* W, int64_t c, int64_t b, int64
   if (a.Bb <= 64)
     hipLaunchKernelGGL((solve_kernel<1, 0>), dim3(solve_grid(c)), dim3(kWaves * 64), 0, s, a);
   else
-    // one workgroup per compute unit fits (M and N take 128 KB of LDS): a grid of
-    // 256 runs in one round, each wave taking its rows in turn
-    hipLaunchKernelGGL((solve_kernel<1, 2>), dim3(solve_grid(c) < 256 ? solve_grid(c) : 256),
-                       dim3(kWaves * 64), 0, s, a);
+    // one workgroup per compute unit fits (M and N take 128 KB of LDS), of 16 waves
+    // (four per SIMD: the eliminations of four rows share each SIMD): a grid of 256
+    // runs in one round, each wave taking its rows in turn
+    hipLaunchKernelGGL((solve_kernel<1, 2, 16>), dim3((unsigned)(cdiv(c, 16) < 256 ? cdiv(c, 16) : 256)),
+                       dim3(16 * 64), 0, s, a);
   return hipGetLastError();
 }
 
